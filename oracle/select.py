@@ -1,0 +1,136 @@
+"""Candidate page selection, in fp64 (oracle; test infrastructure).
+
+EntmaxKV page, §2.B "Politiques de Sélection des Candidats", two policies:
+
+1. Top-k pages: a fixed budget, the k pages with the highest bounding-box
+   upper bounds.  Readings: per (row, KV head) the group's bound
+   U_p = max over the group's query heads of u_{h,p}; ranked on the fp32 U;
+   equal U go to the lowest logical page index; k >= n selects every page;
+   the result is returned in ascending page order.
+
+2. Gaussian-aware entmax selection: estimate the global entmax threshold from
+   the per-page Gaussian statistics by solving an approximate normalisation for
+   tau-hat, then keep the pages whose estimated maximum score clears tau-hat
+   lowered by a safety margin Delta.  Readings:
+     * approximate normalisation, per query head h (z-space):
+         F_h(tau) = sum_p n_p * E[(X_p - tau)_+^gamma] = 1,
+         X_p ~ N((alpha-1) m_{h,p}, (alpha-1)^2 v_{h,p}),
+       i.e. each page's token sum is replaced by its valid-token count times the
+       Gaussian expectation of one token's entmax weight;
+     * the page's "estimated maximum score" is its box bound, so page p is kept
+       when (alpha-1) u_{h,p} >= tau-hat_h - Delta for some head h of the group
+       (Delta in z-space units);
+     * if no page clears the bar, the page with the largest U is kept (ties to
+       the lowest index), so the entmax input is never empty.
+
+Gaussian partial moments, I_g(h) = E[(Z + h)_+^g] for Z ~ N(0, 1):
+   I_0 = Phi(h),  I_1 = h Phi(h) + phi(h),  I_g = h I_{g-1} + (g-1) I_{g-2}
+(the last by Stein's identity E[Z f(Z)] = E[f'(Z)]), and for X ~ N(mu, s^2),
+   E[(X - c)_+^g] = s^g I_g((mu - c)/s).
+F_h is continuous and decreasing; at tau = max_p (alpha-1) m_{h,p} - 1 the page
+with the largest mean alone contributes at least 1 (Jensen), so F_h >= 1 there.
+
+Pins (tests/test_oracle_select.py): top-k against a brute-force full sort and
+hand-built tie cases; I_g against numerical quadrature (scipy.integrate.quad);
+tau-hat for zero-variance pages equals the exact entmax threshold of the
+expanded token multiset (checked against the sort-based sparsemax closed form);
+F(tau-hat) = 1.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import ndtr
+
+
+def topk_pages(U, k: int):
+    """Ascending page indices of the min(k, n) largest fp32 bounds (ties: lowest index)."""
+    U = np.asarray(U, dtype=np.float32)
+    n = U.size
+    if k < 1:
+        raise ValueError("top-k needs k >= 1")
+    order = sorted(range(n), key=lambda p: (-float(U[p]), p))
+    return sorted(order[: min(k, n)])
+
+
+def partial_moment(h, g: int):
+    """I_g(h) = E[(Z + h)_+^g], Z standard normal, integer g >= 0 (vectorised in h)."""
+    h = np.asarray(h, dtype=np.float64)
+    Phi = ndtr(h)
+    phi = np.exp(-0.5 * h * h) / math.sqrt(2.0 * math.pi)
+    if g == 0:
+        return Phi
+    i_prev, i_cur = Phi, h * Phi + phi
+    for k in range(2, g + 1):
+        i_prev, i_cur = i_cur, h * i_cur + (k - 1) * i_prev
+    return i_cur
+
+
+def integer_gamma(alpha: float) -> int:
+    g = 1.0 / (float(alpha) - 1.0)
+    gi = int(round(g))
+    if gi < 1 or abs(g - gi) > 1e-6 * gi:
+        raise ValueError("Gaussian selection needs 1/(alpha-1) to be an integer")
+    return gi
+
+
+def gauss_F(tau, mu_z, sig_z, counts, g: int) -> float:
+    """F(tau) = sum_p n_p E[(X_p - tau)_+^g] with X_p ~ N(mu_z[p], sig_z[p]^2)."""
+    mu_z = np.asarray(mu_z, dtype=np.float64)
+    sig_z = np.asarray(sig_z, dtype=np.float64)
+    counts = np.asarray(counts, dtype=np.float64)
+    pos = sig_z > 0.0
+    terms = np.empty_like(mu_z)
+    sp = sig_z[pos]
+    terms[pos] = sp ** g * partial_moment((mu_z[pos] - tau) / sp, g)
+    terms[~pos] = np.maximum(mu_z[~pos] - tau, 0.0) ** g
+    return math.fsum(counts * terms)
+
+
+def gauss_tau_hat(mu_z, sig_z, counts, g: int, max_iter: int = 400) -> float:
+    """Root of F(tau) = 1 by bracketing then bisection to fp64 convergence."""
+    mu_z = np.asarray(mu_z, dtype=np.float64)
+    lo = float(mu_z.max()) - 1.0
+    if gauss_F(lo, mu_z, sig_z, counts, g) < 1.0:
+        raise AssertionError("bracket violated: F(max mu - 1) < 1")
+    step = 1.0
+    hi = lo + step
+    while gauss_F(hi, mu_z, sig_z, counts, g) >= 1.0:
+        step *= 2.0
+        hi = lo + step
+    for _ in range(max_iter):
+        mid = 0.5 * (lo + hi)
+        if not (lo < mid < hi):
+            break
+        if gauss_F(mid, mu_z, sig_z, counts, g) >= 1.0:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def gauss_select(u_heads, m_heads, v_heads, counts, alpha: float, delta: float):
+    """Gaussian-aware selection for one (row, KV head).
+
+    u_heads: fp32 [G][n] box bounds; m_heads, v_heads: fp64 [G][n] score
+    moments; counts: valid tokens per page [n].
+    Returns (ascending page list, tau_hat [G]).
+    """
+    g = integer_gamma(alpha)
+    a1 = float(alpha) - 1.0
+    u_heads = np.asarray(u_heads, dtype=np.float32)
+    G, n = u_heads.shape
+    keep = np.zeros(n, dtype=bool)
+    taus = np.empty(G)
+    for h in range(G):
+        mu_z = a1 * np.asarray(m_heads[h], dtype=np.float64)
+        sig_z = a1 * np.sqrt(np.asarray(v_heads[h], dtype=np.float64))
+        t = gauss_tau_hat(mu_z, sig_z, counts, g)
+        taus[h] = t
+        keep |= a1 * u_heads[h].astype(np.float64) >= t - float(delta)
+    if not keep.any():
+        U = u_heads.max(axis=0)
+        best = max(range(n), key=lambda p: (float(U[p]), -p))
+        return [best], taus
+    return [int(p) for p in np.nonzero(keep)[0]], taus

@@ -1,0 +1,133 @@
+"""Pins of the oracle's page selection policies.
+
+EntmaxKV summary page, §2.B "Politiques de Sélection des Candidats": top-k on
+the box bounds, and the Gaussian-aware estimate tau-hat of the entmax
+threshold with margin Delta.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy import integrate
+
+from oracle import select
+
+from test_oracle_entmax import entmax15_sort, sparsemax_sort
+
+
+def _rank_rule(U, k):
+    # page p is selected iff fewer than k pages precede it in the order
+    # (larger U first, then smaller index)
+    n = len(U)
+    out = []
+    for p in range(n):
+        before = sum(1 for r in range(n) if U[r] > U[p] or (U[r] == U[p] and r < p))
+        if before < k:
+            out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_topk_rank_rule(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 300))
+    # coarse values force many exact ties
+    U = np.round(rng.normal(0, 3, n) * 2) / 2
+    U = U.astype(np.float32)
+    for k in (1, 2, 5, n // 2 + 1, n, n + 7):
+        assert select.topk_pages(U, k) == _rank_rule(U, k)
+
+
+def test_topk_ties_and_overflow():
+    U = np.ones(10, np.float32)
+    assert select.topk_pages(U, 3) == [0, 1, 2]
+    assert select.topk_pages(U, 50) == list(range(10))
+    U = np.array([1, 5, 5, 2, 5, -1], np.float32)
+    assert select.topk_pages(U, 2) == [1, 2]
+    assert select.topk_pages(U, 4) == [1, 2, 3, 4]
+    with pytest.raises(ValueError):
+        select.topk_pages(U, 0)
+
+
+@pytest.mark.parametrize("g", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("h", [-6.0, -3.0, -1.0, 0.0, 0.7, 2.0, 5.0])
+def test_partial_moments_vs_quadrature(g, h):
+    f = lambda z: (z + h) ** g * math.exp(-0.5 * z * z) / math.sqrt(2 * math.pi)
+    ref, _ = integrate.quad(f, -h, np.inf, epsabs=1e-300, epsrel=1e-13, limit=200)
+    got = float(select.partial_moment(h, g))
+    # the recurrence cancels in the left tail: relative accuracy drops there but
+    # the absolute error (what matters inside a sum that equals 1) stays ~1e-16
+    assert abs(got - ref) <= 1e-12 * abs(ref) + 1e-16, (got, ref)
+    if h >= -1.0:
+        assert abs(got - ref) <= 1e-13 * abs(ref) + 1e-300, (got, ref)
+
+
+def _expand(mu_z, counts):
+    return np.repeat(np.asarray(mu_z, float), counts)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tau_hat_zero_variance_is_exact_threshold(seed):
+    # with zero variance every token of page p has z = mu_z[p]; F is then the
+    # exact entmax normalisation of the expanded multiset
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 60))
+    mu_z = rng.normal(0, 1.5, n)
+    counts = rng.integers(1, 17, n)
+    sig = np.zeros(n)
+    t1 = select.gauss_tau_hat(mu_z, sig, counts, 1)
+    assert abs(t1 - sparsemax_sort(_expand(mu_z, counts))) < 1e-12 * max(1, abs(t1))
+    t2 = select.gauss_tau_hat(mu_z, sig, counts, 2)
+    assert abs(t2 - entmax15_sort(_expand(mu_z, counts))) < 1e-12 * max(1, abs(t2))
+
+
+@pytest.mark.parametrize("g", [1, 2, 4])
+@pytest.mark.parametrize("seed", range(4))
+def test_tau_hat_solves_normalisation(g, seed):
+    rng = np.random.default_rng(50 + seed)
+    n = 500
+    mu_z = rng.normal(0, 1, n)
+    sig = rng.uniform(0.0, 1.0, n)
+    sig[::7] = 0.0
+    counts = np.full(n, 16)
+    t = select.gauss_tau_hat(mu_z, sig, counts, g)
+    assert abs(select.gauss_F(t, mu_z, sig, counts, g) - 1.0) < 1e-12
+    # F is decreasing: a little to the left is above 1, to the right below
+    assert select.gauss_F(t - 1e-6, mu_z, sig, counts, g) > 1.0
+    assert select.gauss_F(t + 1e-6, mu_z, sig, counts, g) < 1.0
+
+
+def test_gauss_F_matches_monte_carlo():
+    # F(tau) = sum_p n_p E[(X_p - tau)_+^g]: check one page by sampling
+    rng = np.random.default_rng(9)
+    mu, s, tau = 0.4, 0.7, 0.9
+    x = rng.normal(mu, s, 2_000_000)
+    for g in (1, 2, 4):
+        mc = np.mean(np.maximum(x - tau, 0.0) ** g) * 16
+        val = select.gauss_F(tau, [mu], [s], [16], g)
+        assert abs(mc - val) < 0.01 * val
+
+
+def test_gauss_select_threshold_rule_and_guard():
+    # two heads; page kept iff (alpha-1) u >= tau_hat - delta for some head
+    alpha, delta = 2.0, 0.1
+    u = np.array([[0.0, 3.0, -1.0, 2.0], [0.5, -2.0, 2.5, 0.0]], np.float32)
+    m = np.array([[0.0, 1.0, -1.0, 0.5], [0.2, -1.0, 1.0, 0.0]])
+    v = np.zeros_like(m)
+    counts = [16, 16, 16, 16]
+    sel, taus = select.gauss_select(u, m, v, counts, alpha, delta)
+    expect = [p for p in range(4) if any(u[h, p] >= taus[h] - delta for h in range(2))]
+    assert sel == expect and len(sel) > 0
+    # guard: bounds far below the estimate -> keep argmax U (lowest index on ties)
+    u2 = np.array([[-5.0, -4.0, -4.0]], np.float32)
+    m2 = np.array([[10.0, 10.0, 10.0]])
+    sel2, _ = select.gauss_select(u2, m2, np.zeros_like(m2), [4, 4, 4], alpha, delta)
+    assert sel2 == [1]
+
+
+def test_integer_gamma_rule():
+    assert select.integer_gamma(1.5) == 2
+    assert select.integer_gamma(2.0) == 1
+    assert select.integer_gamma(1.25) == 4
+    with pytest.raises(ValueError):
+        select.integer_gamma(1.7)
