@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged alpha-entmax decode library on one GPU.
+
+One step = one decode step of one attention layer for every sequence and query
+head of the batch:
+    build_page_meta(first_page = last page, span = 1)   refresh of the page that
+                                                         receives the new token
+    score_pages -> select_pages -> entmax_decode
+Inputs (K/V pages, metadata, queries) are resident in HBM before timing.  R
+independent layers (own K, V, metadata, queries) are cycled so that the bytes
+touched between two visits of a layer exceed the 256 MB Infinity Cache.
+
+Prints one JSON line: steps/s (value), effective KV GB/s and its fraction of
+the 8 TB/s HBM peak, the roofline of the dominant entry point, and the CPU
+oracle timed on a bounded sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--config gqa] [--layers R]
+                    [--no-graph] [--cpu-seconds S] [--sweep FILE]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+ENTRY_POINT = {"refresh": "ekv_build_page_meta", "score": "ekv_score_pages",
+               "select": "ekv_select_pages", "decode": "ekv_entmax_decode"}
+METRIC = "decode steps/s + effective KV GB/s (fraction of HBM peak), batch×ctx sweep"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="gqa", help="tiny | gqa | gauss | ragged | stress")
+    ap.add_argument("--layers", type=int, default=0, help="layers cycled (0 = auto)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
+    ap.add_argument("--sweep", default="", help="also run the batch x ctx sweep, JSON lines to FILE")
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--policy", default=None)
+    ap.add_argument("--top-k", type=int, default=None)
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="query std * sqrt(d) (stress workload)")
+    return ap.parse_args()
+
+
+class Layer:
+    """One attention layer's cache, queries and decoder buffers."""
+
+    def __init__(self, w, seed_offset, dev):
+        import torch
+        from sparse_kv_cache_page_amd import workloads as wl
+        from sparse_kv_cache_page_amd.binding import CacheShape
+        from sparse_kv_cache_page_amd.engine import PagedEntmaxDecoder
+        self.w = wl.variant(w, seed=w.seed + seed_offset)
+        self.inp = wl.make_inputs(self.w, device=dev)
+        inp = self.inp
+        self.shape = CacheShape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                inp["max_pages"], inp["num_phys_pages"],
+                                torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32)
+        self.dec = PagedEntmaxDecoder(self.shape, policy=w.policy, top_k=w.top_k,
+                                      alpha=w.alpha, scale=w.scale, delta=w.delta, device=dev)
+        self.dec.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
+        self.last_page = torch.tensor([n - 1 for n in inp["npages"]], dtype=torch.int32,
+                                      device=dev)
+
+    # the four calls of one step, separately so they can be timed one by one
+    def refresh(self):
+        i = self.inp
+        self.dec.build_meta(i["K"], i["block_table"], i["seq_lens"], first_page=self.last_page,
+                            span=1)
+
+    def score(self):
+        i = self.inp
+        self.dec.score(i["q"], i["block_table"], i["seq_lens"])
+
+    def select(self):
+        self.dec.select(self.inp["seq_lens"])
+
+    def decode(self):
+        i = self.inp
+        self.dec.decode(i["q"], i["K"], i["V"], i["block_table"], i["seq_lens"])
+
+    def step(self):
+        self.refresh()
+        if self.w.policy != "dense":
+            self.score()
+            self.select()
+        self.decode()
+
+
+def stage_bytes(layer):
+    """Algorithmic bytes per launch of each entry point (the method's own traffic).
+
+    refresh: valid K rows of each row's last page + the rewritten metadata;
+    score:   bounding boxes (+ mean/var for the Gaussian policy) of every page,
+             plus the bound written per page;
+    select:  bounds read + page lists written;
+    decode:  K rows of the selected pages' valid tokens, plus the value rows of
+             each head's support (the only value rows entmax needs).
+    """
+    import torch
+    w, inp, dec = layer.w, layer.inp, layer.dec
+    e = 2 if w.kv_dtype == "bf16" else 4
+    d, P, Hkv = w.head_dim, w.page_size, w.num_kv_heads
+    gauss = w.policy == "gauss"
+    lens = inp["lens"]
+    npg = inp["npages"]
+    last_valid = [L - (n - 1) * P for L, n in zip(lens, npg)]
+    meta_pp = 2 * d * e + (2 * d * 4 if gauss else 0)
+    refresh = sum(Hkv * (v * d * e + meta_pp) for v in last_valid)
+    pages = sum(npg) * Hkv
+    score = pages * (meta_pp + 4 + (w.group * (4 + 16) if gauss else 0))
+    if w.policy == "dense":
+        n_sel = torch.tensor(npg)[:, None].expand(w.batch, Hkv)
+    else:
+        n_sel = dec.n_sel.cpu().long()
+    select = pages * 4 + int(n_sel.sum()) * 4
+    # selected valid tokens: every selected page is full except possibly the last
+    ktok = 0
+    sel = None if w.policy == "dense" else dec.sel.cpu()
+    for b in range(w.batch):
+        for g in range(Hkv):
+            ns = int(n_sel[b, g])
+            ktok += ns * P
+            last_sel = (ns - 1) if sel is None else int(sel[b, g, ns - 1])
+            if last_sel == npg[b] - 1:
+                ktok -= P - last_valid[b]
+    vrows = int(dec.n_support.cpu().long().sum())
+    decode = ktok * d * e + vrows * d * e
+    full = sum(lens) * Hkv * d * e * 2
+    return dict(refresh=refresh, score=score if w.policy != "dense" else 0,
+                select=select if w.policy != "dense" else 0, decode=decode,
+                kv_bytes=refresh + (pages * meta_pp if w.policy != "dense" else 0) + decode,
+                full_cache=full, k_tokens=ktok, v_rows=vrows)
+
+
+def time_steps(layers, steps, warmup, graph):
+    import torch
+    R = len(layers)
+    for i in range(warmup):
+        layers[i % R].step()
+    torch.cuda.synchronize()
+    if graph:
+        graphs = []
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for L in layers:          # warm the capture stream
+                L.step()
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        for L in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                L.step()
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            graphs[i % R].replay()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(end) / steps, wall
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        layers[i % R].step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def time_stages(layers, steps, policy):
+    """Average duration (ms) of each entry point, HIP events on the launch stream."""
+    import torch
+    names = ["refresh", "decode"] if policy == "dense" else ["refresh", "score", "select", "decode"]
+    R = len(layers)
+    acc = {n: 0.0 for n in names}
+    evs = []
+    for i in range(steps):
+        L = layers[i % R]
+        marks = []
+        for n in names:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            getattr(L, n)()
+            b.record()
+            marks.append((n, a, b))
+        evs.append(marks)
+    torch.cuda.synchronize()
+    for marks in evs:
+        for n, a, b in marks:
+            acc[n] += a.elapsed_time(b)
+    return {n: acc[n] / steps for n in names}
+
+
+def cpu_baseline(layer, budget_s):
+    """The oracle as it stands, timed on host cores over a bounded sample of pairs."""
+    from threadpoolctl import threadpool_limits
+    from oracle import pipeline
+    w = layer.w
+    pairs = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    # spread the sample over the batch
+    order = pairs[::max(1, len(pairs) // 16)] + pairs
+    seen, sample = set(), []
+    for p in order:
+        if p not in seen:
+            seen.add(p)
+            sample.append(p)
+    timed, done = 0.0, 0
+    with threadpool_limits(limits=1):
+        t_start = time.perf_counter()
+        for b, g in sample:
+            t = {}
+            pipeline.run_pair(layer.inp, b, g, w.policy, timings=t)
+            timed += t.get("score", 0) + t.get("select", 0) + t.get("decode", 0)
+            done += 1
+            if time.perf_counter() - t_start > budget_s:
+                break
+    per_step = timed / done * len(pairs)
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (row, KV head) pairs of one {w.name} step "
+                      f"(score + select + decode, metadata prebuilt), scaled linearly to "
+                      f"all pairs; fp64 numpy, 1 BLAS thread",
+            "seconds_per_step": per_step}
+
+
+def workload_config(w, R, graph, inp):
+    lens = inp["lens"]
+    ctx = lens[0] if w.lens_range is None else f"U[{w.lens_range[0]},{w.lens_range[1]}]"
+    return {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": ctx,
+            "page_size": w.page_size, "kv_dtype": w.kv_dtype, "alpha": w.alpha,
+            "policy": w.policy, "top_k": w.top_k if w.policy == "topk" else None,
+            "delta": w.delta if w.policy == "gauss" else None,
+            "q_std_x_sqrt_d": round(w.q_std * math.sqrt(w.head_dim), 6),
+            "layers_rotated": R, "hip_graph": graph}
+
+
+def run(w, args, dev, emit_cpu=True):
+    import torch
+    R = args.layers
+    if R <= 0:
+        probe = Layer(w, 0, dev)
+        per_layer = stage_bytes_after_step(probe)["kv_bytes"]
+        R = max(2, min(16, math.ceil((1 << 30) / max(per_layer, 1))))
+        layers = [probe] + [Layer(w, 7919 * (i + 1), dev) for i in range(R - 1)]
+    else:
+        layers = [Layer(w, 7919 * i, dev) for i in range(R)]
+    graph = not args.no_graph
+    ms, wall = time_steps(layers, args.steps, args.warmup, graph)
+    stages = time_stages(layers, max(20, min(args.steps, 200)), w.policy)
+    nb = stage_bytes(layers[0])
+    eff = nb["kv_bytes"] / (ms * 1e-3) / 1e9
+    dom = max(stages, key=lambda n: stages[n])
+    dom_bytes = nb[dom]
+    achieved = dom_bytes / (stages[dom] * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": 1000.0 / ms, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic", "config": workload_config(w, R, graph, layers[0].inp),
+        "effective_kv_gbps": eff, "hbm_frac": eff / HBM_PEAK_GBPS,
+        "kv_bytes_per_step": nb["kv_bytes"], "full_cache_bytes": nb["full_cache"],
+        "read_fraction_of_full_cache": nb["kv_bytes"] / nb["full_cache"],
+        "stage_ms": stages, "stage_bytes": {k: nb[k] for k in stages},
+        "host_wall_ms_per_step": wall * 1000.0 / args.steps,
+        "roofline": {"kernel": ENTRY_POINT[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+    }
+    if emit_cpu and args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
+    del layers
+    torch.cuda.empty_cache()
+    return rec
+
+
+def stage_bytes_after_step(layer):
+    import torch
+    layer.step()
+    torch.cuda.synchronize()
+    return stage_bytes(layer)
+
+
+def build_workload(args):
+    from sparse_kv_cache_page_amd import workloads as wl
+    w = wl.CONFIGS[args.config]
+    kw = {}
+    if args.alpha is not None:
+        kw["alpha"] = args.alpha
+    if args.policy is not None:
+        kw["policy"] = args.policy
+    if args.top_k is not None:
+        kw["top_k"] = args.top_k
+    if args.temperature is not None:
+        kw["q_std"] = args.temperature / math.sqrt(w.head_dim)
+    return wl.variant(w, **kw) if kw else w
+
+
+def sweep(args, dev, path):
+    """batch x ctx sweep with the GQA decode heads, top-k = 1/8 of the pages, alpha 1.5."""
+    from sparse_kv_cache_page_amd import workloads as wl
+    with open(path, "w") as f:
+        for B in (1, 8, 32, 64):
+            for ctx in (8192, 32768, 131072):
+                w = wl.variant("gqa", batch=B, seq_len=ctx, top_k=ctx // 16 // 8,
+                               name=f"gqa_b{B}_ctx{ctx}")
+                a = argparse.Namespace(**vars(args))
+                a.steps, a.warmup, a.layers = min(args.steps, 200), 10, 0
+                rec = run(w, a, dev, emit_cpu=False)
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                print(f"[sweep] B={B} ctx={ctx}: {rec['value']:.1f} steps/s, "
+                      f"{rec['effective_kv_gbps']:.0f} GB/s", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(every (row, KV head) pair is independent; see DESIGN.md for how it would "
+              "shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from sparse_kv_cache_page_amd import binding
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    w = build_workload(args)
+    rec = run(w, args, dev)
+    print(json.dumps(rec), flush=True)
+    if args.sweep:
+        sweep(args, dev, args.sweep)
+
+
+if __name__ == "__main__":
+    main()

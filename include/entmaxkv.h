@@ -1,0 +1,191 @@
+/*
+ * entmaxkv.h -- C ABI of the support-aware paged alpha-entmax decode library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the EntmaxKV summary page (gist.science, paper
+ * 2605.21649, "EntmaxKV – Décodage Conscient du Support pour l'Attention
+ * Entmax"):
+ *   ekv_build_page_meta  -- per-page key metadata            (§2.A)
+ *   ekv_score_pages      -- query-aware page upper bounds     (§2.A)
+ *   ekv_select_pages     -- top-k or Gaussian-aware selection (§2.B)
+ *   ekv_entmax_decode    -- alpha-entmax over selected pages  (§2.C)
+ * The alpha-entmax mapping itself is the standard one: with
+ * z_i = (alpha-1) * s_i, p_i = [z_i - tau]_+^(1/(alpha-1)) and tau chosen so
+ * that sum_i p_i = 1.  tau is always reported in that z-space.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Every array argument is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees or copies to the host, and never synchronises.
+ *    Work is enqueued on `stream` (0 = the null stream) and is asynchronous.
+ *  * Arguments are validated on the host before anything is launched; on any
+ *    error nothing is launched and a negative ekv_status is returned.  Values
+ *    that live in device memory (seq_lens, block_table, sel, n_sel) cannot be
+ *    checked without a synchronisation: they must satisfy
+ *        1 <= seq_lens[b] <= max_pages_per_seq * page_size,
+ *        0 <= block_table[b][p] < num_phys_pages  for p < ceil(seq_lens[b]/P),
+ *    and a physical page referenced by several rows must hold the same number
+ *    of valid tokens in each of them.
+ *  * Alignment: K, V, q, out, kmin, kmax, mean and var 16 bytes; int32 and
+ *    fp32 arrays 4 bytes; fp64 arrays 8 bytes; workspaces 256 bytes.
+ *  * Layouts (row-major, innermost last):
+ *        K, V          [num_phys_pages][Hkv][P][d]   bf16 or fp32
+ *        q, out        [B][Hq][d]                    fp32
+ *        block_table   [B][max_pages_per_seq]        int32
+ *        seq_lens      [B]                           int32
+ *        kmin, kmax    [num_phys_pages][Hkv][d]      same dtype as K
+ *        mean, var     [num_phys_pages][Hkv][d]      fp32
+ *    Query head h reads KV head h / (Hq/Hkv) (contiguous query groups).
+ *    Token t of logical page p of row b is valid when p*P + t < seq_lens[b];
+ *    invalid slots of a row's last page are never read.
+ *  * Supported: head_dim in {64, 128}; page_size in {1,2,4,8,16,32,64};
+ *    Hq % Hkv == 0 and Hq/Hkv in {1,2,4,8}; kv dtype bf16 or fp32.
+ *  * Calls are thread-safe: the library holds no mutable global state.
+ */
+#ifndef ENTMAXKV_H
+#define ENTMAXKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EKV_OK = 0,
+  EKV_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad shape or value  */
+  EKV_ERR_UNSUPPORTED = -2, /* valid but not implemented (dims, alpha, ...) */
+  EKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  EKV_ERR_HIP = -4          /* a HIP launch failed (see hipGetLastError)    */
+} ekv_status;
+
+typedef enum { EKV_BF16 = 0, EKV_F32 = 1 } ekv_dtype;
+
+typedef enum {
+  EKV_SELECT_TOPK = 0,  /* fixed budget: k pages with the largest bound     */
+  EKV_SELECT_GAUSS = 1  /* Gaussian estimate tau-hat of the threshold, margin Delta */
+} ekv_policy;
+
+typedef struct {
+  int32_t batch;             /* B                                           */
+  int32_t num_q_heads;       /* Hq                                          */
+  int32_t num_kv_heads;      /* Hkv                                         */
+  int32_t head_dim;          /* d                                           */
+  int32_t page_size;         /* P, tokens per page                          */
+  int32_t max_pages_per_seq; /* maxP, row stride of block_table and scores  */
+  int32_t num_phys_pages;    /* Np, pages in the K/V pool                   */
+  int32_t kv_dtype;          /* ekv_dtype of K, V, kmin, kmax               */
+} ekv_cache_desc;
+
+/*
+ * Page metadata (§2.A "Notation de Page Consciente de la Requête": a
+ * per-coordinate bounding box of the page's keys, and the first and second
+ * moments of the keys so that in-page scores can be modelled as Gaussian).
+ *
+ * For each row b and logical page p with first_page[b] <= p <
+ * first_page[b] + span (and p < ceil(seq_lens[b]/P)), over the page's valid
+ * tokens, writes to physical page pi = block_table[b][p], KV head g:
+ *   kmin[pi][g][j], kmax[pi][g][j]  exact per-coordinate min / max;
+ *   mean[pi][g][j]                  (sum_t k_tj) / n, fp64 then rounded to fp32;
+ *   var[pi][g][j]                   population variance (1/n) sum_t (k_tj - mean)^2,
+ *                                   two-pass in fp64, rounded to fp32.
+ * first_page: device int32 [B] or NULL (= 0 for every row).
+ * span: pages per row to (re)build; span <= 0 means max_pages_per_seq.
+ *       span = 1 with first_page[b] = last page refreshes the page a decode
+ *       step has just appended to.
+ * mean and var may both be NULL (bounding box only).
+ */
+ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* first_page, int32_t span,
+                               void* kmin, void* kmax, float* mean, float* var,
+                               hipStream_t stream);
+
+/*
+ * Page scores (§2.A: a deterministic upper bound on the largest score any
+ * token of the page can reach for the query; Gaussian moments of the scores).
+ * For row b, query head h, logical page p < ceil(seq_lens[b]/P), with
+ * pi = block_table[b][p] and g = h / (Hq/Hkv):
+ *   ub[b][h][p]  = RN_fp32( scale * sum_j max(q_j kmin_j, q_j kmax_j) ),
+ *                  accumulated in fp64 from exact products;
+ *   ubg[b][g][p] = max over the group's query heads of ub[b][h][p];
+ *   gm[b][h][p]  = scale   * sum_j q_j mean_j          (fp64),
+ *   gv[b][h][p]  = scale^2 * sum_j q_j^2 var_j         (fp64).
+ * Entries with p >= ceil(seq_lens[b]/P) are left untouched.
+ * Arrays: q [B][Hq][d]; ub, gm, gv [B][Hq][maxP]; ubg [B][Hkv][maxP].
+ * ub may be NULL (only ubg written).  gm and gv are both NULL or both set;
+ * when set, mean and var must be set.  scale must be finite and > 0.
+ */
+ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float scale,
+                           const void* kmin, const void* kmax,
+                           const float* mean, const float* var,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           float* ub, float* ubg, double* gm, double* gv,
+                           hipStream_t stream);
+
+/*
+ * Candidate selection (§2.B "Politiques de Sélection des Candidats").
+ * Output per (row b, KV head g): sel[b][g][0 .. n_sel[b][g]) ascending logical
+ * page indices; entries past n_sel are left untouched.
+ *
+ * EKV_SELECT_TOPK: the min(top_k, n_b) pages with the largest ubg[b][g][p];
+ *   equal values go to the lower page index.  Uses ubg only.  top_k >= 1.
+ * EKV_SELECT_GAUSS: per query head h, tau_hat[b][h] (fp64) is the root of
+ *   sum_p n_p * E[(X_p - tau)_+^gamma] = 1,
+ *   X_p ~ N((alpha-1) gm[b][h][p], (alpha-1)^2 gv[b][h][p]), n_p = valid tokens
+ *   of page p, gamma = 1/(alpha-1); page p is kept when
+ *   (alpha-1) * ub[b][h][p] >= tau_hat[b][h] - delta for some head h of group g
+ *   (compared in fp64).  If no page is kept, the page with the largest ubg is
+ *   (lowest index on ties).  Needs ub, ubg, gm, gv and tau_hat; gamma must be
+ *   1, 2, 3 or 4 (alpha in {2, 1.5, 4/3, 1.25}) else EKV_ERR_UNSUPPORTED;
+ *   delta >= 0.
+ * Arrays: sel [B][Hkv][maxP] int32; n_sel [B][Hkv] int32; tau_hat [B][Hq] fp64.
+ */
+ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
+                            int32_t policy, int32_t top_k, float alpha, float delta,
+                            const float* ub, const float* ubg,
+                            const double* gm, const double* gv,
+                            int32_t* sel, int32_t* n_sel, double* tau_hat,
+                            hipStream_t stream);
+
+/*
+ * Sparse alpha-entmax attention over the selected pages (§2.C "Attention
+ * Entmax Parcimonieuse": only the selected pages' keys and values are loaded;
+ * the entmax weights are computed over that reduced set; the output is exact
+ * when the set contains the full distribution's support, §3).
+ * For each row b and query head h (KV head g), over the valid tokens i of the
+ * pages sel[b][g][0 .. n_sel[b][g]) (all pages 0 .. n_b-1 when sel is NULL):
+ *   z_i   = (alpha-1) * scale * <q[b][h], k_i>           (fp32 accumulation)
+ *   tau   : sum_i [z_i - tau]_+^(1/(alpha-1)) = 1         (solved in fp64)
+ *   out[b][h] = sum_i p_i v_i / sum_i p_i,  p_i = [z_i - tau]_+^(1/(alpha-1))
+ *   tau_out[b][h] = tau (fp32), if tau_out is not NULL;
+ *   n_support[b][h] = #{i : p_i > 0} (int32), if n_support is not NULL.
+ * Only value rows with p_i > 0 are read (entmax zeros are exact).
+ * max_sel: host upper bound on every n_sel[b][g] (<= max_pages_per_seq; <= 0
+ *   means max_pages_per_seq).  It sizes the launch and the workspace; a row
+ *   whose n_sel exceeds it gets NaN outputs.
+ * ws / ws_bytes: device scratch of at least ekv_decode_workspace_bytes(desc,
+ *   max_sel) bytes, 256-byte aligned; its contents need no initialisation
+ *   and are garbage afterwards.  alpha > 1 and finite; scale > 0.
+ */
+ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float scale,
+                             float alpha, const void* K, const void* V,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+                             float* out, float* tau_out, int32_t* n_support, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Scratch bytes ekv_entmax_decode needs for this cache shape and max_sel
+ * (0 if desc is invalid). */
+size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);
+
+/* Static description of a status code (never NULL). */
+const char* ekv_status_string(ekv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTMAXKV_H */

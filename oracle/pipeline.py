@@ -90,12 +90,23 @@ def decode_heads(q_heads, keys_sel, vals_sel, scale: float, alpha: float):
 
 def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=None,
              delta=None, scale=None, q=None, exact_meta=False, with_full=False,
-             sel_override=None):
+             sel_override=None, timings=None):
     """One decode step of (row b, KV head g) under `policy` ('topk', 'gauss', 'dense').
 
     alpha, scale and delta are the fp32 values handed to the library (widened).
     Returns a dict with the metadata, bounds, selection and entmax outputs.
+    If `timings` is a dict, wall-clock seconds of the phases are added to it
+    under 'read', 'meta', 'score', 'select' and 'decode'.
     """
+    import time
+    clock = [time.perf_counter()]
+
+    def lap(name):
+        if timings is not None:
+            now = time.perf_counter()
+            timings[name] = timings.get(name, 0.0) + now - clock[0]
+            clock[0] = now
+
     w = inputs["workload"]
     alpha = float(np.float32(w.alpha if alpha is None else alpha))
     scale = float(np.float32(w.scale if scale is None else scale))
@@ -106,7 +117,9 @@ def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=Non
 
     phys, counts, keys, vals = pair_keys_values(inputs, b, g)
     n = len(phys)
+    lap("read")
     kmin, kmax, mu, var = pair_meta(keys, exact=exact_meta)
+    lap("meta")
 
     u = np.array([scores.box_bounds(qq[h], kmin, kmax, scale) for h in range(G)],
                  dtype=np.float32)                                     # [G][n]
@@ -114,6 +127,7 @@ def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=Non
     out = dict(phys=phys, counts=counts, kmin=kmin, kmax=kmax, mean=mu, var=var,
                u=u, U=U, tau_hat=None)
 
+    lap("score")
     if sel_override is not None:
         sel = list(sel_override)
     elif policy == "topk":
@@ -131,11 +145,13 @@ def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=Non
     else:
         raise ValueError(policy)
     out["sel"] = sel
+    lap("select")
 
     ks = np.concatenate([keys[p] for p in sel])
     vs = np.concatenate([vals[p] for p in sel])
     tau, p, o = decode_heads(qq, ks, vs, scale, alpha)
     out.update(tau=tau, p=p, o=o, n_tokens=ks.shape[0])
+    lap("decode")
 
     if with_full:
         kf = np.concatenate(keys)

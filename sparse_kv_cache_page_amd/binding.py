@@ -1,0 +1,234 @@
+"""Thin Python binding of libentmaxkv.so (the C ABI in include/entmaxkv.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, turned into raw pointers, and handed to the C entry point together
+with torch's current HIP stream.  Every step of the computation runs in the
+library's HIP kernels; there is no other execution path.  If the library is
+not built, or there is no GPU, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libentmaxkv.so")
+
+EKV_OK = 0
+EKV_BF16, EKV_F32 = 0, 1
+EKV_SELECT_TOPK, EKV_SELECT_GAUSS = 0, 1
+
+EXPORTED = (
+    "ekv_build_page_meta",
+    "ekv_score_pages",
+    "ekv_select_pages",
+    "ekv_entmax_decode",
+    "ekv_decode_workspace_bytes",
+    "ekv_status_string",
+)
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+    ]
+
+
+class EkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the shared library; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m sparse_kv_cache_page_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    dp = ctypes.POINTER(CacheDesc)
+    lib.ekv_build_page_meta.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.ekv_score_pages.argtypes = [dp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ekv_select_pages.argtypes = [dp, vp, i32, i32, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ekv_entmax_decode.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                      vp, sz, vp]
+    lib.ekv_decode_workspace_bytes.argtypes = [dp, i32]
+    lib.ekv_decode_workspace_bytes.restype = sz
+    lib.ekv_status_string.argtypes = [ctypes.c_int]
+    lib.ekv_status_string.restype = ctypes.c_char_p
+    for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
+                 "ekv_entmax_decode"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ekv_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != EKV_OK:
+        raise EkvError(fn, status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+@dataclass(frozen=True)
+class CacheShape:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    max_pages_per_seq: int
+    num_phys_pages: int
+    kv_dtype: torch.dtype = torch.bfloat16
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def desc(self) -> CacheDesc:
+        if self.kv_dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("K/V must be bfloat16 or float32")
+        return CacheDesc(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
+                         self.page_size, self.max_pages_per_seq, self.num_phys_pages,
+                         EKV_BF16 if self.kv_dtype == torch.bfloat16 else EKV_F32)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _kv_shape(s: CacheShape):
+    return (s.num_phys_pages, s.num_kv_heads, s.page_size, s.head_dim)
+
+
+def build_page_meta(s: CacheShape, K, block_table, seq_lens, kmin, kmax, mean=None, var=None,
+                    first_page=None, span: int = 0):
+    """ekv_build_page_meta: per-page bounding box and key moments."""
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq))
+    _need(seq_lens, "seq_lens", torch.int32, (s.batch,))
+    mshape = (s.num_phys_pages, s.num_kv_heads, s.head_dim)
+    _need(kmin, "kmin", s.kv_dtype, mshape)
+    _need(kmax, "kmax", s.kv_dtype, mshape)
+    if mean is not None or var is not None:
+        _need(mean, "mean", torch.float32, mshape)
+        _need(var, "var", torch.float32, mshape)
+    if first_page is not None:
+        _need(first_page, "first_page", torch.int32, (s.batch,))
+    d = s.desc()
+    _check("ekv_build_page_meta", load_library().ekv_build_page_meta(
+        ctypes.byref(d), _ptr(K), _ptr(block_table), _ptr(seq_lens), _ptr(first_page),
+        int(span), _ptr(kmin), _ptr(kmax), _ptr(mean), _ptr(var), _stream()))
+
+
+def score_pages(s: CacheShape, q, scale: float, kmin, kmax, block_table, seq_lens, ubg,
+                ub=None, mean=None, var=None, gm=None, gv=None):
+    """ekv_score_pages: box upper bounds (and Gaussian moments when gm/gv given)."""
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    mshape = (s.num_phys_pages, Hkv, d)
+    _need(kmin, "kmin", s.kv_dtype, mshape)
+    _need(kmax, "kmax", s.kv_dtype, mshape)
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
+    if ub is not None:
+        _need(ub, "ub", torch.float32, (B, Hq, mp))
+    if gm is not None or gv is not None:
+        _need(gm, "gm", torch.float64, (B, Hq, mp))
+        _need(gv, "gv", torch.float64, (B, Hq, mp))
+        _need(mean, "mean", torch.float32, mshape)
+        _need(var, "var", torch.float32, mshape)
+    d_ = s.desc()
+    _check("ekv_score_pages", load_library().ekv_score_pages(
+        ctypes.byref(d_), _ptr(q), float(scale), _ptr(kmin), _ptr(kmax), _ptr(mean), _ptr(var),
+        _ptr(block_table), _ptr(seq_lens), _ptr(ub), _ptr(ubg), _ptr(gm), _ptr(gv), _stream()))
+
+
+def select_pages(s: CacheShape, seq_lens, policy: int, top_k: int, alpha: float, delta: float,
+                 ubg, sel, n_sel, ub=None, gm=None, gv=None, tau_hat=None):
+    """ekv_select_pages: top-k (policy 0) or Gaussian-aware (policy 1) selection."""
+    B, Hq, Hkv, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.max_pages_per_seq
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
+    _need(sel, "sel", torch.int32, (B, Hkv, mp))
+    _need(n_sel, "n_sel", torch.int32, (B, Hkv))
+    if policy == EKV_SELECT_GAUSS:
+        _need(ub, "ub", torch.float32, (B, Hq, mp))
+        _need(gm, "gm", torch.float64, (B, Hq, mp))
+        _need(gv, "gv", torch.float64, (B, Hq, mp))
+        _need(tau_hat, "tau_hat", torch.float64, (B, Hq))
+    d = s.desc()
+    _check("ekv_select_pages", load_library().ekv_select_pages(
+        ctypes.byref(d), _ptr(seq_lens), int(policy), int(top_k), float(alpha), float(delta),
+        _ptr(ub), _ptr(ubg), _ptr(gm), _ptr(gv), _ptr(sel), _ptr(n_sel), _ptr(tau_hat),
+        _stream()))
+
+
+def decode_workspace_bytes(s: CacheShape, max_sel: int = 0) -> int:
+    d = s.desc()
+    return int(load_library().ekv_decode_workspace_bytes(ctypes.byref(d), int(max_sel)))
+
+
+def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_table, seq_lens,
+                  out, ws, sel=None, n_sel=None, max_sel: int = 0, tau=None, n_support=None):
+    """ekv_entmax_decode: alpha-entmax attention over the selected pages (all if sel is None)."""
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(V, "V", s.kv_dtype, _kv_shape(s))
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(out, "out", torch.float32, (B, Hq, d))
+    if sel is not None or n_sel is not None:
+        _need(sel, "sel", torch.int32, (B, Hkv, mp))
+        _need(n_sel, "n_sel", torch.int32, (B, Hkv))
+    if tau is not None:
+        _need(tau, "tau", torch.float32, (B, Hq))
+    if n_support is not None:
+        _need(n_support, "n_support", torch.int32, (B, Hq))
+    if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.dtype == torch.uint8
+            and ws.is_contiguous()):
+        raise TypeError("ws must be a contiguous uint8 GPU tensor")
+    d_ = s.desc()
+    _check("ekv_entmax_decode", load_library().ekv_entmax_decode(
+        ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
+        _ptr(block_table), _ptr(seq_lens), _ptr(sel), _ptr(n_sel), int(max_sel), _ptr(out),
+        _ptr(tau), _ptr(n_support), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))

@@ -1,0 +1,165 @@
+// C ABI of the paged entmax decode library: host-side validation, launch
+// planning and dispatch to the gfx950 kernels.  Nothing here allocates,
+// frees or synchronises; every error is reported before any launch.
+#include <math.h>
+#include <stdint.h>
+
+#include "entmaxkv.h"
+#include "kernels.h"
+
+namespace {
+
+using ekv::Shape;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int log2_exact(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return (1 << l) == x ? l : -1;
+}
+
+ekv_status make_shape(const ekv_cache_desc* d, Shape* s) {
+  if (d == nullptr) return EKV_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 ||
+      d->page_size < 1 || d->max_pages_per_seq < 1 || d->num_phys_pages < 1)
+    return EKV_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return EKV_ERR_INVALID_ARG;
+  if (d->kv_dtype != EKV_BF16 && d->kv_dtype != EKV_F32) return EKV_ERR_INVALID_ARG;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return EKV_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return EKV_ERR_UNSUPPORTED;
+  const int l2 = log2_exact(d->page_size);
+  if (l2 < 0 || d->page_size > 64) return EKV_ERR_UNSUPPORTED;
+  // token slots of one row and page counts must stay inside int32 indexing
+  if ((long long)d->max_pages_per_seq * d->page_size > (1LL << 30)) return EKV_ERR_UNSUPPORTED;
+  s->B = d->batch;
+  s->Hq = d->num_q_heads;
+  s->Hkv = d->num_kv_heads;
+  s->G = G;
+  s->D = d->head_dim;
+  s->P = d->page_size;
+  s->log2P = l2;
+  s->maxP = d->max_pages_per_seq;
+  s->Np = d->num_phys_pages;
+  s->bf16 = d->kv_dtype == EKV_BF16;
+  return EKV_OK;
+}
+
+bool ok_vec(const void* p) { return p != nullptr && aligned(p, 16); }
+bool ok_i32(const void* p) { return p != nullptr && aligned(p, 4); }
+bool ok_f64(const void* p) { return p != nullptr && aligned(p, 8); }
+
+ekv_status from_hip(hipError_t e) { return e == hipSuccess ? EKV_OK : EKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ekv_status_string(ekv_status status) {
+  switch (status) {
+    case EKV_OK: return "ok";
+    case EKV_ERR_INVALID_ARG: return "invalid argument";
+    case EKV_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case EKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case EKV_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* first_page, int32_t span, void* kmin, void* kmax,
+                               float* mean, float* var, hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(K) || !ok_i32(block_table) || !ok_i32(seq_lens) || !ok_vec(kmin) || !ok_vec(kmax))
+    return EKV_ERR_INVALID_ARG;
+  if (first_page != nullptr && !aligned(first_page, 4)) return EKV_ERR_INVALID_ARG;
+  if ((mean == nullptr) != (var == nullptr)) return EKV_ERR_INVALID_ARG;
+  if (mean != nullptr && (!ok_vec(mean) || !ok_vec(var))) return EKV_ERR_INVALID_ARG;
+  if (span <= 0 || span > s.maxP) span = s.maxP;
+  return from_hip(ekv::launch_build_meta(s, K, block_table, seq_lens, first_page, span, kmin,
+                                         kmax, mean, var, stream));
+}
+
+ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float scale,
+                           const void* kmin, const void* kmax, const float* mean,
+                           const float* var, const int32_t* block_table,
+                           const int32_t* seq_lens, float* ub, float* ubg, double* gm,
+                           double* gv, hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(q) || !ok_vec(kmin) || !ok_vec(kmax) || !ok_i32(block_table) ||
+      !ok_i32(seq_lens) || !ok_i32(ubg))
+    return EKV_ERR_INVALID_ARG;
+  if (ub != nullptr && !aligned(ub, 4)) return EKV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
+  if ((gm == nullptr) != (gv == nullptr)) return EKV_ERR_INVALID_ARG;
+  if (gm != nullptr) {
+    if (!ok_f64(gm) || !ok_f64(gv) || !ok_vec(mean) || !ok_vec(var)) return EKV_ERR_INVALID_ARG;
+  }
+  return from_hip(ekv::launch_score(s, q, scale, kmin, kmax, mean, var, block_table, seq_lens,
+                                    ub, ubg, gm, gv, stream));
+}
+
+ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens, int32_t policy,
+                            int32_t top_k, float alpha, float delta, const float* ub,
+                            const float* ubg, const double* gm, const double* gv,
+                            int32_t* sel, int32_t* n_sel, double* tau_hat,
+                            hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_i32(seq_lens) || !ok_i32(ubg) || !ok_i32(sel) || !ok_i32(n_sel))
+    return EKV_ERR_INVALID_ARG;
+  if (policy == EKV_SELECT_TOPK) {
+    if (top_k < 1) return EKV_ERR_INVALID_ARG;
+    return from_hip(ekv::launch_topk(s, seq_lens, top_k, ubg, sel, n_sel, stream));
+  }
+  if (policy != EKV_SELECT_GAUSS) return EKV_ERR_INVALID_ARG;
+  if (!ok_i32(ub) || !ok_f64(gm) || !ok_f64(gv) || !ok_f64(tau_hat)) return EKV_ERR_INVALID_ARG;
+  if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
+  if (!(delta >= 0.0f) || !isfinite(delta)) return EKV_ERR_INVALID_ARG;
+  const double gamma = 1.0 / ((double)alpha - 1.0);
+  const double gr = rint(gamma);
+  if (gr < 1.0 || gr > 4.0 || fabs(gamma - gr) > 1e-6 * gr) return EKV_ERR_UNSUPPORTED;
+  return from_hip(ekv::launch_gauss(s, seq_lens, alpha, (int)gr, delta, ub, ubg, gm, gv, sel,
+                                    n_sel, tau_hat, stream));
+}
+
+size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK) return 0;
+  if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
+  return ekv::make_decode_plan(s, max_sel).total;
+}
+
+ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float scale,
+                             float alpha, const void* K, const void* V,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+                             float* out, float* tau_out, int32_t* n_support, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(q) || !ok_vec(K) || !ok_vec(V) || !ok_i32(block_table) || !ok_i32(seq_lens) ||
+      !ok_vec(out))
+    return EKV_ERR_INVALID_ARG;
+  if ((sel == nullptr) != (n_sel == nullptr)) return EKV_ERR_INVALID_ARG;
+  if (sel != nullptr && (!aligned(sel, 4) || !aligned(n_sel, 4))) return EKV_ERR_INVALID_ARG;
+  if (tau_out != nullptr && !aligned(tau_out, 4)) return EKV_ERR_INVALID_ARG;
+  if (n_support != nullptr && !aligned(n_support, 4)) return EKV_ERR_INVALID_ARG;
+  if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
+  if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
+  const ekv::DecodePlan plan = ekv::make_decode_plan(s, max_sel);
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < plan.total) return EKV_ERR_WORKSPACE;
+  return from_hip(ekv::launch_decode(s, plan, q, scale, alpha, K, V, block_table, seq_lens, sel,
+                                     n_sel, out, tau_out, n_support, ws, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Internal helpers shared by the gfx950 kernels of the paged entmax decode
+// library: element types, 16-byte vector loads, and wave64 cross-lane
+// reductions built on DPP row operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "entmaxkv.h"
+
+namespace ekv {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element types.  Keys/values are bf16 (stored as raw 16-bit patterns) or fp32.
+// A lane always moves 16 bytes at a time: 8 bf16 or 4 fp32 elements.
+// ---------------------------------------------------------------------------
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16_t> {
+  static constexpr int kVec = 8;  // elements per 16-byte chunk
+  // Widening a bf16 pattern to fp32 is exact: the pattern is the top half of
+  // the fp32 word.
+  __device__ static inline void unpack(const uint4& w, float* out) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(u[i] << 16);
+      out[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static inline void unpack(const uint4& w, float* out) {
+    out[0] = __uint_as_float(w.x);
+    out[1] = __uint_as_float(w.y);
+    out[2] = __uint_as_float(w.z);
+    out[3] = __uint_as_float(w.w);
+  }
+};
+
+__device__ inline uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming loads for data touched once per step (K/V tiles, page metadata).
+__device__ inline uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline uint2 load8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// ---------------------------------------------------------------------------
+// DPP helpers (gfx9 encodings).  Within a row of 16 lanes, the butterfly
+//   quad_perm[1,0,3,2], quad_perm[2,3,0,1], row_half_mirror, row_mirror
+// leaves the full 16-lane sum in every lane of the row.
+// ---------------------------------------------------------------------------
+enum : int {
+  kDppQuadSwap1 = 0xB1,      // quad_perm [1,0,3,2]
+  kDppQuadSwap2 = 0x4E,      // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+};
+
+template <int kCtrl>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+template <int kCtrl>
+__device__ inline double dpp_f64(double x) {
+  const int2 v = *reinterpret_cast<int2*>(&x);
+  int2 r;
+  r.x = __builtin_amdgcn_update_dpp(0, v.x, kCtrl, 0xF, 0xF, false);
+  r.y = __builtin_amdgcn_update_dpp(0, v.y, kCtrl, 0xF, 0xF, false);
+  return *reinterpret_cast<double*>(&r);
+}
+
+// Sum over groups of `kLanes` consecutive lanes (kLanes in {1,2,4,8,16,32,64});
+// every lane of a group receives the group's total.
+template <int kLanes>
+__device__ inline float group_sum_f32(float x) {
+  if constexpr (kLanes >= 2) x += dpp_f32<kDppQuadSwap1>(x);
+  if constexpr (kLanes >= 4) x += dpp_f32<kDppQuadSwap2>(x);
+  if constexpr (kLanes >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
+  if constexpr (kLanes >= 16) x += dpp_f32<kDppRowMirror>(x);
+  if constexpr (kLanes >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (kLanes >= 64) x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+template <int kLanes>
+__device__ inline double group_sum_f64(double x) {
+  if constexpr (kLanes >= 2) x += dpp_f64<kDppQuadSwap1>(x);
+  if constexpr (kLanes >= 4) x += dpp_f64<kDppQuadSwap2>(x);
+  if constexpr (kLanes >= 8) x += dpp_f64<kDppRowHalfMirror>(x);
+  if constexpr (kLanes >= 16) x += dpp_f64<kDppRowMirror>(x);
+  if constexpr (kLanes >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (kLanes >= 64) x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+__device__ inline float wave_max_f32(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+__device__ inline double wave_sum_f64(double x) {
+  return group_sum_f64<64>(x);
+}
+
+__device__ inline int wave_sum_i32(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Number of valid tokens of logical page p in a row of length L.
+__device__ inline int page_valid(int L, int p, int P) {
+  const int r = L - p * P;
+  return r < P ? r : P;
+}
+
+}  // namespace ekv

@@ -1,0 +1,355 @@
+// Candidate page selection (EntmaxKV summary page, §2.B).
+//
+// Top-k: per (row, KV head) one 256-thread workgroup runs an MSB-first radix
+// select over distinct 64-bit keys
+//     key(p) = (order-preserving bits of fp32 U_p) << 32 | (2^32 - 1 - p),
+// so larger U wins and, among equal U, the lower page index wins.  Each pass
+// histograms one 8-bit digit of the keys that still match the chosen prefix
+// (LDS atomics), a block scan picks the digit holding the k-th largest key,
+// and the search stops as soon as every key with the chosen prefix is in the
+// answer.  The selected pages are exactly the keys >= that prefix; a block
+// prefix sum over page order writes them ascending.
+//
+// Gaussian-aware: per query head, tau-hat solves
+//     F(tau) = sum_p n_p E[(X_p - tau)_+^gamma] = 1,  X_p ~ N(mu_p, s_p^2),
+// with E[(X - c)_+^g] = s^g I_g((mu - c)/s) and I_0 = Phi, I_1 = h Phi + phi,
+// I_g = h I_{g-1} + (g-1) I_{g-2}.  F is convex and decreasing (gamma >= 1),
+// F >= 1 at max_p mu_p - 1, and F' = -gamma sum_p n_p s^(g-1) I_{g-1}, so
+// Newton's method started there climbs monotonically to the root.  A second
+// kernel keeps page p when (alpha-1) u_{h,p} >= tau-hat_h - delta for some head
+// of the group and compacts the kept pages in ascending order.
+#include "common.h"
+#include "kernels.h"
+
+namespace ekv {
+namespace {
+
+constexpr int kSelBlock = 256;
+constexpr int kTopkLdsKeys = 16384;   // 64 KiB of LDS keys; longer rows read U from global
+constexpr int kGaussLdsPages = 4096;  // 64 KiB of LDS (mu, sigma) per head
+
+// Inclusive prefix sum over a 256-thread block; `sh` holds 4 ints of LDS.
+__device__ inline int block_incl_scan(int x, int* sh) {
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) sh[w] = x;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += sh[i];
+  __syncthreads();
+  return x + add;
+}
+
+__device__ inline double block_sum_f64(double x, double* sh) {
+  x = wave_sum_f64(x);
+  const int w = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) sh[w] = x;
+  __syncthreads();
+  const double t = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  __syncthreads();
+  return t;
+}
+
+// fp32 -> uint32 with the same order (-0 folded onto +0 so they tie).
+__device__ inline uint32_t order_key(float x) {
+  if (x == 0.0f) x = 0.0f;
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline uint64_t compose(uint32_t ukey, int p) {
+  return ((uint64_t)ukey << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+}
+
+// Ascending compaction of flag(p) for p < n into out[]; returns the count.
+template <typename Flag>
+__device__ int compact_ascending(int n, Flag flag, int32_t* out, int* sh) {
+  const int chunk = (n + kSelBlock - 1) / kSelBlock;
+  const int p0 = threadIdx.x * chunk;
+  const int p1 = min(n, p0 + chunk);
+  int cnt = 0;
+  for (int p = p0; p < p1; ++p) cnt += flag(p) ? 1 : 0;
+  const int incl = block_incl_scan(cnt, sh);
+  int pos = incl - cnt;
+  for (int p = p0; p < p1; ++p)
+    if (flag(p)) out[pos++] = p;
+  // total = inclusive scan of the last thread
+  __shared__ int total;
+  if (threadIdx.x == kSelBlock - 1) total = incl;
+  __syncthreads();
+  return total;
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kSelBlock) void topk_kernel(
+    const float* __restrict__ ubg, const int32_t* __restrict__ lens, int P, int maxP, int Hkv,
+    int top_k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
+  __shared__ uint32_t keys[kLds ? kTopkLdsKeys : 1];
+  __shared__ int hist[256];
+  __shared__ int scan_sh[4];
+  __shared__ int s_digit, s_above, s_cnt;
+
+  const int pair = blockIdx.x;
+  const int b = pair / Hkv;
+  const int n = (lens[b] + P - 1) / P;
+  const int k = min(top_k, n);
+  const float* U = ubg + (size_t)pair * maxP;
+  int32_t* out = sel + (size_t)pair * maxP;
+  if (k >= n) {
+    for (int p = threadIdx.x; p < n; p += kSelBlock) out[p] = p;
+    if (threadIdx.x == 0) n_sel[pair] = n;
+    return;
+  }
+  if constexpr (kLds) {
+    for (int p = threadIdx.x; p < n; p += kSelBlock) keys[p] = order_key(U[p]);
+  }
+  auto key_of = [&](int p) -> uint64_t {
+    if constexpr (kLds) return compose(keys[p], p);
+    else return compose(order_key(U[p]), p);
+  };
+
+  uint64_t prefix = 0, mask = 0;
+  int remaining = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int p = threadIdx.x; p < n; p += kSelBlock) {
+      const uint64_t key = key_of(p);
+      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 0xFF)], 1);
+    }
+    __syncthreads();
+    // thread t owns digit 255 - t: inclusive scan gives #keys with digit >= d
+    const int hcount = hist[255 - threadIdx.x];
+    const int incl = block_incl_scan(hcount, scan_sh);
+    const int excl = incl - hcount;
+    if (excl < remaining && remaining <= incl) {
+      s_digit = 255 - threadIdx.x;
+      s_above = excl;
+      s_cnt = hcount;
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s_digit << shift;
+    mask |= (uint64_t)0xFF << shift;
+    remaining -= s_above;
+    const bool done = (s_cnt == remaining);
+    __syncthreads();
+    if (done) break;
+  }
+  const uint64_t thresh = prefix;  // selected <=> key >= thresh
+  const int got = compact_ascending(n, [&](int p) { return key_of(p) >= thresh; }, out, scan_sh);
+  if (threadIdx.x == 0) n_sel[pair] = got;
+}
+
+// --------------------------------------------------------------------------
+// Gaussian-aware selection
+// --------------------------------------------------------------------------
+template <int kG>
+__device__ inline void partial_moments(double h, double& ig, double& igm1) {
+  // I_g(h) and I_{g-1}(h) for Z ~ N(0,1)
+  const double Phi = 0.5 * erfc(-h * 0.70710678118654752440);
+  const double phi = exp(-0.5 * h * h) * 0.39894228040143267794;
+  double i_prev = Phi;             // I_0
+  double i_cur = fma(h, Phi, phi); // I_1
+  if constexpr (kG == 1) {
+    ig = i_cur;
+    igm1 = i_prev;
+    return;
+  }
+#pragma unroll
+  for (int k = 2; k <= kG; ++k) {
+    const double nxt = fma(h, i_cur, (double)(k - 1) * i_prev);
+    i_prev = i_cur;
+    i_cur = nxt;
+  }
+  ig = i_cur;
+  igm1 = i_prev;
+}
+
+template <int kG>
+__device__ inline double ipow(double x) {
+  double r = 1.0;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) r *= x;
+  return r;
+}
+
+template <int kG, bool kLds>
+__global__ __launch_bounds__(kSelBlock) void gauss_tau_kernel(
+    const double* __restrict__ gm, const double* __restrict__ gv, const int32_t* __restrict__ lens,
+    int P, int maxP, int Hq, double a1, double* __restrict__ tau_hat) {
+  __shared__ double s_mu[kLds ? kGaussLdsPages : 1];
+  __shared__ double s_sd[kLds ? kGaussLdsPages : 1];
+  __shared__ double red[4];
+  const int bh = blockIdx.x;
+  const int b = bh / Hq;
+  const int L = lens[b];
+  const int n = (L + P - 1) / P;
+  const double* M = gm + (size_t)bh * maxP;
+  const double* V = gv + (size_t)bh * maxP;
+
+  auto mu_of = [&](int p) -> double {
+    if constexpr (kLds) return s_mu[p];
+    else return a1 * M[p];
+  };
+  auto sd_of = [&](int p) -> double {
+    if constexpr (kLds) return s_sd[p];
+    else return a1 * sqrt(V[p]);
+  };
+  double zmax = -__builtin_huge_val();
+  for (int p = threadIdx.x; p < n; p += kSelBlock) {
+    const double mz = a1 * M[p];
+    if constexpr (kLds) {
+      s_mu[p] = mz;
+      s_sd[p] = a1 * sqrt(V[p]);
+    }
+    zmax = fmax(zmax, mz);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) zmax = fmax(zmax, __shfl_xor(zmax, o, kWave));
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = zmax;
+  __syncthreads();
+  zmax = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  __syncthreads();
+
+  double tau = zmax - 1.0;  // F(tau) >= 1 here
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fd = 0.0;
+    for (int p = threadIdx.x; p < n; p += kSelBlock) {
+      const double cnt = (double)page_valid(L, p, P);
+      const double mz = mu_of(p);
+      const double sd = sd_of(p);
+      if (sd > 0.0) {
+        const double h = (mz - tau) / sd;
+        double ig, igm1;
+        partial_moments<kG>(h, ig, igm1);
+        const double sg1 = ipow<kG - 1>(sd);
+        f = fma(cnt, sg1 * sd * ig, f);
+        fd = fma(cnt, (double)kG * sg1 * igm1, fd);
+      } else {
+        const double x = mz - tau;
+        if (x > 0.0) {
+          const double xg1 = ipow<kG - 1>(x);
+          f = fma(cnt, xg1 * x, f);
+          fd = fma(cnt, (double)kG * xg1, fd);
+        }
+      }
+    }
+    f = block_sum_f64(f, red) - 1.0;
+    fd = block_sum_f64(fd, red);
+    if (!(f > 0.0) || !(fd > 0.0)) break;
+    const double nxt = tau + f / fd;
+    if (!(nxt > tau)) break;
+    tau = nxt;
+  }
+  if (threadIdx.x == 0) tau_hat[bh] = tau;
+}
+
+__global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
+    const float* __restrict__ ub, const float* __restrict__ ubg, const double* __restrict__ tau_hat,
+    const int32_t* __restrict__ lens, int P, int maxP, int Hkv, int G, double a1, double delta,
+    int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
+  __shared__ int scan_sh[4];
+  __shared__ float s_best[4];
+  __shared__ int s_bestp[4];
+  const int pair = blockIdx.x;
+  const int b = pair / Hkv;
+  const int g = pair % Hkv;
+  const int Hq = Hkv * G;
+  const int n = (lens[b] + P - 1) / P;
+  const float* ubh = ub + ((size_t)b * Hq + g * G) * maxP;
+  const double* th = tau_hat + (size_t)b * Hq + g * G;
+  int32_t* out = sel + (size_t)pair * maxP;
+  auto keep = [&](int p) -> bool {
+    for (int h = 0; h < G; ++h)
+      if (a1 * (double)ubh[(size_t)h * maxP + p] >= th[h] - delta) return true;
+    return false;
+  };
+  const int got = compact_ascending(n, keep, out, scan_sh);
+  if (got > 0) {
+    if (threadIdx.x == 0) n_sel[pair] = got;
+    return;
+  }
+  // nothing cleared the bar: keep the page with the largest group bound
+  const float* U = ubg + (size_t)pair * maxP;
+  float best = -__builtin_huge_valf();
+  int bestp = 0x7fffffff;
+  for (int p = threadIdx.x; p < n; p += kSelBlock) {
+    const float u = U[p];
+    if (u > best || (u == best && p < bestp)) {
+      best = u;
+      bestp = p;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ob = __shfl_xor(best, o, kWave);
+    const int op = __shfl_xor(bestp, o, kWave);
+    if (ob > best || (ob == best && op < bestp)) {
+      best = ob;
+      bestp = op;
+    }
+  }
+  if (threadIdx.x % kWave == 0) {
+    s_best[threadIdx.x / kWave] = best;
+    s_bestp[threadIdx.x / kWave] = bestp;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (s_best[w] > best || (s_best[w] == best && s_bestp[w] < bestp)) {
+        best = s_best[w];
+        bestp = s_bestp[w];
+      }
+    out[0] = bestp;
+    n_sel[pair] = 1;
+  }
+}
+
+template <int kG>
+hipError_t launch_gauss_tau(const Shape& s, const int32_t* lens, double a1, const double* gm,
+                            const double* gv, double* tau_hat, hipStream_t stream) {
+  if (s.maxP <= kGaussLdsPages)
+    hipLaunchKernelGGL((gauss_tau_kernel<kG, true>), dim3(s.B * s.Hq), dim3(kSelBlock), 0, stream,
+                       gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat);
+  else
+    hipLaunchKernelGGL((gauss_tau_kernel<kG, false>), dim3(s.B * s.Hq), dim3(kSelBlock), 0,
+                       stream, gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const float* ubg,
+                       int32_t* sel, int32_t* n_sel, hipStream_t stream) {
+  if (s.maxP <= kTopkLdsKeys)
+    hipLaunchKernelGGL((topk_kernel<true>), dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream, ubg,
+                       lens, s.P, s.maxP, s.Hkv, top_k, sel, n_sel);
+  else
+    hipLaunchKernelGGL((topk_kernel<false>), dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream, ubg,
+                       lens, s.P, s.maxP, s.Hkv, top_k, sel, n_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int gamma, float delta,
+                        const float* ub, const float* ubg, const double* gm, const double* gv,
+                        int32_t* sel, int32_t* n_sel, double* tau_hat, hipStream_t stream) {
+  const double a1 = (double)alpha - 1.0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (gamma) {
+    case 1: e = launch_gauss_tau<1>(s, lens, a1, gm, gv, tau_hat, stream); break;
+    case 2: e = launch_gauss_tau<2>(s, lens, a1, gm, gv, tau_hat, stream); break;
+    case 3: e = launch_gauss_tau<3>(s, lens, a1, gm, gv, tau_hat, stream); break;
+    case 4: e = launch_gauss_tau<4>(s, lens, a1, gm, gv, tau_hat, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gauss_mark_kernel, dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream, ub, ubg,
+                     tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1, (double)delta, sel, n_sel);
+  return hipGetLastError();
+}
+
+}  // namespace ekv

@@ -1,0 +1,92 @@
+"""Buffers and call sequence of one paged entmax decode step.
+
+`PagedEntmaxDecoder` owns the device buffers a decode step needs for one cache
+shape (page metadata, page bounds, selections, decode workspace; all torch
+allocations, made once) and issues the library calls in order:
+
+    build_page_meta   (once per prefill; span=1 refresh of the last page per step)
+    score_pages -> select_pages -> entmax_decode   (every decode step)
+
+This is the pipeline of the EntmaxKV summary page, §2 "Méthodologie": score
+pages from lightweight per-page metadata, select candidates, then run sparse
+alpha-entmax over the selected pages only.  All arithmetic happens in the HIP
+library; this class only allocates and sequences.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as B
+from .binding import CacheShape
+
+
+class PagedEntmaxDecoder:
+    def __init__(self, shape: CacheShape, *, policy: str = "topk", top_k: int = 256,
+                 alpha: float = 1.5, scale: float = 1.0, delta: float = 0.1,
+                 device: Optional[torch.device] = None):
+        if policy not in ("topk", "gauss", "dense"):
+            raise ValueError("policy must be 'topk', 'gauss' or 'dense'")
+        self.shape = s = shape
+        self.policy = policy
+        self.top_k = int(top_k)
+        self.alpha = float(alpha)
+        self.scale = float(scale)
+        self.delta = float(delta)
+        dev = torch.device(device) if device is not None else torch.device("cuda")
+        self.device = dev
+        Bt, Hq, Hkv, d, mp, Np = (s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                  s.max_pages_per_seq, s.num_phys_pages)
+        gauss = policy == "gauss"
+        self.kmin = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
+        self.kmax = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
+        self.mean = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
+        self.var = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
+        self.ubg = torch.empty(Bt, Hkv, mp, dtype=torch.float32, device=dev)
+        self.ub = torch.empty(Bt, Hq, mp, dtype=torch.float32, device=dev) if gauss else None
+        self.gm = torch.empty(Bt, Hq, mp, dtype=torch.float64, device=dev) if gauss else None
+        self.gv = torch.empty(Bt, Hq, mp, dtype=torch.float64, device=dev) if gauss else None
+        self.tau_hat = torch.empty(Bt, Hq, dtype=torch.float64, device=dev) if gauss else None
+        self.sel = torch.empty(Bt, Hkv, mp, dtype=torch.int32, device=dev)
+        self.n_sel = torch.empty(Bt, Hkv, dtype=torch.int32, device=dev)
+        self.out = torch.empty(Bt, Hq, d, dtype=torch.float32, device=dev)
+        self.tau = torch.empty(Bt, Hq, dtype=torch.float32, device=dev)
+        self.n_support = torch.empty(Bt, Hq, dtype=torch.int32, device=dev)
+        self.max_sel = min(self.top_k, mp) if policy == "topk" else mp
+        ws_bytes = B.decode_workspace_bytes(s, self.max_sel)
+        self.ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    # -- metadata -----------------------------------------------------------
+    def build_meta(self, K, block_table, seq_lens, first_page=None, span: int = 0):
+        B.build_page_meta(self.shape, K, block_table, seq_lens, self.kmin, self.kmax,
+                          self.mean, self.var, first_page=first_page, span=span)
+
+    # -- one decode step ----------------------------------------------------
+    def score(self, q, block_table, seq_lens):
+        B.score_pages(self.shape, q, self.scale, self.kmin, self.kmax, block_table, seq_lens,
+                      self.ubg, ub=self.ub, mean=self.mean, var=self.var, gm=self.gm, gv=self.gv)
+
+    def select(self, seq_lens):
+        if self.policy == "topk":
+            B.select_pages(self.shape, seq_lens, B.EKV_SELECT_TOPK, self.top_k, self.alpha,
+                           self.delta, self.ubg, self.sel, self.n_sel)
+        elif self.policy == "gauss":
+            B.select_pages(self.shape, seq_lens, B.EKV_SELECT_GAUSS, self.top_k, self.alpha,
+                           self.delta, self.ubg, self.sel, self.n_sel, ub=self.ub, gm=self.gm,
+                           gv=self.gv, tau_hat=self.tau_hat)
+
+    def decode(self, q, K, V, block_table, seq_lens):
+        dense = self.policy == "dense"
+        B.entmax_decode(self.shape, q, self.scale, self.alpha, K, V, block_table, seq_lens,
+                        self.out, self.ws, sel=None if dense else self.sel,
+                        n_sel=None if dense else self.n_sel, max_sel=self.max_sel, tau=self.tau,
+                        n_support=self.n_support)
+
+    def step(self, q, K, V, block_table, seq_lens):
+        """score -> select -> decode; returns (out, tau) views of the owned buffers."""
+        if self.policy != "dense":
+            self.score(q, block_table, seq_lens)
+            self.select(seq_lens)
+        self.decode(q, K, V, block_table, seq_lens)
+        return self.out, self.tau

@@ -1,0 +1,188 @@
+"""Host-side checks of the C ABI library (no GPU needed).
+
+The library must load, export every function include/entmaxkv.h declares,
+and reject invalid arguments on the host -- before any launch -- with the
+documented status codes.  Every call below fails validation, so nothing is
+ever launched (the pointer values are never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_kv_cache_page_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "entmaxkv.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p(0x10004)  # misaligned for 16-byte arrays
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ekv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libentmaxkv.so not built")
+    return B.load_library()
+
+
+def desc(**kw):
+    d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+             max_pages_per_seq=10, num_phys_pages=20, kv_dtype=B.EKV_BF16)
+    d.update(kw)
+    return B.CacheDesc(**d)
+
+
+def test_header_declares_the_four_operations():
+    fns = declared_functions()
+    for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
+                 "ekv_entmax_decode"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    fns = declared_functions()
+    assert set(fns) == set(B.EXPORTED)
+    for name in fns:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s(ekv_\w+)", out))
+    assert set(fns) <= exported
+    # the C entry points are not C++-mangled
+    assert not any(s.startswith("_Z") and "ekv_" in s for s in exported)
+
+
+def test_status_strings(lib):
+    assert B.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, 7):
+        assert isinstance(B.status_string(s), str) and B.status_string(s)
+
+
+def test_workspace_size(lib):
+    d = desc()
+    n = lib.ekv_decode_workspace_bytes(ctypes.byref(d), 4)
+    assert n > 0 and n % 256 == 0
+    # z slots: B*Hq*max_sel*P floats at least
+    assert n >= 2 * 8 * 4 * 16 * 4
+    assert lib.ekv_decode_workspace_bytes(ctypes.byref(d), 10) >= n
+    # max_sel <= 0 or beyond maxP means maxP
+    assert lib.ekv_decode_workspace_bytes(ctypes.byref(d), 0) == \
+        lib.ekv_decode_workspace_bytes(ctypes.byref(d), 10)
+    bad = desc(head_dim=96)
+    assert lib.ekv_decode_workspace_bytes(ctypes.byref(bad), 4) == 0
+    assert lib.ekv_decode_workspace_bytes(None, 4) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), INVALID),
+    (dict(num_q_heads=6, num_kv_heads=4), INVALID),
+    (dict(num_q_heads=32, num_kv_heads=2), UNSUPPORTED),   # group of 16
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(page_size=12), UNSUPPORTED),
+    (dict(page_size=128), UNSUPPORTED),
+    (dict(kv_dtype=5), INVALID),
+    (dict(max_pages_per_seq=0), INVALID),
+])
+def test_bad_descriptor(lib, kw, status):
+    d = desc(**kw)
+    r = lib.ekv_entmax_decode(ctypes.byref(d), FAKE, 1.0, 1.5, FAKE, FAKE, FAKE, FAKE, None,
+                              None, 0, FAKE, None, None, FAKE, 1 << 30, None)
+    assert r == status
+    r = lib.ekv_build_page_meta(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None,
+                                None, None)
+    assert r == status
+
+
+def test_decode_argument_errors(lib):
+    d = desc()
+    ws_need = lib.ekv_decode_workspace_bytes(ctypes.byref(d), 0)
+
+    def call(q=FAKE, scale=1.0, alpha=1.5, K=FAKE, V=FAKE, sel=None, n_sel=None, out=FAKE,
+             ws=FAKE, ws_bytes=ws_need):
+        return lib.ekv_entmax_decode(ctypes.byref(d), q, scale, alpha, K, V, FAKE, FAKE, sel,
+                                     n_sel, 0, out, None, None, ws, ws_bytes, None)
+
+    assert call(alpha=1.0) == INVALID
+    assert call(alpha=0.5) == INVALID
+    assert call(alpha=float("nan")) == INVALID
+    assert call(alpha=float("inf")) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(scale=-1.0) == INVALID
+    assert call(q=None) == INVALID
+    assert call(K=FAKE_MIS) == INVALID
+    assert call(out=None) == INVALID
+    assert call(sel=FAKE, n_sel=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=ws_need - 1) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE   # not 256-byte aligned
+    assert lib.ekv_entmax_decode(None, FAKE, 1.0, 1.5, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                                 FAKE, None, None, FAKE, ws_need, None) == INVALID
+
+
+def test_select_argument_errors(lib):
+    d = desc()
+
+    def call(policy=0, top_k=4, alpha=1.5, delta=0.1, ub=FAKE, gm=FAKE, gv=FAKE, tau=FAKE,
+             sel=FAKE):
+        return lib.ekv_select_pages(ctypes.byref(d), FAKE, policy, top_k, alpha, delta, ub,
+                                    FAKE, gm, gv, sel, FAKE, tau, None)
+
+    assert call(top_k=0) == INVALID
+    assert call(top_k=-3) == INVALID
+    assert call(policy=7) == INVALID
+    assert call(sel=None) == INVALID
+    assert call(policy=1, alpha=1.0) == INVALID
+    assert call(policy=1, delta=-0.1) == INVALID
+    assert call(policy=1, delta=float("nan")) == INVALID
+    assert call(policy=1, alpha=1.7) == UNSUPPORTED    # gamma = 1/0.7 not an integer
+    assert call(policy=1, alpha=1.1) == UNSUPPORTED    # gamma = 10 > 4
+    assert call(policy=1, tau=None) == INVALID
+    assert call(policy=1, gm=None) == INVALID
+
+
+def test_score_argument_errors(lib):
+    d = desc()
+
+    def call(q=FAKE, scale=1.0, mean=None, var=None, gm=None, gv=None, ubg=FAKE):
+        return lib.ekv_score_pages(ctypes.byref(d), q, scale, FAKE, FAKE, mean, var, FAKE, FAKE,
+                                   None, ubg, gm, gv, None)
+
+    assert call(scale=0.0) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(q=FAKE_MIS) == INVALID
+    assert call(ubg=None) == INVALID
+    assert call(gm=FAKE, gv=None) == INVALID
+    assert call(gm=FAKE, gv=FAKE) == INVALID           # moments need mean/var
+    assert call(gm=FAKE, gv=FAKE, mean=FAKE, var=None) == INVALID
+
+
+def test_meta_argument_errors(lib):
+    d = desc()
+
+    def call(K=FAKE, kmin=FAKE, mean=None, var=None, first=None):
+        return lib.ekv_build_page_meta(ctypes.byref(d), K, FAKE, FAKE, first, 0, kmin, FAKE,
+                                       mean, var, None)
+
+    assert call(K=None) == INVALID
+    assert call(kmin=FAKE_MIS) == INVALID
+    assert call(mean=FAKE, var=None) == INVALID
+    assert call(first=ctypes.c_void_p(0x10001)) == INVALID
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    s = B.CacheShape(1, 1, 1, 64, 16, 4, 4, torch.float32)
+    with pytest.raises(ValueError):
+        B.build_page_meta(s, torch.zeros(4, 1, 16, 64), torch.zeros(1, 4, dtype=torch.int32),
+                          torch.ones(1, dtype=torch.int32), torch.zeros(4, 1, 64),
+                          torch.zeros(4, 1, 64))

@@ -1,0 +1,109 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (PagedEntmaxDecoder), on sampled (row, KV head) pairs that the
+oracle recomputes one by one, plus properties checked on every pair.
+
+Workloads (seeded, synthetic; see sparse_kv_cache_page_amd/workloads.py):
+  gqa     B8, 32q/8kv, d128, L 32768, P16, bf16, alpha 1.5, top-256
+  gauss   gqa shapes, clustered keys, alpha 2, Gaussian-aware, delta 0.1
+  ragged  B64, L ~ U[4096, 65536], permuted pool, alpha 1.5, top-512
+  stress  B32, 64q/8kv, L 131072, P32, alpha in {1.25, 1.5, 2},
+          top-512 / top-128 / Gaussian / dense, query temperature sets the
+          support size (about 16 to 4096 tokens)
+"""
+import math
+
+import pytest
+import torch
+
+from sparse_kv_cache_page_amd import binding as B
+from sparse_kv_cache_page_amd import workloads as wl
+from sparse_kv_cache_page_amd.engine import PagedEntmaxDecoder
+
+from gpu_util import cache_shape, check_pair, run_gpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def check_properties(inp, gpu, policy, top_k):
+    """Selection well-formed and outputs finite on every pair."""
+    w = inp["workload"]
+    lens = torch.tensor(inp["npages"], device=DEV)
+    if policy != "dense":
+        n_sel = gpu["n_sel"]
+        if policy == "topk":
+            assert torch.equal(n_sel, torch.minimum(lens, torch.tensor(top_k, device=DEV))[:, None]
+                               .expand_as(n_sel).to(n_sel.dtype))
+        assert bool((n_sel >= 1).all())
+        sel = gpu["sel"].cpu()
+        for b in range(w.batch):
+            for g in range(w.num_kv_heads):
+                s = sel[b, g, :int(n_sel[b, g])]
+                assert bool((s[1:] > s[:-1]).all()) and int(s[0]) >= 0
+                assert int(s[-1]) < inp["npages"][b]
+    assert bool(torch.isfinite(gpu["out"]).all())
+    assert bool(torch.isfinite(gpu["tau"]).all())
+
+
+def decoder_matches(inp, gpu, policy, alpha, top_k, delta, scale, q):
+    """The benchmark's call sequence gives bit-identical results."""
+    s = cache_shape(inp)
+    dec = PagedEntmaxDecoder(s, policy=policy, top_k=top_k, alpha=alpha, scale=scale,
+                             delta=delta)
+    dec.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
+    out, tau = dec.step(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, gpu["out"]) and torch.equal(tau, gpu["tau"])
+    if policy != "dense":
+        assert torch.equal(dec.n_sel, gpu["n_sel"])
+    return dec
+
+
+@pytest.mark.parametrize("name,pairs", [
+    ("gqa", [(0, 0), (3, 5), (7, 7)]),
+    ("gauss", [(0, 0), (5, 3)]),
+    ("ragged", [(0, 0), (17, 4), (63, 7)]),
+])
+def test_fullsize_config(name, pairs):
+    w = wl.CONFIGS[name]
+    print(f"[fullsize] {name}: generating", flush=True)
+    inp = wl.make_inputs(w, device=DEV)
+    pol = w.policy
+    gpu = run_gpu(inp, pol)
+    check_properties(inp, gpu, pol, w.top_k)
+    for b, g in pairs:
+        print(f"[fullsize] {name}: oracle pair b{b} g{g}", flush=True)
+        check_pair(inp, gpu, b, g, pol)
+    decoder_matches(inp, gpu, pol, w.alpha, w.top_k, w.delta, w.scale, inp["q"])
+
+
+@pytest.fixture(scope="module")
+def stress_inputs():
+    w = wl.CONFIGS["stress"]
+    print("[fullsize] stress: generating 16 GiB of K/V", flush=True)
+    inp = wl.make_inputs(w, device=DEV)
+    yield inp
+    del inp
+    torch.cuda.empty_cache()
+
+
+STRESS_CASES = [
+    (1.25, 0, "topk", 512), (1.25, 1, "topk", 128), (1.25, 2, "dense", 0),
+    (1.5, 0, "gauss", 0), (1.5, 1, "topk", 512), (1.5, 2, "topk", 128),
+    (2.0, 0, "dense", 0), (2.0, 1, "gauss", 0), (2.0, 2, "topk", 512),
+]
+
+
+@pytest.mark.parametrize("alpha,ti,policy,top_k", STRESS_CASES)
+def test_fullsize_stress(stress_inputs, alpha, ti, policy, top_k):
+    inp = stress_inputs
+    w = wl.variant("stress", alpha=alpha, policy=policy, top_k=top_k or 512, delta=0.1,
+                   q_std=wl.STRESS_TEMPERATURE[alpha][ti] / math.sqrt(128))
+    inp = dict(inp, workload=w)
+    q = wl.fresh_query(w, inp, seed=5005 + 10 * ti + int(alpha * 100))
+    inp["q"] = q
+    print(f"[fullsize] stress alpha={alpha} T#{ti} {policy} k={top_k}", flush=True)
+    gpu = run_gpu(inp, policy, top_k=w.top_k)
+    check_properties(inp, gpu, policy, w.top_k)
+    check_pair(inp, gpu, 0, 0, policy, top_k=w.top_k, check_meta=(ti == 0 and alpha == 1.25))
+    check_pair(inp, gpu, 31, 7, policy, top_k=w.top_k, check_meta=False)

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases that the oracle finishes in seconds, spanning several workgroup
+tiles and ragged tails, over every supported dtype / head_dim / group size /
+page size and both selection policies, plus the degenerate cases of the
+method.  Full-size workloads are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pipeline
+from sparse_kv_cache_page_amd import binding as B
+from sparse_kv_cache_page_amd import workloads as wl
+
+from gpu_util import check_pair, run_gpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def small(seed, **kw):
+    base = dict(name="small", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                page_size=16, lens_range=(37, 1500), kv_dtype="bf16",
+                q_std=2.0 / np.sqrt(128), scale=1.0, alpha=1.5, policy="topk", top_k=9,
+                planted_per_kv_head=8, permute_pool=True, seed=seed)
+    base.update(kw)
+    return wl.Workload(**base)
+
+
+def all_pairs(w):
+    return [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+
+
+def test_tiny_config_full_pipeline():
+    w = wl.CONFIGS["tiny"]
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "topk")
+    ref = check_pair(inp, gpu, 0, 0, "topk")
+    assert len(ref["sel"]) == 32
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("heads", [(4, 4), (4, 2), (8, 2), (16, 2)])
+def test_topk_shapes(kv_dtype, head_dim, heads):
+    Hq, Hkv = heads
+    w = small(11 + head_dim + Hq, kv_dtype=kv_dtype, head_dim=head_dim, num_q_heads=Hq,
+              num_kv_heads=Hkv, q_std=2.0 / np.sqrt(head_dim))
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "topk")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "topk")
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 8, 32, 64])
+def test_topk_page_sizes(page_size):
+    w = small(31 + page_size, page_size=page_size, lens_range=(5, 900),
+              top_k=max(1, 150 // page_size))
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "topk")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "topk")
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0, 1.1])
+def test_alpha_values(alpha):
+    w = small(41, alpha=alpha, planted_per_kv_head=4)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "topk")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "topk")
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_dense_all_pages(alpha):
+    w = small(51, alpha=alpha, lens_range=(200, 3000))
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "dense")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "dense")
+
+
+def test_caller_page_list():
+    # decode over an explicit random page list (no selection stage)
+    w = small(61, lens_range=(300, 2500))
+    inp = wl.make_inputs(w, device=DEV)
+    rng = np.random.default_rng(5)
+    mp = inp["max_pages"]
+    sel = np.full((w.batch, w.num_kv_heads, mp), -1, np.int32)
+    nsel = np.zeros((w.batch, w.num_kv_heads), np.int32)
+    lists = {}
+    for b, g in all_pairs(w):
+        n = inp["npages"][b]
+        pick = sorted(rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False).tolist())
+        sel[b, g, :len(pick)] = pick
+        nsel[b, g] = len(pick)
+        lists[(b, g)] = pick
+    gpu = run_gpu(inp, "topk", sel=torch.tensor(sel, device=DEV),
+                  n_sel=torch.tensor(nsel, device=DEV))
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "topk", sel_override=lists[(b, g)])
+
+
+@pytest.mark.parametrize("alpha", [2.0, 1.5, 1.25])
+def test_gauss_policy(alpha):
+    w = small(71, alpha=alpha, policy="gauss", clusters=16, planted_per_kv_head=0,
+              lens_range=(100, 1200), delta=0.1)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "gauss")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "gauss")
+
+
+def test_gauss_guard_keeps_argmax():
+    # every page holds 8 zero keys and 8 copies of e_0, so u = m + sigma exactly
+    # for every head; with ~40 such pages per row the Gaussian estimate tau-hat
+    # lies above every (alpha-1) u and nothing clears the bar: the guard keeps
+    # the largest bound, and since all bounds tie, page 0
+    w = small(81, alpha=2.0, policy="gauss", planted_per_kv_head=0, lens_range=(600, 700),
+              delta=0.0)
+    inp = wl.make_inputs(w, device=DEV)
+    K = inp["K"]
+    K.zero_()
+    K[:, :, 8:, 0] = 1.0
+    gpu = run_gpu(inp, "gauss")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "gauss")
+        assert int(gpu["n_sel"][b, g]) == 1 and int(gpu["sel"][b, g, 0]) == 0
+
+
+def test_edge_single_token_rows():
+    w = small(91, lens_range=None, seq_len=1, batch=2, top_k=3)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "topk")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "topk")
+        assert float(gpu["tau"][b, 0]) == pytest.approx(
+            float(0.5 * w.scale * (pipeline.widen(inp["q"][b, 0]) @
+                                   pipeline.widen(inp["K"][inp["block_table"][b, 0].long(), 0, 0])) - 1),
+            abs=1e-5)
+
+
+def test_edge_topk_covers_all_and_one():
+    for k in (1, 10_000):
+        w = small(101 + k, top_k=k)
+        inp = wl.make_inputs(w, device=DEV)
+        gpu = run_gpu(inp, "topk")
+        for b, g in all_pairs(w):
+            check_pair(inp, gpu, b, g, "topk")
+            n = inp["npages"][b]
+            assert int(gpu["n_sel"][b, g]) == min(k, n)
+
+
+def test_edge_ties_shared_pages_constant_keys():
+    # rows 0 and 1 share every physical page and the query; page 5 carries a
+    # planted key and is copied onto pages 0, 3, 6, ... so 15 pages tie for the
+    # largest bound (the tie rule, lowest index, decides the top-7); page 7
+    # holds one constant key (zero variance) for the Gaussian branch
+    for pol in ("topk", "gauss"):
+        w = small(111, batch=2, lens_range=None, seq_len=16 * 40, permute_pool=False,
+                  planted_per_kv_head=0, top_k=7, policy=pol)
+        inp = wl.make_inputs(w, device=DEV)
+        bt = inp["block_table"].clone()
+        bt[1] = bt[0]
+        inp["block_table"] = bt
+        q = inp["q"]
+        q[1] = q[0]
+        K = inp["K"]
+        G = w.group
+        src = int(bt[0, 5])
+        for g in range(w.num_kv_heads):
+            K[src, g, 0] = (3.0 * q[0, g * G] / w.q_std).to(K.dtype)
+        for p in range(0, 40, 3):
+            K[int(bt[0, p])] = K[src]
+        c = int(bt[0, 7])
+        K[c] = K[c][:, :1, :].expand(-1, w.page_size, -1).clone()
+        gpu = run_gpu(inp, pol)
+        for b, g in all_pairs(w):
+            check_pair(inp, gpu, b, g, pol)
+        assert torch.equal(gpu["sel"][0], gpu["sel"][1])
+        assert torch.equal(gpu["out"][0], gpu["out"][1])
+        if pol == "topk":
+            assert gpu["sel"][0, 0, :7].tolist() == [0, 3, 5, 6, 9, 12, 15]
+
+
+def test_max_sel_too_small_flags_nan():
+    w = small(121, top_k=20, lens_range=(400, 900))
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "topk")
+    s = B.CacheShape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                     inp["max_pages"], inp["num_phys_pages"], torch.bfloat16)
+    out = torch.zeros_like(gpu["out"])
+    ws = torch.empty(B.decode_workspace_bytes(s, 5), dtype=torch.uint8, device=DEV)
+    B.entmax_decode(s, inp["q"], w.scale, w.alpha, inp["K"], inp["V"], inp["block_table"],
+                    inp["seq_lens"], out, ws, sel=gpu["sel"], n_sel=gpu["n_sel"], max_sel=5)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+
+
+def test_refresh_last_page_matches_full_build():
+    # append tokens to every row, refresh only the last page, compare with a
+    # from-scratch build
+    w = small(131, lens_range=(40, 700), planted_per_kv_head=0)
+    inp = wl.make_inputs(w, device=DEV)
+    s = B.CacheShape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                     inp["max_pages"], inp["num_phys_pages"], torch.bfloat16)
+    lens = torch.tensor([L - 3 for L in inp["lens"]], dtype=torch.int32, device=DEV)
+    mk = lambda: [torch.zeros(s.num_phys_pages, s.num_kv_heads, s.head_dim, dtype=t, device=DEV)
+                  for t in (torch.bfloat16, torch.bfloat16, torch.float32, torch.float32)]
+    a = mk()
+    B.build_page_meta(s, inp["K"], inp["block_table"], lens, *a)
+    # three decode steps append one token each; refresh the page holding it
+    P = w.page_size
+    for _ in range(3):
+        lens += 1
+        last = ((lens + P - 1) // P - 1).to(torch.int32)
+        B.build_page_meta(s, inp["K"], inp["block_table"], lens, *a, first_page=last, span=1)
+    b_ = mk()
+    B.build_page_meta(s, inp["K"], inp["block_table"], lens, *b_)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b_):
+        assert torch.equal(x, y)
+
+
+def test_deterministic_repeat():
+    w = small(141, lens_range=(500, 2000))
+    inp = wl.make_inputs(w, device=DEV)
+    g1 = run_gpu(inp, "topk")
+    g2 = run_gpu(inp, "topk")
+    for k in ("ubg", "sel", "n_sel", "out", "tau"):
+        assert torch.equal(g1[k], g2[k]), k
