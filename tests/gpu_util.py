@@ -8,7 +8,9 @@ Tolerances (GPU vs oracle, same input bits):
                         rounded once; the oracle rounds the exact sum)
   sel, n_sel           bit-exact
   tau-hat              <= 1e-12 relative (both fp64; different root finders)
-  tau (entmax)         <= 1e-5 absolute, z-space
+  tau (entmax)         <= 1e-5 absolute, z-space (or 4 fp32 ulps of |tau|
+                        when larger: above |tau| ~ 40 fp32 scores cannot
+                        resolve 1e-5)
   out                  relative L2 <= 1e-3 per query head
 """
 from __future__ import annotations
@@ -20,6 +22,7 @@ from oracle import pipeline
 from sparse_kv_cache_page_amd import binding as B
 
 TAU_TOL = 1e-5
+TAU_TOL_REL = 4.0 * 2.0 ** -24
 OUT_TOL = 1e-3
 TAU_HAT_RTOL = 1e-12
 
@@ -133,7 +136,8 @@ def check_pair(inp, gpu, b, g, policy, *, alpha=None, top_k=None, delta=None, sc
         got = gpu["sel"][b, g, :ns].cpu().tolist()
         assert got == list(ref["sel"]), f"sel b{b} g{g}: gpu {got[:12]}.. vs {ref['sel'][:12]}.."
     tau = gpu["tau"][b, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(tau - ref["tau"]) <= TAU_TOL), \
+    tol = np.maximum(TAU_TOL, TAU_TOL_REL * np.abs(ref["tau"]))
+    assert np.all(np.abs(tau - ref["tau"]) <= tol), \
         f"tau b{b} g{g}: {tau} vs {ref['tau']} (diff {np.abs(tau - ref['tau']).max():.3e})"
     out = gpu["out"][b, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
     for h in range(G):
