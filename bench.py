@@ -28,7 +28,8 @@ import time
 
 HBM_PEAK_GBPS = 8000.0
 ENTRY_POINT = {"refresh": "ekv_build_page_meta", "score": "ekv_score_pages",
-               "select": "ekv_select_pages", "decode": "ekv_entmax_decode"}
+               "select": "ekv_select_pages", "decode": "ekv_entmax_decode",
+               "score_select": "ekv_score_select_pages"}
 METRIC = "decode steps/s + effective KV GB/s (fraction of HBM peak), batch×ctx sweep"
 
 
@@ -48,6 +49,9 @@ def parse():
     ap.add_argument("--top-k", type=int, default=None)
     ap.add_argument("--temperature", type=float, default=None,
                     help="query std * sqrt(d) (stress workload)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference for "
+                         "HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -66,12 +70,26 @@ class Layer:
                                 inp["max_pages"], inp["num_phys_pages"],
                                 torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32)
         self.dec = PagedEntmaxDecoder(self.shape, policy=w.policy, top_k=w.top_k,
-                                      alpha=w.alpha, scale=w.scale, delta=w.delta, device=dev)
+                                      alpha=w.alpha, scale=w.scale, delta=w.delta, device=dev,
+                                      fused=w.policy == "topk")
         self.dec.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
         self.last_page = torch.tensor([n - 1 for n in inp["npages"]], dtype=torch.int32,
                                       device=dev)
 
-    # the four calls of one step, separately so they can be timed one by one
+    # the calls of one step, separately so they can be timed one by one
+    @property
+    def stages(self):
+        if self.w.policy == "topk":
+            return ["score_select", "decode"]
+        if self.w.policy == "dense":
+            return ["refresh", "decode"]
+        return ["refresh", "score", "select", "decode"]
+
+    def score_select(self):
+        i = self.inp
+        self.dec.score_select(i["q"], i["K"], i["block_table"], i["seq_lens"],
+                              refresh_last_page=True)
+
     def refresh(self):
         i = self.inp
         self.dec.build_meta(i["K"], i["block_table"], i["seq_lens"], first_page=self.last_page,
@@ -89,11 +107,8 @@ class Layer:
         self.dec.decode(i["q"], i["K"], i["V"], i["block_table"], i["seq_lens"])
 
     def step(self):
-        self.refresh()
-        if self.w.policy != "dense":
-            self.score()
-            self.select()
-        self.decode()
+        for n in self.stages:
+            getattr(self, n)()
 
 
 def stage_bytes(layer):
@@ -138,6 +153,7 @@ def stage_bytes(layer):
     full = sum(lens) * Hkv * d * e * 2
     return dict(refresh=refresh, score=score if w.policy != "dense" else 0,
                 select=select if w.policy != "dense" else 0, decode=decode,
+                score_select=refresh + score + select,
                 kv_bytes=refresh + (pages * meta_pp if w.policy != "dense" else 0) + decode,
                 full_cache=full, k_tokens=ktok, v_rows=vrows)
 
@@ -188,7 +204,7 @@ def time_steps(layers, steps, warmup, graph):
 def time_stages(layers, steps, policy):
     """Average duration (ms) of each entry point, HIP events on the launch stream."""
     import torch
-    names = ["refresh", "decode"] if policy == "dense" else ["refresh", "score", "select", "decode"]
+    names = layers[0].stages
     R = len(layers)
     acc = {n: 0.0 for n in names}
     evs = []
@@ -340,6 +356,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}))
+        return
     from sparse_kv_cache_page_amd import binding
     binding.load_library()
     dev = torch.device("cuda:0")

@@ -177,6 +177,53 @@ ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float s
                              float* out, float* tau_out, int32_t* n_support, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Fused first half of a decode step with the top-k policy (§2.A + §2.B(1)):
+ * the same results as
+ *   ekv_build_page_meta(first_page = last page of each row, span = 1,
+ *                       mean = var = NULL)          [only if refresh_last_page]
+ *   ekv_score_pages(ub = NULL, gm = gv = NULL)  ->  ekv_select_pages(TOPK, top_k)
+ * in one launch: each workgroup scores a slice of one (row, KV head)'s pages
+ * (the one holding the row's last page first rebuilds that page's bounding
+ * box), and the last workgroup to finish a (row, KV head) runs its top-k over
+ * the bounds it finds in L2.  kmin/kmax are read (and, for the refreshed page,
+ * written); mean/var are not maintained by this call.
+ * ws / ws_bytes: at least ekv_score_select_workspace_bytes(desc) bytes of
+ *   arrival counters, 256-byte aligned, ZERO-FILLED before first use; every
+ *   completed call leaves them zero, so the workspace can be reused (and the
+ *   call captured in a graph) without clearing.  Calls sharing a workspace
+ *   must not overlap.
+ * With refresh_last_page set, a row's last page must not be referenced by
+ * another row (it is rebuilt while other rows are being scored).
+ */
+ekv_status ekv_score_select_pages(const ekv_cache_desc* desc, const float* q, float scale,
+                                  const void* K, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t refresh_last_page,
+                                  int32_t top_k, void* kmin, void* kmax, float* ubg,
+                                  int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* Counter bytes ekv_score_select_pages needs (0 if desc is invalid). */
+size_t ekv_score_select_workspace_bytes(const ekv_cache_desc* desc);
+
+/*
+ * One whole decode step with the top-k policy (the pipeline of §2: scoring
+ * from page metadata, candidate selection, sparse entmax over the selected
+ * pages): ekv_score_select_pages followed by ekv_entmax_decode(sel, n_sel,
+ * max_sel = min(top_k, max_pages_per_seq)), sharing one workspace of
+ * ekv_step_workspace_bytes(desc, top_k) bytes (zero-filled before first use,
+ * reusable afterwards, as for ekv_score_select_pages).
+ */
+ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
+                           const void* K, const void* V, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t refresh_last_page, int32_t top_k,
+                           void* kmin, void* kmax, float* ubg, int32_t* sel, int32_t* n_sel,
+                           float* out, float* tau_out, int32_t* n_support, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Scratch bytes ekv_decode_step needs (0 if desc is invalid or top_k < 1). */
+size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k);
+
 /* Scratch bytes ekv_entmax_decode needs for this cache shape and max_sel
  * (0 if desc is invalid). */
 size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);

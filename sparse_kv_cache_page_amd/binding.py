@@ -27,6 +27,10 @@ EXPORTED = (
     "ekv_select_pages",
     "ekv_entmax_decode",
     "ekv_decode_workspace_bytes",
+    "ekv_score_select_pages",
+    "ekv_score_select_workspace_bytes",
+    "ekv_decode_step",
+    "ekv_step_workspace_bytes",
     "ekv_status_string",
 )
 
@@ -70,12 +74,20 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_select_pages.argtypes = [dp, vp, i32, i32, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ekv_entmax_decode.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                       vp, sz, vp]
+    lib.ekv_decode_step.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
+                                    vp, vp, vp, vp, sz, vp]
+    lib.ekv_score_select_pages.argtypes = [dp, vp, f32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
+                                           vp, sz, vp]
+    lib.ekv_score_select_workspace_bytes.argtypes = [dp]
+    lib.ekv_score_select_workspace_bytes.restype = sz
+    lib.ekv_step_workspace_bytes.argtypes = [dp, i32]
+    lib.ekv_step_workspace_bytes.restype = sz
     lib.ekv_decode_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_decode_workspace_bytes.restype = sz
     lib.ekv_status_string.argtypes = [ctypes.c_int]
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
-                 "ekv_entmax_decode"):
+                 "ekv_entmax_decode", "ekv_decode_step", "ekv_score_select_pages"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -232,3 +244,77 @@ def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_tabl
         ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
         _ptr(block_table), _ptr(seq_lens), _ptr(sel), _ptr(n_sel), int(max_sel), _ptr(out),
         _ptr(tau), _ptr(n_support), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+
+
+def step_workspace_bytes(s: CacheShape, top_k: int) -> int:
+    d = s.desc()
+    return int(load_library().ekv_step_workspace_bytes(ctypes.byref(d), int(top_k)))
+
+
+def decode_step(s: CacheShape, q, scale: float, alpha: float, K, V, block_table, seq_lens,
+                top_k: int, kmin, kmax, ubg, sel, n_sel, out, ws, refresh_last_page: bool = False,
+                tau=None, n_support=None):
+    """ekv_decode_step: [last-page refresh] + score + top-k + entmax decode, two launches.
+
+    `ws` must be a uint8 GPU tensor of step_workspace_bytes() bytes, zero-filled
+    before its first use (torch.zeros); every call leaves it reusable.
+    """
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(V, "V", s.kv_dtype, _kv_shape(s))
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    mshape = (s.num_phys_pages, Hkv, d)
+    _need(kmin, "kmin", s.kv_dtype, mshape)
+    _need(kmax, "kmax", s.kv_dtype, mshape)
+    _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
+    _need(sel, "sel", torch.int32, (B, Hkv, mp))
+    _need(n_sel, "n_sel", torch.int32, (B, Hkv))
+    _need(out, "out", torch.float32, (B, Hq, d))
+    if tau is not None:
+        _need(tau, "tau", torch.float32, (B, Hq))
+    if n_support is not None:
+        _need(n_support, "n_support", torch.int32, (B, Hq))
+    if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.dtype == torch.uint8
+            and ws.is_contiguous()):
+        raise TypeError("ws must be a contiguous uint8 GPU tensor")
+    d_ = s.desc()
+    _check("ekv_decode_step", load_library().ekv_decode_step(
+        ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
+        _ptr(block_table), _ptr(seq_lens), int(bool(refresh_last_page)), int(top_k), _ptr(kmin),
+        _ptr(kmax), _ptr(ubg), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(tau), _ptr(n_support),
+        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+
+
+def score_select_workspace_bytes(s: CacheShape) -> int:
+    d = s.desc()
+    return int(load_library().ekv_score_select_workspace_bytes(ctypes.byref(d)))
+
+
+def score_select_pages(s: CacheShape, q, scale: float, K, block_table, seq_lens, top_k: int,
+                       kmin, kmax, ubg, sel, n_sel, ws, refresh_last_page: bool = False):
+    """ekv_score_select_pages: [last-page refresh] + scores + top-k in one launch.
+
+    `ws`: uint8 GPU tensor of score_select_workspace_bytes() bytes, zero-filled
+    before first use (torch.zeros); every call leaves it reusable.
+    """
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    mshape = (s.num_phys_pages, Hkv, d)
+    _need(kmin, "kmin", s.kv_dtype, mshape)
+    _need(kmax, "kmax", s.kv_dtype, mshape)
+    _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
+    _need(sel, "sel", torch.int32, (B, Hkv, mp))
+    _need(n_sel, "n_sel", torch.int32, (B, Hkv))
+    if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.dtype == torch.uint8
+            and ws.is_contiguous()):
+        raise TypeError("ws must be a contiguous uint8 GPU tensor")
+    d_ = s.desc()
+    _check("ekv_score_select_pages", load_library().ekv_score_select_pages(
+        ctypes.byref(d_), _ptr(q), float(scale), _ptr(K), _ptr(block_table), _ptr(seq_lens),
+        int(bool(refresh_last_page)), int(top_k), _ptr(kmin), _ptr(kmax), _ptr(ubg), _ptr(sel),
+        _ptr(n_sel), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))

@@ -134,6 +134,7 @@ size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel) {
   Shape s;
   if (make_shape(desc, &s) != EKV_OK) return 0;
   if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return 0;
   return ekv::make_decode_plan(s, max_sel).total;
 }
 
@@ -156,10 +157,78 @@ ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float s
   if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
   if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
   const ekv::DecodePlan plan = ekv::make_decode_plan(s, max_sel);
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < plan.total) return EKV_ERR_WORKSPACE;
   return from_hip(ekv::launch_decode(s, plan, q, scale, alpha, K, V, block_table, seq_lens, sel,
                                      n_sel, out, tau_out, n_support, ws, stream));
+}
+
+// Arrival counters of the fused score + select launch: B*Hkv ints, zero
+// between calls.
+static size_t step_counter_bytes(const Shape& s) {
+  return (((size_t)s.B * s.Hkv * sizeof(int)) + 255) & ~(size_t)255;
+}
+
+size_t ekv_score_select_workspace_bytes(const ekv_cache_desc* desc) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK) return 0;
+  return step_counter_bytes(s);
+}
+
+ekv_status ekv_score_select_pages(const ekv_cache_desc* desc, const float* q, float scale,
+                                  const void* K, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t refresh_last_page,
+                                  int32_t top_k, void* kmin, void* kmax, float* ubg,
+                                  int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(q) || !ok_vec(K) || !ok_i32(block_table) || !ok_i32(seq_lens) || !ok_vec(kmin) ||
+      !ok_vec(kmax) || !ok_i32(ubg) || !ok_i32(sel) || !ok_i32(n_sel))
+    return EKV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
+  if (top_k < 1) return EKV_ERR_INVALID_ARG;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < step_counter_bytes(s))
+    return EKV_ERR_WORKSPACE;
+  return from_hip(ekv::launch_score_select(s, q, scale, K, kmin, kmax, block_table, seq_lens,
+                                           refresh_last_page ? 1 : 0, ubg, top_k, sel, n_sel,
+                                           (int*)ws, stream));
+}
+
+size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK || top_k < 1) return 0;
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return 0;
+  return step_counter_bytes(s) + ekv::make_decode_plan(s, max_sel).total;
+}
+
+ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
+                           const void* K, const void* V, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t refresh_last_page, int32_t top_k,
+                           void* kmin, void* kmax, float* ubg, int32_t* sel, int32_t* n_sel,
+                           float* out, float* tau_out, int32_t* n_support, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(V) || !ok_vec(out)) return EKV_ERR_INVALID_ARG;
+  if (tau_out != nullptr && !aligned(tau_out, 4)) return EKV_ERR_INVALID_ARG;
+  if (n_support != nullptr && !aligned(n_support, 4)) return EKV_ERR_INVALID_ARG;
+  if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
+  if (top_k < 1) return EKV_ERR_INVALID_ARG;
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
+  const size_t cbytes = step_counter_bytes(s);
+  const size_t dbytes = ekv::make_decode_plan(s, max_sel).total;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < cbytes + dbytes) return EKV_ERR_WORKSPACE;
+  st = ekv_score_select_pages(desc, q, scale, K, block_table, seq_lens, refresh_last_page, top_k,
+                              kmin, kmax, ubg, sel, n_sel, ws, cbytes, stream);
+  if (st != EKV_OK) return st;
+  return ekv_entmax_decode(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel,
+                           max_sel, out, tau_out, n_support, (char*)ws + cbytes, dbytes, stream);
 }
 
 }  // extern "C"

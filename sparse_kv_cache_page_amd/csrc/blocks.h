@@ -1,0 +1,432 @@
+// Workgroup-level building blocks shared by the select kernels and the fused
+// decode-step kernels (256-thread workgroups, wave64).
+#pragma once
+
+#include "common.h"
+
+namespace ekv {
+
+constexpr int kBlk = 256;
+constexpr int kTopkLdsKeys = 16384;  // 64 KiB of LDS keys; longer rows read U from global
+
+// Inclusive prefix sum over a 256-thread block; `sh` holds 4 ints of LDS.
+__device__ __forceinline__ int block_incl_scan(int x, int* sh) {
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) sh[w] = x;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += sh[i];
+  __syncthreads();
+  return x + add;
+}
+
+// fp32 -> uint32 with the same order (-0 folded onto +0 so they tie).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  if (x == 0.0f) x = 0.0f;
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// LDS scratch of one top-k selection (keys of rows up to kCap pages).
+template <int kCap = kTopkLdsKeys>
+struct alignas(16) TopkLds {
+  static constexpr int kKeyCap = kCap;
+  uint32_t keys[kCap];
+  int hist[2048];
+  int scan_sh[4];
+  int s_digit, s_above, s_cnt;
+};
+
+// Top-k pages of one (row, KV head): the min(k, n) largest bounds U[0..n),
+// ties to the lower page index, written ascending to out[0..k).  k < n.
+// Called by all 256 threads of the workgroup.
+// kCoherentU: U was written by other workgroups of the same launch with
+// device-coherent stores; read it with device-coherent loads.
+template <bool kLds, bool kCoherentU, typename Lds>
+__device__ __forceinline__ void topk_block(const float* __restrict__ U, int n, int k,
+                                           int32_t* __restrict__ out, Lds& sm) {
+  uint32_t* keys = sm.keys;
+  int* hist = sm.hist;
+  int* scan_sh = sm.scan_sh;
+  int& s_digit = sm.s_digit;
+  int& s_above = sm.s_above;
+  int& s_cnt = sm.s_cnt;
+  constexpr int kSelBlock = kBlk;
+  auto load_u = [&](int p) -> float {
+    if constexpr (kCoherentU)
+      return __hip_atomic_load(U + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      return U[p];
+  };
+  if constexpr (kLds) {
+    for (int p = threadIdx.x; p < n; p += kSelBlock) keys[p] = order_key(load_u(p));
+    __syncthreads();
+  }
+  auto key_of = [&](int p) -> uint32_t {
+    if constexpr (kLds) return keys[p];
+    else return order_key(load_u(p));
+  };
+
+  // radix select of the k-th largest key over the keys' actual range [lo, hi]:
+  // each pass splits the current range into <= 2048 bins of 2^shift keys (so
+  // nearly equal bounds do not pile into one LDS counter), picks the bin that
+  // holds the k-th largest key and narrows [lo, hi] to it
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+  for (int p = threadIdx.x; p < n; p += kSelBlock) {
+    const uint32_t key = key_of(p);
+    kmn = min(kmn, key);
+    kmx = max(kmx, key);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, kWave));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, kWave));
+  }
+  if (threadIdx.x % kWave == 0) {
+    hist[threadIdx.x / kWave] = (int)kmn;
+    hist[4 + threadIdx.x / kWave] = (int)kmx;
+  }
+  __syncthreads();
+  uint32_t lo = min(min((uint32_t)hist[0], (uint32_t)hist[1]), min((uint32_t)hist[2], (uint32_t)hist[3]));
+  uint32_t hi = max(max((uint32_t)hist[4], (uint32_t)hist[5]), max((uint32_t)hist[6], (uint32_t)hist[7]));
+  __syncthreads();
+  int remaining = k;
+  bool cut = false;  // every key >= lo is selected
+  for (int pass = 0; pass < 4; ++pass) {
+    const uint32_t span = hi - lo;
+    const int width = span == 0u ? 0 : 32 - __clz((int)span);
+    const int shift = width > 11 ? width - 11 : 0;
+    for (int i = threadIdx.x; i < 2048; i += kSelBlock) hist[i] = 0;
+    __syncthreads();
+    for (int p = threadIdx.x; p < n; p += kSelBlock) {
+      const uint32_t key = key_of(p);
+      if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1);
+    }
+    __syncthreads();
+    // thread t owns digits 2047-8t down to 2040-8t
+    const int dhi = 2047 - threadIdx.x * 8;
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) local += hist[dhi - i];
+    const int incl = block_incl_scan(local, scan_sh);
+    const int excl = incl - local;
+    if (excl < remaining && remaining <= incl) {
+      int acc = excl;
+      for (int i = 0; i < 8; ++i) {
+        const int hcount = hist[dhi - i];
+        if (acc + hcount >= remaining) {
+          s_digit = dhi - i;
+          s_above = acc;
+          s_cnt = hcount;
+          break;
+        }
+        acc += hcount;
+      }
+    }
+    __syncthreads();
+    const uint32_t nlo = lo + ((uint32_t)s_digit << shift);
+    const uint32_t top = shift == 0 ? nlo : nlo + ((1u << shift) - 1u);
+    hi = top < hi ? top : hi;
+    lo = nlo;
+    remaining -= s_above;
+    cut = (s_cnt == remaining);
+    __syncthreads();
+    if (cut || shift == 0) break;
+  }
+  // selected: key > T, or key == T among the first `remaining` such pages;
+  // with `cut`, every key >= T is selected
+  const uint32_t T = lo;
+  const int chunk = (n + kSelBlock - 1) / kSelBlock;
+  const int p0 = threadIdx.x * chunk;
+  const int p1 = min(n, p0 + chunk);
+  int cg = 0, ce = 0;
+  for (int p = p0; p < p1; ++p) {
+    const uint32_t key = key_of(p);
+    if (cut ? key >= T : key > T) ++cg;
+    else if (!cut && key == T) ++ce;
+  }
+  const int gt_incl = block_incl_scan(cg, scan_sh);
+  const int eq_incl = block_incl_scan(ce, scan_sh);
+  int eq_seen = eq_incl - ce;
+  int pos = (gt_incl - cg) + min(eq_seen, remaining);
+  for (int p = p0; p < p1; ++p) {
+    const uint32_t key = key_of(p);
+    if (cut ? key >= T : key > T) {
+      out[pos++] = p;
+    } else if (!cut && key == T) {
+      if (eq_seen < remaining) out[pos++] = p;
+      ++eq_seen;
+    }
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Workgroup top-k with the keys in registers (kPerThread consecutive pages per
+// thread, n <= 256 * kPerThread, k < n): range-adaptive radix passes over a
+// double-buffered LDS histogram (the next pass's buffer is cleared while the
+// current one is read), three barriers per pass, and one ordered placement.
+struct alignas(16) TopkRegLds {
+  int hist[2][2048];
+  int wsum[4];
+  int wsum2[4];
+  uint32_t mm[8];
+  int s_digit, s_above, s_cnt;
+};
+
+template <int kPerThread, bool kCoherentU>
+__device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int n, int k,
+                                               int32_t* __restrict__ out, TopkRegLds& sm) {
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int p0 = tid * kPerThread;
+  const int nv = max(0, min(kPerThread, n - p0));
+  uint32_t key[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    float u = 0.0f;
+    if (i < nv) {
+      if constexpr (kCoherentU)
+        u = __hip_atomic_load(U + p0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        u = U[p0 + i];
+    }
+    key[i] = order_key(u);
+  }
+  // clear both histogram buffers; min / max of the keys
+  for (int i = tid; i < 2 * 2048; i += kBlk) (&sm.hist[0][0])[i] = 0;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (i < nv) {
+      kmn = min(kmn, key[i]);
+      kmx = max(kmx, key[i]);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, kWave));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, kWave));
+  }
+  if (lane == 0) {
+    sm.mm[wave] = kmn;
+    sm.mm[4 + wave] = kmx;
+  }
+  __syncthreads();
+  uint32_t lo = min(min(sm.mm[0], sm.mm[1]), min(sm.mm[2], sm.mm[3]));
+  uint32_t hi = max(max(sm.mm[4], sm.mm[5]), max(sm.mm[6], sm.mm[7]));
+  int remaining = k;
+  bool cut = false;
+  for (int pass = 0; pass < 4; ++pass) {
+    int* hist = sm.hist[pass & 1];
+    int* next = sm.hist[(pass + 1) & 1];
+    const uint32_t span = hi - lo;
+    const int width = span == 0u ? 0 : 32 - __clz((int)span);
+    const int shift = width > 11 ? width - 11 : 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      if (i < nv && key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> shift], 1);
+    __syncthreads();                                     // (1) histogram complete
+    // thread t owns digits 2047-8t .. 2040-8t; clear the other buffer meanwhile
+    const int4* h4 = reinterpret_cast<const int4*>(hist + 2040 - 8 * tid);
+    const int4 a = h4[0], b = h4[1];
+    const int bins[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};  // bins[7] = highest digit
+    reinterpret_cast<int4*>(next + 2040 - 8 * tid)[0] = make_int4(0, 0, 0, 0);
+    reinterpret_cast<int4*>(next + 2040 - 8 * tid)[1] = make_int4(0, 0, 0, 0);
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) local += bins[i];
+    int incl = wave_incl_scan(local);
+    if (lane == kWave - 1) sm.wsum[wave] = incl;
+    __syncthreads();                                     // (2) wave totals
+    for (int w = 0; w < wave; ++w) incl += sm.wsum[w];
+    const int excl = incl - local;
+    if (excl < remaining && remaining <= incl) {
+      int acc = excl;
+      bool found = false;
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        if (!found && acc + bins[i] >= remaining) {
+          sm.s_digit = 2040 - 8 * tid + i;
+          sm.s_above = acc;
+          sm.s_cnt = bins[i];
+          found = true;
+        }
+        if (!found) acc += bins[i];
+      }
+    }
+    __syncthreads();                                     // (3) chosen bin
+    const int digit = sm.s_digit, above = sm.s_above, cnt = sm.s_cnt;
+    const uint32_t nlo = lo + ((uint32_t)digit << shift);
+    const uint32_t top = shift == 0 ? nlo : nlo + ((1u << shift) - 1u);
+    hi = top < hi ? top : hi;
+    lo = nlo;
+    remaining -= above;
+    cut = (cnt == remaining);
+    if (cut || shift == 0) break;
+  }
+  // ordered placement: every key > T, and the first `remaining` keys == T
+  const uint32_t T = lo;
+  int cg = 0, ce = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (i < nv) {
+      if (cut ? key[i] >= T : key[i] > T) ++cg;
+      else if (!cut && key[i] == T) ++ce;
+    }
+  int gi = wave_incl_scan(cg);
+  int ei = wave_incl_scan(ce);
+  __syncthreads();  // wsum reuse: every thread has read the last pass's totals
+  if (lane == kWave - 1) {
+    sm.wsum[wave] = gi;
+    sm.wsum2[wave] = ei;
+  }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    gi += sm.wsum[w];
+    ei += sm.wsum2[w];
+  }
+  int eq_seen = ei - ce;
+  int pos = (gi - cg) + min(eq_seen, remaining);
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (i < nv) {
+      if (cut ? key[i] >= T : key[i] > T) {
+        out[pos++] = p0 + i;
+      } else if (!cut && key[i] == T) {
+        if (eq_seen < remaining) out[pos++] = p0 + i;
+        ++eq_seen;
+      }
+    }
+}
+
+// Metadata of one (physical page pi, KV head g) tile with nv valid tokens,
+// computed by one wave (all 64 lanes call it): exact per-coordinate min/max,
+// mean and population variance (two passes, fp64 sums, one rounding to fp32).
+template <typename T, int D>
+__device__ __forceinline__ void meta_tile(const T* __restrict__ K, int Hkv, int P, int pi, int g,
+                                          int nv, T* __restrict__ kmin, T* __restrict__ kmax,
+                                          float* __restrict__ mean, float* __restrict__ var) {
+  constexpr int kVec = Elem<T>::kVec;
+  constexpr int kLpr = D / kVec;      // lanes per key row
+  constexpr int kRows = kWave / kLpr; // rows per wave instruction
+  constexpr int kBatch = 8;           // rows per lane loaded together
+  const int lane = threadIdx.x % kWave;
+  const size_t tile_off = ((size_t)pi * Hkv + g) * (size_t)P * D;
+  const T* src = K + tile_off;
+  const int c = lane % kLpr;
+  const int r0 = lane / kLpr;
+
+  float mn[kVec], mx[kVec];
+  double sm[kVec];
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) {
+    mn[v] = __builtin_huge_valf();
+    mx[v] = -__builtin_huge_valf();
+    sm[v] = 0.0;
+  }
+  // rows in batches of kBatch, all loads of a batch in flight together
+  for (int t0 = r0; t0 < nv; t0 += kRows * kBatch) {
+    uint4 w[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int t = t0 + i * kRows;
+      if (t < nv) w[i] = load16(src + (size_t)t * D + c * kVec);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (t0 + i * kRows >= nv) break;
+      float x[kVec];
+      Elem<T>::unpack(w[i], x);
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        mn[v] = fminf(mn[v], x[v]);
+        mx[v] = fmaxf(mx[v], x[v]);
+        sm[v] += (double)x[v];
+      }
+    }
+  }
+#pragma unroll
+  for (int o = kLpr; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) {
+      mn[v] = fminf(mn[v], __shfl_xor(mn[v], o, kWave));
+      mx[v] = fmaxf(mx[v], __shfl_xor(mx[v], o, kWave));
+      sm[v] += __shfl_xor(sm[v], o, kWave);
+    }
+  }
+  double mu[kVec], sq[kVec];
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) {
+    mu[v] = sm[v] / (double)nv;
+    sq[v] = 0.0;
+  }
+  for (int t0 = r0; t0 < nv; t0 += kRows * kBatch) {
+    uint4 w[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int t = t0 + i * kRows;
+      if (t < nv) w[i] = load16(src + (size_t)t * D + c * kVec);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (t0 + i * kRows >= nv) break;
+      float x[kVec];
+      Elem<T>::unpack(w[i], x);
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        const double dlt = (double)x[v] - mu[v];
+        sq[v] = fma(dlt, dlt, sq[v]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = kLpr; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) sq[v] += __shfl_xor(sq[v], o, kWave);
+  }
+  if (r0 != 0) return;
+
+  const size_t m_off = ((size_t)pi * Hkv + g) * D + c * kVec;
+  if constexpr (sizeof(T) == 2) {
+    // min/max of bf16 values are bf16 values: repack the top halves
+    uint32_t wn[4], wx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wn[i] = (__float_as_uint(mn[2 * i]) >> 16) | (__float_as_uint(mn[2 * i + 1]) & 0xffff0000u);
+      wx[i] = (__float_as_uint(mx[2 * i]) >> 16) | (__float_as_uint(mx[2 * i + 1]) & 0xffff0000u);
+    }
+    *reinterpret_cast<uint4*>(kmin + m_off) = make_uint4(wn[0], wn[1], wn[2], wn[3]);
+    *reinterpret_cast<uint4*>(kmax + m_off) = make_uint4(wx[0], wx[1], wx[2], wx[3]);
+  } else {
+    *reinterpret_cast<float4*>(kmin + m_off) = make_float4(mn[0], mn[1], mn[2], mn[3]);
+    *reinterpret_cast<float4*>(kmax + m_off) = make_float4(mx[0], mx[1], mx[2], mx[3]);
+  }
+  if (mean != nullptr) {
+#pragma unroll
+    for (int v = 0; v < kVec; v += 4) {
+      *reinterpret_cast<float4*>(mean + m_off + v) =
+          make_float4((float)mu[v], (float)mu[v + 1], (float)mu[v + 2], (float)mu[v + 3]);
+      *reinterpret_cast<float4*>(var + m_off + v) = make_float4(
+          (float)(sq[v] / nv), (float)(sq[v + 1] / nv), (float)(sq[v + 2] / nv),
+          (float)(sq[v + 3] / nv));
+    }
+  }
+}
+
+}  // namespace ekv

@@ -120,8 +120,25 @@ __device__ inline float wave_max_f32(float x) {
   return x;
 }
 
+// Sum over the 64 lanes, returned to every lane (wave-uniform): DPP row
+// butterfly, then row_bcast15 / row_bcast31 carry the row sums into the last
+// row, and lane 63 is read back into a scalar register.  No LDS traffic.
 __device__ inline double wave_sum_f64(double x) {
-  return group_sum_f64<64>(x);
+  x = group_sum_f64<16>(x);
+  const int2 v = *reinterpret_cast<int2*>(&x);
+  int2 t;
+  t.x = __builtin_amdgcn_update_dpp(0, v.x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  t.y = __builtin_amdgcn_update_dpp(0, v.y, 0x142, 0xA, 0xF, false);
+  x += *reinterpret_cast<double*>(&t);
+  const int2 v2 = *reinterpret_cast<int2*>(&x);
+  t.x = __builtin_amdgcn_update_dpp(0, v2.x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  t.y = __builtin_amdgcn_update_dpp(0, v2.y, 0x143, 0xC, 0xF, false);
+  x += *reinterpret_cast<double*>(&t);
+  const int2 v3 = *reinterpret_cast<int2*>(&x);
+  int2 r;
+  r.x = __builtin_amdgcn_readlane(v3.x, 63);
+  r.y = __builtin_amdgcn_readlane(v3.y, 63);
+  return *reinterpret_cast<double*>(&r);
 }
 
 __device__ inline int wave_sum_i32(int x) {

@@ -3,26 +3,26 @@
 // entmax weights over that reduced set).
 //
 // Entmax has no online merge rule: tau depends on every score of the head.
-// The decode therefore runs in two launches:
+// The threshold does satisfy tau >= z_max - 1 (the largest weight is at most
+// 1), so only tokens with z > z_max - 1 can carry weight, and since a split's
+// own maximum is at most z_max, z > split_max - 1 keeps every such token.
+// The decode runs in two launches:
 //
-//  1. qk_kernel -- grid (splits, B*Hkv).  Each workgroup walks a contiguous
-//     range of the pair's selected pages, reads each K row once (16-byte lanes,
-//     kLpr lanes per row, rows of a page tile are contiguous) and forms the
-//     scores of all G query heads of the group from that one read:
-//         z = (alpha-1) * scale * <q_h, k>     (fp32 FMA, DPP row reduction).
-//     z goes to the workspace (one slot per selected token, -inf for the
-//     invalid tail of a row's last page) and each split's max per head to a
-//     small side array.
+//  1. qk_kernel -- work items (row, KV head, split of kR token slots).  The
+//     workgroup stages the split's page map in LDS, issues all of its K-row
+//     loads at once (16-byte lanes, kLpr lanes per row; rows of a page tile are
+//     contiguous), and forms the scores of all G query heads of the group from
+//     that one read:  z = (alpha-1) * scale * <q_h, k>  (fp32 FMA, DPP row
+//     reduction).  Each wave then owns one head: it takes the split maximum and
+//     writes only the candidates z > split_max - 1, as (z, physical token)
+//     pairs, plus the split's count and maximum.
 //
-//  2. tau_pv_kernel -- grid (B*Hq).  The threshold satisfies
-//     tau >= z_max - 1 (the largest weight is at most 1), so only tokens with
-//     z > z_max - 1 can carry weight.  The workgroup compacts those candidates
-//     into LDS (deterministic ballot order), solves
-//         sum_i [z_i - tau]_+^gamma = 1
-//     in fp64 with a bracketed Newton iteration (the left end of the bracket
-//     has f >= 0, f is convex and decreasing for gamma >= 1), and then reads
-//     only the value rows with z_i > tau -- the weights off the support are
-//     exact zeros, so no other value row is needed:
+//  2. tau_pv_kernel -- one workgroup per (row, query head).  It gathers the
+//     candidates of every split that clear z_max - 1 into LDS (in split order,
+//     so results are reproducible), solves  sum_i [z_i - tau]_+^gamma = 1  in
+//     fp64 with a bracketed Newton iteration (one wave, no barriers, when there
+//     are at most 64 candidates), and then reads only the value rows with
+//     z_i > tau -- the weights off the support are exact zeros:
 //         out = sum_i p_i v_i / sum_i p_i,   p_i = (z_i - tau)^gamma.
 #include "common.h"
 #include "kernels.h"
@@ -31,78 +31,98 @@ namespace ekv {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kQkUnroll = 4;
-constexpr int kCandCap = 8192;  // LDS candidates per head; more falls back to global z
+constexpr int kRowsPerThread = 16;  // K rows each thread has in flight per item
+constexpr int kCandCap = 4096;      // LDS candidates per head; more falls back to global
+constexpr int kMaxSplits = 4096;    // splits per head whose offsets fit in LDS
+
+template <typename T, int D>
+struct Geo {
+  static constexpr int kVec = Elem<T>::kVec;
+  static constexpr int kLpr = D / kVec;                 // lanes per K row
+  static constexpr int kRowsPerPass = kBlock / kLpr;    // rows per block-wide load
+  static constexpr int kR = kRowsPerPass * kRowsPerThread;  // token slots per item
+};
+
+__device__ inline int bits_of(float x) { return __float_as_int(x); }
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kBlock) void qk_kernel(
     const float* __restrict__ q, float zscale, const T* __restrict__ K,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int max_sel, int pps,
-    int Hkv, int P, int log2P, int maxP, long long tmax, int splits, float* __restrict__ zws,
-    float* __restrict__ smax) {
-  constexpr int kVec = Elem<T>::kVec;
-  constexpr int kLpr = D / kVec;
-  constexpr int kRowsPerPass = kBlock / kLpr;
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int max_sel, int Hkv,
+    int P, int log2P, int maxP, int splits, long long n_items, float2* __restrict__ cand,
+    int* __restrict__ cnt, float* __restrict__ smax) {
+  using GE = Geo<T, D>;
+  constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kRowsPerPass = GE::kRowsPerPass, kR = GE::kR;
   static_assert(G <= kLpr, "lane c < G stores head c");
-  __shared__ float red[kBlock / kWave][G];
-
-  const int pair = blockIdx.y;
-  const int b = pair / Hkv;
-  const int g = pair % Hkv;
-  const int Hq = Hkv * G;
-  const int L = lens[b];
-  const int np = (L + P - 1) / P;
-  int nsel = sel ? n_sel[pair] : np;
-  nsel = min(nsel, max_sel);
-  const int j0 = blockIdx.x * pps;
-  if (j0 >= nsel) return;
-  const int j1 = min(nsel, j0 + pps);
-  const int r_begin = j0 << log2P;
-  const int r_end = j1 << log2P;
+  __shared__ float zl[G][kR];
+  __shared__ int pg_phys[kR + 1];
+  __shared__ int pg_valid[kR + 1];
 
   const int c = threadIdx.x % kLpr;
   const int rg = threadIdx.x / kLpr;
-  const int32_t* selrow = sel ? sel + (size_t)pair * maxP : nullptr;
-  const int32_t* btrow = bt + (size_t)b * maxP;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int Hq = Hkv * G;
   const size_t tile_stride = (size_t)P * D;
 
-  float qf[G][kVec];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = q + ((size_t)b * Hq + g * G + h) * D + c * kVec;
-#pragma unroll
-    for (int v = 0; v < kVec; ++v) qf[h][v] = qh[v];
-  }
-  float zmx[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) zmx[h] = -__builtin_huge_valf();
+  for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int pair = (int)(item / splits);
+    const int s = (int)(item % splits);
+    const int b = pair / Hkv;
+    const int g = pair % Hkv;
+    const int L = lens[b];
+    const int np = (L + P - 1) / P;
+    const int nsel = min(sel ? n_sel[pair] : np, max_sel);
+    const int r_begin = s * kR;
+    const int r_end = min(nsel << log2P, r_begin + kR);
+    if (r_begin >= r_end) continue;  // uniform over the block
+    const int j_begin = r_begin >> log2P;
+    const int n_pg = ((r_end - 1) >> log2P) - j_begin + 1;
 
-  float* zbase = zws + ((size_t)b * Hq + g * G) * tmax;
-
-  for (int base = r_begin; base < r_end; base += kRowsPerPass * kQkUnroll) {
-    uint4 raw[kQkUnroll];
-    bool valid[kQkUnroll];
+    // page map of this split: physical page and valid tokens per selected page
+    for (int i = threadIdx.x; i < n_pg; i += kBlock) {
+      const int j = j_begin + i;
+      const int page = sel ? sel[(size_t)pair * maxP + j] : j;
+      pg_phys[i] = bt[(size_t)b * maxP + page];
+      pg_valid[i] = page_valid(L, page, P);
+    }
+    float qf[G][kVec];
 #pragma unroll
-    for (int u = 0; u < kQkUnroll; ++u) {
-      const int r = base + rg + u * kRowsPerPass;
+    for (int h = 0; h < G; ++h) {
+      const float4* qh = reinterpret_cast<const float4*>(q + ((size_t)b * Hq + g * G + h) * D + c * kVec);
+#pragma unroll
+      for (int v4 = 0; v4 < kVec / 4; ++v4) {
+        const float4 x = qh[v4];
+        qf[h][4 * v4] = x.x;
+        qf[h][4 * v4 + 1] = x.y;
+        qf[h][4 * v4 + 2] = x.z;
+        qf[h][4 * v4 + 3] = x.w;
+      }
+    }
+    __syncthreads();
+
+    uint4 raw[kRowsPerThread];
+    bool valid[kRowsPerThread];
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+      const int r = r_begin + rg + u * kRowsPerPass;
       raw[u] = make_uint4(0u, 0u, 0u, 0u);
       valid[u] = false;
       if (r < r_end) {
-        const int j = r >> log2P;
+        const int jl = (r >> log2P) - j_begin;
         const int t = r & (P - 1);
-        const int page = selrow ? selrow[j] : j;
-        if (t < page_valid(L, page, P)) {
+        if (t < pg_valid[jl]) {
           valid[u] = true;
-          const int pi = btrow[page];
-          const T* row = K + ((size_t)pi * Hkv + g) * tile_stride + (size_t)t * D + c * kVec;
+          const T* row = K + (size_t)pg_phys[jl] * Hkv * tile_stride + g * tile_stride +
+                         (size_t)t * D + c * kVec;
           raw[u] = load16_stream(row);
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kQkUnroll; ++u) {
-      const int r = base + rg + u * kRowsPerPass;
+    for (int u = 0; u < kRowsPerThread; ++u) {
+      const int rl = rg + u * kRowsPerPass;  // slot inside the item
       float x[kVec];
       Elem<T>::unpack(raw[u], x);
       float zsel = 0.0f;
@@ -112,30 +132,42 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(
 #pragma unroll
         for (int v = 0; v < kVec; ++v) a = fmaf(qf[h][v], x[v], a);
         a = group_sum_f32<kLpr>(a);
-        const float z = valid[u] ? a * zscale : -__builtin_huge_valf();
-        zmx[h] = fmaxf(zmx[h], z);
-        if (c == h) zsel = z;
+        if (c == h) zsel = valid[u] ? a * zscale : -__builtin_huge_valf();
       }
-      if (c < G && r < r_end) zbase[(size_t)c * tmax + r] = zsel;
+      if (c < G) zl[c][rl] = zsel;
     }
-  }
-  // split max per head: identical in the kLpr lanes of a row, reduce row groups
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int o = kLpr; o < kWave; o <<= 1) zmx[h] = fmaxf(zmx[h], __shfl_xor(zmx[h], o, kWave));
-  }
-  const int w = threadIdx.x / kWave;
-  if (threadIdx.x % kWave == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) red[w][h] = zmx[h];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float m = red[0][threadIdx.x];
-#pragma unroll
-    for (int i = 1; i < kBlock / kWave; ++i) m = fmaxf(m, red[i][threadIdx.x]);
-    smax[((size_t)b * Hq + g * G + threadIdx.x) * splits + blockIdx.x] = m;
+    __syncthreads();
+
+    // one wave per head: split maximum, then the candidates z > max - 1
+    const int nrows = r_end - r_begin;
+    for (int h = wave; h < G; h += kBlock / kWave) {
+      float m = -__builtin_huge_valf();
+      for (int r = lane; r < nrows; r += kWave) m = fmaxf(m, zl[h][r]);
+      m = wave_max_f32(m);
+      const double thr = (double)m - 1.0;
+      const size_t bh = (size_t)b * Hq + g * G + h;
+      float2* out = cand + (bh * splits + s) * kR;
+      int total = 0;
+      for (int r0 = 0; r0 < nrows; r0 += kWave) {
+        const int r = r0 + lane;
+        const float z = r < nrows ? zl[h][r] : -__builtin_huge_valf();
+        const bool flag = (double)z > thr;
+        const uint64_t mask = __ballot(flag);
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+        if (flag) {
+          const int rr = r_begin + r;
+          const int jl = (rr >> log2P) - j_begin;
+          const int ptok = pg_phys[jl] * P + (rr & (P - 1));
+          out[total + __popcll(mask & lt)] = make_float2(z, __int_as_float(ptok));
+        }
+        total += __popcll(mask);
+      }
+      if (lane == 0) {
+        cnt[bh * splits + s] = total;
+        smax[bh * splits + s] = m;
+      }
+    }
+    __syncthreads();  // zl and the page map are reused by the next item
   }
 }
 
@@ -164,6 +196,23 @@ __device__ inline void block_sum2(double& a, double& b, double* sh) {
   __syncthreads();
 }
 
+// Inclusive prefix sum over the block; sh holds 4 ints.
+__device__ inline int block_incl_scan(int x, int* sh) {
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) sh[w] = x;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += sh[i];
+  __syncthreads();
+  return x + add;
+}
+
 // Ballot compaction of one 256-wide chunk: returns this thread's slot (or -1)
 // and the chunk total through `total`.
 __device__ inline int chunk_slot(bool flag, int* sh4, int& total) {
@@ -181,24 +230,37 @@ __device__ inline int chunk_slot(bool flag, int* sh4, int& total) {
   return flag ? off + before : -1;
 }
 
+// Candidate k of a head, in split order: split by binary search over the
+// exclusive offsets s_off[0..nsplit] held in LDS.
+__device__ inline float2 cand_at(const float2* __restrict__ cand_bh, const int* s_off, int nsplit,
+                                 int kR, int k) {
+  int lo = 0, hi = nsplit;  // s_off[lo] <= k < s_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_off[mid] <= k) lo = mid;
+    else hi = mid;
+  }
+  return cand_bh[(size_t)lo * kR + (k - s_off[lo])];
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
-    const float* __restrict__ zws, const float* __restrict__ smax, long long tmax, int splits,
-    int pps, const T* __restrict__ V, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ n_sel, int max_sel, int Hq, int Hkv, int P, int log2P, int maxP,
-    double alpha, double gamma, int gamma_int, float* __restrict__ out,
+    const float2* __restrict__ cand, const int* __restrict__ cnt, const float* __restrict__ smax,
+    int splits, const T* __restrict__ V, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ n_sel, bool has_sel, int max_sel, int Hq, int Hkv, int P,
+    int log2P, double alpha, double gamma, int gamma_int, float* __restrict__ out,
     float* __restrict__ tau_out, int32_t* __restrict__ n_support) {
-  constexpr int kVec = Elem<T>::kVec;
-  constexpr int kLpr = D / kVec;
-  constexpr int kRowsPerPass = kBlock / kLpr;
+  using GE = Geo<T, D>;
+  constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kRowsPerPass = GE::kRowsPerPass, kR = GE::kR;
   __shared__ float c_z[kCandCap];
-  __shared__ int c_i[kCandCap];
+  __shared__ int c_t[kCandCap];
+  __shared__ int s_off[kMaxSplits + 1];
   __shared__ float st_p[kBlock];
-  __shared__ int st_i[kBlock];
+  __shared__ int st_t[kBlock];
   __shared__ float acc_sh[kRowsPerPass][D + 1];
   __shared__ int sh4[4];
   __shared__ double shd[8];
+  __shared__ double s_tau;
 
   const int bh = blockIdx.x;
   const int b = bh / Hq;
@@ -208,7 +270,9 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
   const int pair = b * Hkv + g;
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  const int nsel = sel ? n_sel[pair] : np;
+  const int nsel = has_sel ? n_sel[pair] : np;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
   if (nsel > max_sel || nsel < 1) {
     // outside the launch's bound: flag the row instead of reading past the workspace
     for (int t = threadIdx.x; t < D; t += kBlock) out[(size_t)bh * D + t] = __builtin_nanf("");
@@ -216,102 +280,148 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
     if (n_support && threadIdx.x == 0) n_support[bh] = -1;
     return;
   }
-  const int ntok = nsel << log2P;
-  const float* zrow = zws + (size_t)bh * tmax;
-  const int nsplit = (nsel + pps - 1) / pps;
+  const int nsplit = ((nsel << log2P) + kR - 1) / kR;
+  const float2* cand_bh = cand + (size_t)bh * splits * kR;
+  const int* cnt_bh = cnt + (size_t)bh * splits;
+  const float* smax_bh = smax + (size_t)bh * splits;
 
-  // global max from the split maxima
+  // global max and the exclusive offsets of the per-split candidate lists
   float zm = -__builtin_huge_valf();
-  for (int s = threadIdx.x; s < nsplit; s += kBlock) zm = fmaxf(zm, smax[(size_t)bh * splits + s]);
+  int running = 0;
+  for (int s0 = 0; s0 < nsplit; s0 += kBlock) {
+    const int s = s0 + threadIdx.x;
+    int v = 0;
+    if (s < nsplit) {
+      zm = fmaxf(zm, smax_bh[s]);
+      v = cnt_bh[s];
+    }
+    const int incl = block_incl_scan(v, sh4);
+    if (s < nsplit) s_off[s] = running + incl - v;
+    if (threadIdx.x == kBlock - 1) sh4[0] = incl;  // chunk total (read after the barrier)
+    __syncthreads();
+    running += sh4[0];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) s_off[nsplit] = running;
   zm = wave_max_f32(zm);
-  if (threadIdx.x % kWave == 0) st_p[threadIdx.x / kWave] = zm;
+  if (lane == 0) st_p[wave] = zm;
   __syncthreads();
   zm = fmaxf(fmaxf(st_p[0], st_p[1]), fmaxf(st_p[2], st_p[3]));
-  __syncthreads();
   const double zmax = (double)zm;
   const double thr = zmax - 1.0;
+  const int total_c = running;
 
-  // candidates z > zmax - 1, in slot order
+  // candidates that clear the global bar, in split order
   int count = 0;
-  int nvalid_local = 0;
-  for (int base = 0; base < ntok; base += kBlock) {
-    const int i = base + threadIdx.x;
-    const float z = i < ntok ? zrow[i] : -__builtin_huge_valf();
-    nvalid_local += (z > -__builtin_huge_valf()) ? 1 : 0;
-    const bool flag = (double)z > thr;
-    int total;
-    const int slot = chunk_slot(flag, sh4, total);
+  for (int k0 = 0; k0 < total_c; k0 += kBlock) {
+    const int k = k0 + threadIdx.x;
+    float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
+    if (k < total_c) e = cand_at(cand_bh, s_off, nsplit, kR, k);
+    const bool flag = (double)e.x > thr;
+    int tot;
+    const int slot = chunk_slot(flag, sh4, tot);
     if (slot >= 0 && count + slot < kCandCap) {
-      c_z[count + slot] = z;
-      c_i[count + slot] = i;
+      c_z[count + slot] = e.x;
+      c_t[count + slot] = bits_of(e.y);
     }
-    count += total;
+    count += tot;
   }
   __syncthreads();
   const bool overflow = count > kCandCap;
-  double nv_d = (double)nvalid_local, dummy = 0.0;
-  block_sum2(nv_d, dummy, shd);
-  const double nvalid = nv_d;
+  // number of tokens (an upper bound is enough for the upper end of the bracket)
+  const double nvalid = has_sel ? (double)nsel * P : (double)L;
 
-  auto eval = [&](double tau, double& f, double& fd) {
-    f = 0.0;
-    fd = 0.0;
-    const int lim = overflow ? ntok : count;
-    for (int k = threadIdx.x; k < lim; k += kBlock) {
-      const double z = overflow ? (double)zrow[k] : (double)c_z[k];
-      const double x = z - tau;
-      if (x > 0.0) {
-        const double xg1 = gamma_int == 1 ? 1.0 : pos_pow(x, gamma - 1.0, gamma_int - 1);
-        f += xg1 * x;
-        fd += gamma * xg1;
-      }
+  // bracketed Newton for  f(tau) = sum [z - tau]_+^gamma - 1 = 0  on
+  // [zmax - 1, zmax - n^(1-alpha)];  f' = -gamma sum [z - tau]_+^(gamma-1)
+  auto term = [&](double z, double tau, double& f, double& fd) {
+    const double x = z - tau;
+    if (x > 0.0) {
+      const double xg1 = gamma_int == 1 ? 1.0 : pos_pow(x, gamma - 1.0, gamma_int - 1);
+      f += xg1 * x;
+      fd += gamma * xg1;
     }
-    block_sum2(f, fd, shd);
+  };
+  auto newton = [&](auto&& eval) -> double {
+    double lo = thr;
+    double hi = zmax - pow(nvalid, 1.0 - alpha);
+    if (hi < lo) hi = lo;
+    double tau = lo;
+    for (int it = 0; it < 200; ++it) {
+      double f, fd;
+      eval(tau, f, fd);
+      f -= 1.0;
+      if (f == 0.0) break;
+      if (f > 0.0) lo = tau;
+      else hi = tau;
+      double nt = fd > 0.0 ? tau + f / fd : 0.5 * (lo + hi);
+      // a Newton step below fp64 resolution means converged (checked before
+      // the bracket test, which would otherwise turn it into a bisection jump)
+      if (fd > 0.0 && fabs(nt - tau) <= 4e-16 * fmax(1.0, fabs(tau))) {
+        tau = nt > lo && nt < hi ? nt : tau;
+        break;
+      }
+      if (!(nt > lo && nt < hi)) {
+        nt = 0.5 * (lo + hi);
+        if (!(nt > lo && nt < hi)) break;
+      }
+      tau = nt;
+    }
+    return tau;
   };
 
-  // bracketed Newton for sum [z - tau]_+^gamma = 1 on [zmax - 1, zmax - n^(1-alpha)]
-  double lo = thr;
-  double hi = zmax - pow(nvalid, 1.0 - alpha);
-  if (hi < lo) hi = lo;
-  double tau = lo;
-  for (int it = 0; it < 200; ++it) {
-    double f, fd;
-    eval(tau, f, fd);
-    f -= 1.0;
-    if (f == 0.0) break;
-    if (f > 0.0) lo = tau;
-    else hi = tau;
-    double nt = fd > 0.0 ? tau + f / fd : 0.5 * (lo + hi);
-    if (!(nt > lo && nt < hi)) {
-      nt = 0.5 * (lo + hi);
-      if (!(nt > lo && nt < hi)) break;
+  double tau;
+  if (!overflow && count <= kWave) {
+    // one wave, no barriers inside the iteration
+    if (wave == 0) {
+      const double zc = lane < count ? (double)c_z[lane] : -__builtin_huge_val();
+      const double t = newton([&](double tt, double& f, double& fd) {
+        f = 0.0;
+        fd = 0.0;
+        term(zc, tt, f, fd);
+        f = wave_sum_f64(f);
+        fd = wave_sum_f64(fd);
+      });
+      if (lane == 0) s_tau = t;
     }
-    if (fabs(nt - tau) <= 4e-16 * fmax(1.0, fabs(tau))) {
-      tau = nt;
-      break;
-    }
-    tau = nt;
+    __syncthreads();
+    tau = s_tau;
+  } else {
+    tau = newton([&](double tt, double& f, double& fd) {
+      f = 0.0;
+      fd = 0.0;
+      if (!overflow) {
+        for (int k = threadIdx.x; k < count; k += kBlock) term((double)c_z[k], tt, f, fd);
+      } else {
+        for (int k = threadIdx.x; k < total_c; k += kBlock)
+          term((double)cand_at(cand_bh, s_off, nsplit, kR, k).x, tt, f, fd);
+      }
+      block_sum2(f, fd, shd);
+    });
   }
 
   // weights and the value rows of the support
   const int c = threadIdx.x % kLpr;
   const int rg = threadIdx.x / kLpr;
-  const int32_t* selrow = sel ? sel + (size_t)pair * maxP : nullptr;
-  const int32_t* btrow = bt + (size_t)b * maxP;
   const size_t tile_stride = (size_t)P * D;
   float acc[kVec];
 #pragma unroll
   for (int v = 0; v < kVec; ++v) acc[v] = 0.0f;
   double psum = 0.0;
   int nsupp = 0;
-  const int lim = overflow ? ntok : count;
+  const int lim = overflow ? total_c : count;
   for (int base = 0; base < lim; base += kBlock) {
     const int k = base + threadIdx.x;
     float z = -__builtin_huge_valf();
-    int idx = 0;
+    int ptok = 0;
     if (k < lim) {
-      z = overflow ? zrow[k] : c_z[k];
-      idx = overflow ? k : c_i[k];
+      if (overflow) {
+        const float2 e = cand_at(cand_bh, s_off, nsplit, kR, k);
+        z = e.x;
+        ptok = bits_of(e.y);
+      } else {
+        z = c_z[k];
+        ptok = c_t[k];
+      }
     }
     const double x = (double)z - tau;
     const bool flag = x > 0.0;
@@ -321,29 +431,27 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
     if (slot >= 0) {
       const float p = (float)pos_pow(x, gamma, gamma_int);
       st_p[slot] = p;
-      st_i[slot] = idx;
+      st_t[slot] = ptok;
       psum += (double)p;
     }
     __syncthreads();
     for (int r = rg; r < m; r += kRowsPerPass) {
-      const int i = st_i[r];
+      const int pt = st_t[r];
       const float p = st_p[r];
-      const int j = i >> log2P;
-      const int t = i & (P - 1);
-      const int page = selrow ? selrow[j] : j;
-      const int pi = btrow[page];
-      const T* row = V + ((size_t)pi * Hkv + g) * tile_stride + (size_t)t * D + c * kVec;
-      float x8[kVec];
-      Elem<T>::unpack(load16(row), x8);
+      const int pi = pt >> log2P;
+      const int t = pt & (P - 1);
+      const T* row = V + (size_t)pi * Hkv * tile_stride + g * tile_stride + (size_t)t * D + c * kVec;
+      float xv[kVec];
+      Elem<T>::unpack(load16(row), xv);
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) acc[v] = fmaf(p, x8[v], acc[v]);
+      for (int v = 0; v < kVec; ++v) acc[v] = fmaf(p, xv[v], acc[v]);
     }
     __syncthreads();
   }
 #pragma unroll
   for (int v = 0; v < kVec; ++v) acc_sh[rg][c * kVec + v] = acc[v];
-  double ps = psum;
-  block_sum2(ps, dummy, shd);  // includes the __syncthreads that publishes acc_sh
+  double ps = psum, dummy = 0.0;
+  block_sum2(ps, dummy, shd);  // includes the barrier that publishes acc_sh
   const float inv = (float)(1.0 / ps);
   for (int t = threadIdx.x; t < D; t += kBlock) {
     float o = 0.0f;
@@ -357,11 +465,13 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
 template <typename T, int D, int G>
 hipError_t launch_qk_t(const Shape& s, const DecodePlan& pl, const float* q, float zscale,
                        const void* K, const int32_t* bt, const int32_t* lens, const int32_t* sel,
-                       const int32_t* n_sel, float* zws, float* smax, hipStream_t stream) {
-  dim3 grid(pl.splits, s.B * s.Hkv);
-  hipLaunchKernelGGL((qk_kernel<T, D, G>), grid, dim3(kBlock), 0, stream, q, zscale,
-                     (const T*)K, bt, lens, sel, n_sel, pl.max_sel, pl.pages_per_split, s.Hkv,
-                     s.P, s.log2P, s.maxP, pl.tmax, pl.splits, zws, smax);
+                       const int32_t* n_sel, float2* cand, int* cnt, float* smax,
+                       hipStream_t stream) {
+  const long long items = (long long)s.B * s.Hkv * pl.splits;
+  const long long grid = items < pl.qk_grid_cap ? items : pl.qk_grid_cap;
+  hipLaunchKernelGGL((qk_kernel<T, D, G>), dim3((unsigned)grid), dim3(kBlock), 0, stream, q,
+                     zscale, (const T*)K, bt, lens, sel, n_sel, pl.max_sel, s.Hkv, s.P, s.log2P,
+                     s.maxP, pl.splits, items, cand, cnt, smax);
   return hipGetLastError();
 }
 
@@ -371,49 +481,58 @@ hipError_t launch_decode_t(const Shape& s, const DecodePlan& pl, const float* q,
                            const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
                            float* out, float* tau_out, int32_t* n_support, void* ws,
                            hipStream_t stream) {
-  float* zws = (float*)((char*)ws + pl.z_off);
+  float2* cand = (float2*)((char*)ws + pl.cand_off);
+  int* cnt = (int*)((char*)ws + pl.cnt_off);
   float* smax = (float*)((char*)ws + pl.smax_off);
   const double a1 = (double)alpha - 1.0;
   const float zscale = (float)(a1 * (double)scale);
   hipError_t e = hipErrorInvalidValue;
   switch (s.G) {
-    case 1: e = launch_qk_t<T, D, 1>(s, pl, q, zscale, K, bt, lens, sel, n_sel, zws, smax, stream); break;
-    case 2: e = launch_qk_t<T, D, 2>(s, pl, q, zscale, K, bt, lens, sel, n_sel, zws, smax, stream); break;
-    case 4: e = launch_qk_t<T, D, 4>(s, pl, q, zscale, K, bt, lens, sel, n_sel, zws, smax, stream); break;
-    case 8: e = launch_qk_t<T, D, 8>(s, pl, q, zscale, K, bt, lens, sel, n_sel, zws, smax, stream); break;
+    case 1: e = launch_qk_t<T, D, 1>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
+    case 2: e = launch_qk_t<T, D, 2>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
+    case 4: e = launch_qk_t<T, D, 4>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
+    case 8: e = launch_qk_t<T, D, 8>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
   }
   if (e != hipSuccess) return e;
   const double gamma = 1.0 / a1;
   const double gr = rint(gamma);
   const int gamma_int = (gr >= 1.0 && gr <= 64.0 && fabs(gamma - gr) <= 1e-12 * gr) ? (int)gr : 0;
-  hipLaunchKernelGGL((tau_pv_kernel<T, D>), dim3(s.B * s.Hq), dim3(kBlock), 0, stream, zws, smax,
-                     pl.tmax, pl.splits, pl.pages_per_split, (const T*)V, bt, lens, sel, n_sel,
-                     pl.max_sel, s.Hq, s.Hkv, s.P, s.log2P, s.maxP, (double)alpha,
-                     gamma_int ? gr : gamma, gamma_int, out, tau_out, n_support);
+  hipLaunchKernelGGL((tau_pv_kernel<T, D>), dim3(s.B * s.Hq), dim3(kBlock), 0, stream, cand, cnt,
+                     smax, pl.splits, (const T*)V, lens, n_sel, sel != nullptr, pl.max_sel, s.Hq,
+                     s.Hkv, s.P, s.log2P, (double)alpha, gamma_int ? gr : gamma, gamma_int, out,
+                     tau_out, n_support);
   return hipGetLastError();
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int slots_per_item(const Shape& s) {
+  if (s.bf16) return s.D == 128 ? Geo<bf16_t, 128>::kR : Geo<bf16_t, 64>::kR;
+  return s.D == 128 ? Geo<float, 128>::kR : Geo<float, 64>::kR;
+}
+
 }  // namespace
+
+bool decode_shape_supported(const Shape& s, int max_sel) {
+  const long long slots = (long long)max_sel * s.P;
+  const long long splits = (slots + slots_per_item(s) - 1) / slots_per_item(s);
+  return splits <= kMaxSplits && (long long)s.Np * s.P < (1LL << 31);
+}
 
 DecodePlan make_decode_plan(const Shape& s, int max_sel) {
   DecodePlan pl{};
   pl.max_sel = max_sel;
-  const long long pairs = (long long)s.B * s.Hkv;
-  // aim for >= 2048 workgroups, 64..256 rows each
-  const int min_pps = s.P >= 64 ? 1 : 64 / s.P;
-  const int max_pps = s.P >= 256 ? 1 : 256 / s.P;
-  long long want = (max_sel * pairs + 2047) / 2048;
-  int pps = (int)(want < min_pps ? min_pps : (want > max_pps ? max_pps : want));
-  if (pps < 1) pps = 1;
-  pl.pages_per_split = pps;
-  pl.splits = (max_sel + pps - 1) / pps;
-  pl.tmax = (long long)max_sel * s.P;
-  pl.z_off = 0;
-  pl.z_bytes = align256((size_t)s.B * s.Hq * (size_t)pl.tmax * sizeof(float));
-  pl.smax_off = pl.z_off + pl.z_bytes;
-  pl.smax_bytes = align256((size_t)s.B * s.Hq * (size_t)pl.splits * sizeof(float));
+  pl.slots_per_item = slots_per_item(s);
+  const long long slots = (long long)max_sel * s.P;
+  pl.splits = (int)((slots + pl.slots_per_item - 1) / pl.slots_per_item);
+  pl.qk_grid_cap = 256LL * 16;  // CUs x resident workgroups; items beyond loop
+  const size_t heads = (size_t)s.B * s.Hq;
+  pl.cand_off = 0;
+  pl.cand_bytes = align256(heads * pl.splits * (size_t)pl.slots_per_item * sizeof(float) * 2);
+  pl.cnt_off = pl.cand_off + pl.cand_bytes;
+  pl.cnt_bytes = align256(heads * pl.splits * sizeof(int));
+  pl.smax_off = pl.cnt_off + pl.cnt_bytes;
+  pl.smax_bytes = align256(heads * pl.splits * sizeof(float));
   pl.total = pl.smax_off + pl.smax_bytes;
   return pl;
 }

@@ -24,6 +24,14 @@ hipError_t launch_score(const Shape& s, const float* q, float scale, const void*
                         const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
                         double* gm, double* gv, hipStream_t stream);
 
+// Fused: last-page metadata refresh (optional) + scores + top-k by the last
+// workgroup of each (row, KV head); `counters` [B*Hkv] start at zero and are
+// left at zero.
+hipError_t launch_score_select(const Shape& s, const float* q, float scale, const void* K,
+                               void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
+                               int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
+                               int* counters, hipStream_t stream);
+
 hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const float* ubg,
                        int32_t* sel, int32_t* n_sel, hipStream_t stream);
 
@@ -32,18 +40,21 @@ hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int ga
                         const double* gv, int32_t* sel, int32_t* n_sel, double* tau_hat,
                         hipStream_t stream);
 
-// Decode plan: how the selected pages of a (row, KV head) pair are split over
-// workgroups, and where the scratch arrays sit inside the caller's workspace.
+// Decode plan: the selected token slots of a (row, KV head) pair are cut into
+// splits of `slots_per_item` slots (one qk work item each); the scratch arrays
+// sit at fixed offsets inside the caller's workspace.
 struct DecodePlan {
-  int max_sel;       // upper bound on selected pages per pair
-  int pages_per_split;
-  int splits;        // ceil(max_sel / pages_per_split)
-  long long tmax;    // token slots per query head = max_sel * P
-  size_t z_off, z_bytes;        // fp32 [B*Hq][tmax]
-  size_t smax_off, smax_bytes;  // fp32 [B*Hq][splits]
+  int max_sel;          // upper bound on selected pages per pair
+  int slots_per_item;   // token slots per qk work item
+  int splits;           // ceil(max_sel * P / slots_per_item)
+  long long qk_grid_cap;
+  size_t cand_off, cand_bytes;  // (z, physical token) [B*Hq][splits][slots_per_item]
+  size_t cnt_off, cnt_bytes;    // int   [B*Hq][splits]
+  size_t smax_off, smax_bytes;  // fp32  [B*Hq][splits]
   size_t total;
 };
 
+bool decode_shape_supported(const Shape& s, int max_sel);
 DecodePlan make_decode_plan(const Shape& s, int max_sel);
 
 hipError_t launch_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,

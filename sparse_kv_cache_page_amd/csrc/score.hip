@@ -14,60 +14,70 @@
 // kmax), so a wave scores 64/kLpr pages per step for all G query heads of the
 // group; per-head partial sums are reduced over the kLpr lanes with DPP.
 // q+ and q- stay in registers as fp64 for the whole launch.
-#include "common.h"
+#include "blocks.h"
 #include "kernels.h"
 
 namespace ekv {
 namespace {
 
-template <typename T, int N> struct VecLoad;
-template <> struct VecLoad<bf16_t, 8> {
-  __device__ static void load(const bf16_t* p, float* x) { Elem<bf16_t>::unpack(load16_stream(p), x); }
+// Raw storage of one lane's slice of a metadata row (kVec elements of T).
+template <int kBytes> struct RawT;
+template <> struct RawT<16> {
+  using type = uint4;
+  __device__ static type load(const void* p) { return load16_stream(p); }
 };
-template <> struct VecLoad<bf16_t, 4> {
-  __device__ static void load(const bf16_t* p, float* x) {
-    const uint2 w = load8_stream(p);
+template <> struct RawT<8> {
+  using type = uint2;
+  __device__ static type load(const void* p) { return load8_stream(p); }
+};
+
+template <typename T, int N> struct Unpack;
+template <> struct Unpack<bf16_t, 8> {
+  __device__ static void run(const uint4& w, float* x) { Elem<bf16_t>::unpack(w, x); }
+};
+template <> struct Unpack<bf16_t, 4> {
+  __device__ static void run(const uint2& w, float* x) {
     x[0] = __uint_as_float(w.x << 16);
     x[1] = __uint_as_float(w.x & 0xffff0000u);
     x[2] = __uint_as_float(w.y << 16);
     x[3] = __uint_as_float(w.y & 0xffff0000u);
   }
 };
-template <> struct VecLoad<float, 4> {
-  __device__ static void load(const float* p, float* x) { Elem<float>::unpack(load16_stream(p), x); }
+template <> struct Unpack<float, 4> {
+  __device__ static void run(const uint4& w, float* x) { Elem<float>::unpack(w, x); }
 };
-template <> struct VecLoad<float, 2> {
-  __device__ static void load(const float* p, float* x) {
-    const uint2 w = load8_stream(p);
+template <> struct Unpack<float, 2> {
+  __device__ static void run(const uint2& w, float* x) {
     x[0] = __uint_as_float(w.x);
     x[1] = __uint_as_float(w.y);
   }
 };
 
 constexpr int kScoreBlock = 256;
+constexpr int kMaxPagesPerBlock = 2048;  // block-table slice staged in LDS
+constexpr int kStepTopkKeys = 4096;
+// workgroups resident at once (256 CUs x 2 at this kernel's register use):
+// one round of blocks avoids a second ramp-up
+constexpr int kScoreResidentBlocks = 512;      // LDS keys of the fused select; longer rows read U from L2
 
-template <typename T, int D, int G, int kVec, bool kGauss>
-__global__ __launch_bounds__(kScoreBlock) void score_kernel(
+// Scores of pages [p_begin, p_end) of one (row b, KV head g) for the G query
+// heads of the group; s_pi holds the block-table slice block_table[b][p_begin..).
+template <typename T, int D, int G, int kVec, bool kGauss, bool kCoherentU = false>
+__device__ __forceinline__ void score_range(
     const float* __restrict__ q, float scale, const T* __restrict__ kmin,
     const T* __restrict__ kmax, const float* __restrict__ mean, const float* __restrict__ var,
-    const int32_t* __restrict__ bt, const int32_t* __restrict__ lens, int Hkv, int P, int maxP,
-    int pages_per_block, float* __restrict__ ub, float* __restrict__ ubg,
-    double* __restrict__ gm, double* __restrict__ gv) {
+    const int* s_pi, int b, int g, int pair, int Hkv, int maxP, int p_begin, int p_end,
+    float* __restrict__ ub, float* __restrict__ ubg, double* __restrict__ gm,
+    double* __restrict__ gv) {
   constexpr int kLpr = D / kVec;
   constexpr int kPagesPerWave = kWave / kLpr;
   constexpr int kPagesPerStep = kPagesPerWave * (kScoreBlock / kWave);
+  constexpr int kU = kGauss ? 2 : 4;  // pages in flight per lane
+  constexpr int kRawBytes = kVec * (int)sizeof(T);
+  constexpr int kMomRaw = kVec * 4;   // bytes of fp32 mean (or var) per lane
+  using Raw = RawT<kRawBytes>;
   static_assert(G <= kLpr, "one lane per head writes the result");
-
-  const int pair = blockIdx.y;
-  const int b = pair / Hkv;
-  const int g = pair % Hkv;
   const int Hq = Hkv * G;
-  const int L = lens[b];
-  const int np = (L + P - 1) / P;
-  const int p_begin = blockIdx.x * pages_per_block;
-  if (p_begin >= np) return;
-  const int p_end = min(np, p_begin + pages_per_block);
-
   const int lane = threadIdx.x % kWave;
   const int c = lane % kLpr;
   const int slot = threadIdx.x / kLpr;  // page slot inside a step
@@ -85,67 +95,200 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
   }
   const double dscale = (double)scale;
 
-  for (int p = p_begin + slot; p - slot < p_end; p += kPagesPerStep) {
-    const bool live = p < p_end;
-    const int pp = live ? p : p_begin;
-    const int pi = bt[(size_t)b * maxP + pp];
-    const size_t off = ((size_t)pi * Hkv + g) * D + c * kVec;
-    float lo[kVec], hi[kVec];
-    VecLoad<T, kVec>::load(kmin + off, lo);
-    VecLoad<T, kVec>::load(kmax + off, hi);
-    double acc[G];
+  // one batch = kU pages per lane; the next batch's loads are issued before
+  // the current batch is reduced, so a wave always has loads in flight
+  struct Batch {
+    typename Raw::type lo[kU], hi[kU];
+    float mu[kGauss ? kU : 1][kVec], s2[kGauss ? kU : 1][kVec];
+  };
+  auto issue = [&](int base, Batch& bt_) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      double a = 0.0;
-#pragma unroll
-      for (int v = 0; v < kVec; ++v) {
-        a = fma(qp[h][v], (double)hi[v], a);
-        a = fma(qn[h][v], (double)lo[v], a);
-      }
-      acc[h] = group_sum_f64<kLpr>(a);
-    }
-    double mg[G], vg[G];
-    if constexpr (kGauss) {
-      float mu[kVec], s2[kVec];
-      if constexpr (kVec >= 4) {
-#pragma unroll
-        for (int v = 0; v < kVec; v += 4) {
-          VecLoad<float, 4>::load(mean + off + v, mu + v);
-          VecLoad<float, 4>::load(var + off + v, s2 + v);
+    for (int u = 0; u < kU; ++u) {
+      const int p = base + slot + u * kPagesPerStep;
+      const int pl = (p < p_end ? p : p_begin) - p_begin;
+      const size_t off = ((size_t)s_pi[pl] * Hkv + g) * D + c * kVec;
+      bt_.lo[u] = Raw::load(kmin + off);
+      bt_.hi[u] = Raw::load(kmax + off);
+      if constexpr (kGauss) {
+        if constexpr (kMomRaw == 32) {
+          Elem<float>::unpack(load16_stream(mean + off), bt_.mu[u]);
+          Elem<float>::unpack(load16_stream(mean + off + 4), bt_.mu[u] + 4);
+          Elem<float>::unpack(load16_stream(var + off), bt_.s2[u]);
+          Elem<float>::unpack(load16_stream(var + off + 4), bt_.s2[u] + 4);
+        } else if constexpr (kMomRaw == 16) {
+          Elem<float>::unpack(load16_stream(mean + off), bt_.mu[u]);
+          Elem<float>::unpack(load16_stream(var + off), bt_.s2[u]);
+        } else {
+          Unpack<float, 2>::run(load8_stream(mean + off), bt_.mu[u]);
+          Unpack<float, 2>::run(load8_stream(var + off), bt_.s2[u]);
         }
-      } else {
-        VecLoad<float, 2>::load(mean + off, mu);
-        VecLoad<float, 2>::load(var + off, s2);
       }
+    }
+  };
+  auto consume = [&](int base, const Batch& bt_) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int p = base + slot + u * kPagesPerStep;
+      const bool live = p < p_end;
+      float lo[kVec], hi[kVec];
+      Unpack<T, kVec>::run(bt_.lo[u], lo);
+      Unpack<T, kVec>::run(bt_.hi[u], hi);
+      double acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        double am = 0.0, av = 0.0;
+        double a = 0.0;
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
-          const double qd = qp[h][v] + qn[h][v];
-          am = fma(qd, (double)mu[v], am);
-          av = fma(qd * qd, (double)s2[v], av);
+          a = fma(qp[h][v], (double)hi[v], a);
+          a = fma(qn[h][v], (double)lo[v], a);
         }
-        mg[h] = group_sum_f64<kLpr>(am);
-        vg[h] = group_sum_f64<kLpr>(av);
+        acc[h] = group_sum_f64<kLpr>(a);
       }
-    }
-    if (!live) continue;
-    float best = -__builtin_huge_valf();
+      double mg[G], vg[G];
+      if constexpr (kGauss) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float u = (float)(dscale * acc[h]);
-      best = fmaxf(best, u);
-      if (c == h) {
-        const size_t o = ((size_t)b * Hq + g * G + h) * maxP + p;
-        if (ub != nullptr) ub[o] = u;
-        if constexpr (kGauss) {
-          gm[o] = dscale * mg[h];
-          gv[o] = dscale * dscale * vg[h];
+        for (int h = 0; h < G; ++h) {
+          double am = 0.0, av = 0.0;
+#pragma unroll
+          for (int v = 0; v < kVec; ++v) {
+            const double qd = qp[h][v] + qn[h][v];
+            am = fma(qd, (double)bt_.mu[u][v], am);
+            av = fma(qd * qd, (double)bt_.s2[u][v], av);
+          }
+          mg[h] = group_sum_f64<kLpr>(am);
+          vg[h] = group_sum_f64<kLpr>(av);
         }
       }
+      if (!live) continue;
+      float best = -__builtin_huge_valf();
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float uh = (float)(dscale * acc[h]);
+        best = fmaxf(best, uh);
+        if (c == h) {
+          const size_t o = ((size_t)b * Hq + g * G + h) * maxP + p;
+          if (ub != nullptr) ub[o] = uh;
+          if constexpr (kGauss) {
+            gm[o] = dscale * mg[h];
+            gv[o] = dscale * dscale * vg[h];
+          }
+        }
+      }
+      if (c == 0) {
+        // the fused select reads these bounds from another workgroup (maybe
+        // on another XCD): device-coherent stores there, plain ones otherwise
+        if constexpr (kCoherentU)
+          __hip_atomic_store(ubg + (size_t)pair * maxP + p, best, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        else
+          ubg[(size_t)pair * maxP + p] = best;
+      }
     }
-    if (c == 0) ubg[(size_t)pair * maxP + p] = best;
+  };
+  constexpr int kStride = kPagesPerStep * kU;
+  Batch A, Bb;
+  int base = p_begin;
+  issue(base, A);
+  while (true) {
+    const int nb = base + kStride;
+    if (nb < p_end) issue(nb, Bb);
+    consume(base, A);
+    if (nb >= p_end) break;
+    const int nb2 = nb + kStride;
+    if (nb2 < p_end) issue(nb2, A);
+    consume(nb, Bb);
+    if (nb2 >= p_end) break;
+    base = nb2;
+  }
+}
+
+template <typename T, int D, int G, int kVec, bool kGauss>
+__global__ __launch_bounds__(kScoreBlock) void score_kernel(
+    const float* __restrict__ q, float scale, const T* __restrict__ kmin,
+    const T* __restrict__ kmax, const float* __restrict__ mean, const float* __restrict__ var,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ lens, int Hkv, int P, int maxP,
+    int pages_per_block, float* __restrict__ ub, float* __restrict__ ubg,
+    double* __restrict__ gm, double* __restrict__ gv) {
+  __shared__ int s_pi[kMaxPagesPerBlock];
+  const int pair = blockIdx.y;
+  const int b = pair / Hkv;
+  const int g = pair % Hkv;
+  const int L = lens[b];
+  const int np = (L + P - 1) / P;
+  const int p_begin = blockIdx.x * pages_per_block;
+  if (p_begin >= np) return;
+  const int p_end = min(np, p_begin + pages_per_block);
+  for (int i = threadIdx.x; i < p_end - p_begin; i += kScoreBlock)
+    s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
+  __syncthreads();
+  score_range<T, D, G, kVec, kGauss>(q, scale, kmin, kmax, mean, var, s_pi, b, g, pair, Hkv, maxP,
+                                     p_begin, p_end, ub, ubg, gm, gv);
+}
+
+// Fused first half of a decode step (top-k policy): optionally rebuild the
+// metadata of each row's last page (the page the new token went to), score
+// the pages, and let the last workgroup to finish a (row, KV head) run the
+// top-k selection over that pair's bounds.  Arrivals are counted in
+// `counters` [B*Hkv], which start at zero and are reset by the last arrival.
+template <typename T, int D, int G, int kVec, bool kKeysLds>
+__global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
+    const float* __restrict__ q, float scale, const T* __restrict__ K, T* __restrict__ kmin,
+    T* __restrict__ kmax, const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
+    int refresh, int Hkv, int P, int maxP, int pages_per_block, float* __restrict__ ubg,
+    int top_k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+    int* __restrict__ counters) {
+  __shared__ int s_pi[kMaxPagesPerBlock];
+  __shared__ TopkRegLds tkr;
+  __shared__ TopkLds<1> tk;
+  __shared__ int s_last;
+  const int pair = blockIdx.y;
+  const int b = pair / Hkv;
+  const int g = pair % Hkv;
+  const int L = lens[b];
+  const int np = (L + P - 1) / P;
+  const int p_begin = blockIdx.x * pages_per_block;
+  if (p_begin >= np) return;
+  const int p_end = min(np, p_begin + pages_per_block);
+  for (int i = threadIdx.x; i < p_end - p_begin; i += kScoreBlock)
+    s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
+  if (refresh && p_end == np && threadIdx.x < kWave) {
+    // only this workgroup reads the refreshed page's box: the barrier below
+    // (which waits for the stores) is enough to publish it
+    meta_tile<T, D>(K, Hkv, P, bt[(size_t)b * maxP + np - 1], g, page_valid(L, np - 1, P), kmin,
+                    kmax, nullptr, nullptr);
+  }
+  __syncthreads();
+  score_range<T, D, G, kVec, false, true>(q, scale, kmin, kmax, nullptr, nullptr, s_pi, b, g, pair,
+                                          Hkv, maxP, p_begin, p_end, nullptr, ubg, nullptr,
+                                          nullptr);
+  // arrival: every wave waits until its device-coherent bound stores have
+  // completed, the barrier gathers the waves, then one relaxed device-scope
+  // increment counts the block; the last block of the pair reads every bound
+  // back with device-coherent loads.  No cache-wide write-back or
+  // invalidation is needed.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int nblk = (np + pages_per_block - 1) / pages_per_block;
+    s_last = __hip_atomic_fetch_add(&counters[pair], 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == nblk - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const int k = min(top_k, np);
+  int32_t* out = sel + (size_t)pair * maxP;
+  if (k >= np) {
+    for (int p = threadIdx.x; p < np; p += kScoreBlock) out[p] = p;
+  } else if (np <= kBlk * 8) {
+    topk_block_reg<8, true>(ubg + (size_t)pair * maxP, np, k, out, tkr);
+  } else if (np <= kBlk * 16) {
+    topk_block_reg<16, true>(ubg + (size_t)pair * maxP, np, k, out, tkr);
+  } else {
+    topk_block<false, true>(ubg + (size_t)pair * maxP, np, k, out, tk);
+  }
+  if (threadIdx.x == 0) {
+    n_sel[pair] = k;
+    __hip_atomic_store(&counters[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -156,12 +299,18 @@ hipError_t launch_score_t(const Shape& s, const float* q, float scale, const voi
                           double* gm, double* gv, hipStream_t stream) {
   constexpr int kLpr = D / kVec;
   constexpr int kPagesPerStep = (kWave / kLpr) * (kScoreBlock / kWave);
-  // several steps per block keep q's register preload amortised; enough blocks
-  // per pair to spread a long row over the chip
-  const int steps = s.maxP >= 64 * kPagesPerStep ? 8 : (s.maxP >= 8 * kPagesPerStep ? 4 : 1);
-  const int ppb = kPagesPerStep * steps;
-  dim3 grid((s.maxP + ppb - 1) / ppb, s.B * s.Hkv);
-  if (gm != nullptr) {
+  const bool gauss = gm != nullptr;
+  const int per_iter = kPagesPerStep * (gauss ? 2 : 4);
+  // enough blocks to spread the pairs over the chip (~4 per CU), each block
+  // a whole number of iterations
+  const long long pairs = (long long)s.B * s.Hkv;
+  long long want_blocks_per_pair = (kScoreResidentBlocks + pairs - 1) / pairs;
+  int iters = (int)((s.maxP + per_iter * want_blocks_per_pair - 1) / (per_iter * want_blocks_per_pair));
+  if (iters < 1) iters = 1;
+  if (iters * per_iter > kMaxPagesPerBlock) iters = kMaxPagesPerBlock / per_iter;
+  const int ppb = per_iter * iters;
+  dim3 grid((s.maxP + ppb - 1) / ppb, (unsigned)pairs);
+  if (gauss) {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0, stream, q,
                        scale, (const T*)kmin, (const T*)kmax, mean, var, bt, lens, s.Hkv, s.P,
                        s.maxP, ppb, ub, ubg, gm, gv);
@@ -191,6 +340,48 @@ hipError_t launch_score_d(const Shape& s, const float* q, float scale, const voi
   return hipErrorInvalidValue;
 }
 
+template <typename T, int D, int G, int kVec>
+hipError_t launch_score_select_t(const Shape& s, const float* q, float scale, const void* K,
+                                 void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
+                                 int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
+                                 int* counters, hipStream_t stream) {
+  constexpr int kLpr = D / kVec;
+  constexpr int kPagesPerStep = (kWave / kLpr) * (kScoreBlock / kWave);
+  const int per_iter = kPagesPerStep * 4;
+  const long long pairs = (long long)s.B * s.Hkv;
+  long long want_blocks_per_pair = (kScoreResidentBlocks + pairs - 1) / pairs;
+  int iters = (int)((s.maxP + per_iter * want_blocks_per_pair - 1) / (per_iter * want_blocks_per_pair));
+  if (iters < 1) iters = 1;
+  if (iters * per_iter > kMaxPagesPerBlock) iters = kMaxPagesPerBlock / per_iter;
+  const int ppb = per_iter * iters;
+  dim3 grid((s.maxP + ppb - 1) / ppb, (unsigned)pairs);
+  if (s.maxP <= kStepTopkKeys)
+    hipLaunchKernelGGL((score_select_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0,
+                       stream, q, scale, (const T*)K, (T*)kmin, (T*)kmax, bt, lens, refresh, s.Hkv,
+                       s.P, s.maxP, ppb, ubg, top_k, sel, n_sel, counters);
+  else
+    hipLaunchKernelGGL((score_select_kernel<T, D, G, kVec, false>), grid, dim3(kScoreBlock), 0,
+                       stream, q, scale, (const T*)K, (T*)kmin, (T*)kmax, bt, lens, refresh, s.Hkv,
+                       s.P, s.maxP, ppb, ubg, top_k, sel, n_sel, counters);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_score_select_d(const Shape& s, const float* q, float scale, const void* K,
+                                 void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
+                                 int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
+                                 int* counters, hipStream_t stream) {
+  constexpr int kV16 = 16 / sizeof(T);
+  constexpr int kV8 = 8 / sizeof(T);
+  switch (s.G) {
+    case 1: return launch_score_select_t<T, D, 1, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+    case 2: return launch_score_select_t<T, D, 2, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+    case 4: return launch_score_select_t<T, D, 4, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+    case 8: return launch_score_select_t<T, D, 8, kV8>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_score(const Shape& s, const float* q, float scale, const void* kmin,
@@ -203,6 +394,18 @@ hipError_t launch_score(const Shape& s, const float* q, float scale, const void*
   }
   if (s.D == 128) return launch_score_d<float, 128>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
   return launch_score_d<float, 64>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
+}
+
+hipError_t launch_score_select(const Shape& s, const float* q, float scale, const void* K,
+                               void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
+                               int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
+                               int* counters, hipStream_t stream) {
+  if (s.bf16) {
+    if (s.D == 128) return launch_score_select_d<bf16_t, 128>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+    return launch_score_select_d<bf16_t, 64>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+  }
+  if (s.D == 128) return launch_score_select_d<float, 128>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+  return launch_score_select_d<float, 64>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
 }
 
 }  // namespace ekv

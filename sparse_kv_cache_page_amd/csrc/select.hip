@@ -1,14 +1,14 @@
 // Candidate page selection (EntmaxKV summary page, §2.B).
 //
-// Top-k: per (row, KV head) one 256-thread workgroup runs an MSB-first radix
-// select over distinct 64-bit keys
-//     key(p) = (order-preserving bits of fp32 U_p) << 32 | (2^32 - 1 - p),
-// so larger U wins and, among equal U, the lower page index wins.  Each pass
-// histograms one 8-bit digit of the keys that still match the chosen prefix
-// (LDS atomics), a block scan picks the digit holding the k-th largest key,
-// and the search stops as soon as every key with the chosen prefix is in the
-// answer.  The selected pages are exactly the keys >= that prefix; a block
-// prefix sum over page order writes them ascending.
+// Top-k: per (row, KV head) one 256-thread workgroup selects the k largest
+// bounds with a radix select on the order-preserving uint32 image of the fp32
+// bounds.  Each pass splits the keys' current range [lo, hi] into at most 2048
+// bins (LDS histogram), a block scan finds the bin holding the k-th largest
+// key, and the range narrows to that bin.  The search stops early when every
+// key in the chosen bin belongs to the answer; otherwise it ends with the exact
+// k-th largest key T and the number r of pages equal to T that still fit.  A block prefix sum over page order then writes, in
+// ascending order, every page with key > T and the r lowest-index pages with
+// key == T (ties go to the lower page index).
 //
 // Gaussian-aware: per query head, tau-hat solves
 //     F(tau) = sum_p n_p E[(X_p - tau)_+^gamma] = 1,  X_p ~ N(mu_p, s_p^2),
@@ -18,32 +18,14 @@
 // Newton's method started there climbs monotonically to the root.  A second
 // kernel keeps page p when (alpha-1) u_{h,p} >= tau-hat_h - delta for some head
 // of the group and compacts the kept pages in ascending order.
-#include "common.h"
+#include "blocks.h"
 #include "kernels.h"
 
 namespace ekv {
 namespace {
 
 constexpr int kSelBlock = 256;
-constexpr int kTopkLdsKeys = 16384;   // 64 KiB of LDS keys; longer rows read U from global
 constexpr int kGaussLdsPages = 4096;  // 64 KiB of LDS (mu, sigma) per head
-
-// Inclusive prefix sum over a 256-thread block; `sh` holds 4 ints of LDS.
-__device__ inline int block_incl_scan(int x, int* sh) {
-  const int lane = threadIdx.x % kWave;
-  const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) sh[w] = x;
-  __syncthreads();
-  int add = 0;
-  for (int i = 0; i < w; ++i) add += sh[i];
-  __syncthreads();
-  return x + add;
-}
 
 __device__ inline double block_sum_f64(double x, double* sh) {
   x = wave_sum_f64(x);
@@ -53,17 +35,6 @@ __device__ inline double block_sum_f64(double x, double* sh) {
   const double t = (sh[0] + sh[1]) + (sh[2] + sh[3]);
   __syncthreads();
   return t;
-}
-
-// fp32 -> uint32 with the same order (-0 folded onto +0 so they tie).
-__device__ inline uint32_t order_key(float x) {
-  if (x == 0.0f) x = 0.0f;
-  const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ inline uint64_t compose(uint32_t ukey, int p) {
-  return ((uint64_t)ukey << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
 }
 
 // Ascending compaction of flag(p) for p < n into out[]; returns the count.
@@ -89,60 +60,23 @@ template <bool kLds>
 __global__ __launch_bounds__(kSelBlock) void topk_kernel(
     const float* __restrict__ ubg, const int32_t* __restrict__ lens, int P, int maxP, int Hkv,
     int top_k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
-  __shared__ uint32_t keys[kLds ? kTopkLdsKeys : 1];
-  __shared__ int hist[256];
-  __shared__ int scan_sh[4];
-  __shared__ int s_digit, s_above, s_cnt;
-
+  __shared__ TopkLds<kLds ? kTopkLdsKeys : 1> sm;
+  __shared__ TopkRegLds smr;
   const int pair = blockIdx.x;
   const int b = pair / Hkv;
   const int n = (lens[b] + P - 1) / P;
   const int k = min(top_k, n);
-  const float* U = ubg + (size_t)pair * maxP;
   int32_t* out = sel + (size_t)pair * maxP;
   if (k >= n) {
     for (int p = threadIdx.x; p < n; p += kSelBlock) out[p] = p;
-    if (threadIdx.x == 0) n_sel[pair] = n;
-    return;
+  } else if (n <= kBlk * 8) {
+    topk_block_reg<8, false>(ubg + (size_t)pair * maxP, n, k, out, smr);
+  } else if (n <= kBlk * 16) {
+    topk_block_reg<16, false>(ubg + (size_t)pair * maxP, n, k, out, smr);
+  } else {
+    topk_block<kLds, false>(ubg + (size_t)pair * maxP, n, k, out, sm);
   }
-  if constexpr (kLds) {
-    for (int p = threadIdx.x; p < n; p += kSelBlock) keys[p] = order_key(U[p]);
-  }
-  auto key_of = [&](int p) -> uint64_t {
-    if constexpr (kLds) return compose(keys[p], p);
-    else return compose(order_key(U[p]), p);
-  };
-
-  uint64_t prefix = 0, mask = 0;
-  int remaining = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int p = threadIdx.x; p < n; p += kSelBlock) {
-      const uint64_t key = key_of(p);
-      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 0xFF)], 1);
-    }
-    __syncthreads();
-    // thread t owns digit 255 - t: inclusive scan gives #keys with digit >= d
-    const int hcount = hist[255 - threadIdx.x];
-    const int incl = block_incl_scan(hcount, scan_sh);
-    const int excl = incl - hcount;
-    if (excl < remaining && remaining <= incl) {
-      s_digit = 255 - threadIdx.x;
-      s_above = excl;
-      s_cnt = hcount;
-    }
-    __syncthreads();
-    prefix |= (uint64_t)s_digit << shift;
-    mask |= (uint64_t)0xFF << shift;
-    remaining -= s_above;
-    const bool done = (s_cnt == remaining);
-    __syncthreads();
-    if (done) break;
-  }
-  const uint64_t thresh = prefix;  // selected <=> key >= thresh
-  const int got = compact_ascending(n, [&](int p) { return key_of(p) >= thresh; }, out, scan_sh);
-  if (threadIdx.x == 0) n_sel[pair] = got;
+  if (threadIdx.x == 0) n_sel[pair] = k;
 }
 
 // --------------------------------------------------------------------------

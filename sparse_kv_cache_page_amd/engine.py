@@ -25,7 +25,7 @@ from .binding import CacheShape
 class PagedEntmaxDecoder:
     def __init__(self, shape: CacheShape, *, policy: str = "topk", top_k: int = 256,
                  alpha: float = 1.5, scale: float = 1.0, delta: float = 0.1,
-                 device: Optional[torch.device] = None):
+                 device: Optional[torch.device] = None, fused: bool = False):
         if policy not in ("topk", "gauss", "dense"):
             raise ValueError("policy must be 'topk', 'gauss' or 'dense'")
         self.shape = s = shape
@@ -56,6 +56,14 @@ class PagedEntmaxDecoder:
         self.max_sel = min(self.top_k, mp) if policy == "topk" else mp
         ws_bytes = B.decode_workspace_bytes(s, self.max_sel)
         self.ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        # the fused step (top-k only) keeps arrival counters in its workspace:
+        # zero-filled once here, left zeroed by every call
+        self.fused = bool(fused) and policy == "topk"
+        if self.fused:
+            self.step_ws = torch.zeros(B.step_workspace_bytes(s, self.top_k), dtype=torch.uint8,
+                                       device=dev)
+            self.sel_ws = torch.zeros(B.score_select_workspace_bytes(s), dtype=torch.uint8,
+                                      device=dev)
 
     # -- metadata -----------------------------------------------------------
     def build_meta(self, K, block_table, seq_lens, first_page=None, span: int = 0):
@@ -83,8 +91,24 @@ class PagedEntmaxDecoder:
                         n_sel=None if dense else self.n_sel, max_sel=self.max_sel, tau=self.tau,
                         n_support=self.n_support)
 
+    def score_select(self, q, K, block_table, seq_lens, refresh_last_page: bool = False):
+        """[last-page refresh] + scores + top-k in one fused launch."""
+        B.score_select_pages(self.shape, q, self.scale, K, block_table, seq_lens, self.top_k,
+                             self.kmin, self.kmax, self.ubg, self.sel, self.n_sel, self.sel_ws,
+                             refresh_last_page=refresh_last_page)
+
+    def fused_step(self, q, K, V, block_table, seq_lens, refresh_last_page: bool = False):
+        """[last-page refresh] + score + top-k + decode in two fused launches."""
+        B.decode_step(self.shape, q, self.scale, self.alpha, K, V, block_table, seq_lens,
+                      self.top_k, self.kmin, self.kmax, self.ubg, self.sel, self.n_sel, self.out,
+                      self.step_ws, refresh_last_page=refresh_last_page, tau=self.tau,
+                      n_support=self.n_support)
+        return self.out, self.tau
+
     def step(self, q, K, V, block_table, seq_lens):
         """score -> select -> decode; returns (out, tau) views of the owned buffers."""
+        if self.fused:
+            return self.fused_step(q, K, V, block_table, seq_lens)
         if self.policy != "dense":
             self.score(q, block_table, seq_lens)
             self.select(seq_lens)

@@ -186,3 +186,24 @@ def test_binding_rejects_cpu_tensors(lib):
         B.build_page_meta(s, torch.zeros(4, 1, 16, 64), torch.zeros(1, 4, dtype=torch.int32),
                           torch.ones(1, dtype=torch.int32), torch.zeros(4, 1, 64),
                           torch.zeros(4, 1, 64))
+
+
+def test_step_argument_errors(lib):
+    d = desc()
+    need = lib.ekv_step_workspace_bytes(ctypes.byref(d), 4)
+    assert need > lib.ekv_decode_workspace_bytes(ctypes.byref(d), 4)
+    assert lib.ekv_step_workspace_bytes(ctypes.byref(d), 0) == 0
+
+    def call(alpha=1.5, scale=1.0, top_k=4, ws=FAKE, ws_bytes=need, q=FAKE, sel=FAKE, kmin=FAKE):
+        return lib.ekv_decode_step(ctypes.byref(d), q, scale, alpha, FAKE, FAKE, FAKE, FAKE, 1,
+                                   top_k, kmin, FAKE, FAKE, sel, FAKE, FAKE, None, None, ws,
+                                   ws_bytes, None)
+
+    assert call(alpha=1.0) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(top_k=0) == INVALID
+    assert call(q=None) == INVALID
+    assert call(sel=None) == INVALID
+    assert call(kmin=FAKE_MIS) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE

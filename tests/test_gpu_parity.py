@@ -234,3 +234,15 @@ def test_deterministic_repeat():
     for k in ("ubg", "sel", "n_sel", "out", "tau"):
         # entries past a row's pages are never written (NaN / sentinel in both)
         assert torch.equal(torch.nan_to_num(g1[k], nan=-1.0), torch.nan_to_num(g2[k], nan=-1.0)), k
+
+
+@pytest.mark.parametrize("lens", [(2100, 4000), (5000, 9000), (16500, 17500)])
+def test_topk_long_rows(lens):
+    # page size 1 gives rows of thousands of pages: the wave select (<= 4096
+    # pages), the block select with LDS keys (<= 16384) and with keys in L2
+    w = small(151, page_size=1, lens_range=lens, num_q_heads=4, num_kv_heads=2,
+              head_dim=64, q_std=2.0 / 8.0, top_k=700, planted_per_kv_head=4)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "topk")
+    for b, g in [(0, 0), (w.batch - 1, 1)]:
+        check_pair(inp, gpu, b, g, "topk")
