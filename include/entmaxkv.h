@@ -178,6 +178,31 @@ ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float s
                              size_t ws_bytes, hipStream_t stream);
 
 /*
+ * ekv_entmax_decode in one launch: the same arguments and results (up to
+ * summation order), but the tau solve and the support-row gather of each
+ * (row, KV head) are run by the last workgroup to finish that pair's key
+ * scores (one wave per query head), instead of by a second launch.  This
+ * saves a launch but holds more registers during the key stream; on the GQA
+ * decode shape it measured slower than the two-launch ekv_entmax_decode,
+ * which ekv_decode_step therefore uses.  Cross-workgroup data moves through
+ * device-coherent loads and stores and a relaxed arrival counter.
+ * ws / ws_bytes: at least ekv_decode_fused_workspace_bytes(desc, max_sel)
+ *   bytes, 256-byte aligned, ZERO-FILLED before first use; every completed
+ *   call leaves its arrival counters zero again, so the workspace can be
+ *   reused (and the call captured in a graph) without clearing.  Calls that
+ *   share a workspace must not overlap.
+ */
+ekv_status ekv_entmax_decode_fused(const ekv_cache_desc* desc, const float* q, float scale,
+                                   float alpha, const void* K, const void* V,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+                                   float* out, float* tau_out, int32_t* n_support, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/* Scratch bytes ekv_entmax_decode_fused needs (0 if desc is invalid). */
+size_t ekv_decode_fused_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);
+
+/*
  * Fused first half of a decode step with the top-k policy (§2.A + §2.B(1)):
  * the same results as
  *   ekv_build_page_meta(first_page = last page of each row, span = 1,

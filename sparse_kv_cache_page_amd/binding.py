@@ -27,6 +27,8 @@ EXPORTED = (
     "ekv_select_pages",
     "ekv_entmax_decode",
     "ekv_decode_workspace_bytes",
+    "ekv_entmax_decode_fused",
+    "ekv_decode_fused_workspace_bytes",
     "ekv_score_select_pages",
     "ekv_score_select_workspace_bytes",
     "ekv_decode_step",
@@ -82,12 +84,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_score_select_workspace_bytes.restype = sz
     lib.ekv_step_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_step_workspace_bytes.restype = sz
+    lib.ekv_entmax_decode_fused.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, vp, vp, i32, vp,
+                                            vp, vp, vp, sz, vp]
+    lib.ekv_decode_fused_workspace_bytes.argtypes = [dp, i32]
+    lib.ekv_decode_fused_workspace_bytes.restype = sz
     lib.ekv_decode_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_decode_workspace_bytes.restype = sz
     lib.ekv_status_string.argtypes = [ctypes.c_int]
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
-                 "ekv_entmax_decode", "ekv_decode_step", "ekv_score_select_pages"):
+                 "ekv_entmax_decode", "ekv_decode_step", "ekv_score_select_pages",
+                 "ekv_entmax_decode_fused"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -219,9 +226,17 @@ def decode_workspace_bytes(s: CacheShape, max_sel: int = 0) -> int:
     return int(load_library().ekv_decode_workspace_bytes(ctypes.byref(d), int(max_sel)))
 
 
+def decode_fused_workspace_bytes(s: CacheShape, max_sel: int = 0) -> int:
+    d = s.desc()
+    return int(load_library().ekv_decode_fused_workspace_bytes(ctypes.byref(d), int(max_sel)))
+
+
 def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_table, seq_lens,
-                  out, ws, sel=None, n_sel=None, max_sel: int = 0, tau=None, n_support=None):
-    """ekv_entmax_decode: alpha-entmax attention over the selected pages (all if sel is None)."""
+                  out, ws, sel=None, n_sel=None, max_sel: int = 0, tau=None, n_support=None,
+                  fused: bool = False):
+    """ekv_entmax_decode (or, with fused=True, ekv_entmax_decode_fused, whose
+    workspace must be zero-filled before first use): alpha-entmax attention
+    over the selected pages (all if sel is None)."""
     B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
     _need(q, "q", torch.float32, (B, Hq, d))
     _need(K, "K", s.kv_dtype, _kv_shape(s))
@@ -240,7 +255,8 @@ def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_tabl
             and ws.is_contiguous()):
         raise TypeError("ws must be a contiguous uint8 GPU tensor")
     d_ = s.desc()
-    _check("ekv_entmax_decode", load_library().ekv_entmax_decode(
+    name = "ekv_entmax_decode_fused" if fused else "ekv_entmax_decode"
+    _check(name, getattr(load_library(), name)(
         ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
         _ptr(block_table), _ptr(seq_lens), _ptr(sel), _ptr(n_sel), int(max_sel), _ptr(out),
         _ptr(tau), _ptr(n_support), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))

@@ -135,15 +135,25 @@ size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel) {
   if (make_shape(desc, &s) != EKV_OK) return 0;
   if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return 0;
-  return ekv::make_decode_plan(s, max_sel).total;
+  return ekv::make_decode_plan(s, max_sel, false).total;
 }
 
-ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float scale,
-                             float alpha, const void* K, const void* V,
-                             const int32_t* block_table, const int32_t* seq_lens,
-                             const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
-                             float* out, float* tau_out, int32_t* n_support, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+size_t ekv_decode_fused_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK) return 0;
+  if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return 0;
+  return ekv::make_decode_plan(s, max_sel, true).total;
+}
+
+}  // extern "C"
+
+static ekv_status decode_common(const ekv_cache_desc* desc, const float* q, float scale,
+                                float alpha, const void* K, const void* V,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+                                float* out, float* tau_out, int32_t* n_support, void* ws,
+                                size_t ws_bytes, bool fused, hipStream_t stream) {
   Shape s;
   ekv_status st = make_shape(desc, &s);
   if (st != EKV_OK) return st;
@@ -158,10 +168,32 @@ ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float s
   if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
   if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
-  const ekv::DecodePlan plan = ekv::make_decode_plan(s, max_sel);
+  const ekv::DecodePlan plan = ekv::make_decode_plan(s, max_sel, fused);
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < plan.total) return EKV_ERR_WORKSPACE;
   return from_hip(ekv::launch_decode(s, plan, q, scale, alpha, K, V, block_table, seq_lens, sel,
-                                     n_sel, out, tau_out, n_support, ws, stream));
+                                     n_sel, out, tau_out, n_support, ws, fused, stream));
+}
+
+extern "C" {
+
+ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float scale,
+                             float alpha, const void* K, const void* V,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+                             float* out, float* tau_out, int32_t* n_support, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  return decode_common(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel, max_sel,
+                       out, tau_out, n_support, ws, ws_bytes, false, stream);
+}
+
+ekv_status ekv_entmax_decode_fused(const ekv_cache_desc* desc, const float* q, float scale,
+                                   float alpha, const void* K, const void* V,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
+                                   float* out, float* tau_out, int32_t* n_support, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  return decode_common(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel, max_sel,
+                       out, tau_out, n_support, ws, ws_bytes, true, stream);
 }
 
 // Arrival counters of the fused score + select launch: B*Hkv ints, zero
@@ -202,7 +234,7 @@ size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k) {
   if (make_shape(desc, &s) != EKV_OK || top_k < 1) return 0;
   const int max_sel = top_k < s.maxP ? top_k : s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return 0;
-  return step_counter_bytes(s) + ekv::make_decode_plan(s, max_sel).total;
+  return step_counter_bytes(s) + ekv::make_decode_plan(s, max_sel, false).total;
 }
 
 ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
@@ -222,7 +254,7 @@ ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float sca
   const int max_sel = top_k < s.maxP ? top_k : s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
   const size_t cbytes = step_counter_bytes(s);
-  const size_t dbytes = ekv::make_decode_plan(s, max_sel).total;
+  const size_t dbytes = ekv::make_decode_plan(s, max_sel, false).total;
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < cbytes + dbytes) return EKV_ERR_WORKSPACE;
   st = ekv_score_select_pages(desc, q, scale, K, block_table, seq_lens, refresh_last_page, top_k,
                               kmin, kmax, ubg, sel, n_sel, ws, cbytes, stream);

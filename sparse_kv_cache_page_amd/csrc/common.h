@@ -51,6 +51,22 @@ __device__ inline uint4 load16(const void* p) {
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Reinterpret 16 bytes as the 8-element bf16 vector of an MFMA operand.
+__device__ inline bf16x8_t as_bf16x8(const uint4& w) {
+  const u32x4_t v = {w.x, w.y, w.z, w.w};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Round-to-nearest-even of a finite fp32 value to the nearest bf16 value
+// (returned as fp32).
+__device__ inline float bf16_round(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+  return __uint_as_float(r);
+}
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Streaming loads for data touched once per step (K/V tiles, page metadata).

@@ -24,6 +24,8 @@
 //     are at most 64 candidates), and then reads only the value rows with
 //     z_i > tau -- the weights off the support are exact zeros:
 //         out = sum_i p_i v_i / sum_i p_i,   p_i = (z_i - tau)^gamma.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -45,19 +47,280 @@ struct Geo {
 
 __device__ inline int bits_of(float x) { return __float_as_int(x); }
 
+constexpr int kTailCap = 512;  // LDS candidates per head in the fused tail
+
+// Everything the fused tau / PV tail needs beyond the qk arguments.
+template <typename T>
+struct TailArgs {
+  const T* V;
+  int* counters;      // [B*Hkv] arrival counters, zero between launches
+  double alpha, gamma;
+  int gamma_int;
+  float* out;
+  float* tau_out;
+  int32_t* n_support;
+};
+
+struct TailLds {
+  float cz[kBlock / kWave][kTailCap];
+  int ct[kBlock / kWave][kTailCap];
+  int offs[kBlock / kWave][kWave + 1];
+  float sp[kBlock / kWave][kWave];
+  int st[kBlock / kWave][kWave];
+};
+
+__device__ inline uint64_t pack_cand(float z, int ptok) {
+  return ((uint64_t)(uint32_t)ptok << 32) | (uint64_t)__float_as_uint(z);
+}
+
+__device__ inline double pos_pow(double x, double gamma, int gi) {
+  // x > 0
+  if (gi > 0) {
+    double r = x;
+    for (int i = 1; i < gi; ++i) r *= x;
+    return r;
+  }
+  return pow(x, gamma);
+}
+
+__device__ inline int wave_incl_scan_i(int x) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Bracketed Newton for f(tau) = sum [z - tau]_+^gamma - 1 = 0 on
+// [zmax - 1, zmax - n^(1-alpha)]; eval(tau, f, fd) returns the (uniform)
+// sums f = sum [z - tau]_+^gamma and fd = gamma sum [z - tau]_+^(gamma-1).
+template <typename Eval>
+__device__ inline double newton_tau(double zmax, double nvalid, double alpha, Eval&& eval) {
+  double lo = zmax - 1.0;
+  double hi = zmax - pow(nvalid, 1.0 - alpha);
+  if (hi < lo) hi = lo;
+  double tau = lo;
+  for (int it = 0; it < 200; ++it) {
+    double f, fd;
+    eval(tau, f, fd);
+    f -= 1.0;
+    if (f == 0.0) break;
+    if (f > 0.0) lo = tau;
+    else hi = tau;
+    double nt = fd > 0.0 ? tau + f / fd : 0.5 * (lo + hi);
+    // a Newton step below fp64 resolution means converged (checked before the
+    // bracket test, which would otherwise turn it into a bisection jump)
+    if (fd > 0.0 && fabs(nt - tau) <= 4e-16 * fmax(1.0, fabs(tau))) {
+      tau = nt > lo && nt < hi ? nt : tau;
+      break;
+    }
+    if (!(nt > lo && nt < hi)) {
+      nt = 0.5 * (lo + hi);
+      if (!(nt > lo && nt < hi)) break;
+    }
+    tau = nt;
+  }
+  return tau;
+}
+
+__device__ inline void tau_term(double z, double tau, double gamma, int gamma_int, double& f,
+                                double& fd) {
+  const double x = z - tau;
+  if (x > 0.0) {
+    const double xg1 = gamma_int == 1 ? 1.0 : pos_pow(x, gamma - 1.0, gamma_int - 1);
+    f += xg1 * x;
+    fd += gamma * xg1;
+  }
+}
+
+// The tau / PV tail of one (row b, KV head g), run by the last workgroup to
+// finish that pair's qk items; wave w handles query heads w, w+4, ...  All
+// cross-workgroup data is read with device-coherent loads.
 template <typename T, int D, int G>
+__device__ __forceinline__ void pair_tail(const float2* __restrict__ cand,
+                                          const int* __restrict__ cnt,
+                                          const float* __restrict__ smax, int splits,
+                                          const TailArgs<T>& ta, int b, int g, int Hkv, int P,
+                                          int log2P, int L, int nsel, int nsel_raw, int max_sel,
+                                          bool has_sel, TailLds& tl) {
+  using GE = Geo<T, D>;
+  constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kR = GE::kR;
+  constexpr int kRowsW = kWave / kLpr;  // value rows per wave pass
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int Hq = Hkv * G;
+  const size_t tile_stride = (size_t)P * D;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  float* cz = tl.cz[wave];
+  int* ct = tl.ct[wave];
+  int* offs = tl.offs[wave];
+  for (int h = wave; h < G; h += kBlock / kWave) {
+    const size_t bh = (size_t)b * Hq + g * G + h;
+    if (nsel_raw > max_sel || nsel_raw < 1) {
+      for (int t = lane; t < D; t += kWave) ta.out[bh * D + t] = __builtin_nanf("");
+      if (lane == 0) {
+        if (ta.tau_out) ta.tau_out[bh] = __builtin_nanf("");
+        if (ta.n_support) ta.n_support[bh] = -1;
+      }
+      continue;
+    }
+    const int nsplit = ((nsel << log2P) + kR - 1) / kR;
+    const float* smax_bh = smax + bh * splits;
+    const int* cnt_bh = cnt + bh * splits;
+    const uint64_t* cand_bh = reinterpret_cast<const uint64_t*>(cand) + bh * splits * kR;
+    float zm = -__builtin_huge_valf();
+    for (int s = lane; s < nsplit; s += kWave)
+      zm = fmaxf(zm, __hip_atomic_load(smax_bh + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    zm = wave_max_f32(zm);
+    const double zmax = (double)zm;
+    const double thr = zmax - 1.0;
+
+    // walk every split's candidates in split order, 64 at a time; fn(z, ptok,
+    // keep) is called by the whole wave, keep = the candidate clears zmax - 1
+    auto walk = [&](auto&& fn) {
+      for (int s0 = 0; s0 < nsplit; s0 += kWave) {
+        const int s = s0 + lane;
+        const int c = s < nsplit ? __hip_atomic_load(cnt_bh + s, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) : 0;
+        const int incl = wave_incl_scan_i(c);
+        const int tot = __shfl(incl, kWave - 1, kWave);
+        offs[lane] = incl - c;
+        if (lane == kWave - 1) offs[kWave] = incl;
+        __builtin_amdgcn_wave_barrier();
+        for (int k0 = 0; k0 < tot; k0 += kWave) {
+          const int k = k0 + lane;
+          float z = -__builtin_huge_valf();
+          int ptok = 0;
+          if (k < tot) {
+            int lo = 0, hi = kWave;  // offs[lo] <= k < offs[hi]
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (offs[mid] <= k) lo = mid;
+              else hi = mid;
+            }
+            const uint64_t e = __hip_atomic_load(cand_bh + (size_t)(s0 + lo) * kR + (k - offs[lo]),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            z = __uint_as_float((uint32_t)e);
+            ptok = (int)(e >> 32);
+          }
+          fn(z, ptok, (double)z > thr);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    };
+    int count = 0;
+    walk([&](float z, int ptok, bool keep) {
+      const uint64_t mask = __ballot(keep);
+      const int pos = count + __popcll(mask & lt);
+      if (keep && pos < kTailCap) {
+        cz[pos] = z;
+        ct[pos] = ptok;
+      }
+      count += __popcll(mask);
+    });
+    __builtin_amdgcn_wave_barrier();
+    const bool overflow = count > kTailCap;
+    const double nvalid = has_sel ? (double)nsel * P : (double)L;
+    const double tau = newton_tau(zmax, nvalid, ta.alpha, [&](double tt, double& f, double& fd) {
+      f = 0.0;
+      fd = 0.0;
+      if (!overflow) {
+        for (int c = lane; c < count; c += kWave) tau_term((double)cz[c], tt, ta.gamma, ta.gamma_int, f, fd);
+      } else {
+        walk([&](float z, int, bool keep) {
+          if (keep) tau_term((double)z, tt, ta.gamma, ta.gamma_int, f, fd);
+        });
+      }
+      f = wave_sum_f64(f);
+      fd = wave_sum_f64(fd);
+    });
+
+    // weights and the value rows of the support, 64 candidates at a time
+    float acc[kVec];
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) acc[v] = 0.0f;
+    double psum = 0.0;
+    int nsupp = 0;
+    const int c_in = lane % kLpr;
+    const int rsub = lane / kLpr;
+    float* sp = tl.sp[wave];
+    int* st = tl.st[wave];
+    auto pv_group = [&](float z, int ptok, bool keep) {
+      const double x = (double)z - tau;
+      const bool flag = keep && x > 0.0;
+      const uint64_t mask = __ballot(flag);
+      const int m = __popcll(mask);
+      if (flag) {
+        const float p = (float)pos_pow(x, ta.gamma, ta.gamma_int);
+        sp[__popcll(mask & lt)] = p;
+        st[__popcll(mask & lt)] = ptok;
+        psum += (double)p;
+      }
+      nsupp += m;
+      __builtin_amdgcn_wave_barrier();
+      for (int r0 = 0; r0 < m; r0 += kRowsW) {
+        const int r = r0 + rsub;
+        if (r < m) {
+          const int pt = st[r];
+          const float p = sp[r];
+          const T* row = ta.V + (size_t)(pt >> log2P) * Hkv * tile_stride + g * tile_stride +
+                         (size_t)(pt & (P - 1)) * D + c_in * kVec;
+          float xv[kVec];
+          Elem<T>::unpack(load16(row), xv);
+#pragma unroll
+          for (int v = 0; v < kVec; ++v) acc[v] = fmaf(p, xv[v], acc[v]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+    if (!overflow) {
+      for (int k0 = 0; k0 < count; k0 += kWave) {
+        const int k = k0 + lane;
+        pv_group(k < count ? cz[k] : -__builtin_huge_valf(), k < count ? ct[k] : 0, k < count);
+      }
+    } else {
+      walk(pv_group);
+    }
+#pragma unroll
+    for (int o = kLpr; o < kWave; o <<= 1) {
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) acc[v] += __shfl_xor(acc[v], o, kWave);
+    }
+    const double ps = wave_sum_f64(psum);
+    const float inv = (float)(1.0 / ps);
+    if (lane < kLpr) {
+      float* o = ta.out + bh * D + c_in * kVec;
+#pragma unroll
+      for (int v = 0; v < kVec; v += 4)
+        *reinterpret_cast<float4*>(o + v) =
+            make_float4(acc[v] * inv, acc[v + 1] * inv, acc[v + 2] * inv, acc[v + 3] * inv);
+    }
+    if (lane == 0) {
+      if (ta.tau_out) ta.tau_out[bh] = (float)tau;
+      if (ta.n_support) ta.n_support[bh] = nsupp;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <typename T, int D, int G, bool kFused, bool kMfma = std::is_same<T, bf16_t>::value>
 __global__ __launch_bounds__(kBlock) void qk_kernel(
     const float* __restrict__ q, float zscale, const T* __restrict__ K,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel, int max_sel, int Hkv,
     int P, int log2P, int maxP, int splits, long long n_items, float2* __restrict__ cand,
-    int* __restrict__ cnt, float* __restrict__ smax) {
+    int* __restrict__ cnt, float* __restrict__ smax, TailArgs<T> ta) {
   using GE = Geo<T, D>;
   constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kRowsPerPass = GE::kRowsPerPass, kR = GE::kR;
   static_assert(G <= kLpr, "lane c < G stores head c");
   __shared__ float zl[G][kR];
   __shared__ int pg_phys[kR + 1];
   __shared__ int pg_valid[kR + 1];
+  struct NoTail {};
+  __shared__ std::conditional_t<kFused, TailLds, NoTail> tl;
+  __shared__ int s_last;
 
   const int c = threadIdx.x % kLpr;
   const int rg = threadIdx.x / kLpr;
@@ -87,6 +350,86 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(
       pg_phys[i] = bt[(size_t)b * maxP + page];
       pg_valid[i] = page_valid(L, page, P);
     }
+    if constexpr (kMfma) {
+      // ---- matrix cores: [16 tokens x d] . [d x (G heads x 3 bf16 parts)] ----
+      // A rows m = 4*head + part hold q split exactly into three bf16 parts
+      // (hi, mid, lo; part 3 is zero), B = K^T of 16 tokens.  Lane l ends with
+      // the partial scores of head l/16 (+4 for the second A block) for token
+      // l%16 in its 4 accumulators; their sum is the fp32 score.
+      constexpr int kKK = D / 32;                            // k steps of 32 dims
+      constexpr int kBlocksA = G > 4 ? 2 : 1;
+      constexpr int kGroups = kR / 16;                       // 16-token groups per item
+      constexpr int kGPW = kGroups / (kBlock / kWave);       // groups per wave
+      const int mrow = lane % 16;
+      const int kq = lane / 16;
+      bf16x8_t qa[kBlocksA][kKK];
+#pragma unroll
+      for (int ab = 0; ab < kBlocksA; ++ab) {
+        const int h = ab * 4 + mrow / 4;
+        const int part = mrow % 4;
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          if (h < G && part < 3) {
+            const float4* qh = reinterpret_cast<const float4*>(
+                q + ((size_t)b * Hq + g * G + h) * D + kk * 32 + kq * 8);
+            const float4 x0 = qh[0], x1 = qh[1];
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint16_t bits[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float hi = bf16_round(xs[i]);
+              const float mid = bf16_round(xs[i] - hi);
+              const float lo = bf16_round(xs[i] - hi - mid);
+              const float v = part == 0 ? hi : (part == 1 ? mid : lo);
+              bits[i] = (uint16_t)(__float_as_uint(v) >> 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (uint32_t)bits[2 * i] | ((uint32_t)bits[2 * i + 1] << 16);
+          }
+          qa[ab][kk] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      }
+      __syncthreads();
+
+      uint4 kb[kGPW][kKK];
+      bool valid[kGPW];
+#pragma unroll
+      for (int u = 0; u < kGPW; ++u) {
+        const int grp = wave * kGPW + u;
+        const int r = r_begin + grp * 16 + mrow;
+        valid[u] = false;
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) kb[u][kk] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < r_end) {
+          const int jl = (r >> log2P) - j_begin;
+          const int t = r & (P - 1);
+          if (t < pg_valid[jl]) {
+            valid[u] = true;
+            const T* row = K + (size_t)pg_phys[jl] * Hkv * tile_stride + g * tile_stride +
+                           (size_t)t * D + kq * 8;
+#pragma unroll
+            for (int kk = 0; kk < kKK; ++kk) kb[u][kk] = load16_stream(row + kk * 32);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kGPW; ++u) {
+        const int rl = (wave * kGPW + u) * 16 + mrow;  // slot inside the item
+#pragma unroll
+        for (int ab = 0; ab < kBlocksA; ++ab) {
+          f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kk = 0; kk < kKK; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ab][kk], as_bf16x8(kb[u][kk]), acc,
+                                                          0, 0, 0);
+          const int h = ab * 4 + kq;
+          if (h < G)
+            zl[h][rl] = valid[u] ? ((acc[0] + acc[1]) + acc[2]) * zscale : -__builtin_huge_valf();
+        }
+      }
+      __syncthreads();
+    } else {
     float qf[G][kVec];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -138,6 +481,8 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(
     }
     __syncthreads();
 
+    }
+
     // one wave per head: split maximum, then the candidates z > max - 1
     const int nrows = r_end - r_begin;
     for (int h = wave; h < G; h += kBlock / kWave) {
@@ -158,28 +503,47 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(
           const int rr = r_begin + r;
           const int jl = (rr >> log2P) - j_begin;
           const int ptok = pg_phys[jl] * P + (rr & (P - 1));
-          out[total + __popcll(mask & lt)] = make_float2(z, __int_as_float(ptok));
+          if constexpr (kFused)
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(out) + total + __popcll(mask & lt),
+                               pack_cand(z, ptok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            out[total + __popcll(mask & lt)] = make_float2(z, __int_as_float(ptok));
         }
         total += __popcll(mask);
       }
       if (lane == 0) {
-        cnt[bh * splits + s] = total;
-        smax[bh * splits + s] = m;
+        if constexpr (kFused) {
+          __hip_atomic_store(cnt + bh * splits + s, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(smax + bh * splits + s, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          cnt[bh * splits + s] = total;
+          smax[bh * splits + s] = m;
+        }
+      }
+    }
+    if constexpr (kFused) {
+      // arrival: this item's device-coherent stores drain, the block counts
+      // itself once, and the last item of the pair runs the tau / PV tail
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int nsplit = ((nsel << log2P) + kR - 1) / kR;
+        s_last = __hip_atomic_fetch_add(ta.counters + pair, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+      }
+      __syncthreads();
+      if (s_last) {
+        const int nsel_raw = sel ? n_sel[pair] : np;
+        pair_tail<T, D, G>(cand, cnt, smax, splits, ta, b, g, Hkv, P, log2P, L, nsel, nsel_raw,
+                           max_sel, sel != nullptr, tl);
+        if (threadIdx.x == 0)
+          __hip_atomic_store(ta.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();  // zl and the page map are reused by the next item
   }
 }
 
-__device__ inline double pos_pow(double x, double gamma, int gi) {
-  // x > 0
-  if (gi > 0) {
-    double r = x;
-    for (int i = 1; i < gi; ++i) r *= x;
-    return r;
-  }
-  return pow(x, gamma);
-}
 
 // Sum two doubles over the block (fixed order, so results are reproducible).
 __device__ inline void block_sum2(double& a, double& b, double* sh) {
@@ -462,16 +826,19 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
   if (n_support && threadIdx.x == 0) n_support[bh] = nsupp;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kFused>
 hipError_t launch_qk_t(const Shape& s, const DecodePlan& pl, const float* q, float zscale,
                        const void* K, const int32_t* bt, const int32_t* lens, const int32_t* sel,
                        const int32_t* n_sel, float2* cand, int* cnt, float* smax,
-                       hipStream_t stream) {
+                       const TailArgs<T>& ta, hipStream_t stream) {
   const long long items = (long long)s.B * s.Hkv * pl.splits;
-  const long long grid = items < pl.qk_grid_cap ? items : pl.qk_grid_cap;
-  hipLaunchKernelGGL((qk_kernel<T, D, G>), dim3((unsigned)grid), dim3(kBlock), 0, stream, q,
-                     zscale, (const T*)K, bt, lens, sel, n_sel, pl.max_sel, s.Hkv, s.P, s.log2P,
-                     s.maxP, pl.splits, items, cand, cnt, smax);
+  // the fused variant keeps its tail's registers: 2 resident blocks per CU,
+  // so one round of persistent blocks; the plain variant fits 4 per CU
+  const long long cap = kFused ? 256LL * 2 : pl.qk_grid_cap;
+  const long long grid = items < cap ? items : cap;
+  hipLaunchKernelGGL((qk_kernel<T, D, G, kFused>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                     q, zscale, (const T*)K, bt, lens, sel, n_sel, pl.max_sel, s.Hkv, s.P,
+                     s.log2P, s.maxP, pl.splits, items, cand, cnt, smax, ta);
   return hipGetLastError();
 }
 
@@ -480,23 +847,34 @@ hipError_t launch_decode_t(const Shape& s, const DecodePlan& pl, const float* q,
                            float alpha, const void* K, const void* V, const int32_t* bt,
                            const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
                            float* out, float* tau_out, int32_t* n_support, void* ws,
-                           hipStream_t stream) {
+                           bool fused, hipStream_t stream) {
   float2* cand = (float2*)((char*)ws + pl.cand_off);
   int* cnt = (int*)((char*)ws + pl.cnt_off);
   float* smax = (float*)((char*)ws + pl.smax_off);
   const double a1 = (double)alpha - 1.0;
   const float zscale = (float)(a1 * (double)scale);
-  hipError_t e = hipErrorInvalidValue;
-  switch (s.G) {
-    case 1: e = launch_qk_t<T, D, 1>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
-    case 2: e = launch_qk_t<T, D, 2>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
-    case 4: e = launch_qk_t<T, D, 4>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
-    case 8: e = launch_qk_t<T, D, 8>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, stream); break;
-  }
-  if (e != hipSuccess) return e;
   const double gamma = 1.0 / a1;
   const double gr = rint(gamma);
   const int gamma_int = (gr >= 1.0 && gr <= 64.0 && fabs(gamma - gr) <= 1e-12 * gr) ? (int)gr : 0;
+  TailArgs<T> ta{(const T*)V, fused ? (int*)((char*)ws + pl.counter_off) : nullptr, (double)alpha,
+                 gamma_int ? gr : gamma, gamma_int, out, tau_out, n_support};
+  hipError_t e = hipErrorInvalidValue;
+  if (fused) {
+    switch (s.G) {
+      case 1: e = launch_qk_t<T, D, 1, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+      case 2: e = launch_qk_t<T, D, 2, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+      case 4: e = launch_qk_t<T, D, 4, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+      case 8: e = launch_qk_t<T, D, 8, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+    }
+    return e;
+  }
+  switch (s.G) {
+    case 1: e = launch_qk_t<T, D, 1, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+    case 2: e = launch_qk_t<T, D, 2, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+    case 4: e = launch_qk_t<T, D, 4, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+    case 8: e = launch_qk_t<T, D, 8, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+  }
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((tau_pv_kernel<T, D>), dim3(s.B * s.Hq), dim3(kBlock), 0, stream, cand, cnt,
                      smax, pl.splits, (const T*)V, lens, n_sel, sel != nullptr, pl.max_sel, s.Hq,
                      s.Hkv, s.P, s.log2P, (double)alpha, gamma_int ? gr : gamma, gamma_int, out,
@@ -519,7 +897,7 @@ bool decode_shape_supported(const Shape& s, int max_sel) {
   return splits <= kMaxSplits && (long long)s.Np * s.P < (1LL << 31);
 }
 
-DecodePlan make_decode_plan(const Shape& s, int max_sel) {
+DecodePlan make_decode_plan(const Shape& s, int max_sel, bool fused) {
   DecodePlan pl{};
   pl.max_sel = max_sel;
   pl.slots_per_item = slots_per_item(s);
@@ -527,7 +905,9 @@ DecodePlan make_decode_plan(const Shape& s, int max_sel) {
   pl.splits = (int)((slots + pl.slots_per_item - 1) / pl.slots_per_item);
   pl.qk_grid_cap = 256LL * 16;  // CUs x resident workgroups; items beyond loop
   const size_t heads = (size_t)s.B * s.Hq;
-  pl.cand_off = 0;
+  pl.counter_off = 0;
+  pl.counter_bytes = fused ? align256((size_t)s.B * s.Hkv * sizeof(int)) : 0;
+  pl.cand_off = pl.counter_off + pl.counter_bytes;
   pl.cand_bytes = align256(heads * pl.splits * (size_t)pl.slots_per_item * sizeof(float) * 2);
   pl.cnt_off = pl.cand_off + pl.cand_bytes;
   pl.cnt_bytes = align256(heads * pl.splits * sizeof(int));
@@ -540,16 +920,16 @@ DecodePlan make_decode_plan(const Shape& s, int max_sel) {
 hipError_t launch_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,
                          float alpha, const void* K, const void* V, const int32_t* bt,
                          const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
-                         float* out, float* tau_out, int32_t* n_support, void* ws,
+                         float* out, float* tau_out, int32_t* n_support, void* ws, bool fused,
                          hipStream_t stream) {
   if (s.bf16) {
     if (s.D == 128)
-      return launch_decode_t<bf16_t, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, stream);
-    return launch_decode_t<bf16_t, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, stream);
+      return launch_decode_t<bf16_t, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
+    return launch_decode_t<bf16_t, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
   }
   if (s.D == 128)
-    return launch_decode_t<float, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, stream);
-  return launch_decode_t<float, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, stream);
+    return launch_decode_t<float, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
+  return launch_decode_t<float, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
 }
 
 }  // namespace ekv

@@ -48,6 +48,7 @@ struct DecodePlan {
   int slots_per_item;   // token slots per qk work item
   int splits;           // ceil(max_sel * P / slots_per_item)
   long long qk_grid_cap;
+  size_t counter_off, counter_bytes;  // fused tail only: int [B*Hkv], zero between launches
   size_t cand_off, cand_bytes;  // (z, physical token) [B*Hq][splits][slots_per_item]
   size_t cnt_off, cnt_bytes;    // int   [B*Hq][splits]
   size_t smax_off, smax_bytes;  // fp32  [B*Hq][splits]
@@ -55,12 +56,12 @@ struct DecodePlan {
 };
 
 bool decode_shape_supported(const Shape& s, int max_sel);
-DecodePlan make_decode_plan(const Shape& s, int max_sel);
+DecodePlan make_decode_plan(const Shape& s, int max_sel, bool fused);
 
 hipError_t launch_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,
                          float alpha, const void* K, const void* V, const int32_t* bt,
                          const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
-                         float* out, float* tau_out, int32_t* n_support, void* ws,
+                         float* out, float* tau_out, int32_t* n_support, void* ws, bool fused,
                          hipStream_t stream);
 
 }  // namespace ekv

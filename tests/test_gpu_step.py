@@ -1,10 +1,10 @@
 """GPU tests of the fused decode step (ekv_decode_step).
 
-The fused path must give bit-identical selections, outputs and thresholds to
-the sequence of separate entry points on the same inputs (it runs the same
-arithmetic), leave its workspace reusable (arrival counters back at zero), and
-replay correctly from a captured HIP graph.  Selected pairs are also checked
-against the CPU oracle.
+The fused path must give bit-identical bounds and selections to the sequence
+of separate entry points on the same inputs (same scoring arithmetic), and
+the same outputs and thresholds (same decode kernels); it must leave its
+workspace reusable (arrival counters back at zero) and replay correctly from
+a captured HIP graph.  Selected pairs are also checked against the CPU oracle.
 """
 import numpy as np
 import pytest
@@ -118,6 +118,7 @@ def test_fused_step_workspace_reusable():
         outs.append((f.out.clone(), f.sel.clone(), f.n_sel.clone()))
         ncnt = s.batch * s.num_kv_heads
         assert int(f.step_ws[: 4 * ncnt].view(torch.int32).abs().sum()) == 0
+        assert int(f.sel_ws[: 4 * ncnt].view(torch.int32).abs().sum()) == 0
     for o in outs[1:]:
         assert torch.equal(o[0], outs[0][0]) and torch.equal(o[2], outs[0][2])
 
@@ -156,3 +157,48 @@ def test_fused_step_graph_replay():
             assert torch.equal(f.out, out0) and torch.equal(f.tau, tau0), f"replay {r}"
             # unrelated eager work between replays
             torch.randn(1000, device=DEV).sum().item()
+
+
+@pytest.mark.parametrize("alpha,q_std,L,policy", [
+    (1.5, 0.001, 8192, "dense"),      # every token within 1 of the max: > 512 candidates
+    (2.0, 0.002, 3000, "dense"),
+    (1.25, 0.05, 20000, "dense"),
+    (1.5, 0.18, 5000, "dense"),
+    (1.5, 0.01, 30000, "topk"),
+])
+def test_fused_decode_against_oracle(alpha, q_std, L, policy):
+    # ekv_entmax_decode_fused (tau / PV in the last workgroup of each pair)
+    w = small(501, batch=2, num_q_heads=8, num_kv_heads=2, lens_range=None, seq_len=L,
+              alpha=alpha, q_std=q_std, planted_per_kv_head=0, policy=policy, top_k=300)
+    inp = wl.make_inputs(w, device=DEV)
+    s = cache_shape(inp)
+    dec = PagedEntmaxDecoder(s, policy=policy, top_k=w.top_k, alpha=alpha, scale=w.scale)
+    dec.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
+    if policy == "topk":
+        dec.score(inp["q"], inp["block_table"], inp["seq_lens"])
+        dec.select(inp["seq_lens"])
+    ws = torch.zeros(B.decode_fused_workspace_bytes(s, dec.max_sel), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.full_like(dec.out, float("nan"))
+    tau = torch.full_like(dec.tau, float("nan"))
+    dense = policy == "dense"
+    for _ in range(2):   # the second call reuses the workspace as left by the first
+        B.entmax_decode(s, inp["q"], w.scale, alpha, inp["K"], inp["V"], inp["block_table"],
+                        inp["seq_lens"], out, ws, sel=None if dense else dec.sel,
+                        n_sel=None if dense else dec.n_sel, max_sel=dec.max_sel, tau=tau,
+                        fused=True)
+        torch.cuda.synchronize()
+    gpu = dict(kmin=dec.kmin, kmax=dec.kmax, ubg=dec.ubg, sel=dec.sel, n_sel=dec.n_sel, out=out,
+               tau=tau)
+    from oracle import pipeline
+    from gpu_util import OUT_TOL, TAU_TOL, TAU_TOL_REL
+    G = w.group
+    for b, g in [(0, 0), (1, 1)]:
+        ref = pipeline.run_pair(inp, b, g, policy)
+        t = tau[b, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
+        tol = np.maximum(TAU_TOL, TAU_TOL_REL * np.abs(ref["tau"]))
+        assert np.all(np.abs(t - ref["tau"]) <= tol), (t, ref["tau"])
+        o = out[b, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
+        for h in range(G):
+            err = np.linalg.norm(o[h] - ref["o"][h]) / np.linalg.norm(ref["o"][h])
+            assert err <= OUT_TOL, err
