@@ -320,6 +320,7 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(
   __shared__ int pg_valid[kR + 1];
   struct NoTail {};
   __shared__ std::conditional_t<kFused, TailLds, NoTail> tl;
+  __shared__ __attribute__((aligned(16))) uint16_t qparts[kMfma ? G : 1][3][kMfma ? D : 8];
   __shared__ int s_last;
 
   const int c = threadIdx.x % kLpr;
@@ -362,6 +363,18 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(
       constexpr int kGPW = kGroups / (kBlock / kWave);       // groups per wave
       const int mrow = lane % 16;
       const int kq = lane / 16;
+      // split q once per workgroup: qparts[h][part][dim] (bf16 bits)
+      for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+        const int h = idx / D, dd = idx % D;
+        const float x = q[((size_t)b * Hq + g * G + h) * D + dd];
+        const float hi = bf16_round(x);
+        const float mid = bf16_round(x - hi);
+        const float lo = bf16_round(x - hi - mid);
+        qparts[h][0][dd] = (uint16_t)(__float_as_uint(hi) >> 16);
+        qparts[h][1][dd] = (uint16_t)(__float_as_uint(mid) >> 16);
+        qparts[h][2][dd] = (uint16_t)(__float_as_uint(lo) >> 16);
+      }
+      __syncthreads();
       bf16x8_t qa[kBlocksA][kKK];
 #pragma unroll
       for (int ab = 0; ab < kBlocksA; ++ab) {
@@ -369,28 +382,11 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(
         const int part = mrow % 4;
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          if (h < G && part < 3) {
-            const float4* qh = reinterpret_cast<const float4*>(
-                q + ((size_t)b * Hq + g * G + h) * D + kk * 32 + kq * 8);
-            const float4 x0 = qh[0], x1 = qh[1];
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            uint16_t bits[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float hi = bf16_round(xs[i]);
-              const float mid = bf16_round(xs[i] - hi);
-              const float lo = bf16_round(xs[i] - hi - mid);
-              const float v = part == 0 ? hi : (part == 1 ? mid : lo);
-              bits[i] = (uint16_t)(__float_as_uint(v) >> 16);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (uint32_t)bits[2 * i] | ((uint32_t)bits[2 * i + 1] << 16);
-          }
-          qa[ab][kk] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+          uint4 w = make_uint4(0u, 0u, 0u, 0u);
+          if (h < G && part < 3) w = *reinterpret_cast<const uint4*>(&qparts[h][part][kk * 32 + kq * 8]);
+          qa[ab][kk] = as_bf16x8(w);
         }
       }
-      __syncthreads();
 
       uint4 kb[kGPW][kKK];
       bool valid[kGPW];
