@@ -27,6 +27,16 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+# sources whose change invalidates recorded HBM counters, per entry point
+KERNEL_SOURCES = {
+    "ekv_score_select_pages": ["score.hip", "blocks.h", "common.h", "kernels.h"],
+    "ekv_entmax_decode": ["decode.hip", "common.h", "kernels.h"],
+    "ekv_score_pages": ["score.hip", "blocks.h", "common.h", "kernels.h"],
+    "ekv_select_pages": ["select.hip", "blocks.h", "common.h", "kernels.h"],
+    "ekv_build_page_meta": ["meta.hip", "blocks.h", "common.h", "kernels.h"],
+}
 ENTRY_POINT = {"refresh": "ekv_build_page_meta", "score": "ekv_score_pages",
                "select": "ekv_select_pages", "decode": "ekv_entmax_decode",
                "score_select": "ekv_score_select_pages"}
@@ -49,6 +59,9 @@ def parse():
     ap.add_argument("--top-k", type=int, default=None)
     ap.add_argument("--temperature", type=float, default=None,
                     help="query std * sqrt(d) (stress workload)")
+    ap.add_argument("--counter-summary", default="", metavar="CSV",
+                    help="only summarise a rocprofv3 --pmc counter_collection.csv per kernel "
+                         "(dispatches, mean counter value, mean duration) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (reference for "
                          "HBM byte counters) and exit")
@@ -201,11 +214,36 @@ def time_steps(layers, steps, warmup, graph):
     return start.elapsed_time(end) / steps, wall
 
 
-def time_stages(layers, steps, policy):
-    """Average duration (ms) of each entry point, HIP events on the launch stream."""
+def time_stages(layers, steps, graph):
+    """Average duration (ms) of one launch of each entry point.
+
+    With graphs: one graph per entry point holding its launches for every
+    rotated layer in turn; it is replayed between two HIP events on the launch
+    stream, so the figure is the kernel time plus the dispatch gap between two
+    graph nodes.  Without graphs: events around every eager launch.
+    """
     import torch
     names = layers[0].stages
     R = len(layers)
+    res = {}
+    if graph:
+        reps = max(2, steps // R)
+        for n in names:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for L in layers:
+                    getattr(L, n)()
+            g.replay()
+            g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            res[n] = a.elapsed_time(b) / (reps * R)
+            del g
+        return res
     acc = {n: 0.0 for n in names}
     evs = []
     for i in range(steps):
@@ -280,7 +318,7 @@ def run(w, args, dev, emit_cpu=True):
         layers = [Layer(w, 7919 * i, dev) for i in range(R)]
     graph = not args.no_graph
     ms, wall = time_steps(layers, args.steps, args.warmup, graph)
-    stages = time_stages(layers, max(20, min(args.steps, 200)), w.policy)
+    stages = time_stages(layers, max(20, min(args.steps, 400)), graph)
     nb = stage_bytes(layers[0])
     eff = nb["kv_bytes"] / (ms * 1e-3) / 1e9
     dom = max(stages, key=lambda n: stages[n])
@@ -297,13 +335,63 @@ def run(w, args, dev, emit_cpu=True):
         "stage_ms": stages, "stage_bytes": {k: nb[k] for k in stages},
         "host_wall_ms_per_step": wall * 1000.0 / args.steps,
         "roofline": {"kernel": ENTRY_POINT[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(ENTRY_POINT[dom], w.name),
+                     "algorithmic_bytes": dom_bytes, "launch_ms": stages[dom]},
     }
     if emit_cpu and args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
     del layers
     torch.cuda.empty_cache()
     return rec
+
+
+def kernel_source_hash(entry):
+    """sha256 over the HIP sources an entry point's kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[entry]:
+        with open(os.path.join(HERE, "sparse_kv_cache_page_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(entry, workload):
+    """HBM bytes per launch from recorded FETCH_SIZE/WRITE_SIZE runs, or None.
+
+    None when nothing is recorded for this entry point and workload, or when
+    the kernel sources changed after the counters were taken.
+    """
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for r in rec.get("entries", []):
+        if r.get("entry") == entry and r.get("workload") == workload:
+            if r.get("source_sha256") != kernel_source_hash(entry):
+                return None
+            return r.get("hbm_bytes_per_launch")
+    return None
+
+
+def counter_summary(path):
+    """Per-kernel mean of each counter in a rocprofv3 counter_collection.csv."""
+    import csv
+    import re
+    agg = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = re.sub(r"\(anonymous namespace\)::", "", row["Kernel_Name"])
+            name = re.sub(r"\(.*$", "", name.replace("void ", ""))[:100]
+            key = (name, row["Counter_Name"])
+            a = agg.setdefault(key, [0, 0.0, 0.0])
+            a[0] += 1
+            a[1] += float(row["Counter_Value"])
+            a[2] += (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
+    print(f"{'kernel':100s} {'counter':12s} {'dispatches':>10s} {'mean value':>14s} {'mean us':>9s}")
+    for (name, ctr), (n, v, t) in sorted(agg.items(), key=lambda kv: -kv[1][2]):
+        print(f"{name:100s} {ctr:12s} {n:10d} {v / n:14.1f} {t / n:9.2f}")
 
 
 def stage_bytes_after_step(layer):
@@ -347,6 +435,9 @@ def sweep(args, dev, path):
 
 def main():
     args = parse()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
               "(every (row, KV head) pair is independent; see DESIGN.md for how it would "
