@@ -92,17 +92,20 @@ enum : int {
   kDppRowMirror = 0x140,
 };
 
+// The patterns above read a lane of the same row for every lane, so all rows
+// and banks are written and bound_ctrl can be set: the previous contents of
+// the destination are then dead and need no initialisation.
 template <int kCtrl>
 __device__ inline float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
 }
 
 template <int kCtrl>
 __device__ inline double dpp_f64(double x) {
   const int2 v = *reinterpret_cast<int2*>(&x);
   int2 r;
-  r.x = __builtin_amdgcn_update_dpp(0, v.x, kCtrl, 0xF, 0xF, false);
-  r.y = __builtin_amdgcn_update_dpp(0, v.y, kCtrl, 0xF, 0xF, false);
+  r.x = __builtin_amdgcn_update_dpp(0, v.x, kCtrl, 0xF, 0xF, true);
+  r.y = __builtin_amdgcn_update_dpp(0, v.y, kCtrl, 0xF, 0xF, true);
   return *reinterpret_cast<double*>(&r);
 }
 
@@ -116,6 +119,18 @@ __device__ inline float group_sum_f32(float x) {
   if constexpr (kLanes >= 16) x += dpp_f32<kDppRowMirror>(x);
   if constexpr (kLanes >= 32) x += __shfl_xor(x, 16, kWave);
   if constexpr (kLanes >= 64) x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+// Maximum over groups of `kLanes` consecutive lanes (kLanes in {1,2,4,8,16}),
+// returned to every lane of the group.
+template <int kLanes>
+__device__ inline float group_max_f32(float x) {
+  if constexpr (kLanes >= 2) x = fmaxf(x, dpp_f32<kDppQuadSwap1>(x));
+  if constexpr (kLanes >= 4) x = fmaxf(x, dpp_f32<kDppQuadSwap2>(x));
+  if constexpr (kLanes >= 8) x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  if constexpr (kLanes >= 16) x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  static_assert(kLanes <= 16, "groups within one DPP row");
   return x;
 }
 

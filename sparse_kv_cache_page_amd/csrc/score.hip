@@ -54,33 +54,74 @@ template <> struct Unpack<float, 2> {
 };
 
 constexpr int kScoreBlock = 256;
+constexpr int kScoreWaves = kScoreBlock / kWave;
 constexpr int kMaxPagesPerBlock = 2048;  // block-table slice staged in LDS
 constexpr int kStepTopkKeys = 4096;
 // workgroups resident at once (256 CUs x 2 at this kernel's register use):
 // one round of blocks avoids a second ramp-up
-constexpr int kScoreResidentBlocks = 512;      // LDS keys of the fused select; longer rows read U from L2
+constexpr int kScoreResidentBlocks = 512;
+
+// Work split of score_range.  kLpr lanes share one page (kVec coordinates
+// each); a lane scores kU pages per batch and keeps kKinds partial sums per
+// (page, head): the bound, plus the Gaussian mean and variance.  The kM
+// partial sums of a lane are finished through LDS: rows of kPitch doubles
+// (odd, so that both the row-wise writes and the column-wise reads of a
+// half-wave touch distinct banks).
+template <int D, int G, int kVec, bool kGauss>
+struct ScoreGeo {
+  static constexpr int kLpr = D / kVec;
+  static constexpr int kKinds = kGauss ? 3 : 1;
+  static constexpr int kLanesUsed = kLpr < 16 ? kLpr : 16;
+  static constexpr int kUfit = kLanesUsed / (G * kKinds);
+  static constexpr int kU = kUfit < 1 ? 1 : (kUfit > 4 ? 4 : kUfit);
+  static constexpr int kM = kU * kKinds * G;
+  static constexpr int kPitch = kM + 1;
+};
+
+template <int kPitch>
+struct ScoreRedLds {
+  double v[kScoreWaves][kWave][kPitch];
+};
+
+// Orders the LDS accesses of one wave around an exchange between its lanes
+// (a wave's LDS instructions execute in program order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
 
 // Scores of pages [p_begin, p_end) of one (row b, KV head g) for the G query
-// heads of the group; s_pi holds the block-table slice block_table[b][p_begin..).
+// heads of the group; s_pi holds the block-table slice block_table[b][p_begin..),
+// red is this wave's reduction scratch (kWave rows of kPitch doubles).
+//
+// Each lane forms, for each of its kU pages and each head, the fp64 partial
+// sum over its kVec coordinates and stores it in its LDS row; then lane
+// (slot, c) adds column c of the kLpr rows of its page slot in a fixed order,
+// so every (page, head) total is finished by one lane, and the group maximum
+// is taken over the G lanes that hold one page's heads.
 template <typename T, int D, int G, int kVec, bool kGauss, bool kCoherentU = false>
 __device__ __forceinline__ void score_range(
     const float* __restrict__ q, float scale, const T* __restrict__ kmin,
     const T* __restrict__ kmax, const float* __restrict__ mean, const float* __restrict__ var,
     const int* s_pi, int b, int g, int pair, int Hkv, int maxP, int p_begin, int p_end,
     float* __restrict__ ub, float* __restrict__ ubg, double* __restrict__ gm,
-    double* __restrict__ gv) {
-  constexpr int kLpr = D / kVec;
+    double* __restrict__ gv, double (*red)[ScoreGeo<D, G, kVec, kGauss>::kPitch]) {
+  using Geo = ScoreGeo<D, G, kVec, kGauss>;
+  constexpr int kLpr = Geo::kLpr;
   constexpr int kPagesPerWave = kWave / kLpr;
-  constexpr int kPagesPerStep = kPagesPerWave * (kScoreBlock / kWave);
-  constexpr int kU = kGauss ? 2 : 4;  // pages in flight per lane
+  constexpr int kPagesPerStep = kPagesPerWave * kScoreWaves;
+  constexpr int kU = Geo::kU;
+  constexpr int kKinds = Geo::kKinds;
+  constexpr int kM = Geo::kM;
   constexpr int kRawBytes = kVec * (int)sizeof(T);
   constexpr int kMomRaw = kVec * 4;   // bytes of fp32 mean (or var) per lane
   using Raw = RawT<kRawBytes>;
-  static_assert(G <= kLpr, "one lane per head writes the result");
+  static_assert(kLpr % G == 0, "a page's heads sit in aligned lane groups");
   const int Hq = Hkv * G;
   const int lane = threadIdx.x % kWave;
   const int c = lane % kLpr;
   const int slot = threadIdx.x / kLpr;  // page slot inside a step
+  const int r0 = lane - c;              // first LDS row of this lane's slot
 
   double qp[G][kVec], qn[G][kVec];
 #pragma unroll
@@ -126,14 +167,12 @@ __device__ __forceinline__ void score_range(
     }
   };
   auto consume = [&](int base, const Batch& bt_) {
+    double* row = red[lane];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int p = base + slot + u * kPagesPerStep;
-      const bool live = p < p_end;
       float lo[kVec], hi[kVec];
       Unpack<T, kVec>::run(bt_.lo[u], lo);
       Unpack<T, kVec>::run(bt_.hi[u], hi);
-      double acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         double a = 0.0;
@@ -142,9 +181,8 @@ __device__ __forceinline__ void score_range(
           a = fma(qp[h][v], (double)hi[v], a);
           a = fma(qn[h][v], (double)lo[v], a);
         }
-        acc[h] = group_sum_f64<kLpr>(a);
+        row[u * kKinds * G + h] = a;
       }
-      double mg[G], vg[G];
       if constexpr (kGauss) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -155,26 +193,40 @@ __device__ __forceinline__ void score_range(
             am = fma(qd, (double)bt_.mu[u][v], am);
             av = fma(qd * qd, (double)bt_.s2[u][v], av);
           }
-          mg[h] = group_sum_f64<kLpr>(am);
-          vg[h] = group_sum_f64<kLpr>(av);
+          row[(u * kKinds + 1) * G + h] = am;
+          row[(u * kKinds + 2) * G + h] = av;
         }
       }
-      if (!live) continue;
-      float best = -__builtin_huge_valf();
+    }
+    wave_lds_sync();
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float uh = (float)(dscale * acc[h]);
-        best = fmaxf(best, uh);
-        if (c == h) {
-          const size_t o = ((size_t)b * Hq + g * G + h) * maxP + p;
-          if (ub != nullptr) ub[o] = uh;
-          if constexpr (kGauss) {
-            gm[o] = dscale * mg[h];
-            gv[o] = dscale * dscale * vg[h];
-          }
-        }
+    for (int it = 0; it < (kM + kLpr - 1) / kLpr; ++it) {
+      const int m = it * kLpr + c;
+      const bool have = m < kM;
+      const int u = m / (kKinds * G);
+      const int kind = (m / G) % kKinds;
+      const int h = m % G;
+      const int p = base + slot + u * kPagesPerStep;
+      // pairwise sum of the slot's kLpr partials of combination m
+      double part[kLpr];
+#pragma unroll
+      for (int i = 0; i < kLpr; ++i) part[i] = have ? red[r0 + i][m] : 0.0;
+#pragma unroll
+      for (int w = kLpr / 2; w >= 1; w /= 2) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) part[i] += part[i + w];
       }
-      if (c == 0) {
+      const double t = part[0];
+      const bool live = have && p < p_end;
+      const size_t o = ((size_t)b * Hq + g * G + h) * maxP + p;
+      const float uh = (float)(dscale * t);
+      if (kind == 0 && live && ub != nullptr) ub[o] = uh;
+      if constexpr (kGauss) {
+        if (kind == 1 && live) gm[o] = dscale * t;
+        if (kind == 2 && live) gv[o] = dscale * dscale * t;
+      }
+      const float best = group_max_f32<G>(have && kind == 0 ? uh : -__builtin_huge_valf());
+      if (kind == 0 && h == 0 && live) {
         // the fused select reads these bounds from another workgroup (maybe
         // on another XCD): device-coherent stores there, plain ones otherwise
         if constexpr (kCoherentU)
@@ -184,6 +236,7 @@ __device__ __forceinline__ void score_range(
           ubg[(size_t)pair * maxP + p] = best;
       }
     }
+    wave_lds_sync();
   };
   constexpr int kStride = kPagesPerStep * kU;
   Batch A, Bb;
@@ -209,7 +262,9 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens, int Hkv, int P, int maxP,
     int pages_per_block, float* __restrict__ ub, float* __restrict__ ubg,
     double* __restrict__ gm, double* __restrict__ gv) {
+  using Geo = ScoreGeo<D, G, kVec, kGauss>;
   __shared__ int s_pi[kMaxPagesPerBlock];
+  __shared__ ScoreRedLds<Geo::kPitch> red;
   const int pair = blockIdx.y;
   const int b = pair / Hkv;
   const int g = pair % Hkv;
@@ -222,7 +277,8 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
     s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
   __syncthreads();
   score_range<T, D, G, kVec, kGauss>(q, scale, kmin, kmax, mean, var, s_pi, b, g, pair, Hkv, maxP,
-                                     p_begin, p_end, ub, ubg, gm, gv);
+                                     p_begin, p_end, ub, ubg, gm, gv,
+                                     red.v[threadIdx.x / kWave]);
 }
 
 // Fused first half of a decode step (top-k policy): optionally rebuild the
@@ -237,9 +293,15 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
     int refresh, int Hkv, int P, int maxP, int pages_per_block, float* __restrict__ ubg,
     int top_k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
     int* __restrict__ counters) {
+  using Geo = ScoreGeo<D, G, kVec, false>;
+  // the scoring reduction and the selection never use LDS at the same time
+  union Lds {
+    ScoreRedLds<Geo::kPitch> red;
+    TopkRegLds tkr;
+    TopkLds<1> tk;
+  };
   __shared__ int s_pi[kMaxPagesPerBlock];
-  __shared__ TopkRegLds tkr;
-  __shared__ TopkLds<1> tk;
+  __shared__ Lds sm;
   __shared__ int s_last;
   const int pair = blockIdx.y;
   const int b = pair / Hkv;
@@ -260,7 +322,7 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   __syncthreads();
   score_range<T, D, G, kVec, false, true>(q, scale, kmin, kmax, nullptr, nullptr, s_pi, b, g, pair,
                                           Hkv, maxP, p_begin, p_end, nullptr, ubg, nullptr,
-                                          nullptr);
+                                          nullptr, sm.red.v[threadIdx.x / kWave]);
   // arrival: every wave waits until its device-coherent bound stores have
   // completed, the barrier gathers the waves, then one relaxed device-scope
   // increment counts the block; the last block of the pair reads every bound
@@ -280,11 +342,11 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   if (k >= np) {
     for (int p = threadIdx.x; p < np; p += kScoreBlock) out[p] = p;
   } else if (np <= kBlk * 8) {
-    topk_block_reg<8, true>(ubg + (size_t)pair * maxP, np, k, out, tkr);
+    topk_block_reg<8, true>(ubg + (size_t)pair * maxP, np, k, out, sm.tkr);
   } else if (np <= kBlk * 16) {
-    topk_block_reg<16, true>(ubg + (size_t)pair * maxP, np, k, out, tkr);
+    topk_block_reg<16, true>(ubg + (size_t)pair * maxP, np, k, out, sm.tkr);
   } else {
-    topk_block<false, true>(ubg + (size_t)pair * maxP, np, k, out, tk);
+    topk_block<false, true>(ubg + (size_t)pair * maxP, np, k, out, sm.tk);
   }
   if (threadIdx.x == 0) {
     n_sel[pair] = k;
@@ -298,9 +360,10 @@ hipError_t launch_score_t(const Shape& s, const float* q, float scale, const voi
                           const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
                           double* gm, double* gv, hipStream_t stream) {
   constexpr int kLpr = D / kVec;
-  constexpr int kPagesPerStep = (kWave / kLpr) * (kScoreBlock / kWave);
+  constexpr int kPagesPerStep = (kWave / kLpr) * kScoreWaves;
   const bool gauss = gm != nullptr;
-  const int per_iter = kPagesPerStep * (gauss ? 2 : 4);
+  const int per_iter = kPagesPerStep * (gauss ? ScoreGeo<D, G, kVec, true>::kU
+                                              : ScoreGeo<D, G, kVec, false>::kU);
   // enough blocks to spread the pairs over the chip (~4 per CU), each block
   // a whole number of iterations
   const long long pairs = (long long)s.B * s.Hkv;
@@ -346,8 +409,8 @@ hipError_t launch_score_select_t(const Shape& s, const float* q, float scale, co
                                  int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
                                  int* counters, hipStream_t stream) {
   constexpr int kLpr = D / kVec;
-  constexpr int kPagesPerStep = (kWave / kLpr) * (kScoreBlock / kWave);
-  const int per_iter = kPagesPerStep * 4;
+  constexpr int kPagesPerStep = (kWave / kLpr) * kScoreWaves;
+  const int per_iter = kPagesPerStep * ScoreGeo<D, G, kVec, false>::kU;
   const long long pairs = (long long)s.B * s.Hkv;
   long long want_blocks_per_pair = (kScoreResidentBlocks + pairs - 1) / pairs;
   int iters = (int)((s.maxP + per_iter * want_blocks_per_pair - 1) / (per_iter * want_blocks_per_pair));
