@@ -13,11 +13,7 @@ constexpr int kTopkLdsKeys = 16384;  // 64 KiB of LDS keys; longer rows read U f
 __device__ __forceinline__ int block_incl_scan(int x, int* sh) {
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  x = wave_incl_scan_i32(x);
   if (lane == kWave - 1) sh[w] = x;
   __syncthreads();
   int add = 0;
@@ -83,11 +79,8 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ U, int n, i
     kmn = min(kmn, key);
     kmx = max(kmx, key);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, kWave));
-    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, kWave));
-  }
+  kmn = wave_min_u32(kmn);
+  kmx = wave_max_u32(kmx);
   if (threadIdx.x % kWave == 0) {
     hist[threadIdx.x / kWave] = (int)kmn;
     hist[4 + threadIdx.x / kWave] = (int)kmx;
@@ -167,15 +160,7 @@ __device__ __forceinline__ void topk_block(const float* __restrict__ U, int n, i
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
+__device__ __forceinline__ int wave_incl_scan(int x) { return wave_incl_scan_i32(x); }
 
 // Workgroup top-k with the keys in registers (kPerThread consecutive pages per
 // thread, n <= 256 * kPerThread, k < n): range-adaptive radix passes over a
@@ -218,11 +203,8 @@ __device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int 
       kmn = min(kmn, key[i]);
       kmx = max(kmx, key[i]);
     }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, kWave));
-    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, kWave));
-  }
+  kmn = wave_min_u32(kmn);
+  kmx = wave_max_u32(kmx);
   if (lane == 0) {
     sm.mm[wave] = kmn;
     sm.mm[4 + wave] = kmx;

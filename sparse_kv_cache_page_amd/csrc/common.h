@@ -80,6 +80,14 @@ __device__ inline uint2 load8_stream(const void* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight (a full __syncthreads() also waits for them).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // DPP helpers (gfx9 encodings).  Within a row of 16 lanes, the butterfly
 //   quad_perm[1,0,3,2], quad_perm[2,3,0,1], row_half_mirror, row_mirror
@@ -145,9 +153,45 @@ __device__ inline double group_sum_f64(double x) {
   return x;
 }
 
+// Wave-wide reductions of 32-bit values, returned to every lane: the DPP row
+// butterfly leaves each row's result in all its lanes, row_bcast15 /
+// row_bcast31 carry rows 0-2 into row 3, and lane 63 is read back.  Rows that
+// a broadcast does not write keep their own value (old = x).
+template <typename Op>
+__device__ inline int wave_reduce_b32(int x, Op op) {
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, kDppQuadSwap1, 0xF, 0xF, true));
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, kDppQuadSwap2, 0xF, 0xF, true));
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, kDppRowHalfMirror, 0xF, 0xF, true));
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, kDppRowMirror, 0xF, 0xF, true));
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 __device__ inline float wave_max_f32(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return __int_as_float(wave_reduce_b32(__float_as_int(x), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }));
+}
+
+__device__ inline uint32_t wave_min_u32(uint32_t x) {
+  return (uint32_t)wave_reduce_b32((int)x, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+  return (uint32_t)wave_reduce_b32((int)x, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
+}
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele row shifts (lanes
+// shifted in from outside the row read 0), then the row broadcasts add the
+// totals of the rows below.
+__device__ inline int wave_incl_scan_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
@@ -173,9 +217,7 @@ __device__ inline double wave_sum_f64(double x) {
 }
 
 __device__ inline int wave_sum_i32(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  return wave_reduce_b32(x, [](int a, int b) { return a + b; });
 }
 
 // Number of valid tokens of logical page p in a row of length L.

@@ -19,10 +19,13 @@
 //
 //  2. tau_pv_kernel -- one workgroup per (row, query head).  It gathers the
 //     candidates of every split that clear z_max - 1 into LDS (in split order,
-//     so results are reproducible), solves  sum_i [z_i - tau]_+^gamma = 1  in
-//     fp64 with a bracketed Newton iteration (one wave, no barriers, when there
-//     are at most 64 candidates), and then reads only the value rows with
-//     z_i > tau -- the weights off the support are exact zeros:
+//     so results are reproducible; for up to 16 splits the counts, maxima and
+//     first candidate slots are read in one round of loads), solves
+//     sum_i [z_i - tau]_+^gamma = 1  in fp64 -- with at most 64 candidates by
+//     one wave that finds the support first (tau_small), otherwise by a
+//     bracketed Newton iteration -- and reads only the value rows with
+//     z_i > tau (for few candidates, all their rows are requested before the
+//     solve); the weights off the support are exact zeros:
 //         out = sum_i p_i v_i / sum_i p_i,   p_i = (z_i - tau)^gamma.
 #include <type_traits>
 
@@ -83,15 +86,7 @@ __device__ inline double pos_pow(double x, double gamma, int gi) {
   return pow(x, gamma);
 }
 
-__device__ inline int wave_incl_scan_i(int x) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
+__device__ inline int wave_incl_scan_i(int x) { return wave_incl_scan_i32(x); }
 
 // Bracketed Newton for f(tau) = sum [z - tau]_+^gamma - 1 = 0 on
 // [zmax - 1, zmax - n^(1-alpha)]; eval(tau, f, fd) returns the (uniform)
@@ -132,6 +127,92 @@ __device__ inline void tau_term(double z, double tau, double gamma, int gamma_in
     const double xg1 = gamma_int == 1 ? 1.0 : pos_pow(x, gamma - 1.0, gamma_int - 1);
     f += xg1 * x;
     fd += gamma * xg1;
+  }
+}
+
+// x^gamma for x >= 0, with gamma a compile-time positive integer kGi, or any
+// gamma > 0 when kGi == 0.
+template <int kGi>
+__device__ inline double powg(double x, double gamma) {
+  if constexpr (kGi == 0) {
+    return x > 0.0 ? pow(x, gamma) : 0.0;
+  } else {
+    double r = x;
+#pragma unroll
+    for (int i = 1; i < kGi; ++i) r *= x;
+    return r;
+  }
+}
+
+// tau of at most 64 candidates, one per lane of the calling wave (z = -inf
+// in lanes >= count; thr = z_max - 1).  With F(t) = sum_j [z_j - t]_+^gamma,
+// which decreases and equals 1 at tau, candidate i is in the support exactly
+// when F(z_i) < 1, so every lane evaluates F at its own candidate.  On the
+// support S, F is the smooth sum_S (z - t)^gamma: solved in closed form for
+// gamma = 1 (mean) and gamma = 2 (mean and variance), otherwise by Newton
+// from the largest score below the support, where the convex, decreasing F
+// makes the iterates rise monotonically to the root.  Returns false when the
+// tau found disagrees with S (a score within rounding of tau) or gamma < 1;
+// the caller then uses the bracketed solver.
+template <int kGi>
+__device__ inline bool tau_small_t(float zf, int count, double thr, double gamma,
+                                   double& tau_out) {
+  const int lane = threadIdx.x % kWave;
+  const double z = (double)zf;
+  double F0 = 0.0, F1 = 0.0;
+  int j = 0;
+  for (; j + 1 < count; j += 2) {
+    const double x0 = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(zf), j)) - z;
+    const double x1 = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(zf), j + 1)) - z;
+    F0 += powg<kGi>(fmax(x0, 0.0), gamma);
+    F1 += powg<kGi>(fmax(x1, 0.0), gamma);
+  }
+  if (j < count) {
+    const double x0 = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(zf), j)) - z;
+    F0 += powg<kGi>(fmax(x0, 0.0), gamma);
+  }
+  const double F = F0 + F1;
+  const bool live = lane < count;
+  const bool in = live && F < 1.0;
+  const int k = __popcll(__ballot(in));
+  if (k == 0) return false;
+  double tau;
+  if constexpr (kGi == 1) {
+    tau = (wave_sum_f64(in ? z : 0.0) - 1.0) / k;
+  } else if constexpr (kGi == 2) {
+    const double m = wave_sum_f64(in ? z : 0.0) / k;
+    const double v = wave_sum_f64(in ? (z - m) * (z - m) : 0.0);
+    tau = m - sqrt(fmax(0.0, (1.0 - v) / k));
+  } else {
+    if (!(gamma >= 1.0)) return false;  // F is convex only for gamma >= 1
+    const double below = (double)wave_max_f32(live && !in ? zf : -__builtin_huge_valf());
+    tau = fmax(thr, below);
+    for (int it = 0; it < 64; ++it) {
+      const double x = in ? fmax(z - tau, 0.0) : 0.0;
+      const double xg1 = kGi > 0 ? powg<(kGi > 1 ? kGi - 1 : 1)>(x, gamma - 1.0)
+                                 : (x > 0.0 ? pow(x, gamma - 1.0) : 0.0);
+      const double f = wave_sum_f64(xg1 * x) - 1.0;
+      const double fd = gamma * wave_sum_f64(xg1);
+      if (!(fd > 0.0)) break;
+      const double step = f / fd;
+      tau += step;
+      if (fabs(step) <= 4e-16 * fmax(1.0, fabs(tau))) break;
+    }
+  }
+  const bool bad = live && (in ? !(z > tau) : (z > tau));
+  if (__ballot(bad) != 0ull || !(tau >= thr)) return false;
+  tau_out = tau;
+  return true;
+}
+
+__device__ inline bool tau_small(float zf, int count, double thr, double gamma, int gi,
+                                 double& tau_out) {
+  switch (gi) {
+    case 1: return tau_small_t<1>(zf, count, thr, gamma, tau_out);
+    case 2: return tau_small_t<2>(zf, count, thr, gamma, tau_out);
+    case 3: return tau_small_t<3>(zf, count, thr, gamma, tau_out);
+    case 4: return tau_small_t<4>(zf, count, thr, gamma, tau_out);
+    default: return tau_small_t<0>(zf, count, thr, gamma, tau_out);
   }
 }
 
@@ -223,7 +304,11 @@ __device__ __forceinline__ void pair_tail(const float2* __restrict__ cand,
     __builtin_amdgcn_wave_barrier();
     const bool overflow = count > kTailCap;
     const double nvalid = has_sel ? (double)nsel * P : (double)L;
-    const double tau = newton_tau(zmax, nvalid, ta.alpha, [&](double tt, double& f, double& fd) {
+    double tau;
+    if (!(count <= kWave &&
+          tau_small(lane < count ? cz[lane] : -__builtin_huge_valf(), count, thr, ta.gamma,
+                    ta.gamma_int, tau)))
+    tau = newton_tau(zmax, nvalid, ta.alpha, [&](double tt, double& f, double& fd) {
       f = 0.0;
       fd = 0.0;
       if (!overflow) {
@@ -560,11 +645,7 @@ __device__ inline void block_sum2(double& a, double& b, double* sh) {
 __device__ inline int block_incl_scan(int x, int* sh) {
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  x = wave_incl_scan_i32(x);
   if (lane == kWave - 1) sh[w] = x;
   __syncthreads();
   int add = 0;
@@ -645,51 +726,109 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
   const int* cnt_bh = cnt + (size_t)bh * splits;
   const float* smax_bh = smax + (size_t)bh * splits;
 
-  // global max and the exclusive offsets of the per-split candidate lists
   float zm = -__builtin_huge_valf();
-  int running = 0;
-  for (int s0 = 0; s0 < nsplit; s0 += kBlock) {
-    const int s = s0 + threadIdx.x;
-    int v = 0;
-    if (s < nsplit) {
-      zm = fmaxf(zm, smax_bh[s]);
-      v = cnt_bh[s];
-    }
-    const int incl = block_incl_scan(v, sh4);
-    if (s < nsplit) s_off[s] = running + incl - v;
-    if (threadIdx.x == kBlock - 1) sh4[0] = incl;  // chunk total (read after the barrier)
-    __syncthreads();
-    running += sh4[0];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) s_off[nsplit] = running;
-  zm = wave_max_f32(zm);
-  if (lane == 0) st_p[wave] = zm;
-  __syncthreads();
-  zm = fmaxf(fmaxf(st_p[0], st_p[1]), fmaxf(st_p[2], st_p[3]));
-  const double zmax = (double)zm;
-  const double thr = zmax - 1.0;
-  const int total_c = running;
-
-  // candidates that clear the global bar, in split order
-  int count = 0;
-  for (int k0 = 0; k0 < total_c; k0 += kBlock) {
-    const int k = k0 + threadIdx.x;
+  double zmax = 0.0, thr = 0.0;
+  int total_c = 0, count = 0;
+  // First try: each split's count, maximum and first kSpec candidate slots
+  // in one round of independent loads (slots past the count are ignored).
+  constexpr int kSpec = 16;
+  bool spec = nsplit * kSpec <= kBlock;
+  if (spec) {
+    const int s = threadIdx.x / kSpec;
+    const int j = threadIdx.x % kSpec;
+    int cs = 0;
     float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
-    if (k < total_c) e = cand_at(cand_bh, s_off, nsplit, kR, k);
-    const bool flag = (double)e.x > thr;
-    int tot;
-    const int slot = chunk_slot(flag, sh4, tot);
-    if (slot >= 0 && count + slot < kCandCap) {
-      c_z[count + slot] = e.x;
-      c_t[count + slot] = bits_of(e.y);
+    if (s < nsplit) {
+      cs = cnt_bh[s];
+      zm = smax_bh[s];
+      e = cand_bh[(size_t)s * kR + j];
     }
-    count += tot;
+    spec = !__syncthreads_or(cs > kSpec);
+    if (spec) {
+      zm = wave_max_f32(zm);
+      if (lane == 0) st_p[wave] = zm;
+      __syncthreads();
+      zm = fmaxf(fmaxf(st_p[0], st_p[1]), fmaxf(st_p[2], st_p[3]));
+      zmax = (double)zm;
+      thr = zmax - 1.0;
+      // (s, j) runs in split order, so the compacted list is in split order
+      const bool flag = j < cs && (double)e.x > thr;
+      int tot;
+      const int slot = chunk_slot(flag, sh4, tot);
+      if (slot >= 0) {
+        c_z[slot] = e.x;
+        c_t[slot] = bits_of(e.y);
+      }
+      count = tot;  // <= kBlock: never an overflow, so total_c is not needed
+      __syncthreads();
+    }
   }
-  __syncthreads();
+  if (!spec) {
+    // global max and the exclusive offsets of the per-split candidate lists
+    zm = -__builtin_huge_valf();
+    int running = 0;
+    for (int s0 = 0; s0 < nsplit; s0 += kBlock) {
+      const int s = s0 + threadIdx.x;
+      int v = 0;
+      if (s < nsplit) {
+        zm = fmaxf(zm, smax_bh[s]);
+        v = cnt_bh[s];
+      }
+      const int incl = block_incl_scan(v, sh4);
+      if (s < nsplit) s_off[s] = running + incl - v;
+      if (threadIdx.x == kBlock - 1) sh4[0] = incl;  // chunk total (read after the barrier)
+      __syncthreads();
+      running += sh4[0];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) s_off[nsplit] = running;
+    zm = wave_max_f32(zm);
+    if (lane == 0) st_p[wave] = zm;
+    __syncthreads();
+    zm = fmaxf(fmaxf(st_p[0], st_p[1]), fmaxf(st_p[2], st_p[3]));
+    zmax = (double)zm;
+    thr = zmax - 1.0;
+    total_c = running;
+
+    // candidates that clear the global bar, in split order
+    for (int k0 = 0; k0 < total_c; k0 += kBlock) {
+      const int k = k0 + threadIdx.x;
+      float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
+      if (k < total_c) e = cand_at(cand_bh, s_off, nsplit, kR, k);
+      const bool flag = (double)e.x > thr;
+      int tot;
+      const int slot = chunk_slot(flag, sh4, tot);
+      if (slot >= 0 && count + slot < kCandCap) {
+        c_z[count + slot] = e.x;
+        c_t[count + slot] = bits_of(e.y);
+      }
+      count += tot;
+    }
+    __syncthreads();
+  }
   const bool overflow = count > kCandCap;
   // number of tokens (an upper bound is enough for the upper end of the bracket)
   const double nvalid = has_sel ? (double)nsel * P : (double)L;
+
+  // value rows of every candidate requested before tau is known (few
+  // candidates): their latency overlaps the solve
+  constexpr int kPre = 4;
+  const int c = threadIdx.x % kLpr;
+  const int rg = threadIdx.x / kLpr;
+  const size_t tile_stride = (size_t)P * D;
+  const bool prefetch = !overflow && count <= kPre * kRowsPerPass;
+  uint4 vraw[kPre];
+  if (prefetch) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int r = rg + i * kRowsPerPass;
+      if (r < count) {
+        const int pt = c_t[r];
+        vraw[i] = load16(V + (size_t)(pt >> log2P) * Hkv * tile_stride + g * tile_stride +
+                         (size_t)(pt & (P - 1)) * D + c * kVec);
+      }
+    }
+  }
 
   // bracketed Newton for  f(tau) = sum [z - tau]_+^gamma - 1 = 0  on
   // [zmax - 1, zmax - n^(1-alpha)];  f' = -gamma sum [z - tau]_+^(gamma-1)
@@ -731,19 +870,23 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
 
   double tau;
   if (!overflow && count <= kWave) {
-    // one wave, no barriers inside the iteration
+    // one wave, no barriers inside the solve
     if (wave == 0) {
-      const double zc = lane < count ? (double)c_z[lane] : -__builtin_huge_val();
-      const double t = newton([&](double tt, double& f, double& fd) {
-        f = 0.0;
-        fd = 0.0;
-        term(zc, tt, f, fd);
-        f = wave_sum_f64(f);
-        fd = wave_sum_f64(fd);
-      });
+      const float zf = lane < count ? c_z[lane] : -__builtin_huge_valf();
+      double t;
+      if (!tau_small(zf, count, thr, gamma, gamma_int, t)) {
+        const double zc = (double)zf;
+        t = newton([&](double tt, double& f, double& fd) {
+          f = 0.0;
+          fd = 0.0;
+          term(zc, tt, f, fd);
+          f = wave_sum_f64(f);
+          fd = wave_sum_f64(fd);
+        });
+      }
       if (lane == 0) s_tau = t;
     }
-    __syncthreads();
+    lds_barrier();  // the value-row loads stay in flight
     tau = s_tau;
   } else {
     tau = newton([&](double tt, double& f, double& fd) {
@@ -760,58 +903,80 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
   }
 
   // weights and the value rows of the support
-  const int c = threadIdx.x % kLpr;
-  const int rg = threadIdx.x / kLpr;
-  const size_t tile_stride = (size_t)P * D;
   float acc[kVec];
 #pragma unroll
   for (int v = 0; v < kVec; ++v) acc[v] = 0.0f;
   double psum = 0.0;
   int nsupp = 0;
-  const int lim = overflow ? total_c : count;
-  for (int base = 0; base < lim; base += kBlock) {
-    const int k = base + threadIdx.x;
-    float z = -__builtin_huge_valf();
-    int ptok = 0;
-    if (k < lim) {
-      if (overflow) {
-        const float2 e = cand_at(cand_bh, s_off, nsplit, kR, k);
-        z = e.x;
-        ptok = bits_of(e.y);
-      } else {
-        z = c_z[k];
-        ptok = c_t[k];
+  if (prefetch) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int r = rg + i * kRowsPerPass;
+      if (r < count) {
+        const double x = (double)c_z[r] - tau;
+        if (x > 0.0) {
+          const float p = (float)pos_pow(x, gamma, gamma_int);
+          float xv[kVec];
+          Elem<T>::unpack(vraw[i], xv);
+#pragma unroll
+          for (int v = 0; v < kVec; ++v) acc[v] = fmaf(p, xv[v], acc[v]);
+        }
       }
     }
-    const double x = (double)z - tau;
-    const bool flag = x > 0.0;
-    int m;
-    const int slot = chunk_slot(flag, sh4, m);
-    nsupp += m;
-    if (slot >= 0) {
-      const float p = (float)pos_pow(x, gamma, gamma_int);
-      st_p[slot] = p;
-      st_t[slot] = ptok;
-      psum += (double)p;
+    if (threadIdx.x < count) {
+      const double x = (double)c_z[threadIdx.x] - tau;
+      if (x > 0.0) {
+        psum = (double)(float)pos_pow(x, gamma, gamma_int);
+        nsupp = 1;
+      }
     }
-    __syncthreads();
-    for (int r = rg; r < m; r += kRowsPerPass) {
-      const int pt = st_t[r];
-      const float p = st_p[r];
-      const int pi = pt >> log2P;
-      const int t = pt & (P - 1);
-      const T* row = V + (size_t)pi * Hkv * tile_stride + g * tile_stride + (size_t)t * D + c * kVec;
-      float xv[kVec];
-      Elem<T>::unpack(load16(row), xv);
+  } else {
+    const int lim = overflow ? total_c : count;
+    for (int base = 0; base < lim; base += kBlock) {
+      const int k = base + threadIdx.x;
+      float z = -__builtin_huge_valf();
+      int ptok = 0;
+      if (k < lim) {
+        if (overflow) {
+          const float2 e = cand_at(cand_bh, s_off, nsplit, kR, k);
+          z = e.x;
+          ptok = bits_of(e.y);
+        } else {
+          z = c_z[k];
+          ptok = c_t[k];
+        }
+      }
+      const double x = (double)z - tau;
+      const bool flag = x > 0.0;
+      int m;
+      const int slot = chunk_slot(flag, sh4, m);
+      nsupp += m;
+      if (slot >= 0) {
+        const float p = (float)pos_pow(x, gamma, gamma_int);
+        st_p[slot] = p;
+        st_t[slot] = ptok;
+        psum += (double)p;
+      }
+      __syncthreads();
+      for (int r = rg; r < m; r += kRowsPerPass) {
+        const int pt = st_t[r];
+        const float p = st_p[r];
+        const int pi = pt >> log2P;
+        const int t = pt & (P - 1);
+        const T* row = V + (size_t)pi * Hkv * tile_stride + g * tile_stride + (size_t)t * D + c * kVec;
+        float xv[kVec];
+        Elem<T>::unpack(load16(row), xv);
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) acc[v] = fmaf(p, xv[v], acc[v]);
+        for (int v = 0; v < kVec; ++v) acc[v] = fmaf(p, xv[v], acc[v]);
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    if (threadIdx.x != 0) nsupp = 0;  // the chunk totals are block-wide
   }
 #pragma unroll
   for (int v = 0; v < kVec; ++v) acc_sh[rg][c * kVec + v] = acc[v];
-  double ps = psum, dummy = 0.0;
-  block_sum2(ps, dummy, shd);  // includes the barrier that publishes acc_sh
+  double ps = psum, ns = (double)nsupp;
+  block_sum2(ps, ns, shd);  // includes the barrier that publishes acc_sh
   const float inv = (float)(1.0 / ps);
   for (int t = threadIdx.x; t < D; t += kBlock) {
     float o = 0.0f;
@@ -819,7 +984,7 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(
     out[(size_t)bh * D + t] = o * inv;
   }
   if (tau_out && threadIdx.x == 0) tau_out[bh] = (float)tau;
-  if (n_support && threadIdx.x == 0) n_support[bh] = nsupp;
+  if (n_support && threadIdx.x == 0) n_support[bh] = (int)ns;
 }
 
 template <typename T, int D, int G, bool kFused>
