@@ -263,14 +263,18 @@ __device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int 
     if (cut || shift == 0) break;
   }
   // ordered placement: every key > T, and the first `remaining` keys == T
+  // (branch-free: per-key flags, running positions, one masked store per key)
   const uint32_t T = lo;
+  bool gt[kPerThread], eq[kPerThread];
   int cg = 0, ce = 0;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i)
-    if (i < nv) {
-      if (cut ? key[i] >= T : key[i] > T) ++cg;
-      else if (!cut && key[i] == T) ++ce;
-    }
+  for (int i = 0; i < kPerThread; ++i) {
+    const bool v = i < nv;
+    gt[i] = v && (cut ? key[i] >= T : key[i] > T);
+    eq[i] = v && !cut && key[i] == T;
+    cg += gt[i] ? 1 : 0;
+    ce += eq[i] ? 1 : 0;
+  }
   int gi = wave_incl_scan(cg);
   int ei = wave_incl_scan(ce);
   __syncthreads();  // wsum reuse: every thread has read the last pass's totals
@@ -286,15 +290,12 @@ __device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int 
   int eq_seen = ei - ce;
   int pos = (gi - cg) + min(eq_seen, remaining);
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i)
-    if (i < nv) {
-      if (cut ? key[i] >= T : key[i] > T) {
-        out[pos++] = p0 + i;
-      } else if (!cut && key[i] == T) {
-        if (eq_seen < remaining) out[pos++] = p0 + i;
-        ++eq_seen;
-      }
-    }
+  for (int i = 0; i < kPerThread; ++i) {
+    const bool take = gt[i] || (eq[i] && eq_seen < remaining);
+    if (take) out[pos] = p0 + i;
+    pos += take ? 1 : 0;
+    eq_seen += eq[i] ? 1 : 0;
+  }
 }
 
 // Metadata of one (physical page pi, KV head g) tile with nv valid tokens,
