@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QkArgs<T> a, long long n_ite
   __shared__ std::conditional_t<kFused, TailLds, NoTail> tl;
   __shared__ int s_last;
   for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const QkItemInfo it = qk_item<T, D, G, false, kFused>(a, item, sm);
+    const QkItemInfo it = qk_item<T, D, G, kFused>(a, item, sm);
     if (!it.ran) continue;  // uniform over the block
     if constexpr (kFused) {
       // arrival: this item's device-coherent stores drain, the block counts
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QkArgs<T> a, long long n_ite
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void tau_pv_kernel(TauArgs<T> a) {
   __shared__ TauLds<T, D> sm;
-  tau_head<T, D, false>(a, blockIdx.x, sm);
+  tau_head<T, D>(a, blockIdx.x, sm);
 }
 
 template <typename T, int D, int G, bool kFused>

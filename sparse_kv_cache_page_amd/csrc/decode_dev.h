@@ -5,7 +5,7 @@
 
 #include <type_traits>
 
-#include "common.h"
+#include "blocks.h"
 
 namespace ekv {
 namespace {
@@ -366,33 +366,6 @@ __device__ __forceinline__ void pair_tail(const float2* __restrict__ cand,
   }
 }
 
-template <bool kCoherent>
-__device__ __forceinline__ int ld_i32(const int32_t* p) {
-  if constexpr (kCoherent)
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    return *p;
-}
-
-template <bool kCoherent>
-__device__ __forceinline__ float ld_f32(const float* p) {
-  if constexpr (kCoherent)
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    return *p;
-}
-
-template <bool kCoherent>
-__device__ __forceinline__ float2 ld_cand(const float2* p) {
-  if constexpr (kCoherent) {
-    const uint64_t e = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)e), __uint_as_float((uint32_t)(e >> 32)));
-  } else {
-    return *p;
-  }
-}
-
 // Sum two doubles over the block (fixed order, so results are reproducible).
 __device__ inline void block_sum2(double& a, double& b, double* sh) {
   a = wave_sum_f64(a);
@@ -406,19 +379,6 @@ __device__ inline void block_sum2(double& a, double& b, double* sh) {
   a = (sh[0] + sh[2]) + (sh[4] + sh[6]);
   b = (sh[1] + sh[3]) + (sh[5] + sh[7]);
   __syncthreads();
-}
-
-// Inclusive prefix sum over the block; sh holds 4 ints.
-__device__ inline int block_incl_scan(int x, int* sh) {
-  const int lane = threadIdx.x % kWave;
-  const int w = threadIdx.x / kWave;
-  x = wave_incl_scan_i32(x);
-  if (lane == kWave - 1) sh[w] = x;
-  __syncthreads();
-  int add = 0;
-  for (int i = 0; i < w; ++i) add += sh[i];
-  __syncthreads();
-  return x + add;
 }
 
 // Ballot compaction of one 256-wide chunk: returns this thread's slot (or -1)
@@ -440,7 +400,6 @@ __device__ inline int chunk_slot(bool flag, int* sh4, int& total) {
 
 // Candidate k of a head, in split order: split by binary search over the
 // exclusive offsets s_off[0..nsplit] held in LDS.
-template <bool kCoherent>
 __device__ inline float2 cand_at(const float2* __restrict__ cand_bh, const int* s_off, int nsplit,
                                  int kR, int k) {
   int lo = 0, hi = nsplit;  // s_off[lo] <= k < s_off[hi]
@@ -449,7 +408,7 @@ __device__ inline float2 cand_at(const float2* __restrict__ cand_bh, const int* 
     if (s_off[mid] <= k) lo = mid;
     else hi = mid;
   }
-  return ld_cand<kCoherent>(cand_bh + (size_t)lo * kR + (k - s_off[lo]));
+  return cand_bh[(size_t)lo * kR + (k - s_off[lo])];
 }
 
 // Arguments of the qk stage (one (row, KV head, split) work item each).
@@ -485,13 +444,11 @@ struct QkItemInfo {
 
 // One qk work item: scores of one split of a (row, KV head)'s selected token
 // slots for the G heads of the group, then per head the split maximum and the
-// candidates z > split_max - 1.  kSelCoherent: sel / n_sel were written by
-// another workgroup of the same launch (device-coherent loads).  kOutCoherent:
-// the candidates, counts and maxima are read by another workgroup of the same
-// launch (device-coherent stores).  Called by all threads of the workgroup;
-// ends with the LDS of `sm` still in use (callers barrier before reuse).
-template <typename T, int D, int G, bool kSelCoherent, bool kOutCoherent,
-          bool kMfma = std::is_same<T, bf16_t>::value>
+// candidates z > split_max - 1.  kOutCoherent: the candidates, counts and
+// maxima are read by another workgroup of the same launch (device-coherent
+// stores).  Called by all threads of the workgroup; ends with the LDS of `sm`
+// still in use (callers barrier before reuse).
+template <typename T, int D, int G, bool kOutCoherent, bool kMfma = std::is_same<T, bf16_t>::value>
 __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item,
                                               QkLds<T, D, G, kMfma>& sm) {
   using GE = Geo<T, D>;
@@ -528,7 +485,7 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   const int g = pair % Hkv;
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  const int nsel = min(sel ? ld_i32<kSelCoherent>(n_sel + pair) : np, max_sel);
+  const int nsel = min(sel ? n_sel[pair] : np, max_sel);
   const int r_begin = s * kR;
   const int r_end = min(nsel << log2P, r_begin + kR);
   if (r_begin >= r_end) return info;  // uniform over the block
@@ -538,7 +495,7 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   // page map of this split: physical page and valid tokens per selected page
   for (int i = threadIdx.x; i < n_pg; i += kBlock) {
     const int j = j_begin + i;
-    const int page = sel ? ld_i32<kSelCoherent>(sel + (size_t)pair * maxP + j) : j;
+    const int page = sel ? sel[(size_t)pair * maxP + j] : j;
     pg_phys[i] = bt[(size_t)b * maxP + page];
     pg_valid[i] = page_valid(L, page, P);
   }
@@ -746,11 +703,9 @@ struct TauLds {
 
 };
 
-// tau and the output of one (row, query head) bh.  kCoherent: the qk stage's
-// candidates, counts and maxima (and n_sel) were written by other workgroups
-// of the same launch (device-coherent loads).  Called by all threads of the
-// workgroup; the LDS of `sm` is free again when it returns.
-template <typename T, int D, bool kCoherent>
+// tau and the output of one (row, query head) bh.  Called by all threads of
+// the workgroup; the LDS of `sm` is free again when it returns.
+template <typename T, int D>
 __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, D>& sm) {
   const float2* __restrict__ cand = a.cand;
   const int* __restrict__ cnt = a.cnt;
@@ -784,7 +739,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
   const int pair = b * Hkv + g;
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  const int nsel = has_sel ? ld_i32<kCoherent>(n_sel + pair) : np;
+  const int nsel = has_sel ? n_sel[pair] : np;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   if (nsel > max_sel || nsel < 1) {
@@ -812,9 +767,9 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
     int cs = 0;
     float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
     if (s < nsplit) {
-      cs = ld_i32<kCoherent>(cnt_bh + s);
-      zm = ld_f32<kCoherent>(smax_bh + s);
-      e = ld_cand<kCoherent>(cand_bh + (size_t)s * kR + j);
+      cs = cnt_bh[s];
+      zm = smax_bh[s];
+      e = cand_bh[(size_t)s * kR + j];
     }
     spec = !__syncthreads_or(cs > kSpec);
     if (spec) {
@@ -844,8 +799,8 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
       const int s = s0 + threadIdx.x;
       int v = 0;
       if (s < nsplit) {
-        zm = fmaxf(zm, ld_f32<kCoherent>(smax_bh + s));
-        v = ld_i32<kCoherent>(cnt_bh + s);
+        zm = fmaxf(zm, smax_bh[s]);
+        v = cnt_bh[s];
       }
       const int incl = block_incl_scan(v, sh4);
       if (s < nsplit) s_off[s] = running + incl - v;
@@ -867,7 +822,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
     for (int k0 = 0; k0 < total_c; k0 += kBlock) {
       const int k = k0 + threadIdx.x;
       float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
-      if (k < total_c) e = cand_at<kCoherent>(cand_bh, s_off, nsplit, kR, k);
+      if (k < total_c) e = cand_at(cand_bh, s_off, nsplit, kR, k);
       const bool flag = (double)e.x > thr;
       int tot;
       const int slot = chunk_slot(flag, sh4, tot);
@@ -969,7 +924,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
         for (int k = threadIdx.x; k < count; k += kBlock) term((double)c_z[k], tt, f, fd);
       } else {
         for (int k = threadIdx.x; k < total_c; k += kBlock)
-          term((double)cand_at<kCoherent>(cand_bh, s_off, nsplit, kR, k).x, tt, f, fd);
+          term((double)cand_at(cand_bh, s_off, nsplit, kR, k).x, tt, f, fd);
       }
       block_sum2(f, fd, shd);
     });
@@ -1011,7 +966,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
       int ptok = 0;
       if (k < lim) {
         if (overflow) {
-          const float2 e = cand_at<kCoherent>(cand_bh, s_off, nsplit, kR, k);
+          const float2 e = cand_at(cand_bh, s_off, nsplit, kR, k);
           z = e.x;
           ptok = bits_of(e.y);
         } else {
