@@ -13,8 +13,8 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kRowsPerThread = 16;  // K rows each thread has in flight per item
-constexpr int kCandCap = 4096;      // LDS candidates per head; more falls back to global
-constexpr int kMaxSplits = 4096;    // splits per head whose offsets fit in LDS
+constexpr int kCandCap = 2048;      // LDS candidates per head; more falls back to global
+constexpr int kMaxSplits = 2048;    // splits per head whose offsets fit in LDS
 
 template <typename T, int D>
 struct Geo {
@@ -52,6 +52,10 @@ __device__ inline uint64_t pack_cand(float z, int ptok) {
   return ((uint64_t)(uint32_t)ptok << 32) | (uint64_t)__float_as_uint(z);
 }
 
+// fp64 power for the non-integer exponents; out of line, so that its code and
+// constants do not occupy registers in the kernels' hot paths.
+__device__ __attribute__((noinline)) double pow_ool(double x, double y) { return pow(x, y); }
+
 __device__ inline double pos_pow(double x, double gamma, int gi) {
   // x > 0
   if (gi > 0) {
@@ -59,7 +63,7 @@ __device__ inline double pos_pow(double x, double gamma, int gi) {
     for (int i = 1; i < gi; ++i) r *= x;
     return r;
   }
-  return pow(x, gamma);
+  return pow_ool(x, gamma);
 }
 
 __device__ inline int wave_incl_scan_i(int x) { return wave_incl_scan_i32(x); }
@@ -70,7 +74,7 @@ __device__ inline int wave_incl_scan_i(int x) { return wave_incl_scan_i32(x); }
 template <typename Eval>
 __device__ inline double newton_tau(double zmax, double nvalid, double alpha, Eval&& eval) {
   double lo = zmax - 1.0;
-  double hi = zmax - pow(nvalid, 1.0 - alpha);
+  double hi = zmax - pow_ool(nvalid, 1.0 - alpha);
   if (hi < lo) hi = lo;
   double tau = lo;
   for (int it = 0; it < 200; ++it) {
@@ -111,7 +115,7 @@ __device__ inline void tau_term(double z, double tau, double gamma, int gamma_in
 template <int kGi>
 __device__ inline double powg(double x, double gamma) {
   if constexpr (kGi == 0) {
-    return x > 0.0 ? pow(x, gamma) : 0.0;
+    return x > 0.0 ? pow_ool(x, gamma) : 0.0;
   } else {
     double r = x;
 #pragma unroll
@@ -166,7 +170,7 @@ __device__ inline bool tau_small_t(float zf, int count, double thr, double gamma
     for (int it = 0; it < 64; ++it) {
       const double x = in ? fmax(z - tau, 0.0) : 0.0;
       const double xg1 = kGi > 0 ? powg<(kGi > 1 ? kGi - 1 : 1)>(x, gamma - 1.0)
-                                 : (x > 0.0 ? pow(x, gamma - 1.0) : 0.0);
+                                 : (x > 0.0 ? pow_ool(x, gamma - 1.0) : 0.0);
       const double f = wave_sum_f64(xg1 * x) - 1.0;
       const double fd = gamma * wave_sum_f64(xg1);
       if (!(fd > 0.0)) break;
@@ -870,7 +874,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
   };
   auto newton = [&](auto&& eval) -> double {
     double lo = thr;
-    double hi = zmax - pow(nvalid, 1.0 - alpha);
+    double hi = zmax - pow_ool(nvalid, 1.0 - alpha);
     if (hi < lo) hi = lo;
     double tau = lo;
     for (int it = 0; it < 200; ++it) {

@@ -255,6 +255,22 @@ __device__ __forceinline__ void score_range(
   }
 }
 
+// Pages per workgroup: whole batches of per_iter pages, enough workgroups to
+// fill the chip once (kScoreResidentBlocks) for short batches, and at most
+// kSlicePages, so long rows are cut into many slices that later workgroups
+// pick up as earlier ones finish (ragged rows then finish together).
+constexpr int kSlicePages = kMaxPagesPerBlock;
+
+int slice_pages(const Shape& s, int per_iter) {
+  const long long pairs = (long long)s.B * s.Hkv;
+  const long long want_blocks_per_pair = (kScoreResidentBlocks + pairs - 1) / pairs;
+  int iters = (int)((s.maxP + per_iter * want_blocks_per_pair - 1) / (per_iter * want_blocks_per_pair));
+  const int max_iters = kSlicePages > per_iter ? kSlicePages / per_iter : 1;
+  if (iters > max_iters) iters = max_iters;
+  if (iters < 1) iters = 1;
+  return per_iter * iters;
+}
+
 template <typename T, int D, int G, int kVec, bool kGauss>
 __global__ __launch_bounds__(kScoreBlock) void score_kernel(
     const float* __restrict__ q, float scale, const T* __restrict__ kmin,
@@ -367,11 +383,7 @@ hipError_t launch_score_t(const Shape& s, const float* q, float scale, const voi
   // enough blocks to spread the pairs over the chip (~4 per CU), each block
   // a whole number of iterations
   const long long pairs = (long long)s.B * s.Hkv;
-  long long want_blocks_per_pair = (kScoreResidentBlocks + pairs - 1) / pairs;
-  int iters = (int)((s.maxP + per_iter * want_blocks_per_pair - 1) / (per_iter * want_blocks_per_pair));
-  if (iters < 1) iters = 1;
-  if (iters * per_iter > kMaxPagesPerBlock) iters = kMaxPagesPerBlock / per_iter;
-  const int ppb = per_iter * iters;
+  const int ppb = slice_pages(s, per_iter);
   dim3 grid((s.maxP + ppb - 1) / ppb, (unsigned)pairs);
   if (gauss) {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0, stream, q,
@@ -412,11 +424,7 @@ hipError_t launch_score_select_t(const Shape& s, const float* q, float scale, co
   constexpr int kPagesPerStep = (kWave / kLpr) * kScoreWaves;
   const int per_iter = kPagesPerStep * ScoreGeo<D, G, kVec, false>::kU;
   const long long pairs = (long long)s.B * s.Hkv;
-  long long want_blocks_per_pair = (kScoreResidentBlocks + pairs - 1) / pairs;
-  int iters = (int)((s.maxP + per_iter * want_blocks_per_pair - 1) / (per_iter * want_blocks_per_pair));
-  if (iters < 1) iters = 1;
-  if (iters * per_iter > kMaxPagesPerBlock) iters = kMaxPagesPerBlock / per_iter;
-  const int ppb = per_iter * iters;
+  const int ppb = slice_pages(s, per_iter);
   dim3 grid((s.maxP + ppb - 1) / ppb, (unsigned)pairs);
   if (s.maxP <= kStepTopkKeys)
     hipLaunchKernelGGL((score_select_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0,
