@@ -25,17 +25,9 @@ namespace ekv {
 namespace {
 
 constexpr int kSelBlock = 256;
-constexpr int kGaussLdsPages = 4096;  // 64 KiB of LDS (mu, sigma) per head
-
-__device__ inline double block_sum_f64(double x, double* sh) {
-  x = wave_sum_f64(x);
-  const int w = threadIdx.x / kWave;
-  if (threadIdx.x % kWave == 0) sh[w] = x;
-  __syncthreads();
-  const double t = (sh[0] + sh[1]) + (sh[2] + sh[3]);
-  __syncthreads();
-  return t;
-}
+constexpr int kGaussLdsPages = 4096;  // 96 KiB of LDS (mu, sigma in fp64 and fp32) per head
+constexpr int kTauBlock = 1024;
+constexpr int kTauWaves = kTauBlock / kWave;
 
 // Ascending compaction of flag(p) for p < n into out[]; returns the count.
 template <typename Flag>
@@ -82,21 +74,22 @@ __global__ __launch_bounds__(kSelBlock) void topk_kernel(
 // --------------------------------------------------------------------------
 // Gaussian-aware selection
 // --------------------------------------------------------------------------
-template <int kG>
-__device__ inline void partial_moments(double h, double& ig, double& igm1) {
-  // I_g(h) and I_{g-1}(h) for Z ~ N(0,1)
-  const double Phi = 0.5 * erfc(-h * 0.70710678118654752440);
-  const double phi = exp(-0.5 * h * h) * 0.39894228040143267794;
-  double i_prev = Phi;             // I_0
-  double i_cur = fma(h, Phi, phi); // I_1
-  if constexpr (kG == 1) {
-    ig = i_cur;
-    igm1 = i_prev;
-    return;
+// I_g(h) and I_{g-1}(h) for Z ~ N(0,1), in the precision of T
+template <int kG, typename T>
+__device__ inline void partial_moments(T h, T& ig, T& igm1) {
+  T Phi, phi;
+  if constexpr (sizeof(T) == 8) {
+    Phi = 0.5 * erfc(-h * 0.70710678118654752440);
+    phi = exp(-0.5 * h * h) * 0.39894228040143267794;
+  } else {
+    Phi = 0.5f * erfcf(-h * 0.70710678f);
+    phi = expf(-0.5f * h * h) * 0.39894228f;
   }
+  T i_prev = Phi;             // I_0
+  T i_cur = fma(h, Phi, phi); // I_1
 #pragma unroll
   for (int k = 2; k <= kG; ++k) {
-    const double nxt = fma(h, i_cur, (double)(k - 1) * i_prev);
+    const T nxt = fma(h, i_cur, (T)(k - 1) * i_prev);
     i_prev = i_cur;
     i_cur = nxt;
   }
@@ -104,21 +97,71 @@ __device__ inline void partial_moments(double h, double& ig, double& igm1) {
   igm1 = i_prev;
 }
 
-template <int kG>
-__device__ inline double ipow(double x) {
-  double r = 1.0;
+template <int kG, typename T>
+__device__ inline T ipow(T x) {
+  T r = 1;
 #pragma unroll
   for (int i = 0; i < kG; ++i) r *= x;
   return r;
 }
 
+// One page's contribution to F(tau) and -F'(tau) (counted cnt times).
+template <int kG, typename T>
+__device__ inline void gauss_term(T mz, T sd, T tau, T cnt, T& f, T& fd) {
+  if (sd > 0) {
+    const T h = (mz - tau) / sd;
+    T ig, igm1;
+    partial_moments<kG>(h, ig, igm1);
+    const T sg1 = ipow<kG - 1>(sd);
+    f = fma(cnt, sg1 * sd * ig, f);
+    fd = fma(cnt, (T)kG * sg1 * igm1, fd);
+  } else {
+    const T x = mz - tau;
+    if (x > 0) {
+      const T xg1 = ipow<kG - 1>(x);
+      f = fma(cnt, xg1 * x, f);
+      fd = fma(cnt, (T)kG * xg1, fd);
+    }
+  }
+}
+
+// Block-wide sums of (a, b); every thread gets the same two values (same
+// operands, same order).  sh holds 2 x 2 x kTauWaves doubles; successive calls
+// alternate halves by `par`, so one barrier per call suffices.
+__device__ inline void block_sum2_f64(double& a, double& b, double* sh, int par) {
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
+  double* buf = sh + par * 2 * kTauWaves;
+  const int w = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) {
+    buf[w] = a;
+    buf[kTauWaves + w] = b;
+  }
+  __syncthreads();
+  double sa = 0.0, sb = 0.0;
+#pragma unroll
+  for (int i = 0; i < kTauWaves; ++i) {
+    sa += buf[i];
+    sb += buf[kTauWaves + i];
+  }
+  a = sa;
+  b = sb;
+}
+
+// tau-hat for one (row, query head).  A coarse fp32 Newton run approaches the
+// root; the fp64 run then starts a small margin below it when F >= 1 holds
+// there in fp64 (any such point keeps Newton monotone), else at the proven
+// start max mu - 1.  Both runs stop when F - 1 or the step stops being
+// positive, so the fp64 result is the monotone Newton limit either way.
 template <int kG, bool kLds>
-__global__ __launch_bounds__(kSelBlock) void gauss_tau_kernel(
+__global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     const double* __restrict__ gm, const double* __restrict__ gv, const int32_t* __restrict__ lens,
     int P, int maxP, int Hq, double a1, double* __restrict__ tau_hat) {
   __shared__ double s_mu[kLds ? kGaussLdsPages : 1];
   __shared__ double s_sd[kLds ? kGaussLdsPages : 1];
-  __shared__ double red[4];
+  __shared__ float s_mu32[kLds ? kGaussLdsPages : 1];
+  __shared__ float s_sd32[kLds ? kGaussLdsPages : 1];
+  __shared__ double red[4 * kTauWaves];
   const int bh = blockIdx.x;
   const int b = bh / Hq;
   const int L = lens[b];
@@ -134,12 +177,23 @@ __global__ __launch_bounds__(kSelBlock) void gauss_tau_kernel(
     if constexpr (kLds) return s_sd[p];
     else return a1 * sqrt(V[p]);
   };
+  auto mu32_of = [&](int p) -> float {
+    if constexpr (kLds) return s_mu32[p];
+    else return (float)(a1 * M[p]);
+  };
+  auto sd32_of = [&](int p) -> float {
+    if constexpr (kLds) return s_sd32[p];
+    else return (float)(a1 * sqrt(V[p]));
+  };
   double zmax = -__builtin_huge_val();
-  for (int p = threadIdx.x; p < n; p += kSelBlock) {
+  for (int p = threadIdx.x; p < n; p += kTauBlock) {
     const double mz = a1 * M[p];
     if constexpr (kLds) {
+      const double sd = a1 * sqrt(V[p]);
       s_mu[p] = mz;
-      s_sd[p] = a1 * sqrt(V[p]);
+      s_sd[p] = sd;
+      s_mu32[p] = (float)mz;
+      s_sd32[p] = (float)sd;
     }
     zmax = fmax(zmax, mz);
   }
@@ -147,34 +201,41 @@ __global__ __launch_bounds__(kSelBlock) void gauss_tau_kernel(
   for (int o = 32; o >= 1; o >>= 1) zmax = fmax(zmax, __shfl_xor(zmax, o, kWave));
   if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = zmax;
   __syncthreads();
-  zmax = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kTauWaves; ++i) zmax = fmax(zmax, red[i]);
+  const double safe = zmax - 1.0;  // F(safe) >= 1
+  int par = 1;                     // red[0 .. 2*kTauWaves) is still being read
 
-  double tau = zmax - 1.0;  // F(tau) >= 1 here
+  float t32 = (float)safe;
+  for (int it = 0; it < 64; ++it) {
+    float f = 0.0f, fd = 0.0f;
+    for (int p = threadIdx.x; p < n; p += kTauBlock)
+      gauss_term<kG, float>(mu32_of(p), sd32_of(p), t32, (float)page_valid(L, p, P), f, fd);
+    double fs = f, fds = fd;
+    block_sum2_f64(fs, fds, red, par);
+    par ^= 1;
+    fs -= 1.0;
+    if (!(fs > 0.0) || !(fds > 0.0)) break;
+    const float step = (float)(fs / fds);
+    const float nxt = t32 + step;
+    if (!(nxt > t32)) break;
+    t32 = nxt;
+    if (step < 1e-6f * (1.0f + fabsf(t32))) break;  // close enough for a start
+  }
+
+  const double start = fmax(safe, (double)t32 - 2e-5 * (1.0 + fabs((double)t32)));
+  double tau = start;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fd = 0.0;
-    for (int p = threadIdx.x; p < n; p += kSelBlock) {
-      const double cnt = (double)page_valid(L, p, P);
-      const double mz = mu_of(p);
-      const double sd = sd_of(p);
-      if (sd > 0.0) {
-        const double h = (mz - tau) / sd;
-        double ig, igm1;
-        partial_moments<kG>(h, ig, igm1);
-        const double sg1 = ipow<kG - 1>(sd);
-        f = fma(cnt, sg1 * sd * ig, f);
-        fd = fma(cnt, (double)kG * sg1 * igm1, fd);
-      } else {
-        const double x = mz - tau;
-        if (x > 0.0) {
-          const double xg1 = ipow<kG - 1>(x);
-          f = fma(cnt, xg1 * x, f);
-          fd = fma(cnt, (double)kG * xg1, fd);
-        }
-      }
+    for (int p = threadIdx.x; p < n; p += kTauBlock)
+      gauss_term<kG, double>(mu_of(p), sd_of(p), tau, (double)page_valid(L, p, P), f, fd);
+    block_sum2_f64(f, fd, red, par);
+    par ^= 1;
+    f -= 1.0;
+    if (it == 0 && f < 0.0 && tau > safe) {  // F(start) < 1: start over at the proven point
+      tau = safe;
+      continue;
     }
-    f = block_sum_f64(f, red) - 1.0;
-    fd = block_sum_f64(fd, red);
     if (!(f > 0.0) || !(fd > 0.0)) break;
     const double nxt = tau + f / fd;
     if (!(nxt > tau)) break;
@@ -248,10 +309,10 @@ template <int kG>
 hipError_t launch_gauss_tau(const Shape& s, const int32_t* lens, double a1, const double* gm,
                             const double* gv, double* tau_hat, hipStream_t stream) {
   if (s.maxP <= kGaussLdsPages)
-    hipLaunchKernelGGL((gauss_tau_kernel<kG, true>), dim3(s.B * s.Hq), dim3(kSelBlock), 0, stream,
+    hipLaunchKernelGGL((gauss_tau_kernel<kG, true>), dim3(s.B * s.Hq), dim3(kTauBlock), 0, stream,
                        gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat);
   else
-    hipLaunchKernelGGL((gauss_tau_kernel<kG, false>), dim3(s.B * s.Hq), dim3(kSelBlock), 0,
+    hipLaunchKernelGGL((gauss_tau_kernel<kG, false>), dim3(s.B * s.Hq), dim3(kTauBlock), 0,
                        stream, gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat);
   return hipGetLastError();
 }
