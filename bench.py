@@ -32,12 +32,12 @@ HBM_PEAK_GBPS = 8000.0
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 # sources whose change invalidates recorded HBM counters, per entry point
-KERNEL_SOURCES = {
-    "ekv_score_select_pages": ["score.hip", "blocks.h", "common.h", "kernels.h"],
-    "ekv_entmax_decode": ["decode.hip", "common.h", "kernels.h"],
-    "ekv_score_pages": ["score.hip", "blocks.h", "common.h", "kernels.h"],
-    "ekv_select_pages": ["select.hip", "blocks.h", "common.h", "kernels.h"],
-    "ekv_build_page_meta": ["meta.hip", "blocks.h", "common.h", "kernels.h"],
+KERNEL_SOURCES = {  # the HIP file of each entry point; local includes are followed
+    "ekv_score_select_pages": "score.hip",
+    "ekv_entmax_decode": "decode.hip",
+    "ekv_score_pages": "score.hip",
+    "ekv_select_pages": "select.hip",
+    "ekv_build_page_meta": "meta.hip",
 }
 ENTRY_POINT = {"refresh": "ekv_build_page_meta", "score": "ekv_score_pages",
                "select": "ekv_select_pages", "decode": "ekv_entmax_decode",
@@ -361,13 +361,32 @@ def run(w, args, dev, emit_cpu=True):
     return rec
 
 
+def kernel_source_files(entry):
+    """The HIP file of an entry point and every local header it includes."""
+    import re
+    dirs = [os.path.join(HERE, "sparse_kv_cache_page_amd", "csrc"), os.path.join(HERE, "include")]
+    todo, seen = [KERNEL_SOURCES[entry]], []
+    while todo:
+        name = todo.pop(0)
+        if name in seen:
+            continue
+        path = next((os.path.join(d, name) for d in dirs if os.path.exists(os.path.join(d, name))), None)
+        if path is None:
+            continue  # a system header
+        seen.append(name)
+        with open(path) as fh:
+            todo += re.findall(r'^#include "([^"]+)"', fh.read(), flags=re.M)
+    return [(n, next(os.path.join(d, n) for d in dirs if os.path.exists(os.path.join(d, n))))
+            for n in seen]
+
+
 def kernel_source_hash(entry):
-    """sha256 over the HIP sources an entry point's kernels are built from."""
+    """sha256 over the sources an entry point's kernels are built from."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[entry]:
-        with open(os.path.join(HERE, "sparse_kv_cache_page_amd", "csrc", f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+    for name, path in kernel_source_files(entry):
+        with open(path, "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 

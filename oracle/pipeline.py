@@ -91,7 +91,7 @@ def decode_heads(q_heads, keys_sel, vals_sel, scale: float, alpha: float):
 def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=None,
              delta=None, scale=None, q=None, exact_meta=False, with_full=False,
              sel_override=None, timings=None):
-    """One decode step of (row b, KV head g) under `policy` ('topk', 'gauss', 'dense').
+    """One decode step of (row b, KV head g) under `policy` ('topk', 'gauss', 'gauss_est', 'dense').
 
     alpha, scale and delta are the fp32 values handed to the library (widened).
     Returns a dict with the metadata, bounds, selection and entmax outputs.
@@ -134,13 +134,14 @@ def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=Non
         sel = select.topk_pages(U, top_k)
     elif policy == "dense":
         sel = list(range(n))
-    elif policy == "gauss":
+    elif policy in ("gauss", "gauss_est"):
         m = np.empty((G, n))
         v = np.empty((G, n))
         for h in range(G):
             for p in range(n):
                 m[h, p], v[h, p] = scores.gauss_moments(qq[h], mu[p], var[p], scale)
-        sel, tau_hat = select.gauss_select(u, m, v, counts, alpha, delta)
+        rule = select.gauss_select if policy == "gauss" else select.gauss_est_select
+        sel, tau_hat = rule(u, m, v, counts, alpha, delta)
         out.update(m=m, v=v, tau_hat=tau_hat)
     else:
         raise ValueError(policy)

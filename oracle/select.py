@@ -22,6 +22,13 @@ EntmaxKV page, §2.B "Politiques de Sélection des Candidats", two policies:
        (Delta in z-space units);
      * if no page clears the bar, the page with the largest U is kept (ties to
        the lowest index), so the entmax input is never empty.
+   A second reading of the "estimated maximum score" (policy G-est) takes the
+   page's n_p token scores as n_p independent draws from N(m_{h,p}, v_{h,p})
+   and estimates their maximum by its expectation,
+         est_{h,p} = m_{h,p} + e_{n_p} sqrt(v_{h,p}),
+         e_n = E[max of n iid N(0, 1)] = integral of x n phi(x) Phi(x)^(n-1) dx,
+   and keeps p when (alpha-1) est_{h,p} >= tau-hat_h - Delta for some head h
+   of the group, with the same tau-hat and the same empty-set guard.
 
 Gaussian partial moments, I_g(h) = E[(Z + h)_+^g] for Z ~ N(0, 1):
    I_0 = Phi(h),  I_1 = h Phi(h) + phi(h),  I_g = h I_{g-1} + (g-1) I_{g-2}
@@ -31,7 +38,8 @@ F_h is continuous and decreasing; at tau = max_p (alpha-1) m_{h,p} - 1 the page
 with the largest mean alone contributes at least 1 (Jensen), so F_h >= 1 there.
 
 Pins (tests/test_oracle_select.py): top-k against a brute-force full sort and
-hand-built tie cases; I_g against numerical quadrature (scipy.integrate.quad);
+hand-built tie cases; e_n against the closed forms known for n <= 5 and a
+Monte Carlo estimate; I_g against numerical quadrature (scipy.integrate.quad);
 tau-hat for zero-variance pages equals the exact entmax threshold of the
 expanded token multiset (checked against the sort-based sparsemax closed form);
 F(tau-hat) = 1.
@@ -40,7 +48,10 @@ from __future__ import annotations
 
 import math
 
+import warnings
+
 import numpy as np
+from scipy import integrate
 from scipy.special import ndtr
 
 
@@ -129,6 +140,52 @@ def gauss_select(u_heads, m_heads, v_heads, counts, alpha: float, delta: float):
         t = gauss_tau_hat(mu_z, sig_z, counts, g)
         taus[h] = t
         keep |= a1 * u_heads[h].astype(np.float64) >= t - float(delta)
+    if not keep.any():
+        U = u_heads.max(axis=0)
+        best = max(range(n), key=lambda p: (float(U[p]), -p))
+        return [best], taus
+    return [int(p) for p in np.nonzero(keep)[0]], taus
+
+
+def expected_max_std_normal(n: int) -> float:
+    """e_n = E[max of n iid N(0, 1)] = integral of x n phi(x) Phi(x)^(n-1) dx (quadrature)."""
+    n = int(n)
+    if n < 1:
+        raise ValueError("n >= 1")
+    if n == 1:
+        return 0.0
+
+    def f(x):
+        return x * n * math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi) * float(ndtr(x)) ** (n - 1)
+
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", integrate.IntegrationWarning)
+        lo = integrate.quad(f, -40.0, 0.0, epsabs=1e-16, epsrel=2e-14, limit=400)[0]
+        hi = integrate.quad(f, 0.0, 40.0, epsabs=1e-16, epsrel=2e-14, limit=400)[0]
+    return lo + hi
+
+
+def gauss_est_select(u_heads, m_heads, v_heads, counts, alpha: float, delta: float):
+    """Gaussian selection with the expected-maximum estimate (G-est), one (row, KV head).
+
+    Same arguments and results as gauss_select; page p is kept when
+    (alpha-1) * (m + e_{n_p} * sqrt(v)) >= tau_hat - delta for a head of the group.
+    """
+    g = integer_gamma(alpha)
+    a1 = float(alpha) - 1.0
+    u_heads = np.asarray(u_heads, dtype=np.float32)
+    G, n = u_heads.shape
+    e_of = {c: expected_max_std_normal(c) for c in set(int(c) for c in counts)}
+    e = np.array([e_of[int(c)] for c in counts])
+    keep = np.zeros(n, dtype=bool)
+    taus = np.empty(G)
+    for h in range(G):
+        m = np.asarray(m_heads[h], dtype=np.float64)
+        v = np.asarray(v_heads[h], dtype=np.float64)
+        t = gauss_tau_hat(a1 * m, a1 * np.sqrt(v), counts, g)
+        taus[h] = t
+        est = m + e * np.sqrt(v)
+        keep |= a1 * est >= t - float(delta)
     if not keep.any():
         U = u_heads.max(axis=0)
         best = max(range(n), key=lambda p: (float(U[p]), -p))

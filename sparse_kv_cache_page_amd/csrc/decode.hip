@@ -28,7 +28,6 @@
 //     solve); the weights off the support are exact zeros:
 //         out = sum_i p_i v_i / sum_i p_i,   p_i = (z_i - tau)^gamma.
 #include <type_traits>
-#include <type_traits>
 
 #include "decode_dev.h"
 #include "kernels.h"

@@ -131,3 +131,64 @@ def test_integer_gamma_rule():
     assert select.integer_gamma(1.25) == 4
     with pytest.raises(ValueError):
         select.integer_gamma(1.7)
+
+
+# Expected maximum of n independent standard normals: closed forms for n <= 5
+# (order statistics of the normal distribution): e_1 = 0, e_2 = 1/sqrt(pi),
+# e_3 = 3/(2 sqrt(pi)), e_4 = 6/pi^(3/2) * arctan(sqrt(2)),
+# e_5 = 5/(4 sqrt(pi)) * (1 + (6/pi) * arcsin(1/3)).
+E_CLOSED = {
+    1: 0.0,
+    2: 1.0 / math.sqrt(math.pi),
+    3: 3.0 / (2.0 * math.sqrt(math.pi)),
+    4: 6.0 / math.pi ** 1.5 * math.atan(math.sqrt(2.0)),
+    5: 5.0 / (4.0 * math.sqrt(math.pi)) * (1.0 + 6.0 / math.pi * math.asin(1.0 / 3.0)),
+}
+
+
+def test_expected_max_closed_forms():
+    for n, e in E_CLOSED.items():
+        assert abs(select.expected_max_std_normal(n) - e) <= 1e-13, n
+
+
+def test_expected_max_monte_carlo_and_shape():
+    rng = np.random.default_rng(17)
+    for n in (16, 32):
+        x = rng.standard_normal((200_000, n)).max(axis=1)
+        mc, se = x.mean(), x.std() / math.sqrt(x.size)
+        assert abs(select.expected_max_std_normal(n) - mc) < 5 * se, n
+    es = [select.expected_max_std_normal(n) for n in range(1, 65)]
+    assert all(b > a for a, b in zip(es, es[1:]))                      # increasing in n
+    assert all(e < math.sqrt(2 * math.log(n)) for n, e in enumerate(es[1:], start=2))
+
+
+def test_gauss_est_select_rule_and_guard():
+    # est = m + e_n sqrt(v); keep iff (alpha-1) est >= tau_hat - delta for some head
+    alpha, delta = 1.5, 0.05
+    a1 = alpha - 1.0
+    u = np.array([[4.0, 3.0, 2.0, 1.0], [1.0, 2.0, 3.0, 4.0]], np.float32)
+    m = np.array([[6.0, 0.2, -0.5, 4.23], [0.1, 5.5, 3.0, -1.0]])
+    v = np.array([[0.5, 2.0, 0.1, 1.0], [1.0, 0.3, 4.0, 0.2]])
+    counts = [4, 4, 4, 3]                  # a ragged last page uses e_3
+    sel, taus = select.gauss_est_select(u, m, v, counts, alpha, delta)
+    e = np.array([E_CLOSED[c] for c in counts])
+    expect = [p for p in range(4)
+              if any(a1 * (m[h, p] + e[p] * math.sqrt(v[h, p])) >= taus[h] - delta
+                     for h in range(2))]
+    assert sel == expect == [0, 1, 2]
+    # page 2 clears the bar only through its spread; page 3 would with e_4
+    assert a1 * m[1, 2] < taus[1] - delta
+    assert a1 * (m[0, 3] + E_CLOSED[4]) >= taus[0] - delta
+    # the threshold is the Gaussian policy's own tau-hat
+    _, taus_b = select.gauss_select(u, m, v, counts, alpha, delta)
+    assert np.array_equal(taus, taus_b)
+    # zero variance: the estimate is the mean itself
+    sel0, t0 = select.gauss_est_select(u, m, np.zeros_like(v), counts, alpha, delta)
+    assert sel0 == [p for p in range(4) if any(a1 * m[h, p] >= t0[h] - delta for h in range(2))]
+    # guard: single-token pages (e_1 = 0) with a wide spread push tau-hat above
+    # every estimate, so nothing clears the bar -> argmax U, lowest index on ties
+    u2 = np.array([[1.0, 7.0, 7.0]], np.float32)
+    m2 = np.zeros((1, 3))
+    v2 = np.full((1, 3), 4.0)
+    sel2, t2 = select.gauss_est_select(u2, m2, v2, [1, 1, 1], 2.0, 0.1)
+    assert t2[0] - 0.1 > 0.0 and sel2 == [1]
