@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="gqa", help="tiny | gqa | gauss | ragged | stress")
+    ap.add_argument("--config", default="gqa",
+                    help="tiny | gqa | gauss | gauss_est | ragged | stress")
     ap.add_argument("--layers", type=int, default=0, help="layers cycled (0 = auto)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -139,14 +140,16 @@ def stage_bytes(layer):
     w, inp, dec = layer.w, layer.inp, layer.dec
     e = 2 if w.kv_dtype == "bf16" else 4
     d, P, Hkv = w.head_dim, w.page_size, w.num_kv_heads
-    gauss = w.policy == "gauss"
+    gauss = w.policy in ("gauss", "gauss_est")
     lens = inp["lens"]
     npg = inp["npages"]
     last_valid = [L - (n - 1) * P for L, n in zip(lens, npg)]
     meta_pp = 2 * d * e + (2 * d * 4 if gauss else 0)
     refresh = sum(Hkv * (v * d * e + meta_pp) for v in last_valid)
     pages = sum(npg) * Hkv
-    score = pages * (meta_pp + 4 + (w.group * (4 + 16) if gauss else 0))
+    # per query head: ub (box-bound reading only) and the fp64 moments
+    score = pages * (meta_pp + 4 + (w.group * ((4 if w.policy == "gauss" else 0) + 16)
+                                    if gauss else 0))
     if w.policy == "dense":
         n_sel = torch.tensor(npg)[:, None].expand(w.batch, Hkv)
     else:
@@ -310,7 +313,7 @@ def workload_config(w, R, graph, inp):
             "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": ctx,
             "page_size": w.page_size, "kv_dtype": w.kv_dtype, "alpha": w.alpha,
             "policy": w.policy, "top_k": w.top_k if w.policy == "topk" else None,
-            "delta": w.delta if w.policy == "gauss" else None,
+            "delta": w.delta if w.policy in ("gauss", "gauss_est") else None,
             "q_std_x_sqrt_d": round(w.q_std * math.sqrt(w.head_dim), 6),
             "layers_rotated": R, "hip_graph": graph,
             "graph_scope": "one graph per pass over the rotated layers" if graph else None}

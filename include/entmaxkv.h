@@ -65,7 +65,10 @@ typedef enum { EKV_BF16 = 0, EKV_F32 = 1 } ekv_dtype;
 
 typedef enum {
   EKV_SELECT_TOPK = 0,  /* fixed budget: k pages with the largest bound     */
-  EKV_SELECT_GAUSS = 1  /* Gaussian estimate tau-hat of the threshold, margin Delta */
+  EKV_SELECT_GAUSS = 1,     /* Gaussian estimate tau-hat of the threshold, margin Delta;
+                               a page's maximum score estimated by its box bound     */
+  EKV_SELECT_GAUSS_EST = 2  /* same tau-hat and Delta; maximum score estimated as the
+                               expected maximum of its tokens' Gaussian scores       */
 } ekv_policy;
 
 typedef struct {
@@ -141,6 +144,14 @@ ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float sca
  *   (lowest index on ties).  Needs ub, ubg, gm, gv and tau_hat; gamma must be
  *   1, 2, 3 or 4 (alpha in {2, 1.5, 4/3, 1.25}) else EKV_ERR_UNSUPPORTED;
  *   delta >= 0.
+ * EKV_SELECT_GAUSS_EST: as EKV_SELECT_GAUSS, but the estimated maximum score
+ *   of page p for head h is the expected maximum of its n_p token scores
+ *   modelled as independent N(gm, gv) draws (the estimated maximum of §2.B):
+ *   page p is kept when
+ *   (alpha-1) * (gm[b][h][p] + e_{n_p} * sqrt(gv[b][h][p])) >= tau_hat[b][h] - delta
+ *   (fp64, each operation rounded separately), with e_n = E[max of n iid
+ *   N(0,1)] (e_1 = 0, e_16 = 1.76599...).  ub is not read and may be NULL.
+ *   The empty-set guard and every other rule are those of EKV_SELECT_GAUSS.
  * Arrays: sel [B][Hkv][maxP] int32; n_sel [B][Hkv] int32; tau_hat [B][Hq] fp64.
  */
 ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
@@ -252,6 +263,11 @@ size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k);
 /* Scratch bytes ekv_entmax_decode needs for this cache shape and max_sel
  * (0 if desc is invalid). */
 size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);
+
+/* e_n = E[max of n iid N(0,1)] as used by EKV_SELECT_GAUSS_EST for a page of
+ * n valid tokens (tabulated once on the host by quadrature); NaN unless
+ * 1 <= n <= 64.  Host-only: launches nothing, needs no device. */
+double ekv_gauss_expected_max(int32_t n);
 
 /* Static description of a status code (never NULL). */
 const char* ekv_status_string(ekv_status status);

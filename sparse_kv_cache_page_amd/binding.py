@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libentmaxkv
 
 EKV_OK = 0
 EKV_BF16, EKV_F32 = 0, 1
-EKV_SELECT_TOPK, EKV_SELECT_GAUSS = 0, 1
+EKV_SELECT_TOPK, EKV_SELECT_GAUSS, EKV_SELECT_GAUSS_EST = 0, 1, 2
 
 EXPORTED = (
     "ekv_build_page_meta",
@@ -33,6 +33,7 @@ EXPORTED = (
     "ekv_score_select_workspace_bytes",
     "ekv_decode_step",
     "ekv_step_workspace_bytes",
+    "ekv_gauss_expected_max",
     "ekv_status_string",
 )
 
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_decode_fused_workspace_bytes.restype = sz
     lib.ekv_decode_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_decode_workspace_bytes.restype = sz
+    lib.ekv_gauss_expected_max.argtypes = [i32]
+    lib.ekv_gauss_expected_max.restype = ctypes.c_double
     lib.ekv_status_string.argtypes = [ctypes.c_int]
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
@@ -98,6 +101,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def gauss_expected_max(n: int) -> float:
+    """ekv_gauss_expected_max: the library's e_n = E[max of n iid N(0,1)] (host-only)."""
+    return float(load_library().ekv_gauss_expected_max(int(n)))
 
 
 def status_string(status: int) -> str:
@@ -203,7 +211,8 @@ def score_pages(s: CacheShape, q, scale: float, kmin, kmax, block_table, seq_len
 
 def select_pages(s: CacheShape, seq_lens, policy: int, top_k: int, alpha: float, delta: float,
                  ubg, sel, n_sel, ub=None, gm=None, gv=None, tau_hat=None):
-    """ekv_select_pages: top-k (policy 0) or Gaussian-aware (policy 1) selection."""
+    """ekv_select_pages: top-k (policy 0) or Gaussian-aware selection with the box
+    bound (policy 1) or the expected maximum (policy 2) as a page's estimated maximum."""
     B, Hq, Hkv, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.max_pages_per_seq
     _need(seq_lens, "seq_lens", torch.int32, (B,))
     _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
@@ -211,6 +220,7 @@ def select_pages(s: CacheShape, seq_lens, policy: int, top_k: int, alpha: float,
     _need(n_sel, "n_sel", torch.int32, (B, Hkv))
     if policy == EKV_SELECT_GAUSS:
         _need(ub, "ub", torch.float32, (B, Hq, mp))
+    if policy in (EKV_SELECT_GAUSS, EKV_SELECT_GAUSS_EST):
         _need(gm, "gm", torch.float64, (B, Hq, mp))
         _need(gv, "gv", torch.float64, (B, Hq, mp))
         _need(tau_hat, "tau_hat", torch.float64, (B, Hq))

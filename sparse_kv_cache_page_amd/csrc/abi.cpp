@@ -30,7 +30,7 @@ ekv_status make_shape(const ekv_cache_desc* d, Shape* s) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return EKV_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return EKV_ERR_UNSUPPORTED;
   const int l2 = log2_exact(d->page_size);
-  if (l2 < 0 || d->page_size > 64) return EKV_ERR_UNSUPPORTED;
+  if (l2 < 0 || d->page_size > ekv::kMaxPageSize) return EKV_ERR_UNSUPPORTED;
   // token slots of one row and page counts must stay inside int32 indexing
   if ((long long)d->max_pages_per_seq * d->page_size > (1LL << 30)) return EKV_ERR_UNSUPPORTED;
   s->B = d->batch;
@@ -66,6 +66,8 @@ const char* ekv_status_string(ekv_status status) {
   }
   return "unknown status";
 }
+
+double ekv_gauss_expected_max(int32_t n) { return ekv::expected_max_std_normal(n); }
 
 ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
                                const int32_t* block_table, const int32_t* seq_lens,
@@ -119,15 +121,17 @@ ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
     if (top_k < 1) return EKV_ERR_INVALID_ARG;
     return from_hip(ekv::launch_topk(s, seq_lens, top_k, ubg, sel, n_sel, stream));
   }
-  if (policy != EKV_SELECT_GAUSS) return EKV_ERR_INVALID_ARG;
-  if (!ok_i32(ub) || !ok_f64(gm) || !ok_f64(gv) || !ok_f64(tau_hat)) return EKV_ERR_INVALID_ARG;
+  if (policy != EKV_SELECT_GAUSS && policy != EKV_SELECT_GAUSS_EST) return EKV_ERR_INVALID_ARG;
+  const bool est = policy == EKV_SELECT_GAUSS_EST;
+  if ((!est && !ok_i32(ub)) || !ok_f64(gm) || !ok_f64(gv) || !ok_f64(tau_hat))
+    return EKV_ERR_INVALID_ARG;
   if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
   if (!(delta >= 0.0f) || !isfinite(delta)) return EKV_ERR_INVALID_ARG;
   const double gamma = 1.0 / ((double)alpha - 1.0);
   const double gr = rint(gamma);
   if (gr < 1.0 || gr > 4.0 || fabs(gamma - gr) > 1e-6 * gr) return EKV_ERR_UNSUPPORTED;
-  return from_hip(ekv::launch_gauss(s, seq_lens, alpha, (int)gr, delta, ub, ubg, gm, gv, sel,
-                                    n_sel, tau_hat, stream));
+  return from_hip(ekv::launch_gauss(s, seq_lens, alpha, (int)gr, delta, est, ub, ubg, gm, gv,
+                                    sel, n_sel, tau_hat, stream));
 }
 
 size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel) {

@@ -9,6 +9,8 @@
 
 namespace ekv {
 
+constexpr int kMaxPageSize = 64;  // largest supported tokens per page
+
 struct Shape {
   int B, Hq, Hkv, G, D, P, log2P, maxP, Np;
   bool bf16;
@@ -35,10 +37,16 @@ hipError_t launch_score_select(const Shape& s, const float* q, float scale, cons
 hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const float* ubg,
                        int32_t* sel, int32_t* n_sel, hipStream_t stream);
 
+// e_n = E[max of n iid N(0,1)] as tabulated for the expected-maximum policy
+// (NaN outside 1 <= n <= kMaxPageSize).
+double expected_max_std_normal(int n);
+
+// Gaussian-aware selection; `est` picks the expected-maximum estimate
+// m + e_n sqrt(v) of a page's maximum score instead of its box bound ub.
 hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int gamma,
-                        float delta, const float* ub, const float* ubg, const double* gm,
-                        const double* gv, int32_t* sel, int32_t* n_sel, double* tau_hat,
-                        hipStream_t stream);
+                        float delta, bool est, const float* ub, const float* ubg,
+                        const double* gm, const double* gv, int32_t* sel, int32_t* n_sel,
+                        double* tau_hat, hipStream_t stream);
 
 // Decode plan: the selected token slots of a (row, KV head) pair are cut into
 // splits of `slots_per_item` slots (one qk work item each); the scratch arrays

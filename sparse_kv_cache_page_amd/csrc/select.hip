@@ -16,8 +16,12 @@
 // I_g = h I_{g-1} + (g-1) I_{g-2}.  F is convex and decreasing (gamma >= 1),
 // F >= 1 at max_p mu_p - 1, and F' = -gamma sum_p n_p s^(g-1) I_{g-1}, so
 // Newton's method started there climbs monotonically to the root.  A second
-// kernel keeps page p when (alpha-1) u_{h,p} >= tau-hat_h - delta for some head
-// of the group and compacts the kept pages in ascending order.
+// kernel keeps page p when (alpha-1) est_{h,p} >= tau-hat_h - delta for some
+// head of the group and compacts the kept pages in ascending order.  The
+// page's estimated maximum score est is its box bound u (box-bound reading), or
+// m + e_n sqrt(v), the expected maximum of its n valid token scores drawn from
+// N(m, v) (expected-maximum reading), with e_n = E[max of n iid N(0,1)]
+// tabulated once on the host.
 #include "blocks.h"
 #include "kernels.h"
 
@@ -244,10 +248,17 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
   if (threadIdx.x == 0) tau_hat[bh] = tau;
 }
 
+// e_n for n = 0 .. kMaxPageSize (entry 0 unused)
+struct ExpMaxTable {
+  double e[kMaxPageSize + 1];
+};
+
+template <bool kEst>
 __global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
-    const float* __restrict__ ub, const float* __restrict__ ubg, const double* __restrict__ tau_hat,
+    const float* __restrict__ ub, const float* __restrict__ ubg, const double* __restrict__ gm,
+    const double* __restrict__ gv, const double* __restrict__ tau_hat,
     const int32_t* __restrict__ lens, int P, int maxP, int Hkv, int G, double a1, double delta,
-    int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
+    ExpMaxTable et, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
   __shared__ int scan_sh[4];
   __shared__ float s_best[4];
   __shared__ int s_bestp[4];
@@ -255,13 +266,27 @@ __global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
   const int b = pair / Hkv;
   const int g = pair % Hkv;
   const int Hq = Hkv * G;
-  const int n = (lens[b] + P - 1) / P;
-  const float* ubh = ub + ((size_t)b * Hq + g * G) * maxP;
+  const int L = lens[b];
+  const int n = (L + P - 1) / P;
+  const size_t head0 = ((size_t)b * Hq + g * G) * maxP;
   const double* th = tau_hat + (size_t)b * Hq + g * G;
   int32_t* out = sel + (size_t)pair * maxP;
+  // every page but the last holds P tokens
+  const double e_full = et.e[P];
+  const double e_last = et.e[page_valid(L, n - 1, P)];
   auto keep = [&](int p) -> bool {
-    for (int h = 0; h < G; ++h)
-      if (a1 * (double)ubh[(size_t)h * maxP + p] >= th[h] - delta) return true;
+    for (int h = 0; h < G; ++h) {
+      const size_t i = head0 + (size_t)h * maxP + p;
+      double est;
+      if constexpr (kEst) {
+        // m + e_n sqrt(v), each operation rounded on its own (no contraction)
+        const double e = p == n - 1 ? e_last : e_full;
+        est = __dadd_rn(gm[i], __dmul_rn(e, sqrt(gv[i])));
+      } else {
+        est = (double)ub[i];
+      }
+      if (__dmul_rn(a1, est) >= th[h] - delta) return true;
+    }
     return false;
   };
   const int got = compact_ascending(n, keep, out, scan_sh);
@@ -317,7 +342,46 @@ hipError_t launch_gauss_tau(const Shape& s, const int32_t* lens, double a1, cons
   return hipGetLastError();
 }
 
+// e_n = integral of x n phi(x) Phi(x)^(n-1) dx by the trapezoidal rule on
+// [-16, 16] with step 1/128: the integrand is analytic and decays like phi, so
+// the rule converges geometrically and the truncated tails are below 1e-50.
+// The nodes are summed with Neumaier's compensated summation.
+const ExpMaxTable& exp_max_table() {
+  static const ExpMaxTable table = [] {
+    ExpMaxTable t{};
+    double comp[kMaxPageSize + 1] = {};
+    constexpr int kSteps = 4096;
+    constexpr double kHalfWidth = 16.0;
+    constexpr double h = 2.0 * kHalfWidth / kSteps;
+    const double inv_sqrt_2pi = 0.39894228040143267794;
+    for (int i = 0; i <= kSteps; ++i) {
+      const double x = -kHalfWidth + i * h;
+      const double w = (i == 0 || i == kSteps) ? 0.5 * h : h;
+      const double phi = exp(-0.5 * x * x) * inv_sqrt_2pi;
+      const double Phi = 0.5 * erfc(-x * 0.70710678118654752440);
+      double pw = 1.0;  // Phi^(n-1)
+      for (int n = 1; n <= kMaxPageSize; ++n) {
+        const double term = w * x * n * phi * pw;
+        const double sum = t.e[n] + term;
+        comp[n] += fabs(t.e[n]) >= fabs(term) ? (t.e[n] - sum) + term : (term - sum) + t.e[n];
+        t.e[n] = sum;
+        pw *= Phi;
+      }
+    }
+    for (int n = 1; n <= kMaxPageSize; ++n) t.e[n] += comp[n];
+    t.e[0] = 0.0;
+    t.e[1] = 0.0;  // symmetric integrand: exactly zero
+    return t;
+  }();
+  return table;
+}
+
 }  // namespace
+
+double expected_max_std_normal(int n) {
+  if (n < 1 || n > kMaxPageSize) return __builtin_nan("");
+  return exp_max_table().e[n];
+}
 
 hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const float* ubg,
                        int32_t* sel, int32_t* n_sel, hipStream_t stream) {
@@ -331,8 +395,9 @@ hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const flo
 }
 
 hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int gamma, float delta,
-                        const float* ub, const float* ubg, const double* gm, const double* gv,
-                        int32_t* sel, int32_t* n_sel, double* tau_hat, hipStream_t stream) {
+                        bool est, const float* ub, const float* ubg, const double* gm,
+                        const double* gv, int32_t* sel, int32_t* n_sel, double* tau_hat,
+                        hipStream_t stream) {
   const double a1 = (double)alpha - 1.0;
   hipError_t e = hipErrorInvalidValue;
   switch (gamma) {
@@ -342,8 +407,15 @@ hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int ga
     case 4: e = launch_gauss_tau<4>(s, lens, a1, gm, gv, tau_hat, stream); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gauss_mark_kernel, dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream, ub, ubg,
-                     tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1, (double)delta, sel, n_sel);
+  const ExpMaxTable& et = exp_max_table();
+  if (est)
+    hipLaunchKernelGGL((gauss_mark_kernel<true>), dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream,
+                       ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1,
+                       (double)delta, et, sel, n_sel);
+  else
+    hipLaunchKernelGGL((gauss_mark_kernel<false>), dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream,
+                       ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1,
+                       (double)delta, et, sel, n_sel);
   return hipGetLastError();
 }
 

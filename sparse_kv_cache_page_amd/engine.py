@@ -26,8 +26,8 @@ class PagedEntmaxDecoder:
     def __init__(self, shape: CacheShape, *, policy: str = "topk", top_k: int = 256,
                  alpha: float = 1.5, scale: float = 1.0, delta: float = 0.1,
                  device: Optional[torch.device] = None, fused: bool = False):
-        if policy not in ("topk", "gauss", "dense"):
-            raise ValueError("policy must be 'topk', 'gauss' or 'dense'")
+        if policy not in ("topk", "gauss", "gauss_est", "dense"):
+            raise ValueError("policy must be 'topk', 'gauss', 'gauss_est' or 'dense'")
         self.shape = s = shape
         self.policy = policy
         self.top_k = int(top_k)
@@ -38,13 +38,14 @@ class PagedEntmaxDecoder:
         self.device = dev
         Bt, Hq, Hkv, d, mp, Np = (s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim,
                                   s.max_pages_per_seq, s.num_phys_pages)
-        gauss = policy == "gauss"
+        gauss = policy in ("gauss", "gauss_est")
         self.kmin = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
         self.kmax = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
         self.mean = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
         self.var = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
         self.ubg = torch.empty(Bt, Hkv, mp, dtype=torch.float32, device=dev)
-        self.ub = torch.empty(Bt, Hq, mp, dtype=torch.float32, device=dev) if gauss else None
+        self.ub = (torch.empty(Bt, Hq, mp, dtype=torch.float32, device=dev)
+                   if policy == "gauss" else None)
         self.gm = torch.empty(Bt, Hq, mp, dtype=torch.float64, device=dev) if gauss else None
         self.gv = torch.empty(Bt, Hq, mp, dtype=torch.float64, device=dev) if gauss else None
         self.tau_hat = torch.empty(Bt, Hq, dtype=torch.float64, device=dev) if gauss else None
@@ -79,10 +80,11 @@ class PagedEntmaxDecoder:
         if self.policy == "topk":
             B.select_pages(self.shape, seq_lens, B.EKV_SELECT_TOPK, self.top_k, self.alpha,
                            self.delta, self.ubg, self.sel, self.n_sel)
-        elif self.policy == "gauss":
-            B.select_pages(self.shape, seq_lens, B.EKV_SELECT_GAUSS, self.top_k, self.alpha,
-                           self.delta, self.ubg, self.sel, self.n_sel, ub=self.ub, gm=self.gm,
-                           gv=self.gv, tau_hat=self.tau_hat)
+        elif self.policy in ("gauss", "gauss_est"):
+            pol = B.EKV_SELECT_GAUSS if self.policy == "gauss" else B.EKV_SELECT_GAUSS_EST
+            B.select_pages(self.shape, seq_lens, pol, self.top_k, self.alpha, self.delta,
+                           self.ubg, self.sel, self.n_sel, ub=self.ub, gm=self.gm, gv=self.gv,
+                           tau_hat=self.tau_hat)
 
     def decode(self, q, K, V, block_table, seq_lens):
         dense = self.policy == "dense"

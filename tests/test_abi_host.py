@@ -148,6 +148,30 @@ def test_select_argument_errors(lib):
     assert call(policy=1, alpha=1.1) == UNSUPPORTED    # gamma = 10 > 4
     assert call(policy=1, tau=None) == INVALID
     assert call(policy=1, gm=None) == INVALID
+    assert call(policy=1, ub=None) == INVALID
+    # the expected-maximum policy: same checks, ub not needed
+    assert call(policy=2, alpha=1.0, ub=None) == INVALID
+    assert call(policy=2, delta=-0.1, ub=None) == INVALID
+    assert call(policy=2, alpha=1.7, ub=None) == UNSUPPORTED
+    assert call(policy=2, gv=None, ub=None) == INVALID
+    assert call(policy=2, tau=None, ub=None) == INVALID
+    assert call(policy=3) == INVALID
+
+
+def test_library_expected_max_table(lib):
+    # the library tabulates e_n by its own quadrature; the oracle integrates with
+    # scipy, and n <= 5 have closed forms
+    import math
+    from oracle import select
+    from test_oracle_select import E_CLOSED
+    for n in range(1, 65):
+        e = B.gauss_expected_max(n)
+        assert abs(e - select.expected_max_std_normal(n)) <= 4e-15 * max(1.0, e), n
+    for n, e in E_CLOSED.items():
+        assert abs(B.gauss_expected_max(n) - e) <= 4e-15, n
+    assert B.gauss_expected_max(1) == 0.0
+    for n in (0, -1, 65):
+        assert math.isnan(B.gauss_expected_max(n))
 
 
 def test_score_argument_errors(lib):

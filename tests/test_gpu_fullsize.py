@@ -77,6 +77,19 @@ def test_fullsize_config(name, pairs):
     decoder_matches(inp, gpu, pol, w.alpha, w.top_k, w.delta, w.scale, inp["q"])
 
 
+def test_fullsize_gauss_est():
+    # gauss shapes with the expected-maximum estimate of a page's maximum score
+    w = wl.variant("gauss", policy="gauss_est")
+    print("[fullsize] gauss_est: generating", flush=True)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "gauss_est")
+    check_properties(inp, gpu, "gauss_est", w.top_k)
+    for b, g in [(0, 0), (6, 2)]:
+        print(f"[fullsize] gauss_est: oracle pair b{b} g{g}", flush=True)
+        check_pair(inp, gpu, b, g, "gauss_est")
+    decoder_matches(inp, gpu, "gauss_est", w.alpha, w.top_k, w.delta, w.scale, inp["q"])
+
+
 @pytest.fixture(scope="module")
 def stress_inputs():
     w = wl.CONFIGS["stress"]
@@ -91,6 +104,7 @@ STRESS_CASES = [
     (1.25, 0, "topk", 512), (1.25, 1, "topk", 128), (1.25, 2, "dense", 0),
     (1.5, 0, "gauss", 0), (1.5, 1, "topk", 512), (1.5, 2, "topk", 128),
     (2.0, 0, "dense", 0), (2.0, 1, "gauss", 0), (2.0, 2, "topk", 512),
+    (1.25, 1, "gauss_est", 0),
 ]
 
 

@@ -132,6 +132,34 @@ def test_gauss_guard_keeps_argmax():
         assert int(gpu["n_sel"][b, g]) == 1 and int(gpu["sel"][b, g, 0]) == 0
 
 
+@pytest.mark.parametrize("alpha,page_size", [(2.0, 16), (1.5, 8), (1.25, 32), (4.0 / 3.0, 64)])
+def test_gauss_est_policy(alpha, page_size):
+    # expected-maximum estimate m + e_n sqrt(v): e_P on full pages, e_n on the
+    # ragged last page of each row
+    w = small(73, alpha=alpha, policy="gauss_est", clusters=16, planted_per_kv_head=0,
+              page_size=page_size, lens_range=(100, 1200), delta=0.1)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "gauss_est")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "gauss_est")
+
+
+def test_gauss_est_guard_keeps_argmax():
+    # the guard case of the box-bound reading, with tau-hat also above
+    # m + e_16 sigma: F(m + e_16 sigma) = 16 * 40 * sigma * I_1(-e_16) ~ 2.5 > 1
+    w = small(81, alpha=2.0, policy="gauss_est", planted_per_kv_head=0,
+              lens_range=(600, 700), delta=0.0)
+    inp = wl.make_inputs(w, device=DEV)
+    K = inp["K"]
+    K.zero_()
+    K[:, :, 8:, 0] = 1.0
+    inp["q"][:, :, 0] = 0.5
+    gpu = run_gpu(inp, "gauss_est")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "gauss_est")
+        assert int(gpu["n_sel"][b, g]) == 1 and int(gpu["sel"][b, g, 0]) == 0
+
+
 def test_edge_single_token_rows():
     w = small(91, lens_range=None, seq_len=1, batch=2, top_k=3)
     inp = wl.make_inputs(w, device=DEV)
