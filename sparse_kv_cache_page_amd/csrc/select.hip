@@ -32,25 +32,9 @@ constexpr int kSelBlock = 256;
 constexpr int kGaussLdsPages = 4096;  // 96 KiB of LDS (mu, sigma in fp64 and fp32) per head
 constexpr int kTauBlock = 1024;
 constexpr int kTauWaves = kTauBlock / kWave;
-
-// Ascending compaction of flag(p) for p < n into out[]; returns the count.
-template <typename Flag>
-__device__ int compact_ascending(int n, Flag flag, int32_t* out, int* sh) {
-  const int chunk = (n + kSelBlock - 1) / kSelBlock;
-  const int p0 = threadIdx.x * chunk;
-  const int p1 = min(n, p0 + chunk);
-  int cnt = 0;
-  for (int p = p0; p < p1; ++p) cnt += flag(p) ? 1 : 0;
-  const int incl = block_incl_scan(cnt, sh);
-  int pos = incl - cnt;
-  for (int p = p0; p < p1; ++p)
-    if (flag(p)) out[pos++] = p;
-  // total = inclusive scan of the last thread
-  __shared__ int total;
-  if (threadIdx.x == kSelBlock - 1) total = incl;
-  __syncthreads();
-  return total;
-}
+constexpr int kMarkBlock = 1024;
+constexpr int kMarkWaves = kMarkBlock / kWave;
+constexpr int kMarkChunk = 4096;  // pages whose keep flags are staged in LDS at once
 
 template <bool kLds>
 __global__ __launch_bounds__(kSelBlock) void topk_kernel(
@@ -152,11 +136,11 @@ __device__ inline void block_sum2_f64(double& a, double& b, double* sh, int par)
   b = sb;
 }
 
-// tau-hat for one (row, query head).  A coarse fp32 Newton run approaches the
-// root; the fp64 run then starts a small margin below it when F >= 1 holds
-// there in fp64 (any such point keeps Newton monotone), else at the proven
-// start max mu - 1.  Both runs stop when F - 1 or the step stops being
-// positive, so the fp64 result is the monotone Newton limit either way.
+// tau-hat for one (row, query head).  A coarse fp32 run approaches the root;
+// the fp64 run then starts a small margin below it when F >= 1 holds there in
+// fp64 (any such point keeps Newton monotone), else at the proven start
+// max mu - 1, and stops when F - 1 or the step stops being positive, so its
+// result is the monotone Newton limit either way.
 template <int kG, bool kLds>
 __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     const double* __restrict__ gm, const double* __restrict__ gv, const int32_t* __restrict__ lens,
@@ -210,24 +194,42 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
   const double safe = zmax - 1.0;  // F(safe) >= 1
   int par = 1;                     // red[0 .. 2*kTauWaves) is still being read
 
-  float t32 = (float)safe;
-  for (int it = 0; it < 64; ++it) {
+  // Coarse fp32 run: Newton on log F, which is nearly linear where a few
+  // Gaussian tails dominate (about half the steps of Newton on F), kept inside
+  // the bracket (lo, hi) of points seen with F >= 1 and F < 1; a step leaving
+  // it falls back to bisection, or, before any point with F < 1 is seen, to a
+  // Newton step on F itself (which stays left of the root).
+  const double huge = __builtin_huge_val();
+  double lo = safe, hi = huge, t = safe;
+  for (int it = 0; it < 48 && n > 0; ++it) {
     float f = 0.0f, fd = 0.0f;
+    const float tf = (float)t;
     for (int p = threadIdx.x; p < n; p += kTauBlock)
-      gauss_term<kG, float>(mu32_of(p), sd32_of(p), t32, (float)page_valid(L, p, P), f, fd);
+      gauss_term<kG, float>(mu32_of(p), sd32_of(p), tf, (float)page_valid(L, p, P), f, fd);
     double fs = f, fds = fd;
     block_sum2_f64(fs, fds, red, par);
     par ^= 1;
-    fs -= 1.0;
-    if (!(fs > 0.0) || !(fds > 0.0)) break;
-    const float step = (float)(fs / fds);
-    const float nxt = t32 + step;
-    if (!(nxt > t32)) break;
-    t32 = nxt;
-    if (step < 1e-6f * (1.0f + fabsf(t32))) break;  // close enough for a start
+    if (fs >= 1.0) lo = fmax(lo, t);
+    else hi = fmin(hi, t);
+    const bool ok = fs > 0.0 && fds > 0.0;
+    double nxt = ok ? t + log(fs) * fs / fds : t;
+    if (ok && fabs(nxt - t) < 1e-6 * (1.0 + fabs(nxt))) {  // converged as far as fp32 goes
+      t = nxt;
+      break;
+    }
+    if (!(nxt > lo && nxt < hi)) {
+      if (hi < huge) nxt = 0.5 * (lo + hi);
+      else if (fds > 0.0) nxt = t + (fs - 1.0) / fds;
+      else break;
+    }
+    t = nxt;
   }
 
-  const double start = fmax(safe, (double)t32 - 2e-5 * (1.0 + fabs((double)t32)));
+  // fp64 run: monotone Newton on F from a start just below the coarse root
+  // (checked: F(start) >= 1 in fp64, else the proven start max mu - 1).  A step
+  // below 1e-15 |tau| ends it without another evaluation: the next one would
+  // be below rounding.
+  const double start = fmax(safe, t - 4e-6 * (1.0 + fabs(t)));
   double tau = start;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fd = 0.0;
@@ -241,9 +243,11 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
       continue;
     }
     if (!(f > 0.0) || !(fd > 0.0)) break;
-    const double nxt = tau + f / fd;
+    const double step = f / fd;
+    const double nxt = tau + step;
     if (!(nxt > tau)) break;
     tau = nxt;
+    if (step <= 1e-15 * fabs(tau)) break;
   }
   if (threadIdx.x == 0) tau_hat[bh] = tau;
 }
@@ -253,15 +257,45 @@ struct ExpMaxTable {
   double e[kMaxPageSize + 1];
 };
 
+// Ascending compaction of flag(p) for p < n into out[]; returns the count.
+// Per chunk of kMarkChunk pages the flags are evaluated with consecutive
+// threads on consecutive pages (coalesced reads) and staged in LDS; each
+// thread then writes the kept pages of a contiguous run of them at its
+// offset from a block scan.
+template <typename Flag>
+__device__ int compact_ascending(int n, Flag flag, int32_t* out, uint8_t* s_flag, int* sh) {
+  int total = 0;
+  for (int c0 = 0; c0 < n; c0 += kMarkChunk) {
+    const int m = min(kMarkChunk, n - c0);
+    for (int i = threadIdx.x; i < m; i += kMarkBlock) s_flag[i] = flag(c0 + i) ? 1 : 0;
+    __syncthreads();
+    const int per = (m + kMarkBlock - 1) / kMarkBlock;
+    const int p0 = min(m, (int)threadIdx.x * per);
+    const int p1 = min(m, p0 + per);
+    int cnt = 0;
+    for (int i = p0; i < p1; ++i) cnt += s_flag[i];
+    const int incl = block_incl_scan(cnt, sh);
+    int pos = total + incl - cnt;
+    for (int i = p0; i < p1; ++i)
+      if (s_flag[i]) out[pos++] = c0 + i;
+    if (threadIdx.x == kMarkBlock - 1) sh[kMarkWaves] = incl;
+    __syncthreads();
+    total += sh[kMarkWaves];
+    __syncthreads();  // s_flag and sh are rewritten by the next chunk
+  }
+  return total;
+}
+
 template <bool kEst>
-__global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
+__global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
     const float* __restrict__ ub, const float* __restrict__ ubg, const double* __restrict__ gm,
     const double* __restrict__ gv, const double* __restrict__ tau_hat,
     const int32_t* __restrict__ lens, int P, int maxP, int Hkv, int G, double a1, double delta,
     ExpMaxTable et, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
-  __shared__ int scan_sh[4];
-  __shared__ float s_best[4];
-  __shared__ int s_bestp[4];
+  __shared__ uint8_t s_flag[kMarkChunk];
+  __shared__ int scan_sh[kMarkWaves + 1];
+  __shared__ float s_best[kMarkWaves];
+  __shared__ int s_bestp[kMarkWaves];
   const int pair = blockIdx.x;
   const int b = pair / Hkv;
   const int g = pair % Hkv;
@@ -275,6 +309,7 @@ __global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
   const double e_full = et.e[P];
   const double e_last = et.e[page_valid(L, n - 1, P)];
   auto keep = [&](int p) -> bool {
+    bool any = false;
     for (int h = 0; h < G; ++h) {
       const size_t i = head0 + (size_t)h * maxP + p;
       double est;
@@ -285,11 +320,11 @@ __global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
       } else {
         est = (double)ub[i];
       }
-      if (__dmul_rn(a1, est) >= th[h] - delta) return true;
+      any |= __dmul_rn(a1, est) >= th[h] - delta;
     }
-    return false;
+    return any;
   };
-  const int got = compact_ascending(n, keep, out, scan_sh);
+  const int got = compact_ascending(n, keep, out, s_flag, scan_sh);
   if (got > 0) {
     if (threadIdx.x == 0) n_sel[pair] = got;
     return;
@@ -298,7 +333,7 @@ __global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
   const float* U = ubg + (size_t)pair * maxP;
   float best = -__builtin_huge_valf();
   int bestp = 0x7fffffff;
-  for (int p = threadIdx.x; p < n; p += kSelBlock) {
+  for (int p = threadIdx.x; p < n; p += kMarkBlock) {
     const float u = U[p];
     if (u > best || (u == best && p < bestp)) {
       best = u;
@@ -320,7 +355,7 @@ __global__ __launch_bounds__(kSelBlock) void gauss_mark_kernel(
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < kMarkWaves; ++w)
       if (s_best[w] > best || (s_best[w] == best && s_bestp[w] < bestp)) {
         best = s_best[w];
         bestp = s_bestp[w];
@@ -409,12 +444,12 @@ hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int ga
   if (e != hipSuccess) return e;
   const ExpMaxTable& et = exp_max_table();
   if (est)
-    hipLaunchKernelGGL((gauss_mark_kernel<true>), dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream,
+    hipLaunchKernelGGL((gauss_mark_kernel<true>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0, stream,
                        ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1,
                        (double)delta, et, sel, n_sel);
   else
-    hipLaunchKernelGGL((gauss_mark_kernel<false>), dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream,
-                       ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1,
+    hipLaunchKernelGGL((gauss_mark_kernel<false>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
+                       stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1,
                        (double)delta, et, sel, n_sel);
   return hipGetLastError();
 }
