@@ -9,11 +9,16 @@
 // 53 bits) and one of them is an exact zero, so the fp64 FMA chain only rounds
 // in its additions; the bound is then scaled and rounded once to fp32.
 //
-// Mapping: one (row, KV head) pair per blockIdx.y; kLpr lanes cover one page's
-// d coordinates with kVec coordinates each (16- or 8-byte loads of kmin and
+// Mapping: workgroup i scores page slice i / pairs of (row, KV head) pair
+// i % pairs.  Consecutive workgroups go to the 8 XCDs in turn, so with the
+// pair varying fastest every XCD gets the same share of every slice index
+// (with 8 KV heads, XCD g holds KV head g of every row): rows of different
+// lengths, whose late slices exist only for long rows, cannot pile work onto
+// a few XCDs while the others idle.  kLpr lanes cover one page's d
+// coordinates with kVec coordinates each (16- or 8-byte loads of kmin and
 // kmax), so a wave scores 64/kLpr pages per step for all G query heads of the
-// group; per-head partial sums are reduced over the kLpr lanes with DPP.
-// q+ and q- stay in registers as fp64 for the whole launch.
+// group; the per-head partial sums are finished through LDS.  q+ and q- stay
+// in registers as fp64 for the whole launch.
 #include "blocks.h"
 #include "kernels.h"
 
@@ -55,7 +60,7 @@ template <> struct Unpack<float, 2> {
 
 constexpr int kScoreBlock = 256;
 constexpr int kScoreWaves = kScoreBlock / kWave;
-constexpr int kMaxPagesPerBlock = 2048;  // block-table slice staged in LDS
+constexpr int kMaxPagesPerBlock = 512;  // block-table slice staged in LDS
 constexpr int kStepTopkKeys = 4096;
 // workgroups resident at once (256 CUs x 2 at this kernel's register use):
 // one round of blocks avoids a second ramp-up
@@ -276,17 +281,17 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
     const float* __restrict__ q, float scale, const T* __restrict__ kmin,
     const T* __restrict__ kmax, const float* __restrict__ mean, const float* __restrict__ var,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens, int Hkv, int P, int maxP,
-    int pages_per_block, float* __restrict__ ub, float* __restrict__ ubg,
+    int pages_per_block, int npairs, float* __restrict__ ub, float* __restrict__ ubg,
     double* __restrict__ gm, double* __restrict__ gv) {
   using Geo = ScoreGeo<D, G, kVec, kGauss>;
   __shared__ int s_pi[kMaxPagesPerBlock];
   __shared__ ScoreRedLds<Geo::kPitch> red;
-  const int pair = blockIdx.y;
+  const int pair = (int)(blockIdx.x % (unsigned)npairs);
   const int b = pair / Hkv;
   const int g = pair % Hkv;
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  const int p_begin = blockIdx.x * pages_per_block;
+  const int p_begin = (int)(blockIdx.x / (unsigned)npairs) * pages_per_block;
   if (p_begin >= np) return;
   const int p_end = min(np, p_begin + pages_per_block);
   for (int i = threadIdx.x; i < p_end - p_begin; i += kScoreBlock)
@@ -306,7 +311,8 @@ template <typename T, int D, int G, int kVec, bool kKeysLds>
 __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
     const float* __restrict__ q, float scale, const T* __restrict__ K, T* __restrict__ kmin,
     T* __restrict__ kmax, const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
-    int refresh, int Hkv, int P, int maxP, int pages_per_block, float* __restrict__ ubg,
+    int refresh, int Hkv, int P, int maxP, int pages_per_block, int npairs,
+    float* __restrict__ ubg,
     int top_k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
     int* __restrict__ counters) {
   using Geo = ScoreGeo<D, G, kVec, false>;
@@ -319,12 +325,12 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   __shared__ int s_pi[kMaxPagesPerBlock];
   __shared__ Lds sm;
   __shared__ int s_last;
-  const int pair = blockIdx.y;
+  const int pair = (int)(blockIdx.x % (unsigned)npairs);
   const int b = pair / Hkv;
   const int g = pair % Hkv;
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  const int p_begin = blockIdx.x * pages_per_block;
+  const int p_begin = (int)(blockIdx.x / (unsigned)npairs) * pages_per_block;
   if (p_begin >= np) return;
   const int p_end = min(np, p_begin + pages_per_block);
   for (int i = threadIdx.x; i < p_end - p_begin; i += kScoreBlock)
@@ -384,15 +390,18 @@ hipError_t launch_score_t(const Shape& s, const float* q, float scale, const voi
   // a whole number of iterations
   const long long pairs = (long long)s.B * s.Hkv;
   const int ppb = slice_pages(s, per_iter);
-  dim3 grid((s.maxP + ppb - 1) / ppb, (unsigned)pairs);
+  const long long nblocks = (long long)((s.maxP + ppb - 1) / ppb) * pairs;
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)nblocks);
+  const int npairs = (int)pairs;
   if (gauss) {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0, stream, q,
                        scale, (const T*)kmin, (const T*)kmax, mean, var, bt, lens, s.Hkv, s.P,
-                       s.maxP, ppb, ub, ubg, gm, gv);
+                       s.maxP, ppb, npairs, ub, ubg, gm, gv);
   } else {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, false>), grid, dim3(kScoreBlock), 0, stream,
                        q, scale, (const T*)kmin, (const T*)kmax, mean, var, bt, lens, s.Hkv,
-                       s.P, s.maxP, ppb, ub, ubg, gm, gv);
+                       s.P, s.maxP, ppb, npairs, ub, ubg, gm, gv);
   }
   return hipGetLastError();
 }
@@ -425,15 +434,18 @@ hipError_t launch_score_select_t(const Shape& s, const float* q, float scale, co
   const int per_iter = kPagesPerStep * ScoreGeo<D, G, kVec, false>::kU;
   const long long pairs = (long long)s.B * s.Hkv;
   const int ppb = slice_pages(s, per_iter);
-  dim3 grid((s.maxP + ppb - 1) / ppb, (unsigned)pairs);
+  const long long nblocks = (long long)((s.maxP + ppb - 1) / ppb) * pairs;
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)nblocks);
+  const int npairs = (int)pairs;
   if (s.maxP <= kStepTopkKeys)
     hipLaunchKernelGGL((score_select_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0,
                        stream, q, scale, (const T*)K, (T*)kmin, (T*)kmax, bt, lens, refresh, s.Hkv,
-                       s.P, s.maxP, ppb, ubg, top_k, sel, n_sel, counters);
+                       s.P, s.maxP, ppb, npairs, ubg, top_k, sel, n_sel, counters);
   else
     hipLaunchKernelGGL((score_select_kernel<T, D, G, kVec, false>), grid, dim3(kScoreBlock), 0,
                        stream, q, scale, (const T*)K, (T*)kmin, (T*)kmax, bt, lens, refresh, s.Hkv,
-                       s.P, s.maxP, ppb, ubg, top_k, sel, n_sel, counters);
+                       s.P, s.maxP, ppb, npairs, ubg, top_k, sel, n_sel, counters);
   return hipGetLastError();
 }
 
