@@ -487,21 +487,35 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   const int s = (int)(item % splits);
   const int b = pair / Hkv;
   const int g = pair % Hkv;
+  const int r_begin = s * kR;
+  const int j_begin = r_begin >> log2P;
+  // the selected page indices this split can cover, loaded before the row
+  // length and the selection count are known (same round trip); entries past
+  // the count are in bounds but never used
+  constexpr int kSpec = (kR + kBlock - 1) / kBlock;
+  int spec[kSpec];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int i = threadIdx.x + u * kBlock;
+    spec[u] = 0;
+    if (sel && i < kR && j_begin + i < maxP) spec[u] = sel[(size_t)pair * maxP + j_begin + i];
+  }
   const int L = lens[b];
   const int np = (L + P - 1) / P;
   const int nsel = min(sel ? n_sel[pair] : np, max_sel);
-  const int r_begin = s * kR;
   const int r_end = min(nsel << log2P, r_begin + kR);
   if (r_begin >= r_end) return info;  // uniform over the block
-  const int j_begin = r_begin >> log2P;
-  const int n_pg = ((r_end - 1) >> log2P) - j_begin + 1;
+  const int n_pg = ((r_end - 1) >> log2P) - j_begin + 1;  // <= kR
 
   // page map of this split: physical page and valid tokens per selected page
-  for (int i = threadIdx.x; i < n_pg; i += kBlock) {
-    const int j = j_begin + i;
-    const int page = sel ? sel[(size_t)pair * maxP + j] : j;
-    pg_phys[i] = bt[(size_t)b * maxP + page];
-    pg_valid[i] = page_valid(L, page, P);
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int i = threadIdx.x + u * kBlock;
+    if (i < n_pg) {
+      const int page = sel ? spec[u] : j_begin + i;
+      pg_phys[i] = bt[(size_t)b * maxP + page];
+      pg_valid[i] = page_valid(L, page, P);
+    }
   }
   if constexpr (kMfma) {
     // ---- matrix cores: [16 tokens x d] . [d x (G heads x 3 bf16 parts)] ----

@@ -289,13 +289,15 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
   const int pair = (int)(blockIdx.x % (unsigned)npairs);
   const int b = pair / Hkv;
   const int g = pair % Hkv;
+  const int p_begin = (int)(blockIdx.x / (unsigned)npairs) * pages_per_block;
+  // the block-table slice is read in the same round trip as the row length
+  // (entries past the row's pages are in bounds and never used)
+  for (int i = threadIdx.x; i < pages_per_block && p_begin + i < maxP; i += kScoreBlock)
+    s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  const int p_begin = (int)(blockIdx.x / (unsigned)npairs) * pages_per_block;
   if (p_begin >= np) return;
   const int p_end = min(np, p_begin + pages_per_block);
-  for (int i = threadIdx.x; i < p_end - p_begin; i += kScoreBlock)
-    s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
   __syncthreads();
   score_range<T, D, G, kVec, kGauss>(q, scale, kmin, kmax, mean, var, s_pi, b, g, pair, Hkv, maxP,
                                      p_begin, p_end, ub, ubg, gm, gv,
@@ -328,13 +330,15 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   const int pair = (int)(blockIdx.x % (unsigned)npairs);
   const int b = pair / Hkv;
   const int g = pair % Hkv;
+  const int p_begin = (int)(blockIdx.x / (unsigned)npairs) * pages_per_block;
+  // the block-table slice is read in the same round trip as the row length
+  // (entries past the row's pages are in bounds and never used)
+  for (int i = threadIdx.x; i < pages_per_block && p_begin + i < maxP; i += kScoreBlock)
+    s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  const int p_begin = (int)(blockIdx.x / (unsigned)npairs) * pages_per_block;
   if (p_begin >= np) return;
   const int p_end = min(np, p_begin + pages_per_block);
-  for (int i = threadIdx.x; i < p_end - p_begin; i += kScoreBlock)
-    s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
   if (refresh && p_end == np && threadIdx.x < kWave) {
     // only this workgroup reads the refreshed page's box: the barrier below
     // (which waits for the stores) is enough to publish it
