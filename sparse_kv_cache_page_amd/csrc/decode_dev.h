@@ -500,6 +500,16 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
     spec[u] = 0;
     if (sel && i < kR && j_begin + i < maxP) spec[u] = sel[(size_t)pair * maxP + j_begin + i];
   }
+  // the group's queries (matrix-core path), also requested in that round trip
+  constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
+  float qv[kMfma ? kQPer : 1];
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int idx = threadIdx.x + u * kBlock;
+      qv[u] = idx < G * D ? q[((size_t)b * Hq + g * G) * D + idx] : 0.0f;
+    }
+  }
   const int L = lens[b];
   const int np = (L + P - 1) / P;
   const int nsel = min(sel ? n_sel[pair] : np, max_sel);
@@ -530,9 +540,12 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
     const int mrow = lane % 16;
     const int kq = lane / 16;
     // split q once per workgroup: qparts[h][part][dim] (bf16 bits)
-    for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int idx = threadIdx.x + u * kBlock;
+      if (idx >= G * D) break;
       const int h = idx / D, dd = idx % D;
-      const float x = q[((size_t)b * Hq + g * G + h) * D + dd];
+      const float x = qv[u];
       const float hi = bf16_round(x);
       const float mid = bf16_round(x - hi);
       const float lo = bf16_round(x - hi - mid);
