@@ -198,6 +198,22 @@ __device__ inline int wave_incl_scan_i32(int x) {
 // Sum over the 64 lanes, returned to every lane (wave-uniform): DPP row
 // butterfly, then row_bcast15 / row_bcast31 carry the row sums into the last
 // row, and lane 63 is read back into a scalar register.  No LDS traffic.
+__device__ inline float wave_sum_f32(float x) {
+  x = group_sum_f32<16>(x);
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// Lane `l`'s value of a double, in a scalar register.
+__device__ inline double readlane_f64(double x, int l) {
+  const int2 v = *reinterpret_cast<int2*>(&x);
+  int2 r;
+  r.x = __builtin_amdgcn_readlane(v.x, l);
+  r.y = __builtin_amdgcn_readlane(v.y, l);
+  return *reinterpret_cast<double*>(&r);
+}
+
 __device__ inline double wave_sum_f64(double x) {
   x = group_sum_f64<16>(x);
   const int2 v = *reinterpret_cast<int2*>(&x);

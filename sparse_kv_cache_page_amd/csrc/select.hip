@@ -29,7 +29,7 @@ namespace ekv {
 namespace {
 
 constexpr int kSelBlock = 256;
-constexpr int kGaussLdsPages = 4096;  // 96 KiB of LDS (mu, sigma in fp64 and fp32) per head
+constexpr int kGaussLdsPages = 4096;  // 144 KiB of LDS (mu, sigma, 1/sigma in fp64 and fp32) per head
 constexpr int kTauBlock = 1024;
 constexpr int kTauWaves = kTauBlock / kWave;
 constexpr int kMarkBlock = 1024;
@@ -62,9 +62,10 @@ __global__ __launch_bounds__(kSelBlock) void topk_kernel(
 // --------------------------------------------------------------------------
 // Gaussian-aware selection
 // --------------------------------------------------------------------------
-// I_g(h) and I_{g-1}(h) for Z ~ N(0,1), in the precision of T
+// I_g(h), I_{g-1}(h) and J(h) for Z ~ N(0,1), in the precision of T, where
+// dI_g/dh = g I_{g-1} and J = d^2 I_g / dh^2 = g (g-1) I_{g-2} (phi for g = 1)
 template <int kG, typename T>
-__device__ inline void partial_moments(T h, T& ig, T& igm1) {
+__device__ inline void partial_moments(T h, T& ig, T& igm1, T& jdd) {
   T Phi, phi;
   if constexpr (sizeof(T) == 8) {
     Phi = 0.5 * erfc(-h * 0.70710678118654752440);
@@ -73,16 +74,19 @@ __device__ inline void partial_moments(T h, T& ig, T& igm1) {
     Phi = 0.5f * erfcf(-h * 0.70710678f);
     phi = expf(-0.5f * h * h) * 0.39894228f;
   }
+  T i_pp = phi;               // I_{-1} in the recurrence's sense
   T i_prev = Phi;             // I_0
   T i_cur = fma(h, Phi, phi); // I_1
 #pragma unroll
   for (int k = 2; k <= kG; ++k) {
     const T nxt = fma(h, i_cur, (T)(k - 1) * i_prev);
+    i_pp = i_prev;
     i_prev = i_cur;
     i_cur = nxt;
   }
   ig = i_cur;
   igm1 = i_prev;
+  jdd = kG >= 2 ? (T)(kG * (kG - 1)) * i_pp : phi;
 }
 
 template <int kG, typename T>
@@ -93,47 +97,65 @@ __device__ inline T ipow(T x) {
   return r;
 }
 
-// One page's contribution to F(tau) and -F'(tau) (counted cnt times).
-template <int kG, typename T>
-__device__ inline void gauss_term(T mz, T sd, T tau, T cnt, T& f, T& fd) {
+// One page's contribution to F(tau), -F'(tau) and (kCurv) F''(tau), counted
+// cnt times; rs = 1 / sd.
+template <int kG, bool kCurv, typename T>
+__device__ inline void gauss_term(T mz, T sd, T rs, T tau, T cnt, T& f, T& fd, T& fdd) {
   if (sd > 0) {
-    const T h = (mz - tau) / sd;
-    T ig, igm1;
-    partial_moments<kG>(h, ig, igm1);
+    const T h = (mz - tau) * rs;
+    T ig, igm1, jdd;
+    partial_moments<kG>(h, ig, igm1, jdd);
     const T sg1 = ipow<kG - 1>(sd);
     f = fma(cnt, sg1 * sd * ig, f);
     fd = fma(cnt, (T)kG * sg1 * igm1, fd);
+    if constexpr (kCurv) fdd = fma(cnt, sg1 * rs * jdd, fdd);
   } else {
     const T x = mz - tau;
     if (x > 0) {
       const T xg1 = ipow<kG - 1>(x);
       f = fma(cnt, xg1 * x, f);
       fd = fma(cnt, (T)kG * xg1, fd);
+      if constexpr (kCurv && kG >= 2) fdd = fma(cnt, (T)(kG * (kG - 1)) * ipow<kG - 2>(x), fdd);
     }
   }
 }
 
-// Block-wide sums of (a, b); every thread gets the same two values (same
-// operands, same order).  sh holds 2 x 2 x kTauWaves doubles; successive calls
+// Block-wide sums of (a, b, c), returned to every thread: each wave sums its
+// lanes with DPP, lane 0 stores the wave's three partials, and after one
+// barrier every wave re-reduces them at once, quantity k on lanes 16k..16k+15
+// with a 16-lane DPP butterfly (the same order in every wave, so every thread
+// gets the same values).  sh holds 2 x 3 x kTauWaves values; successive calls
 // alternate halves by `par`, so one barrier per call suffices.
-__device__ inline void block_sum2_f64(double& a, double& b, double* sh, int par) {
-  a = wave_sum_f64(a);
-  b = wave_sum_f64(b);
-  double* buf = sh + par * 2 * kTauWaves;
+static_assert(kTauWaves == 16, "one 16-lane row per summed quantity");
+
+__device__ inline float wave_sum_t(float x) { return wave_sum_f32(x); }
+__device__ inline double wave_sum_t(double x) { return wave_sum_f64(x); }
+__device__ inline float row16_sum_t(float x) { return group_sum_f32<16>(x); }
+__device__ inline double row16_sum_t(double x) { return group_sum_f64<16>(x); }
+__device__ inline float readlane_t(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ inline double readlane_t(double x, int l) { return readlane_f64(x, l); }
+
+template <typename T>
+__device__ inline void block_sum3(T& a, T& b, T& c, T* sh, int par) {
+  a = wave_sum_t(a);
+  b = wave_sum_t(b);
+  c = wave_sum_t(c);
+  T* buf = sh + par * 3 * kTauWaves;
   const int w = threadIdx.x / kWave;
-  if (threadIdx.x % kWave == 0) {
+  const int lane = threadIdx.x % kWave;
+  if (lane == 0) {
     buf[w] = a;
     buf[kTauWaves + w] = b;
+    buf[2 * kTauWaves + w] = c;
   }
   __syncthreads();
-  double sa = 0.0, sb = 0.0;
-#pragma unroll
-  for (int i = 0; i < kTauWaves; ++i) {
-    sa += buf[i];
-    sb += buf[kTauWaves + i];
-  }
-  a = sa;
-  b = sb;
+  T x = lane < 3 * kTauWaves ? buf[lane] : (T)0;
+  x = row16_sum_t(x);
+  a = readlane_t(x, 0);
+  b = readlane_t(x, kTauWaves);
+  c = readlane_t(x, 2 * kTauWaves);
 }
 
 // tau-hat for one (row, query head).  A coarse fp32 run approaches the root;
@@ -149,7 +171,10 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
   __shared__ double s_sd[kLds ? kGaussLdsPages : 1];
   __shared__ float s_mu32[kLds ? kGaussLdsPages : 1];
   __shared__ float s_sd32[kLds ? kGaussLdsPages : 1];
-  __shared__ double red[4 * kTauWaves];
+  __shared__ double s_rs[kLds ? kGaussLdsPages : 1];
+  __shared__ float s_rs32[kLds ? kGaussLdsPages : 1];
+  __shared__ double red[6 * kTauWaves];
+  __shared__ float redf[6 * kTauWaves];
   const int bh = blockIdx.x;
   const int b = bh / Hq;
   const int L = lens[b];
@@ -173,6 +198,15 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     if constexpr (kLds) return s_sd32[p];
     else return (float)(a1 * sqrt(V[p]));
   };
+  auto inv = [](auto x) -> decltype(x) { return x > 0 ? (decltype(x))1 / x : (decltype(x))0; };
+  auto rs_of = [&](int p) -> double {
+    if constexpr (kLds) return s_rs[p];
+    else return inv(a1 * sqrt(V[p]));
+  };
+  auto rs32_of = [&](int p) -> float {
+    if constexpr (kLds) return s_rs32[p];
+    else return inv((float)(a1 * sqrt(V[p])));
+  };
   double zmax = -__builtin_huge_val();
   for (int p = threadIdx.x; p < n; p += kTauBlock) {
     const double mz = a1 * M[p];
@@ -182,6 +216,8 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
       s_sd[p] = sd;
       s_mu32[p] = (float)mz;
       s_sd32[p] = (float)sd;
+      s_rs[p] = inv(sd);
+      s_rs32[p] = inv((float)sd);
     }
     zmax = fmax(zmax, mz);
   }
@@ -192,9 +228,9 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
 #pragma unroll
   for (int i = 0; i < kTauWaves; ++i) zmax = fmax(zmax, red[i]);
   const double safe = zmax - 1.0;  // F(safe) >= 1
-  int par = 1;                     // red[0 .. 2*kTauWaves) is still being read
+  int par = 1;                     // red[0 .. kTauWaves) is still being read
 
-  // Coarse fp32 run: Newton on log F, which is nearly linear where a few
+  // Coarse fp32 run: Newton on g = log F, which is nearly linear where a few
   // Gaussian tails dominate (about half the steps of Newton on F), kept inside
   // the bracket (lo, hi) of points seen with F >= 1 and F < 1; a step leaving
   // it falls back to bisection, or, before any point with F < 1 is seen, to a
@@ -202,17 +238,18 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
   const double huge = __builtin_huge_val();
   double lo = safe, hi = huge, t = safe;
   for (int it = 0; it < 48 && n > 0; ++it) {
-    float f = 0.0f, fd = 0.0f;
+    float f = 0.0f, fd = 0.0f, fdd = 0.0f;  // fdd unused here
     const float tf = (float)t;
     for (int p = threadIdx.x; p < n; p += kTauBlock)
-      gauss_term<kG, float>(mu32_of(p), sd32_of(p), tf, (float)page_valid(L, p, P), f, fd);
-    double fs = f, fds = fd;
-    block_sum2_f64(fs, fds, red, par);
+      gauss_term<kG, false, float>(mu32_of(p), sd32_of(p), rs32_of(p), tf,
+                                   (float)page_valid(L, p, P), f, fd, fdd);
+    block_sum3(f, fd, fdd, redf, par);
     par ^= 1;
+    const double fs = f, fds = fd;
     if (fs >= 1.0) lo = fmax(lo, t);
     else hi = fmin(hi, t);
     const bool ok = fs > 0.0 && fds > 0.0;
-    double nxt = ok ? t + log(fs) * fs / fds : t;
+    double nxt = ok ? t + (double)(logf(f) * f / fd) : t;
     if (ok && fabs(nxt - t) < 1e-6 * (1.0 + fabs(nxt))) {  // converged as far as fp32 goes
       t = nxt;
       break;
@@ -227,15 +264,17 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
 
   // fp64 run: monotone Newton on F from a start just below the coarse root
   // (checked: F(start) >= 1 in fp64, else the proven start max mu - 1).  A step
-  // below 1e-15 |tau| ends it without another evaluation: the next one would
-  // be below rounding.
+  // ends it without another evaluation when the step itself is below
+  // 1e-15 |tau|, or when Newton's error bound after it on the convex F,
+  // F'' / (2 |F'|) step^2 (with a factor 4 to spare), is below 1e-16 |tau|.
   const double start = fmax(safe, t - 4e-6 * (1.0 + fabs(t)));
   double tau = start;
   for (int it = 0; it < 200; ++it) {
-    double f = 0.0, fd = 0.0;
+    double f = 0.0, fd = 0.0, fdd = 0.0;
     for (int p = threadIdx.x; p < n; p += kTauBlock)
-      gauss_term<kG, double>(mu_of(p), sd_of(p), tau, (double)page_valid(L, p, P), f, fd);
-    block_sum2_f64(f, fd, red, par);
+      gauss_term<kG, true, double>(mu_of(p), sd_of(p), rs_of(p), tau, (double)page_valid(L, p, P),
+                                   f, fd, fdd);
+    block_sum3(f, fd, fdd, red, par);
     par ^= 1;
     f -= 1.0;
     if (it == 0 && f < 0.0 && tau > safe) {  // F(start) < 1: start over at the proven point
@@ -247,7 +286,7 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     const double nxt = tau + step;
     if (!(nxt > tau)) break;
     tau = nxt;
-    if (step <= 1e-15 * fabs(tau)) break;
+    if (step <= 1e-15 * fabs(tau) || 2.0 * fdd / fd * step * step <= 1e-16 * fabs(tau)) break;
   }
   if (threadIdx.x == 0) tau_hat[bh] = tau;
 }
