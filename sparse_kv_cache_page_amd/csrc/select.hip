@@ -306,6 +306,7 @@ __device__ int compact_ascending(int n, Flag flag, int32_t* out, uint8_t* s_flag
   int total = 0;
   for (int c0 = 0; c0 < n; c0 += kMarkChunk) {
     const int m = min(kMarkChunk, n - c0);
+#pragma unroll 4
     for (int i = threadIdx.x; i < m; i += kMarkBlock) s_flag[i] = flag(c0 + i) ? 1 : 0;
     __syncthreads();
     const int per = (m + kMarkBlock - 1) / kMarkBlock;
@@ -325,11 +326,11 @@ __device__ int compact_ascending(int n, Flag flag, int32_t* out, uint8_t* s_flag
   return total;
 }
 
-template <bool kEst>
+template <bool kEst, int G>
 __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
     const float* __restrict__ ub, const float* __restrict__ ubg, const double* __restrict__ gm,
     const double* __restrict__ gv, const double* __restrict__ tau_hat,
-    const int32_t* __restrict__ lens, int P, int maxP, int Hkv, int G, double a1, double delta,
+    const int32_t* __restrict__ lens, int P, int maxP, int Hkv, double a1, double delta,
     ExpMaxTable et, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
   __shared__ uint8_t s_flag[kMarkChunk];
   __shared__ int scan_sh[kMarkWaves + 1];
@@ -349,6 +350,7 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
   const double e_last = et.e[page_valid(L, n - 1, P)];
   auto keep = [&](int p) -> bool {
     bool any = false;
+#pragma unroll
     for (int h = 0; h < G; ++h) {
       const size_t i = head0 + (size_t)h * maxP + p;
       double est;
@@ -450,6 +452,21 @@ const ExpMaxTable& exp_max_table() {
   return table;
 }
 
+template <int G>
+void launch_mark(const Shape& s, bool est, const float* ub, const float* ubg, const double* gm,
+                 const double* gv, const double* tau_hat, const int32_t* lens, double a1,
+                 double delta, const ExpMaxTable& et, int32_t* sel, int32_t* n_sel,
+                 hipStream_t stream) {
+  if (est)
+    hipLaunchKernelGGL((gauss_mark_kernel<true, G>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
+                       stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, a1, delta, et,
+                       sel, n_sel);
+  else
+    hipLaunchKernelGGL((gauss_mark_kernel<false, G>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
+                       stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, a1, delta, et,
+                       sel, n_sel);
+}
+
 }  // namespace
 
 double expected_max_std_normal(int n) {
@@ -482,14 +499,13 @@ hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int ga
   }
   if (e != hipSuccess) return e;
   const ExpMaxTable& et = exp_max_table();
-  if (est)
-    hipLaunchKernelGGL((gauss_mark_kernel<true>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0, stream,
-                       ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1,
-                       (double)delta, et, sel, n_sel);
-  else
-    hipLaunchKernelGGL((gauss_mark_kernel<false>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
-                       stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, s.G, a1,
-                       (double)delta, et, sel, n_sel);
+  switch (s.G) {
+    case 1: launch_mark<1>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 2: launch_mark<2>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 4: launch_mark<4>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 8: launch_mark<8>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
