@@ -160,6 +160,21 @@ def test_gauss_est_guard_keeps_argmax():
         assert int(gpu["n_sel"][b, g]) == 1 and int(gpu["sel"][b, g, 0]) == 0
 
 
+@pytest.mark.parametrize("policy,alpha", [("gauss", 2.0), ("gauss_est", 1.5)])
+def test_gauss_long_rows(policy, alpha):
+    # pages of 2 tokens, rows of 4500-6000 pages: the tau-hat kernel's variant
+    # that reads the moments from global memory (> 4096 pages) and the marking
+    # kernel's compaction over several 4096-page chunks
+    w = small(161, page_size=2, lens_range=(9000, 12000), num_q_heads=4, num_kv_heads=2,
+              head_dim=64, q_std=2.0 / 8.0, alpha=alpha, policy=policy, clusters=16,
+              planted_per_kv_head=0, delta=0.1, batch=2)
+    inp = wl.make_inputs(w, device=DEV)
+    assert min(inp["npages"]) > 4096
+    gpu = run_gpu(inp, policy)
+    for b, g in [(0, 0), (1, 1)]:
+        check_pair(inp, gpu, b, g, policy)
+
+
 def test_edge_single_token_rows():
     w = small(91, lens_range=None, seq_len=1, batch=2, top_k=3)
     inp = wl.make_inputs(w, device=DEV)
