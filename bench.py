@@ -155,24 +155,52 @@ def stage_bytes(layer):
     else:
         n_sel = dec.n_sel.cpu().long()
     select = pages * 4 + int(n_sel.sum()) * 4
-    # selected valid tokens: every selected page is full except possibly the last
-    ktok = 0
+    # K rows the decode reads: the valid tokens of every selected page it does
+    # not prune (every page is full except a row's last)
+    read = page_read_mask(layer)  # [B][Hkv][maxP] over selection slots, or None
     sel = None if w.policy == "dense" else dec.sel.cpu()
+    ktok = 0
     for b in range(w.batch):
         for g in range(Hkv):
             ns = int(n_sel[b, g])
-            ktok += ns * P
-            last_sel = (ns - 1) if sel is None else int(sel[b, g, ns - 1])
-            if last_sel == npg[b] - 1:
-                ktok -= P - last_valid[b]
+            for j in range(ns):
+                if read is not None and not read[b, g, j]:
+                    continue
+                page = j if sel is None else int(sel[b, g, j])
+                ktok += last_valid[b] if page == npg[b] - 1 else P
     vrows = int(dec.n_support.cpu().long().sum())
     decode = ktok * d * e + vrows * d * e
+    if read is not None:
+        # the probe's page per query head, and the bounds of the selected pages
+        decode += w.batch * w.num_q_heads * P * d * e + int(n_sel.sum()) * w.group * 4
     full = sum(lens) * Hkv * d * e * 2
     return dict(refresh=refresh, score=score if w.policy != "dense" else 0,
                 select=select if w.policy != "dense" else 0, decode=decode,
                 score_select=score + select,
                 kv_bytes=(pages * meta_pp if w.policy != "dense" else 0) + decode,
                 full_cache=full, k_tokens=ktok, v_rows=vrows)
+
+
+def page_read_mask(layer):
+    """Which selection slots the pruned decode reads (its rule, replayed in fp32)."""
+    import torch
+    w, dec = layer.w, layer.dec
+    if not getattr(dec, "prune", False) or dec.zlb is None:
+        return None
+    B_, Hkv, G = w.batch, w.num_kv_heads, w.group
+    mp = dec.ub.shape[-1]
+    a1 = torch.tensor(w.alpha - 1.0, dtype=torch.float32)
+    ub = dec.ub.cpu().view(B_, Hkv, G, mp)
+    zlb = dec.zlb.cpu().view(B_, Hkv, G, 1)
+    if w.policy == "dense":
+        idx = torch.arange(mp).view(1, 1, 1, mp).expand(B_, Hkv, G, mp)
+    else:
+        idx = dec.sel.cpu().long().clamp(0, mp - 1).view(B_, Hkv, 1, mp).expand(B_, Hkv, G, mp)
+    x = a1 * torch.gather(ub, 3, idx)
+    s1 = 1e-3 * (1.0 + x.abs())
+    s2 = 1e-4 * (1.0 + zlb.abs())
+    below = (x + s1 < zlb - 1.0 - s2).all(dim=2)
+    return (~below).numpy()
 
 
 def time_steps(layers, steps, warmup, graph):

@@ -177,6 +177,18 @@ ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
  * max_sel: host upper bound on every n_sel[b][g] (<= max_pages_per_seq; <= 0
  *   means max_pages_per_seq).  It sizes the launch and the workspace; a row
  *   whose n_sel exceeds it gets NaN outputs.
+ * ub / zlb (both NULL, or both set): page pruning.  ub [B][Hq][maxP] fp32 holds
+ *   per-head page bounds as written by ekv_score_pages or
+ *   ekv_score_select_pages (u[b][h][p] >= scale * <q[b][h], k> for every valid
+ *   key k of page p).  A first launch writes zlb[b][h] (fp32, [B][Hq]): the
+ *   largest z over the valid tokens of the selected page with the largest
+ *   ub[b][h] (a lower bound of z_max over the selected tokens; -inf if none).
+ *   The keys of a selected page are then not read when, for every head h of
+ *   its group, (alpha-1) u[b][h][p] plus a rounding slack is below
+ *   zlb[b][h] - 1 minus a rounding slack: since tau >= z_max - 1 (the largest
+ *   weight is at most 1), none of its tokens can carry weight, so tau, out
+ *   and n_support are those of the unpruned call (§2.C, §3: only support
+ *   tokens matter).  How many pages this skips depends on the data.
  * ws / ws_bytes: device scratch of at least ekv_decode_workspace_bytes(desc,
  *   max_sel) bytes, 256-byte aligned; its contents need no initialisation
  *   and are garbage afterwards.  alpha > 1 and finite; scale > 0.
@@ -185,8 +197,9 @@ ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float s
                              float alpha, const void* K, const void* V,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
-                             float* out, float* tau_out, int32_t* n_support, void* ws,
-                             size_t ws_bytes, hipStream_t stream);
+                             const float* ub, float* zlb, float* out, float* tau_out,
+                             int32_t* n_support, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /*
  * ekv_entmax_decode in one launch: the same arguments and results (up to
@@ -207,8 +220,9 @@ ekv_status ekv_entmax_decode_fused(const ekv_cache_desc* desc, const float* q, f
                                    float alpha, const void* K, const void* V,
                                    const int32_t* block_table, const int32_t* seq_lens,
                                    const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
-                                   float* out, float* tau_out, int32_t* n_support, void* ws,
-                                   size_t ws_bytes, hipStream_t stream);
+                                   const float* ub, float* zlb, float* out, float* tau_out,
+                                   int32_t* n_support, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* Scratch bytes ekv_entmax_decode_fused needs (0 if desc is invalid). */
 size_t ekv_decode_fused_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);
@@ -218,8 +232,8 @@ size_t ekv_decode_fused_workspace_bytes(const ekv_cache_desc* desc, int32_t max_
  * the same results as
  *   ekv_build_page_meta(first_page = last page of each row, span = 1,
  *                       mean = var = NULL)          [only if refresh_last_page]
- *   ekv_score_pages(ub = NULL, gm = gv = NULL)  ->  ekv_select_pages(TOPK, top_k)
- * in one launch: each workgroup scores a slice of one (row, KV head)'s pages
+ *   ekv_score_pages(ub, gm = gv = NULL)  ->  ekv_select_pages(TOPK, top_k)
+ * in one launch (ub may be NULL: then the per-head bounds are not written): each workgroup scores a slice of one (row, KV head)'s pages
  * (the one holding the row's last page first rebuilds that page's bounding
  * box), and the last workgroup to finish a (row, KV head) runs its top-k over
  * the bounds it finds in L2.  kmin/kmax are read (and, for the refreshed page,
@@ -235,9 +249,9 @@ size_t ekv_decode_fused_workspace_bytes(const ekv_cache_desc* desc, int32_t max_
 ekv_status ekv_score_select_pages(const ekv_cache_desc* desc, const float* q, float scale,
                                   const void* K, const int32_t* block_table,
                                   const int32_t* seq_lens, int32_t refresh_last_page,
-                                  int32_t top_k, void* kmin, void* kmax, float* ubg,
-                                  int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
-                                  hipStream_t stream);
+                                  int32_t top_k, void* kmin, void* kmax, float* ub,
+                                  float* ubg, int32_t* sel, int32_t* n_sel, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* Counter bytes ekv_score_select_pages needs (0 if desc is invalid). */
 size_t ekv_score_select_workspace_bytes(const ekv_cache_desc* desc);
@@ -245,10 +259,11 @@ size_t ekv_score_select_workspace_bytes(const ekv_cache_desc* desc);
 /*
  * One whole decode step with the top-k policy (the pipeline of §2: scoring
  * from page metadata, candidate selection, sparse entmax over the selected
- * pages): ekv_score_select_pages followed by ekv_entmax_decode(sel, n_sel,
- * max_sel = min(top_k, max_pages_per_seq)), sharing one workspace of
- * ekv_step_workspace_bytes(desc, top_k) bytes (zero-filled before first use,
- * reusable afterwards, as for ekv_score_select_pages).
+ * pages): ekv_score_select_pages (per-head bounds written to the workspace)
+ * followed by ekv_entmax_decode(sel, n_sel, max_sel = min(top_k,
+ * max_pages_per_seq)) with page pruning on those bounds, sharing one
+ * workspace of ekv_step_workspace_bytes(desc, top_k) bytes (zero-filled
+ * before first use, reusable afterwards, as for ekv_score_select_pages).
  */
 ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
                            const void* K, const void* V, const int32_t* block_table,

@@ -76,17 +76,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_score_pages.argtypes = [dp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ekv_select_pages.argtypes = [dp, vp, i32, i32, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ekv_entmax_decode.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
-                                      vp, sz, vp]
+                                      vp, vp, vp, sz, vp]
     lib.ekv_decode_step.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp, sz, vp]
     lib.ekv_score_select_pages.argtypes = [dp, vp, f32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
-                                           vp, sz, vp]
+                                           vp, vp, sz, vp]
     lib.ekv_score_select_workspace_bytes.argtypes = [dp]
     lib.ekv_score_select_workspace_bytes.restype = sz
     lib.ekv_step_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_step_workspace_bytes.restype = sz
     lib.ekv_entmax_decode_fused.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, vp, vp, i32, vp,
-                                            vp, vp, vp, sz, vp]
+                                            vp, vp, vp, vp, vp, sz, vp]
     lib.ekv_decode_fused_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_decode_fused_workspace_bytes.restype = sz
     lib.ekv_decode_workspace_bytes.argtypes = [dp, i32]
@@ -243,10 +243,12 @@ def decode_fused_workspace_bytes(s: CacheShape, max_sel: int = 0) -> int:
 
 def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_table, seq_lens,
                   out, ws, sel=None, n_sel=None, max_sel: int = 0, tau=None, n_support=None,
-                  fused: bool = False):
+                  fused: bool = False, ub=None, zlb=None):
     """ekv_entmax_decode (or, with fused=True, ekv_entmax_decode_fused, whose
     workspace must be zero-filled before first use): alpha-entmax attention
-    over the selected pages (all if sel is None)."""
+    over the selected pages (all if sel is None).  With ub (per-head page
+    bounds [B, Hq, maxP]) and zlb ([B, Hq], written), selected pages that
+    cannot hold any head's support are not read."""
     B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
     _need(q, "q", torch.float32, (B, Hq, d))
     _need(K, "K", s.kv_dtype, _kv_shape(s))
@@ -261,6 +263,9 @@ def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_tabl
         _need(tau, "tau", torch.float32, (B, Hq))
     if n_support is not None:
         _need(n_support, "n_support", torch.int32, (B, Hq))
+    if ub is not None or zlb is not None:
+        _need(ub, "ub", torch.float32, (B, Hq, mp))
+        _need(zlb, "zlb", torch.float32, (B, Hq))
     if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.dtype == torch.uint8
             and ws.is_contiguous()):
         raise TypeError("ws must be a contiguous uint8 GPU tensor")
@@ -268,8 +273,9 @@ def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_tabl
     name = "ekv_entmax_decode_fused" if fused else "ekv_entmax_decode"
     _check(name, getattr(load_library(), name)(
         ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
-        _ptr(block_table), _ptr(seq_lens), _ptr(sel), _ptr(n_sel), int(max_sel), _ptr(out),
-        _ptr(tau), _ptr(n_support), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+        _ptr(block_table), _ptr(seq_lens), _ptr(sel), _ptr(n_sel), int(max_sel), _ptr(ub),
+        _ptr(zlb), _ptr(out), _ptr(tau), _ptr(n_support), _ptr(ws),
+        ctypes.c_size_t(ws.numel()), _stream()))
 
 
 def step_workspace_bytes(s: CacheShape, top_k: int) -> int:
@@ -319,8 +325,9 @@ def score_select_workspace_bytes(s: CacheShape) -> int:
 
 
 def score_select_pages(s: CacheShape, q, scale: float, K, block_table, seq_lens, top_k: int,
-                       kmin, kmax, ubg, sel, n_sel, ws, refresh_last_page: bool = False):
-    """ekv_score_select_pages: [last-page refresh] + scores + top-k in one launch.
+                       kmin, kmax, ubg, sel, n_sel, ws, refresh_last_page: bool = False, ub=None):
+    """ekv_score_select_pages: [last-page refresh] + scores + top-k in one launch
+    (per-head bounds also written to ub [B, Hq, maxP] when given).
 
     `ws`: uint8 GPU tensor of score_select_workspace_bytes() bytes, zero-filled
     before first use (torch.zeros); every call leaves it reusable.
@@ -340,7 +347,9 @@ def score_select_pages(s: CacheShape, q, scale: float, K, block_table, seq_lens,
             and ws.is_contiguous()):
         raise TypeError("ws must be a contiguous uint8 GPU tensor")
     d_ = s.desc()
+    if ub is not None:
+        _need(ub, "ub", torch.float32, (B, Hq, mp))
     _check("ekv_score_select_pages", load_library().ekv_score_select_pages(
         ctypes.byref(d_), _ptr(q), float(scale), _ptr(K), _ptr(block_table), _ptr(seq_lens),
-        int(bool(refresh_last_page)), int(top_k), _ptr(kmin), _ptr(kmax), _ptr(ubg), _ptr(sel),
-        _ptr(n_sel), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+        int(bool(refresh_last_page)), int(top_k), _ptr(kmin), _ptr(kmax), _ptr(ub), _ptr(ubg),
+        _ptr(sel), _ptr(n_sel), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))

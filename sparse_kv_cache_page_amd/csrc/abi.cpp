@@ -156,11 +156,14 @@ static ekv_status decode_common(const ekv_cache_desc* desc, const float* q, floa
                                 float alpha, const void* K, const void* V,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
-                                float* out, float* tau_out, int32_t* n_support, void* ws,
-                                size_t ws_bytes, bool fused, hipStream_t stream) {
+                                const float* ub, float* zlb, float* out, float* tau_out,
+                                int32_t* n_support, void* ws, size_t ws_bytes, bool fused,
+                                hipStream_t stream) {
   Shape s;
   ekv_status st = make_shape(desc, &s);
   if (st != EKV_OK) return st;
+  if ((ub == nullptr) != (zlb == nullptr)) return EKV_ERR_INVALID_ARG;
+  if (ub != nullptr && (!aligned(ub, 4) || !aligned(zlb, 4))) return EKV_ERR_INVALID_ARG;
   if (!ok_vec(q) || !ok_vec(K) || !ok_vec(V) || !ok_i32(block_table) || !ok_i32(seq_lens) ||
       !ok_vec(out))
     return EKV_ERR_INVALID_ARG;
@@ -175,7 +178,7 @@ static ekv_status decode_common(const ekv_cache_desc* desc, const float* q, floa
   const ekv::DecodePlan plan = ekv::make_decode_plan(s, max_sel, fused);
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < plan.total) return EKV_ERR_WORKSPACE;
   return from_hip(ekv::launch_decode(s, plan, q, scale, alpha, K, V, block_table, seq_lens, sel,
-                                     n_sel, out, tau_out, n_support, ws, fused, stream));
+                                     n_sel, ub, zlb, out, tau_out, n_support, ws, fused, stream));
 }
 
 extern "C" {
@@ -184,20 +187,22 @@ ekv_status ekv_entmax_decode(const ekv_cache_desc* desc, const float* q, float s
                              float alpha, const void* K, const void* V,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
-                             float* out, float* tau_out, int32_t* n_support, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+                             const float* ub, float* zlb, float* out, float* tau_out,
+                             int32_t* n_support, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   return decode_common(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel, max_sel,
-                       out, tau_out, n_support, ws, ws_bytes, false, stream);
+                       ub, zlb, out, tau_out, n_support, ws, ws_bytes, false, stream);
 }
 
 ekv_status ekv_entmax_decode_fused(const ekv_cache_desc* desc, const float* q, float scale,
                                    float alpha, const void* K, const void* V,
                                    const int32_t* block_table, const int32_t* seq_lens,
                                    const int32_t* sel, const int32_t* n_sel, int32_t max_sel,
-                                   float* out, float* tau_out, int32_t* n_support, void* ws,
-                                   size_t ws_bytes, hipStream_t stream) {
+                                   const float* ub, float* zlb, float* out, float* tau_out,
+                                   int32_t* n_support, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
   return decode_common(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel, max_sel,
-                       out, tau_out, n_support, ws, ws_bytes, true, stream);
+                       ub, zlb, out, tau_out, n_support, ws, ws_bytes, true, stream);
 }
 
 // Arrival counters of the fused score + select launch: B*Hkv ints, zero
@@ -215,22 +220,32 @@ size_t ekv_score_select_workspace_bytes(const ekv_cache_desc* desc) {
 ekv_status ekv_score_select_pages(const ekv_cache_desc* desc, const float* q, float scale,
                                   const void* K, const int32_t* block_table,
                                   const int32_t* seq_lens, int32_t refresh_last_page,
-                                  int32_t top_k, void* kmin, void* kmax, float* ubg,
-                                  int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+                                  int32_t top_k, void* kmin, void* kmax, float* ub,
+                                  float* ubg, int32_t* sel, int32_t* n_sel, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
   Shape s;
   ekv_status st = make_shape(desc, &s);
   if (st != EKV_OK) return st;
   if (!ok_vec(q) || !ok_vec(K) || !ok_i32(block_table) || !ok_i32(seq_lens) || !ok_vec(kmin) ||
       !ok_vec(kmax) || !ok_i32(ubg) || !ok_i32(sel) || !ok_i32(n_sel))
     return EKV_ERR_INVALID_ARG;
+  if (ub != nullptr && !aligned(ub, 4)) return EKV_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
   if (top_k < 1) return EKV_ERR_INVALID_ARG;
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < step_counter_bytes(s))
     return EKV_ERR_WORKSPACE;
   return from_hip(ekv::launch_score_select(s, q, scale, K, kmin, kmax, block_table, seq_lens,
-                                           refresh_last_page ? 1 : 0, ubg, top_k, sel, n_sel,
-                                           (int*)ws, stream));
+                                           refresh_last_page ? 1 : 0, ub, ubg, top_k, sel,
+                                           n_sel, (int*)ws, stream));
+}
+
+// Per-head page bounds [B][Hq][maxP] and z_max lower bounds [B][Hq] (fp32) of
+// the decode step's page pruning, after its arrival counters.
+static size_t step_bound_bytes(const Shape& s) {
+  return (((size_t)s.B * s.Hq * s.maxP * sizeof(float)) + 255) & ~(size_t)255;
+}
+static size_t step_zlb_bytes(const Shape& s) {
+  return (((size_t)s.B * s.Hq * sizeof(float)) + 255) & ~(size_t)255;
 }
 
 size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k) {
@@ -238,7 +253,8 @@ size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k) {
   if (make_shape(desc, &s) != EKV_OK || top_k < 1) return 0;
   const int max_sel = top_k < s.maxP ? top_k : s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return 0;
-  return step_counter_bytes(s) + ekv::make_decode_plan(s, max_sel, false).total;
+  return step_counter_bytes(s) + step_bound_bytes(s) + step_zlb_bytes(s) +
+         ekv::make_decode_plan(s, max_sel, false).total;
 }
 
 ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
@@ -258,13 +274,19 @@ ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float sca
   const int max_sel = top_k < s.maxP ? top_k : s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
   const size_t cbytes = step_counter_bytes(s);
+  const size_t ubytes = step_bound_bytes(s);
+  const size_t zbytes = step_zlb_bytes(s);
   const size_t dbytes = ekv::make_decode_plan(s, max_sel, false).total;
-  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < cbytes + dbytes) return EKV_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < cbytes + ubytes + zbytes + dbytes)
+    return EKV_ERR_WORKSPACE;
+  float* ub = (float*)((char*)ws + cbytes);
+  float* zlb = (float*)((char*)ws + cbytes + ubytes);
   st = ekv_score_select_pages(desc, q, scale, K, block_table, seq_lens, refresh_last_page, top_k,
-                              kmin, kmax, ubg, sel, n_sel, ws, cbytes, stream);
+                              kmin, kmax, ub, ubg, sel, n_sel, ws, cbytes, stream);
   if (st != EKV_OK) return st;
   return ekv_entmax_decode(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel,
-                           max_sel, out, tau_out, n_support, (char*)ws + cbytes, dbytes, stream);
+                           max_sel, ub, zlb, out, tau_out, n_support,
+                           (char*)ws + cbytes + ubytes + zbytes, dbytes, stream);
 }
 
 }  // extern "C"

@@ -71,6 +71,11 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QkArgs<T> a, long long n_ite
 }
 
 template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void zlb_kernel(ZlbArgs<T> a) {
+  zlb_head<T, D>(a, blockIdx.x);
+}
+
+template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void tau_pv_kernel(TauArgs<T> a) {
   __shared__ TauLds<T, D> sm;
   tau_head<T, D>(a, blockIdx.x, sm);
@@ -78,16 +83,18 @@ __global__ __launch_bounds__(kBlock) void tau_pv_kernel(TauArgs<T> a) {
 
 template <typename T, int D, int G, bool kFused>
 hipError_t launch_qk_t(const Shape& s, const DecodePlan& pl, const float* q, float zscale,
-                       const void* K, const int32_t* bt, const int32_t* lens, const int32_t* sel,
-                       const int32_t* n_sel, float2* cand, int* cnt, float* smax,
+                       float a1, const void* K, const int32_t* bt, const int32_t* lens,
+                       const int32_t* sel, const int32_t* n_sel, const float* ub,
+                       const float* zlb, float2* cand, int* cnt, float* smax,
                        const TailArgs<T>& ta, hipStream_t stream) {
   const long long items = (long long)s.B * s.Hkv * pl.splits;
   // the fused variant keeps its tail's registers: 2 resident blocks per CU,
   // so one round of persistent blocks; the plain variant fits 4 per CU
   const long long cap = kFused ? 256LL * 2 : pl.qk_grid_cap;
   const long long grid = items < cap ? items : cap;
-  const QkArgs<T> a{q, zscale, (const T*)K, bt, lens, sel, n_sel, pl.max_sel, s.Hkv, s.P,
-                    s.log2P, s.maxP, pl.splits, cand, cnt, smax};
+  const QkArgs<T> a{q,      zscale,  (const T*)K, bt,       lens,      sel,  n_sel,
+                    pl.max_sel, s.Hkv, s.P,    s.log2P,  s.maxP,    pl.splits,
+                    cand,   cnt,     smax,        ub,       zlb,       a1};
   hipLaunchKernelGGL((qk_kernel<T, D, G, kFused>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
                      a, items, ta);
   return hipGetLastError();
@@ -97,8 +104,8 @@ template <typename T, int D>
 hipError_t launch_decode_t(const Shape& s, const DecodePlan& pl, const float* q, float scale,
                            float alpha, const void* K, const void* V, const int32_t* bt,
                            const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
-                           float* out, float* tau_out, int32_t* n_support, void* ws,
-                           bool fused, hipStream_t stream) {
+                           const float* ub, float* zlb, float* out, float* tau_out,
+                           int32_t* n_support, void* ws, bool fused, hipStream_t stream) {
   float2* cand = (float2*)((char*)ws + pl.cand_off);
   int* cnt = (int*)((char*)ws + pl.cnt_off);
   float* smax = (float*)((char*)ws + pl.smax_off);
@@ -109,21 +116,29 @@ hipError_t launch_decode_t(const Shape& s, const DecodePlan& pl, const float* q,
   const int gamma_int = (gr >= 1.0 && gr <= 64.0 && fabs(gamma - gr) <= 1e-12 * gr) ? (int)gr : 0;
   TailArgs<T> ta{(const T*)V, fused ? (int*)((char*)ws + pl.counter_off) : nullptr, (double)alpha,
                  gamma_int ? gr : gamma, gamma_int, out, tau_out, n_support};
+  if (ub != nullptr) {
+    // page pruning: per-head lower bounds of z_max, read by the qk stage
+    const ZlbArgs<T> za{q, zscale, (const T*)K, bt, lens, sel, n_sel, pl.max_sel, s.Hq, s.Hkv,
+                        s.P, s.maxP, ub, zlb};
+    hipLaunchKernelGGL((zlb_kernel<T, D>), dim3(s.B * s.Hq), dim3(kBlock), 0, stream, za);
+    const hipError_t pe = hipGetLastError();
+    if (pe != hipSuccess) return pe;
+  }
   hipError_t e = hipErrorInvalidValue;
   if (fused) {
     switch (s.G) {
-      case 1: e = launch_qk_t<T, D, 1, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
-      case 2: e = launch_qk_t<T, D, 2, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
-      case 4: e = launch_qk_t<T, D, 4, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
-      case 8: e = launch_qk_t<T, D, 8, true>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+      case 1: e = launch_qk_t<T, D, 1, true>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
+      case 2: e = launch_qk_t<T, D, 2, true>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
+      case 4: e = launch_qk_t<T, D, 4, true>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
+      case 8: e = launch_qk_t<T, D, 8, true>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
     }
     return e;
   }
   switch (s.G) {
-    case 1: e = launch_qk_t<T, D, 1, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
-    case 2: e = launch_qk_t<T, D, 2, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
-    case 4: e = launch_qk_t<T, D, 4, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
-    case 8: e = launch_qk_t<T, D, 8, false>(s, pl, q, zscale, K, bt, lens, sel, n_sel, cand, cnt, smax, ta, stream); break;
+    case 1: e = launch_qk_t<T, D, 1, false>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
+    case 2: e = launch_qk_t<T, D, 2, false>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
+    case 4: e = launch_qk_t<T, D, 4, false>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
+    case 8: e = launch_qk_t<T, D, 8, false>(s, pl, q, zscale, (float)a1, K, bt, lens, sel, n_sel, ub, zlb, cand, cnt, smax, ta, stream); break;
   }
   if (e != hipSuccess) return e;
   const TauArgs<T> ta2{cand, cnt, smax, pl.splits, (const T*)V, lens, n_sel, sel != nullptr,
@@ -171,16 +186,16 @@ DecodePlan make_decode_plan(const Shape& s, int max_sel, bool fused) {
 hipError_t launch_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,
                          float alpha, const void* K, const void* V, const int32_t* bt,
                          const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
-                         float* out, float* tau_out, int32_t* n_support, void* ws, bool fused,
-                         hipStream_t stream) {
+                         const float* ub, float* zlb, float* out, float* tau_out,
+                         int32_t* n_support, void* ws, bool fused, hipStream_t stream) {
   if (s.bf16) {
     if (s.D == 128)
-      return launch_decode_t<bf16_t, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
-    return launch_decode_t<bf16_t, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
+      return launch_decode_t<bf16_t, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, ub, zlb, out, tau_out, n_support, ws, fused, stream);
+    return launch_decode_t<bf16_t, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, ub, zlb, out, tau_out, n_support, ws, fused, stream);
   }
   if (s.D == 128)
-    return launch_decode_t<float, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
-  return launch_decode_t<float, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, out, tau_out, n_support, ws, fused, stream);
+    return launch_decode_t<float, 128>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, ub, zlb, out, tau_out, n_support, ws, fused, stream);
+  return launch_decode_t<float, 64>(s, plan, q, scale, alpha, K, V, bt, lens, sel, n_sel, ub, zlb, out, tau_out, n_support, ws, fused, stream);
 }
 
 }  // namespace ekv

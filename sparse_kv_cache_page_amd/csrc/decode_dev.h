@@ -429,7 +429,24 @@ struct QkArgs {
   float2* cand;
   int* cnt;
   float* smax;
+  // page pruning (both set, or both NULL): per-head page bounds and per-head
+  // lower bounds of z_max over the selected tokens
+  const float* ub;
+  const float* zlb;
+  float a1;  // alpha - 1
 };
+
+// A selected page whose tokens cannot reach z_max - 1 for any head of the
+// group carries no weight (tau >= z_max - 1): its keys need not be read.  The
+// test uses z <= (alpha-1) u (the page's box bound) and z_max >= zlb, with
+// slack for the fp32 rounding of u and of the key scores (s1) and of zlb
+// against the scores the qk stage computes (s2), so a pruned token would have
+// been below every head's z_max - 1 in the unpruned computation too.
+__device__ inline bool page_below_support(float a1u, float zlb) {
+  const float s1 = 1e-3f * (1.0f + fabsf(a1u));
+  const float s2 = 1e-4f * (1.0f + fabsf(zlb));
+  return a1u + s1 < zlb - 1.0f - s2;
+}
 
 template <typename T, int D, int G, bool kMfma = std::is_same<T, bf16_t>::value>
 struct QkLds {
@@ -518,13 +535,27 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   const int n_pg = ((r_end - 1) >> log2P) - j_begin + 1;  // <= kR
 
   // page map of this split: physical page and valid tokens per selected page
+  // (0 for a page below every head's support, which is then not read)
+  float zlb_h[G];
+  if (a.ub) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) zlb_h[h] = a.zlb[(size_t)b * Hq + g * G + h];
+  }
 #pragma unroll
   for (int u = 0; u < kSpec; ++u) {
     const int i = threadIdx.x + u * kBlock;
     if (i < n_pg) {
       const int page = sel ? spec[u] : j_begin + i;
       pg_phys[i] = bt[(size_t)b * maxP + page];
-      pg_valid[i] = page_valid(L, page, P);
+      bool needed = true;
+      if (a.ub) {
+        needed = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          needed |= !page_below_support(a.a1 * a.ub[((size_t)b * Hq + g * G + h) * maxP + page],
+                                        zlb_h[h]);
+      }
+      pg_valid[i] = needed ? page_valid(L, page, P) : 0;
     }
   }
   if constexpr (kMfma) {
@@ -698,6 +729,108 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   }
   info = QkItemInfo{true, pair, b, g, L, np, nsel};
   return info;
+}
+
+// Arguments of the page-pruning probe (one (row, query head) each).
+template <typename T>
+struct ZlbArgs {
+  const float* q;
+  float zscale;
+  const T* K;
+  const int32_t* bt;
+  const int32_t* lens;
+  const int32_t* sel;
+  const int32_t* n_sel;
+  int max_sel, Hq, Hkv, P, maxP;
+  const float* ub;
+  float* zlb;
+};
+
+// Lower bound of z_max over a (row, query head)'s selected tokens: the largest
+// score among the valid tokens of the selected page with the largest bound
+// for that head (lowest page on ties), in fp32 with kLpr lanes per key row.
+// -inf when nothing is selected.
+template <typename T, int D>
+__device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
+  constexpr int kVec = Elem<T>::kVec;
+  constexpr int kLpr = D / kVec;
+  constexpr int kRowsPerPass = kBlock / kLpr;
+  constexpr int kWaves = kBlock / kWave;
+  __shared__ float s_best[kWaves];
+  __shared__ int s_bestp[kWaves];
+  __shared__ float s_z[kWaves];
+  const int G = a.Hq / a.Hkv;
+  const int b = bh / a.Hq;
+  const int g = (bh % a.Hq) / G;
+  const int pair = b * a.Hkv + g;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int L = a.lens[b];
+  const int np = (L + a.P - 1) / a.P;
+  const int nsel = min(a.sel ? a.n_sel[pair] : np, a.max_sel);
+  const float* U = a.ub + (size_t)bh * a.maxP;
+  float best = -__builtin_huge_valf();
+  int bestp = 0x7fffffff;
+  for (int j = threadIdx.x; j < nsel; j += kBlock) {
+    const int page = a.sel ? a.sel[(size_t)pair * a.maxP + j] : j;
+    const float u = U[page];
+    if (u > best || (u == best && page < bestp)) {
+      best = u;
+      bestp = page;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ob = __shfl_xor(best, o, kWave);
+    const int op = __shfl_xor(bestp, o, kWave);
+    if (ob > best || (ob == best && op < bestp)) {
+      best = ob;
+      bestp = op;
+    }
+  }
+  if (lane == 0) {
+    s_best[wave] = best;
+    s_bestp[wave] = bestp;
+  }
+  __syncthreads();
+  best = s_best[0];
+  bestp = s_bestp[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w)
+    if (s_best[w] > best || (s_best[w] == best && s_bestp[w] < bestp)) {
+      best = s_best[w];
+      bestp = s_bestp[w];
+    }
+  if (bestp == 0x7fffffff) {  // uniform: no selected page
+    if (threadIdx.x == 0) a.zlb[bh] = -__builtin_huge_valf();
+    return;
+  }
+  const int nv = page_valid(L, bestp, a.P);
+  const size_t tile = ((size_t)a.bt[(size_t)b * a.maxP + bestp] * a.Hkv + g) * (size_t)a.P * D;
+  const int c = threadIdx.x % kLpr;
+  float qv[kVec];
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) qv[v] = a.q[(size_t)bh * D + c * kVec + v];
+  float zmax = -__builtin_huge_valf();
+  // every lane of a kLpr-lane row group has the same t, so the group sum
+  // only combines active lanes
+  for (int t = threadIdx.x / kLpr; t < nv; t += kRowsPerPass) {
+    float x[kVec];
+    Elem<T>::unpack(load16_stream(a.K + tile + (size_t)t * D + c * kVec), x);
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) acc = fmaf(qv[v], x[v], acc);
+    acc = group_sum_f32<kLpr>(acc);
+    zmax = fmaxf(zmax, acc * a.zscale);
+  }
+  zmax = wave_max_f32(zmax);
+  if (lane == 0) s_z[wave] = zmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = s_z[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_z[w]);
+    a.zlb[bh] = m;
+  }
 }
 
 // Arguments of the tau / PV stage (one (row, query head) each).

@@ -31,8 +31,8 @@ hipError_t launch_score(const Shape& s, const float* q, float scale, const void*
 // left at zero.
 hipError_t launch_score_select(const Shape& s, const float* q, float scale, const void* K,
                                void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
-                               int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
-                               int* counters, hipStream_t stream);
+                               int refresh, float* ub, float* ubg, int top_k, int32_t* sel,
+                               int32_t* n_sel, int* counters, hipStream_t stream);
 
 hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const float* ubg,
                        int32_t* sel, int32_t* n_sel, hipStream_t stream);
@@ -66,10 +66,13 @@ struct DecodePlan {
 bool decode_shape_supported(const Shape& s, int max_sel);
 DecodePlan make_decode_plan(const Shape& s, int max_sel, bool fused);
 
+// ub / zlb (both set or both NULL): per-head page bounds [B][Hq][maxP] in, and
+// per-head lower bounds of z_max [B][Hq] out; with them the selected pages
+// that cannot hold any head's support are not read.
 hipError_t launch_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,
                          float alpha, const void* K, const void* V, const int32_t* bt,
                          const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
-                         float* out, float* tau_out, int32_t* n_support, void* ws, bool fused,
-                         hipStream_t stream);
+                         const float* ub, float* zlb, float* out, float* tau_out,
+                         int32_t* n_support, void* ws, bool fused, hipStream_t stream);
 
 }  // namespace ekv

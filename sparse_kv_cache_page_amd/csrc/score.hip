@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
     const float* __restrict__ q, float scale, const T* __restrict__ K, T* __restrict__ kmin,
     T* __restrict__ kmax, const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
     int refresh, int Hkv, int P, int maxP, int pages_per_block, int npairs,
-    float* __restrict__ ubg,
+    float* __restrict__ ub, float* __restrict__ ubg,
     int top_k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
     int* __restrict__ counters) {
   using Geo = ScoreGeo<D, G, kVec, false>;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   }
   __syncthreads();
   score_range<T, D, G, kVec, false, true>(q, scale, kmin, kmax, nullptr, nullptr, s_pi, b, g, pair,
-                                          Hkv, maxP, p_begin, p_end, nullptr, ubg, nullptr,
+                                          Hkv, maxP, p_begin, p_end, ub, ubg, nullptr,
                                           nullptr, sm.red.v[threadIdx.x / kWave]);
   // arrival: every wave waits until its device-coherent bound stores have
   // completed, the barrier gathers the waves, then one relaxed device-scope
@@ -431,8 +431,8 @@ hipError_t launch_score_d(const Shape& s, const float* q, float scale, const voi
 template <typename T, int D, int G, int kVec>
 hipError_t launch_score_select_t(const Shape& s, const float* q, float scale, const void* K,
                                  void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
-                                 int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
-                                 int* counters, hipStream_t stream) {
+                                 int refresh, float* ub, float* ubg, int top_k, int32_t* sel,
+                                 int32_t* n_sel, int* counters, hipStream_t stream) {
   constexpr int kLpr = D / kVec;
   constexpr int kPagesPerStep = (kWave / kLpr) * kScoreWaves;
   const int per_iter = kPagesPerStep * ScoreGeo<D, G, kVec, false>::kU;
@@ -445,26 +445,26 @@ hipError_t launch_score_select_t(const Shape& s, const float* q, float scale, co
   if (s.maxP <= kStepTopkKeys)
     hipLaunchKernelGGL((score_select_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0,
                        stream, q, scale, (const T*)K, (T*)kmin, (T*)kmax, bt, lens, refresh, s.Hkv,
-                       s.P, s.maxP, ppb, npairs, ubg, top_k, sel, n_sel, counters);
+                       s.P, s.maxP, ppb, npairs, ub, ubg, top_k, sel, n_sel, counters);
   else
     hipLaunchKernelGGL((score_select_kernel<T, D, G, kVec, false>), grid, dim3(kScoreBlock), 0,
                        stream, q, scale, (const T*)K, (T*)kmin, (T*)kmax, bt, lens, refresh, s.Hkv,
-                       s.P, s.maxP, ppb, npairs, ubg, top_k, sel, n_sel, counters);
+                       s.P, s.maxP, ppb, npairs, ub, ubg, top_k, sel, n_sel, counters);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_score_select_d(const Shape& s, const float* q, float scale, const void* K,
                                  void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
-                                 int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
-                                 int* counters, hipStream_t stream) {
+                                 int refresh, float* ub, float* ubg, int top_k, int32_t* sel,
+                                 int32_t* n_sel, int* counters, hipStream_t stream) {
   constexpr int kV16 = 16 / sizeof(T);
   constexpr int kV8 = 8 / sizeof(T);
   switch (s.G) {
-    case 1: return launch_score_select_t<T, D, 1, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
-    case 2: return launch_score_select_t<T, D, 2, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
-    case 4: return launch_score_select_t<T, D, 4, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
-    case 8: return launch_score_select_t<T, D, 8, kV8>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+    case 1: return launch_score_select_t<T, D, 1, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
+    case 2: return launch_score_select_t<T, D, 2, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
+    case 4: return launch_score_select_t<T, D, 4, kV16>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
+    case 8: return launch_score_select_t<T, D, 8, kV8>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -485,14 +485,14 @@ hipError_t launch_score(const Shape& s, const float* q, float scale, const void*
 
 hipError_t launch_score_select(const Shape& s, const float* q, float scale, const void* K,
                                void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
-                               int refresh, float* ubg, int top_k, int32_t* sel, int32_t* n_sel,
-                               int* counters, hipStream_t stream) {
+                               int refresh, float* ub, float* ubg, int top_k, int32_t* sel,
+                               int32_t* n_sel, int* counters, hipStream_t stream) {
   if (s.bf16) {
-    if (s.D == 128) return launch_score_select_d<bf16_t, 128>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
-    return launch_score_select_d<bf16_t, 64>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+    if (s.D == 128) return launch_score_select_d<bf16_t, 128>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
+    return launch_score_select_d<bf16_t, 64>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
   }
-  if (s.D == 128) return launch_score_select_d<float, 128>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
-  return launch_score_select_d<float, 64>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ubg, top_k, sel, n_sel, counters, stream);
+  if (s.D == 128) return launch_score_select_d<float, 128>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
+  return launch_score_select_d<float, 64>(s, q, scale, K, kmin, kmax, bt, lens, refresh, ub, ubg, top_k, sel, n_sel, counters, stream);
 }
 
 }  // namespace ekv

@@ -25,7 +25,8 @@ from .binding import CacheShape
 class PagedEntmaxDecoder:
     def __init__(self, shape: CacheShape, *, policy: str = "topk", top_k: int = 256,
                  alpha: float = 1.5, scale: float = 1.0, delta: float = 0.1,
-                 device: Optional[torch.device] = None, fused: bool = False):
+                 device: Optional[torch.device] = None, fused: bool = False,
+                 prune: bool = True):
         if policy not in ("topk", "gauss", "gauss_est", "dense"):
             raise ValueError("policy must be 'topk', 'gauss', 'gauss_est' or 'dense'")
         self.shape = s = shape
@@ -44,8 +45,12 @@ class PagedEntmaxDecoder:
         self.mean = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
         self.var = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
         self.ubg = torch.empty(Bt, Hkv, mp, dtype=torch.float32, device=dev)
+        # per-head page bounds: read by the box-bound Gaussian rule, and by the
+        # decode's page pruning (prune=True) for every selecting policy
+        self.prune = bool(prune) and policy != "dense"
         self.ub = (torch.empty(Bt, Hq, mp, dtype=torch.float32, device=dev)
-                   if policy == "gauss" else None)
+                   if policy == "gauss" or self.prune else None)
+        self.zlb = torch.empty(Bt, Hq, dtype=torch.float32, device=dev) if self.prune else None
         self.gm = torch.empty(Bt, Hq, mp, dtype=torch.float64, device=dev) if gauss else None
         self.gv = torch.empty(Bt, Hq, mp, dtype=torch.float64, device=dev) if gauss else None
         self.tau_hat = torch.empty(Bt, Hq, dtype=torch.float64, device=dev) if gauss else None
@@ -91,13 +96,14 @@ class PagedEntmaxDecoder:
         B.entmax_decode(self.shape, q, self.scale, self.alpha, K, V, block_table, seq_lens,
                         self.out, self.ws, sel=None if dense else self.sel,
                         n_sel=None if dense else self.n_sel, max_sel=self.max_sel, tau=self.tau,
-                        n_support=self.n_support)
+                        n_support=self.n_support, ub=self.ub if self.prune else None,
+                        zlb=self.zlb)
 
     def score_select(self, q, K, block_table, seq_lens, refresh_last_page: bool = False):
         """[last-page refresh] + scores + top-k in one fused launch."""
         B.score_select_pages(self.shape, q, self.scale, K, block_table, seq_lens, self.top_k,
                              self.kmin, self.kmax, self.ubg, self.sel, self.n_sel, self.sel_ws,
-                             refresh_last_page=refresh_last_page)
+                             refresh_last_page=refresh_last_page, ub=self.ub)
 
     def fused_step(self, q, K, V, block_table, seq_lens, refresh_last_page: bool = False):
         """[last-page refresh] + score + top-k + decode in two fused launches."""

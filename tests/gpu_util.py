@@ -35,11 +35,12 @@ def cache_shape(inp) -> B.CacheShape:
 
 
 def run_gpu(inp, policy, *, alpha=None, top_k=None, delta=None, scale=None, q=None,
-            sel=None, n_sel=None, max_sel=0):
+            sel=None, n_sel=None, max_sel=0, prune=True):
     """Whole step on the GPU with every intermediate kept (ub, gm, gv ...).
 
     With `sel`/`n_sel` given (device int32), selection is skipped and the
-    decode runs over that page list.
+    decode runs over that page list.  prune: the decode skips the pages its
+    per-head bounds place below every head's support (ub / zlb arguments).
     """
     w = inp["workload"]
     s = cache_shape(inp)
@@ -84,10 +85,13 @@ def run_gpu(inp, policy, *, alpha=None, top_k=None, delta=None, scale=None, q=No
         use_sel = use_n = None
     o["out"] = torch.full((Bt, Hq, d), float("nan"), dtype=torch.float32, device=dev)
     o["tau"] = torch.full((Bt, Hq), float("nan"), dtype=torch.float32, device=dev)
+    o["n_support"] = torch.full((Bt, Hq), -7, dtype=torch.int32, device=dev)
+    o["zlb"] = torch.full((Bt, Hq), float("nan"), dtype=torch.float32, device=dev)
     ws = torch.empty(B.decode_workspace_bytes(s, max_sel), dtype=torch.uint8, device=dev)
     B.entmax_decode(s, q, scale, alpha, inp["K"], inp["V"], inp["block_table"],
                     inp["seq_lens"], o["out"], ws, sel=use_sel, n_sel=use_n, max_sel=max_sel,
-                    tau=o["tau"])
+                    tau=o["tau"], n_support=o["n_support"], ub=o["ub"] if prune else None,
+                    zlb=o["zlb"] if prune else None)
     torch.cuda.synchronize()
     return o
 

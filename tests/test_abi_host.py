@@ -96,7 +96,7 @@ def test_workspace_size(lib):
 def test_bad_descriptor(lib, kw, status):
     d = desc(**kw)
     r = lib.ekv_entmax_decode(ctypes.byref(d), FAKE, 1.0, 1.5, FAKE, FAKE, FAKE, FAKE, None,
-                              None, 0, FAKE, None, None, FAKE, 1 << 30, None)
+                              None, 0, None, None, FAKE, None, None, FAKE, 1 << 30, None)
     assert r == status
     r = lib.ekv_build_page_meta(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None,
                                 None, None)
@@ -108,9 +108,9 @@ def test_decode_argument_errors(lib):
     ws_need = lib.ekv_decode_workspace_bytes(ctypes.byref(d), 0)
 
     def call(q=FAKE, scale=1.0, alpha=1.5, K=FAKE, V=FAKE, sel=None, n_sel=None, out=FAKE,
-             ws=FAKE, ws_bytes=ws_need):
+             ws=FAKE, ws_bytes=ws_need, ub=None, zlb=None):
         return lib.ekv_entmax_decode(ctypes.byref(d), q, scale, alpha, K, V, FAKE, FAKE, sel,
-                                     n_sel, 0, out, None, None, ws, ws_bytes, None)
+                                     n_sel, 0, ub, zlb, out, None, None, ws, ws_bytes, None)
 
     assert call(alpha=1.0) == INVALID
     assert call(alpha=0.5) == INVALID
@@ -125,8 +125,11 @@ def test_decode_argument_errors(lib):
     assert call(ws=None) == WORKSPACE
     assert call(ws_bytes=ws_need - 1) == WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE   # not 256-byte aligned
+    assert call(ub=FAKE, zlb=None) == INVALID                # page pruning needs both
+    assert call(ub=None, zlb=FAKE) == INVALID
+    assert call(ub=ctypes.c_void_p(0x10002), zlb=FAKE) == INVALID
     assert lib.ekv_entmax_decode(None, FAKE, 1.0, 1.5, FAKE, FAKE, FAKE, FAKE, None, None, 0,
-                                 FAKE, None, None, FAKE, ws_need, None) == INVALID
+                                 None, None, FAKE, None, None, FAKE, ws_need, None) == INVALID
 
 
 def test_select_argument_errors(lib):

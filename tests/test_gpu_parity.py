@@ -13,7 +13,7 @@ from oracle import pipeline
 from sparse_kv_cache_page_amd import binding as B
 from sparse_kv_cache_page_amd import workloads as wl
 
-from gpu_util import check_pair, run_gpu
+from gpu_util import cache_shape, check_pair, run_gpu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -173,6 +173,66 @@ def test_gauss_long_rows(policy, alpha):
     gpu = run_gpu(inp, policy)
     for b, g in [(0, 0), (1, 1)]:
         check_pair(inp, gpu, b, g, policy)
+
+
+def _skipped_pages(gpu, w, alpha):
+    # the decode's pruning rule, replayed on the host in fp32
+    a1 = np.float32(alpha - 1.0)
+    ub = gpu["ub"].cpu().numpy()
+    zlb = gpu["zlb"].cpu().numpy()
+    sel = gpu["sel"].cpu().numpy()
+    nsel = gpu["n_sel"].cpu().numpy()
+    G = w.group
+    skipped = total = 0
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            for p in sel[b, g, :nsel[b, g]]:
+                below = True
+                for h in range(g * G, (g + 1) * G):
+                    x = a1 * ub[b, h, p]
+                    s1 = np.float32(1e-3) * (np.float32(1) + abs(x))
+                    s2 = np.float32(1e-4) * (np.float32(1) + abs(zlb[b, h]))
+                    below &= bool(x + s1 < zlb[b, h] - np.float32(1) - s2)
+                skipped += below
+                total += 1
+    return skipped, total
+
+
+@pytest.mark.parametrize("case", ["planted", "random", "dense", "fused"])
+def test_page_pruning_is_exact(case):
+    # with per-head bounds the decode skips the selected pages that cannot hold
+    # any head's support; tau, the output and the support sizes must be those
+    # of the unpruned decode, bit for bit
+    w = small(171, lens_range=(2000, 6000), top_k=200,
+              planted_per_kv_head=0 if case == "random" else 8)
+    inp = wl.make_inputs(w, device=DEV)
+    pol = "dense" if case == "dense" else "topk"
+    if case == "fused":
+        s = cache_shape(inp)
+        ref = run_gpu(inp, pol, prune=False)
+        outs = []
+        for ub, zlb in [(None, None), (ref["ub"], torch.empty_like(ref["tau"]))]:
+            ws = torch.zeros(B.decode_fused_workspace_bytes(s, w.top_k), dtype=torch.uint8,
+                             device=DEV)
+            o = torch.empty_like(ref["out"])
+            t = torch.empty_like(ref["tau"])
+            B.entmax_decode(s, inp["q"], w.scale, w.alpha, inp["K"], inp["V"],
+                            inp["block_table"], inp["seq_lens"], o, ws, sel=ref["sel"],
+                            n_sel=ref["n_sel"], max_sel=w.top_k, tau=t, fused=True, ub=ub,
+                            zlb=zlb)
+            outs.append((o, t))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+        return
+    plain = run_gpu(inp, pol, prune=False)
+    pruned = run_gpu(inp, pol, prune=True)
+    for k in ("out", "tau", "n_support"):
+        assert torch.equal(plain[k], pruned[k]), k
+    if case == "planted":
+        skipped, total = _skipped_pages(pruned, w, w.alpha)
+        assert skipped > 0.8 * total, (skipped, total)
+    for b, g in [(0, 0), (w.batch - 1, 1)]:
+        check_pair(inp, pruned, b, g, pol)
 
 
 def test_edge_single_token_rows():
