@@ -188,9 +188,9 @@ def page_read_mask(layer):
     if not getattr(dec, "prune", False) or dec.zlb is None:
         return None
     B_, Hkv, G = w.batch, w.num_kv_heads, w.group
-    mp = dec.ub.shape[-1]
+    mp = dec.ub.shape[2]
     a1 = torch.tensor(w.alpha - 1.0, dtype=torch.float32)
-    ub = dec.ub.cpu().view(B_, Hkv, G, mp)
+    ub = dec.ub.cpu().permute(0, 1, 3, 2).contiguous()   # [B][Hkv][G][maxP]
     zlb = dec.zlb.cpu().view(B_, Hkv, G, 1)
     if w.policy == "dense":
         idx = torch.arange(mp).view(1, 1, 1, mp).expand(B_, Hkv, G, mp)

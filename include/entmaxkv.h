@@ -109,15 +109,16 @@ ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
 /*
  * Page scores (§2.A: a deterministic upper bound on the largest score any
  * token of the page can reach for the query; Gaussian moments of the scores).
- * For row b, query head h, logical page p < ceil(seq_lens[b]/P), with
- * pi = block_table[b][p] and g = h / (Hq/Hkv):
- *   ub[b][h][p]  = RN_fp32( scale * sum_j max(q_j kmin_j, q_j kmax_j) ),
- *                  accumulated in fp64 from exact products;
- *   ubg[b][g][p] = max over the group's query heads of ub[b][h][p];
+ * For row b, query head h = g G + i (G = Hq/Hkv, KV head g), logical page
+ * p < ceil(seq_lens[b]/P), with pi = block_table[b][p]:
+ *   ub[b][g][p][i] = RN_fp32( scale * sum_j max(q_j kmin_j, q_j kmax_j) ),
+ *                    accumulated in fp64 from exact products;
+ *   ubg[b][g][p]   = max over i of ub[b][g][p][i];
  *   gm[b][h][p]  = scale   * sum_j q_j mean_j          (fp64),
  *   gv[b][h][p]  = scale^2 * sum_j q_j^2 var_j         (fp64).
  * Entries with p >= ceil(seq_lens[b]/P) are left untouched.
- * Arrays: q [B][Hq][d]; ub, gm, gv [B][Hq][maxP]; ubg [B][Hkv][maxP].
+ * Arrays: q [B][Hq][d]; ub [B][Hkv][maxP][G] (page-major: the G bounds of a
+ * page are adjacent); gm, gv [B][Hq][maxP]; ubg [B][Hkv][maxP].
  * ub may be NULL (only ubg written).  gm and gv are both NULL or both set;
  * when set, mean and var must be set.  scale must be finite and > 0.
  */
@@ -139,7 +140,7 @@ ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float sca
  *   sum_p n_p * E[(X_p - tau)_+^gamma] = 1,
  *   X_p ~ N((alpha-1) gm[b][h][p], (alpha-1)^2 gv[b][h][p]), n_p = valid tokens
  *   of page p, gamma = 1/(alpha-1); page p is kept when
- *   (alpha-1) * ub[b][h][p] >= tau_hat[b][h] - delta for some head h of group g
+ *   (alpha-1) * ub[b][g][p][i] >= tau_hat[b][g G + i] - delta for some i < G
  *   (compared in fp64).  If no page is kept, the page with the largest ubg is
  *   (lowest index on ties).  Needs ub, ubg, gm, gv and tau_hat; gamma must be
  *   1, 2, 3 or 4 (alpha in {2, 1.5, 4/3, 1.25}) else EKV_ERR_UNSUPPORTED;
@@ -177,14 +178,15 @@ ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
  * max_sel: host upper bound on every n_sel[b][g] (<= max_pages_per_seq; <= 0
  *   means max_pages_per_seq).  It sizes the launch and the workspace; a row
  *   whose n_sel exceeds it gets NaN outputs.
- * ub / zlb (both NULL, or both set): page pruning.  ub [B][Hq][maxP] fp32 holds
- *   per-head page bounds as written by ekv_score_pages or
- *   ekv_score_select_pages (u[b][h][p] >= scale * <q[b][h], k> for every valid
- *   key k of page p).  A first launch writes zlb[b][h] (fp32, [B][Hq]): the
- *   largest z over the valid tokens of the selected page with the largest
- *   ub[b][h] (a lower bound of z_max over the selected tokens; -inf if none).
- *   The keys of a selected page are then not read when, for every head h of
- *   its group, (alpha-1) u[b][h][p] plus a rounding slack is below
+ * ub / zlb (both NULL, or both set): page pruning.  ub [B][Hkv][maxP][G] fp32
+ *   holds per-head page bounds as written by ekv_score_pages or
+ *   ekv_score_select_pages (ub[b][g][p][i] >= scale * <q[b][h], k> for every
+ *   valid key k of page p, h = g G + i).  A first launch writes zlb[b][h]
+ *   (fp32, [B][Hq]): the largest z over the valid tokens of the selected page
+ *   with the largest bound for head h, lowest page on ties (a lower bound of
+ *   z_max over the selected tokens; -inf if none).  The keys of a selected
+ *   page are then not read when, for every head h of its group, (alpha-1)
+ *   times its bound plus a rounding slack is below
  *   zlb[b][h] - 1 minus a rounding slack: since tau >= z_max - 1 (the largest
  *   weight is at most 1), none of its tokens can carry weight, so tau, out
  *   and n_support are those of the unpruned call (§2.C, §3: only support

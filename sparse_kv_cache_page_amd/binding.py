@@ -197,7 +197,7 @@ def score_pages(s: CacheShape, q, scale: float, kmin, kmax, block_table, seq_len
     _need(seq_lens, "seq_lens", torch.int32, (B,))
     _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
     if ub is not None:
-        _need(ub, "ub", torch.float32, (B, Hq, mp))
+        _need(ub, "ub", torch.float32, (B, Hkv, mp, Hq // Hkv))
     if gm is not None or gv is not None:
         _need(gm, "gm", torch.float64, (B, Hq, mp))
         _need(gv, "gv", torch.float64, (B, Hq, mp))
@@ -219,7 +219,7 @@ def select_pages(s: CacheShape, seq_lens, policy: int, top_k: int, alpha: float,
     _need(sel, "sel", torch.int32, (B, Hkv, mp))
     _need(n_sel, "n_sel", torch.int32, (B, Hkv))
     if policy == EKV_SELECT_GAUSS:
-        _need(ub, "ub", torch.float32, (B, Hq, mp))
+        _need(ub, "ub", torch.float32, (B, Hkv, mp, Hq // Hkv))
     if policy in (EKV_SELECT_GAUSS, EKV_SELECT_GAUSS_EST):
         _need(gm, "gm", torch.float64, (B, Hq, mp))
         _need(gv, "gv", torch.float64, (B, Hq, mp))
@@ -247,7 +247,7 @@ def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_tabl
     """ekv_entmax_decode (or, with fused=True, ekv_entmax_decode_fused, whose
     workspace must be zero-filled before first use): alpha-entmax attention
     over the selected pages (all if sel is None).  With ub (per-head page
-    bounds [B, Hq, maxP]) and zlb ([B, Hq], written), selected pages that
+    bounds [B, Hkv, maxP, G]) and zlb ([B, Hq], written), selected pages that
     cannot hold any head's support are not read."""
     B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
     _need(q, "q", torch.float32, (B, Hq, d))
@@ -264,7 +264,7 @@ def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_tabl
     if n_support is not None:
         _need(n_support, "n_support", torch.int32, (B, Hq))
     if ub is not None or zlb is not None:
-        _need(ub, "ub", torch.float32, (B, Hq, mp))
+        _need(ub, "ub", torch.float32, (B, Hkv, mp, Hq // Hkv))
         _need(zlb, "zlb", torch.float32, (B, Hq))
     if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.dtype == torch.uint8
             and ws.is_contiguous()):
@@ -327,7 +327,7 @@ def score_select_workspace_bytes(s: CacheShape) -> int:
 def score_select_pages(s: CacheShape, q, scale: float, K, block_table, seq_lens, top_k: int,
                        kmin, kmax, ubg, sel, n_sel, ws, refresh_last_page: bool = False, ub=None):
     """ekv_score_select_pages: [last-page refresh] + scores + top-k in one launch
-    (per-head bounds also written to ub [B, Hq, maxP] when given).
+    (per-head bounds also written to ub [B, Hkv, maxP, G] when given).
 
     `ws`: uint8 GPU tensor of score_select_workspace_bytes() bytes, zero-filled
     before first use (torch.zeros); every call leaves it reusable.
@@ -348,7 +348,7 @@ def score_select_pages(s: CacheShape, q, scale: float, K, block_table, seq_lens,
         raise TypeError("ws must be a contiguous uint8 GPU tensor")
     d_ = s.desc()
     if ub is not None:
-        _need(ub, "ub", torch.float32, (B, Hq, mp))
+        _need(ub, "ub", torch.float32, (B, Hkv, mp, Hq // Hkv))
     _check("ekv_score_select_pages", load_library().ekv_score_select_pages(
         ctypes.byref(d_), _ptr(q), float(scale), _ptr(K), _ptr(block_table), _ptr(seq_lens),
         int(bool(refresh_last_page)), int(top_k), _ptr(kmin), _ptr(kmax), _ptr(ub), _ptr(ubg),

@@ -552,7 +552,7 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
         needed = false;
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          needed |= !page_below_support(a.a1 * a.ub[((size_t)b * Hq + g * G + h) * maxP + page],
+          needed |= !page_below_support(a.a1 * a.ub[((size_t)pair * maxP + page) * G + h],
                                         zlb_h[h]);
       }
       pg_valid[i] = needed ? page_valid(L, page, P) : 0;
@@ -767,12 +767,12 @@ __device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
   const int L = a.lens[b];
   const int np = (L + a.P - 1) / a.P;
   const int nsel = min(a.sel ? a.n_sel[pair] : np, a.max_sel);
-  const float* U = a.ub + (size_t)bh * a.maxP;
+  const float* U = a.ub + (size_t)pair * a.maxP * G + (bh % a.Hq) % G;  // stride G per page
   float best = -__builtin_huge_valf();
   int bestp = 0x7fffffff;
   for (int j = threadIdx.x; j < nsel; j += kBlock) {
     const int page = a.sel ? a.sel[(size_t)pair * a.maxP + j] : j;
-    const float u = U[page];
+    const float u = U[(size_t)page * G];
     if (u > best || (u == best && page < bestp)) {
       best = u;
       bestp = page;

@@ -225,7 +225,10 @@ __device__ __forceinline__ void score_range(
       const bool live = have && p < p_end;
       const size_t o = ((size_t)b * Hq + g * G + h) * maxP + p;
       const float uh = (float)(dscale * t);
-      if (kind == 0 && live && ub != nullptr) ub[o] = uh;
+      // per-head bounds page-major ([pair][page][G]): the G heads of a page sit
+      // in adjacent lanes and adjacent words, so the stores coalesce and a
+      // reader of one page gets all its heads from one 4G-byte chunk
+      if (kind == 0 && live && ub != nullptr) ub[((size_t)pair * maxP + p) * G + h] = uh;
       if constexpr (kGauss) {
         if (kind == 1 && live) gm[o] = dscale * t;
         if (kind == 2 && live) gv[o] = dscale * dscale * t;

@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
         const double e = p == n - 1 ? e_last : e_full;
         est = __dadd_rn(gm[i], __dmul_rn(e, sqrt(gv[i])));
       } else {
-        est = (double)ub[i];
+        est = (double)ub[((size_t)pair * maxP + p) * G + h];
       }
       any |= __dmul_rn(a1, est) >= th[h] - delta;
     }

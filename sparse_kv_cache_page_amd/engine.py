@@ -48,7 +48,7 @@ class PagedEntmaxDecoder:
         # per-head page bounds: read by the box-bound Gaussian rule, and by the
         # decode's page pruning (prune=True) for every selecting policy
         self.prune = bool(prune) and policy != "dense"
-        self.ub = (torch.empty(Bt, Hq, mp, dtype=torch.float32, device=dev)
+        self.ub = (torch.empty(Bt, Hkv, mp, Hq // Hkv, dtype=torch.float32, device=dev)
                    if policy == "gauss" or self.prune else None)
         self.zlb = torch.empty(Bt, Hq, dtype=torch.float32, device=dev) if self.prune else None
         self.gm = torch.empty(Bt, Hq, mp, dtype=torch.float64, device=dev) if gauss else None

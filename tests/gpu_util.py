@@ -59,7 +59,8 @@ def run_gpu(inp, policy, *, alpha=None, top_k=None, delta=None, scale=None, q=No
     o["var"] = torch.full((Np, Hkv, d), float("nan"), dtype=torch.float32, device=dev)
     B.build_page_meta(s, inp["K"], inp["block_table"], inp["seq_lens"], o["kmin"], o["kmax"],
                       o["mean"], o["var"])
-    o["ub"] = torch.full((Bt, Hq, mp), float("nan"), dtype=torch.float32, device=dev)
+    o["ub"] = torch.full((Bt, w.num_kv_heads, mp, w.group), float("nan"), dtype=torch.float32,
+                         device=dev)
     o["ubg"] = torch.full((Bt, Hkv, mp), float("nan"), dtype=torch.float32, device=dev)
     gauss = policy in ("gauss", "gauss_est")
     if gauss:
@@ -128,7 +129,7 @@ def check_pair(inp, gpu, b, g, policy, *, alpha=None, top_k=None, delta=None, sc
             va = gpu["var"][idx, g].cpu().numpy()
             assert ulp_dist(mu, np.stack(ref["mean"])).max() <= 1, f"mean b{b} g{g}"
             assert ulp_dist(va, np.stack(ref["var"])).max() <= 1, f"var b{b} g{g}"
-    ub = gpu["ub"][b, g * G:(g + 1) * G, :n].cpu().numpy()
+    ub = gpu["ub"][b, g, :n, :].T.cpu().numpy()   # [G][n]
     assert ulp_dist(ub, ref["u"]).max() <= 1, f"u b{b} g{g}"
     ubg = gpu["ubg"][b, g, :n].cpu().numpy()
     assert ulp_dist(ubg, ref["U"]).max() <= 1, f"U b{b} g{g}"

@@ -189,7 +189,7 @@ def _skipped_pages(gpu, w, alpha):
             for p in sel[b, g, :nsel[b, g]]:
                 below = True
                 for h in range(g * G, (g + 1) * G):
-                    x = a1 * ub[b, h, p]
+                    x = a1 * ub[b, g, p, h - g * G]
                     s1 = np.float32(1e-3) * (np.float32(1) + abs(x))
                     s2 = np.float32(1e-4) * (np.float32(1) + abs(zlb[b, h]))
                     below &= bool(x + s1 < zlb[b, h] - np.float32(1) - s2)
