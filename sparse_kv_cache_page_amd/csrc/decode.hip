@@ -70,9 +70,17 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QkArgs<T> a, long long n_ite
   }
 }
 
+// Workgroup i probes query head i / pairs of (row, KV head) pair i % pairs:
+// consecutive workgroups go to the 8 XCDs in turn, so (for a pair count that
+// is a multiple of 8) the G heads of a pair run on one XCD and share its L2
+// lines of the pair's page-major bounds.
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void zlb_kernel(ZlbArgs<T> a) {
-  zlb_head<T, D>(a, blockIdx.x);
+  const int G = a.Hq / a.Hkv;
+  const int npairs = (int)(gridDim.x / (unsigned)G);  // B * Hkv
+  const int pair = (int)(blockIdx.x % (unsigned)npairs);
+  const int i = (int)(blockIdx.x / (unsigned)npairs);
+  zlb_head<T, D>(a, (pair / a.Hkv) * a.Hq + (pair % a.Hkv) * G + i);
 }
 
 template <typename T, int D>
