@@ -38,10 +38,11 @@ KERNEL_SOURCES = {  # the HIP file of each entry point; local includes are follo
     "ekv_score_pages": "score.hip",
     "ekv_select_pages": "select.hip",
     "ekv_build_page_meta": "meta.hip",
+    "ekv_append_token": "meta.hip",
 }
 ENTRY_POINT = {"refresh": "ekv_build_page_meta", "score": "ekv_score_pages",
                "select": "ekv_select_pages", "decode": "ekv_entmax_decode",
-               "score_select": "ekv_score_select_pages"}
+               "score_select": "ekv_score_select_pages", "append": "ekv_append_token"}
 METRIC = "decode steps/s + effective KV GB/s (fraction of HBM peak), batch×ctx sweep"
 
 
@@ -91,6 +92,12 @@ class Layer:
         self.dec.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
         self.last_page = torch.tensor([n - 1 for n in inp["npages"]], dtype=torch.int32,
                                       device=dev)
+        # each row's last token, re-appended by the timed append (idempotent)
+        rows = torch.arange(w.batch, device=dev)
+        t = (inp["seq_lens"] - 1).long()
+        pi = inp["block_table"][rows, t // w.page_size].long()
+        self.k_last = inp["K"][pi, :, t % w.page_size].contiguous()
+        self.v_last = inp["V"][pi, :, t % w.page_size].contiguous()
 
     # the calls of one step, separately so they can be timed one by one
     @property
@@ -109,6 +116,11 @@ class Layer:
         i = self.inp
         self.dec.build_meta(i["K"], i["block_table"], i["seq_lens"], first_page=self.last_page,
                             span=1)
+
+    def append(self):
+        i = self.inp
+        self.dec.append(self.k_last, self.v_last, i["K"], i["V"], i["block_table"],
+                        i["seq_lens"])
 
     def score(self):
         i = self.inp
@@ -174,7 +186,14 @@ def stage_bytes(layer):
         # the probe's page per query head, and the bounds of the selected pages
         decode += w.batch * w.num_q_heads * P * d * e + int(n_sel.sum()) * w.group * 4
     full = sum(lens) * Hkv * d * e * 2
-    return dict(refresh=refresh, score=score if w.policy != "dense" else 0,
+    # append: the new K and V rows read and written, the page's box read and
+    # written (box-only metadata), or its valid rows read and box + moments
+    # written (Gaussian metadata)
+    if gauss:
+        append = sum(Hkv * (4 * d * e + v * d * e + meta_pp) for v in last_valid)
+    else:
+        append = w.batch * Hkv * (4 * d * e + 2 * 2 * d * e)
+    return dict(refresh=refresh, append=append, score=score if w.policy != "dense" else 0,
                 select=select if w.policy != "dense" else 0, decode=decode,
                 score_select=score + select,
                 kv_bytes=(pages * meta_pp if w.policy != "dense" else 0) + decode,
@@ -361,6 +380,7 @@ def run(w, args, dev, emit_cpu=True):
     ms, wall = time_steps(layers, args.steps, args.warmup, graph)
     stages = time_stages(layers, max(20, min(args.steps, 400)), graph)
     refresh_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["refresh"])["refresh"]
+    append_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["append"])["append"]
     nb = stage_bytes(layers[0])
     eff = nb["kv_bytes"] / (ms * 1e-3) / 1e9
     dom = max(stages, key=lambda n: stages[n])
@@ -380,6 +400,10 @@ def run(w, args, dev, emit_cpu=True):
                               "gbps": nb["refresh"] / (refresh_ms * 1e-3) / 1e9,
                               "note": "build_page_meta of each row's last page, timed "
                                       "separately, not part of the step"},
+        "append_token": {"ms": append_ms, "bytes": nb["append"],
+                         "gbps": nb["append"] / (append_ms * 1e-3) / 1e9,
+                         "note": "ekv_append_token of one token per row (K/V rows written, "
+                                 "page metadata updated), timed separately"},
         "roofline": {"kernel": ENTRY_POINT[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(ENTRY_POINT[dom], w.name),

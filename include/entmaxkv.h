@@ -107,6 +107,29 @@ ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
                                hipStream_t stream);
 
 /*
+ * Decode-time append of one token per row (§2.A: the page metadata is stored
+ * per page, so a new token changes only its own page's record).  For every
+ * row b, with t = seq_lens[b] - 1 (seq_lens already counts the new token),
+ * p = t / P, slot = t % P and pi = block_table[b][p]:
+ *   K[pi][g][slot][:] = k_new[b][g][:],  V[pi][g][slot][:] = v_new[b][g][:]
+ * for every KV head g, and the metadata of (pi, g) becomes that of the page's
+ * slot + 1 valid tokens, exactly as ekv_build_page_meta would compute it:
+ * without mean/var, the box is updated in place (a page's first token starts
+ * a new box; min and max over the same tokens are the same exact values);
+ * with mean/var, the page's box and moments are rebuilt from its rows.
+ * Arrays: k_new, v_new [B][Hkv][d] in the K dtype (16-byte aligned); K, V,
+ * kmin, kmax, mean, var as for ekv_build_page_meta.  mean and var are both
+ * NULL or both set.  Rows with seq_lens[b] < 1 are skipped.  Device-side
+ * preconditions (not checked): page p of every row is allocated in
+ * block_table, and no other row references it (it is rewritten in place).
+ * Everything else of the cache is left untouched.  One launch.
+ */
+ekv_status ekv_append_token(const ekv_cache_desc* desc, const void* k_new, const void* v_new,
+                            const int32_t* block_table, const int32_t* seq_lens, void* K,
+                            void* V, void* kmin, void* kmax, float* mean, float* var,
+                            hipStream_t stream);
+
+/*
  * Page scores (§2.A: a deterministic upper bound on the largest score any
  * token of the page can reach for the query; Gaussian moments of the scores).
  * For row b, query head h = g G + i (G = Hq/Hkv, KV head g), logical page

@@ -30,6 +30,7 @@ EXPORTED = (
     "ekv_entmax_decode_fused",
     "ekv_decode_fused_workspace_bytes",
     "ekv_score_select_pages",
+    "ekv_append_token",
     "ekv_score_select_workspace_bytes",
     "ekv_decode_step",
     "ekv_step_workspace_bytes",
@@ -82,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_score_select_pages.argtypes = [dp, vp, f32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                            vp, vp, sz, vp]
     lib.ekv_score_select_workspace_bytes.argtypes = [dp]
+    lib.ekv_append_token.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ekv_score_select_workspace_bytes.restype = sz
     lib.ekv_step_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_step_workspace_bytes.restype = sz
@@ -97,7 +99,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
                  "ekv_entmax_decode", "ekv_decode_step", "ekv_score_select_pages",
-                 "ekv_entmax_decode_fused"):
+                 "ekv_entmax_decode_fused", "ekv_append_token"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -183,6 +185,29 @@ def build_page_meta(s: CacheShape, K, block_table, seq_lens, kmin, kmax, mean=No
     _check("ekv_build_page_meta", load_library().ekv_build_page_meta(
         ctypes.byref(d), _ptr(K), _ptr(block_table), _ptr(seq_lens), _ptr(first_page),
         int(span), _ptr(kmin), _ptr(kmax), _ptr(mean), _ptr(var), _stream()))
+
+
+def append_token(s: CacheShape, k_new, v_new, block_table, seq_lens, K, V, kmin, kmax,
+                 mean=None, var=None):
+    """ekv_append_token: write each row's token at position seq_lens[b] - 1 into the
+    paged cache and bring its page's metadata up to date (one launch)."""
+    kv_new = (s.batch, s.num_kv_heads, s.head_dim)
+    _need(k_new, "k_new", s.kv_dtype, kv_new)
+    _need(v_new, "v_new", s.kv_dtype, kv_new)
+    _need(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq))
+    _need(seq_lens, "seq_lens", torch.int32, (s.batch,))
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(V, "V", s.kv_dtype, _kv_shape(s))
+    mshape = (s.num_phys_pages, s.num_kv_heads, s.head_dim)
+    _need(kmin, "kmin", s.kv_dtype, mshape)
+    _need(kmax, "kmax", s.kv_dtype, mshape)
+    if mean is not None or var is not None:
+        _need(mean, "mean", torch.float32, mshape)
+        _need(var, "var", torch.float32, mshape)
+    d = s.desc()
+    _check("ekv_append_token", load_library().ekv_append_token(
+        ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(seq_lens), _ptr(K),
+        _ptr(V), _ptr(kmin), _ptr(kmax), _ptr(mean), _ptr(var), _stream()))
 
 
 def score_pages(s: CacheShape, q, scale: float, kmin, kmax, block_table, seq_lens, ubg,

@@ -86,6 +86,22 @@ ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
                                          kmax, mean, var, stream));
 }
 
+ekv_status ekv_append_token(const ekv_cache_desc* desc, const void* k_new, const void* v_new,
+                            const int32_t* block_table, const int32_t* seq_lens, void* K,
+                            void* V, void* kmin, void* kmax, float* mean, float* var,
+                            hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(k_new) || !ok_vec(v_new) || !ok_i32(block_table) || !ok_i32(seq_lens) ||
+      !ok_vec(K) || !ok_vec(V) || !ok_vec(kmin) || !ok_vec(kmax))
+    return EKV_ERR_INVALID_ARG;
+  if ((mean == nullptr) != (var == nullptr)) return EKV_ERR_INVALID_ARG;
+  if (mean != nullptr && (!ok_vec(mean) || !ok_vec(var))) return EKV_ERR_INVALID_ARG;
+  return from_hip(ekv::launch_append(s, k_new, v_new, block_table, seq_lens, K, V, kmin, kmax,
+                                     mean, var, stream));
+}
+
 ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float scale,
                            const void* kmin, const void* kmax, const float* mean,
                            const float* var, const int32_t* block_table,

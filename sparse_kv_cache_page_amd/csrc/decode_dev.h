@@ -756,60 +756,85 @@ __device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
   constexpr int kLpr = D / kVec;
   constexpr int kRowsPerPass = kBlock / kLpr;
   constexpr int kWaves = kBlock / kWave;
+  constexpr int kSpecSel = 2;  // selection slots per thread requested up front
   __shared__ float s_best[kWaves];
   __shared__ int s_bestp[kWaves];
+  __shared__ int s_bestphys[kWaves];
   __shared__ float s_z[kWaves];
   const int G = a.Hq / a.Hkv;
   const int b = bh / a.Hq;
   const int g = (bh % a.Hq) / G;
   const int pair = b * a.Hkv + g;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int c = threadIdx.x % kLpr;
+  float qv[kVec];
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) qv[v] = a.q[(size_t)bh * D + c * kVec + v];
+  // the first slots of the selection are requested in the same round trip as
+  // the row length and the selection size (slots past n_sel are in bounds and
+  // never used)
+  int spec[kSpecSel];
+#pragma unroll
+  for (int u = 0; u < kSpecSel; ++u) {
+    const int j = threadIdx.x + u * kBlock;
+    spec[u] = j;
+    if (a.sel && j < a.max_sel) spec[u] = a.sel[(size_t)pair * a.maxP + j];
+  }
   const int L = a.lens[b];
   const int np = (L + a.P - 1) / a.P;
   const int nsel = min(a.sel ? a.n_sel[pair] : np, a.max_sel);
   const float* U = a.ub + (size_t)pair * a.maxP * G + (bh % a.Hq) % G;  // stride G per page
+  // each page's bound and block-table entry in one round; the winner's
+  // physical page travels with it through the reduction
   float best = -__builtin_huge_valf();
-  int bestp = 0x7fffffff;
-  for (int j = threadIdx.x; j < nsel; j += kBlock) {
-    const int page = a.sel ? a.sel[(size_t)pair * a.maxP + j] : j;
+  int bestp = 0x7fffffff, bestphys = 0;
+  auto consider = [&](int page) {
     const float u = U[(size_t)page * G];
+    const int phys = a.bt[(size_t)b * a.maxP + page];
     if (u > best || (u == best && page < bestp)) {
       best = u;
       bestp = page;
+      bestphys = phys;
     }
-  }
+  };
+#pragma unroll
+  for (int u = 0; u < kSpecSel; ++u)
+    if (threadIdx.x + u * kBlock < nsel) consider(spec[u]);
+  for (int j = threadIdx.x + kSpecSel * kBlock; j < nsel; j += kBlock)
+    consider(a.sel ? a.sel[(size_t)pair * a.maxP + j] : j);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ob = __shfl_xor(best, o, kWave);
     const int op = __shfl_xor(bestp, o, kWave);
+    const int oph = __shfl_xor(bestphys, o, kWave);
     if (ob > best || (ob == best && op < bestp)) {
       best = ob;
       bestp = op;
+      bestphys = oph;
     }
   }
   if (lane == 0) {
     s_best[wave] = best;
     s_bestp[wave] = bestp;
+    s_bestphys[wave] = bestphys;
   }
   __syncthreads();
   best = s_best[0];
   bestp = s_bestp[0];
+  bestphys = s_bestphys[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w)
     if (s_best[w] > best || (s_best[w] == best && s_bestp[w] < bestp)) {
       best = s_best[w];
       bestp = s_bestp[w];
+      bestphys = s_bestphys[w];
     }
   if (bestp == 0x7fffffff) {  // uniform: no selected page
     if (threadIdx.x == 0) a.zlb[bh] = -__builtin_huge_valf();
     return;
   }
   const int nv = page_valid(L, bestp, a.P);
-  const size_t tile = ((size_t)a.bt[(size_t)b * a.maxP + bestp] * a.Hkv + g) * (size_t)a.P * D;
-  const int c = threadIdx.x % kLpr;
-  float qv[kVec];
-#pragma unroll
-  for (int v = 0; v < kVec; ++v) qv[v] = a.q[(size_t)bh * D + c * kVec + v];
+  const size_t tile = ((size_t)bestphys * a.Hkv + g) * (size_t)a.P * D;
   float zmax = -__builtin_huge_valf();
   // every lane of a kLpr-lane row group has the same t, so the group sum
   // only combines active lanes

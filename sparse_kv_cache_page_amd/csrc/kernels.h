@@ -16,6 +16,13 @@ struct Shape {
   bool bf16;
 };
 
+// Decode-time append of the token at position lens[b] - 1 of every row: K/V
+// rows written, the page's box updated (and its moments rebuilt when mean/var
+// are given).
+hipError_t launch_append(const Shape& s, const void* k_new, const void* v_new,
+                         const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,
+                         void* kmax, float* mean, float* var, hipStream_t stream);
+
 hipError_t launch_build_meta(const Shape& s, const void* K, const int32_t* bt,
                              const int32_t* lens, const int32_t* first_page, int span,
                              void* kmin, void* kmax, float* mean, float* var,

@@ -1,5 +1,6 @@
-// Page metadata builder (EntmaxKV summary page, §2.A: per-page bounding box
-// k_min/k_max and per-page key mean/variance).
+// Page metadata builder and decode-time append (EntmaxKV summary page, §2.A:
+// per-page bounding box k_min/k_max and per-page key mean/variance, stored per
+// page, so a new token changes only its own page's record).
 //
 // One wave64 per (physical page, KV head) tile.  The P x d tile is contiguous,
 // so lanes read 16-byte chunks of consecutive rows: lane = (row group, chunk),
@@ -46,7 +47,107 @@ hipError_t launch_meta_t(const Shape& s, const void* K, const int32_t* bt, const
   return hipGetLastError();
 }
 
+// Decode-time append: one wave per (row b, KV head g).  The token at position
+// t = lens[b] - 1 goes to slot t % P of page t / P; lanes of the first row
+// group write its K and V rows.  Without moments the page's box is updated in
+// place: min/max over the page's tokens taken in another order is the same
+// exact value, so it equals a rebuild (the first token of a page starts a new
+// box).  With moments the page is rebuilt by meta_tile over its valid tokens,
+// as ekv_build_page_meta does; a workgroup-scope release/acquire pair makes
+// the new row, stored by this wave's lanes, visible to the lanes that read it
+// back (all lanes of a workgroup share one CU's vector L1).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_kernel(
+    const T* __restrict__ k_new, const T* __restrict__ v_new, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ lens, int B, int Hkv, int P, int maxP, T* __restrict__ K,
+    T* __restrict__ V, T* __restrict__ kmin, T* __restrict__ kmax, float* __restrict__ mean,
+    float* __restrict__ var) {
+  constexpr int kVec = Elem<T>::kVec;
+  constexpr int kLpr = D / kVec;
+  const int lane = threadIdx.x % kWave;
+  const long long unit = (long long)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (unit >= (long long)B * Hkv) return;  // uniform over the wave
+  const int b = (int)(unit / Hkv);
+  const int g = (int)(unit % Hkv);
+  const int L = lens[b];
+  if (L < 1) return;
+  const int t = L - 1;
+  const int p = t / P;
+  const int slot = t - p * P;
+  const int pi = bt[(size_t)b * maxP + p];
+  if (lane < kLpr) {
+    const int c = lane;
+    const size_t src = ((size_t)b * Hkv + g) * D + c * kVec;
+    const size_t dst = (((size_t)pi * Hkv + g) * P + slot) * D + c * kVec;
+    const uint4 kw = load16(k_new + src);
+    const uint4 vw = load16(v_new + src);
+    *reinterpret_cast<uint4*>(K + dst) = kw;
+    *reinterpret_cast<uint4*>(V + dst) = vw;
+    if (mean == nullptr) {
+      const size_t m_off = ((size_t)pi * Hkv + g) * D + c * kVec;
+      float x[kVec], mn[kVec], mx[kVec];
+      Elem<T>::unpack(kw, x);
+      if (slot == 0) {
+#pragma unroll
+        for (int v = 0; v < kVec; ++v) mn[v] = mx[v] = x[v];
+      } else {
+        Elem<T>::unpack(load16(kmin + m_off), mn);
+        Elem<T>::unpack(load16(kmax + m_off), mx);
+#pragma unroll
+        for (int v = 0; v < kVec; ++v) {
+          mn[v] = fminf(mn[v], x[v]);
+          mx[v] = fmaxf(mx[v], x[v]);
+        }
+      }
+      if constexpr (sizeof(T) == 2) {
+        uint32_t wn[4], wx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wn[i] = (__float_as_uint(mn[2 * i]) >> 16) | (__float_as_uint(mn[2 * i + 1]) & 0xffff0000u);
+          wx[i] = (__float_as_uint(mx[2 * i]) >> 16) | (__float_as_uint(mx[2 * i + 1]) & 0xffff0000u);
+        }
+        *reinterpret_cast<uint4*>(kmin + m_off) = make_uint4(wn[0], wn[1], wn[2], wn[3]);
+        *reinterpret_cast<uint4*>(kmax + m_off) = make_uint4(wx[0], wx[1], wx[2], wx[3]);
+      } else {
+        *reinterpret_cast<float4*>(kmin + m_off) = make_float4(mn[0], mn[1], mn[2], mn[3]);
+        *reinterpret_cast<float4*>(kmax + m_off) = make_float4(mx[0], mx[1], mx[2], mx[3]);
+      }
+    }
+  }
+  if (mean != nullptr) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    meta_tile<T, D>(K, Hkv, P, pi, g, slot + 1, kmin, kmax, mean, var);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_append_t(const Shape& s, const void* k_new, const void* v_new,
+                           const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,
+                           void* kmax, float* mean, float* var, hipStream_t stream) {
+  const long long units = (long long)s.B * s.Hkv;
+  const long long blocks = (units + 3) / 4;
+  hipLaunchKernelGGL((append_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const T*)k_new, (const T*)v_new, bt, lens, s.B, s.Hkv, s.P, s.maxP, (T*)K,
+                     (T*)V, (T*)kmin, (T*)kmax, mean, var);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_append(const Shape& s, const void* k_new, const void* v_new,
+                         const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,
+                         void* kmax, float* mean, float* var, hipStream_t stream) {
+  if (s.bf16) {
+    if (s.D == 128)
+      return launch_append_t<bf16_t, 128>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
+    return launch_append_t<bf16_t, 64>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
+  }
+  if (s.D == 128)
+    return launch_append_t<float, 128>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
+  return launch_append_t<float, 64>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
+}
 
 hipError_t launch_build_meta(const Shape& s, const void* K, const int32_t* bt,
                              const int32_t* lens, const int32_t* first_page, int span,

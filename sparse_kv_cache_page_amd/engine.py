@@ -76,6 +76,12 @@ class PagedEntmaxDecoder:
         B.build_page_meta(self.shape, K, block_table, seq_lens, self.kmin, self.kmax,
                           self.mean, self.var, first_page=first_page, span=span)
 
+    def append(self, k_new, v_new, K, V, block_table, seq_lens):
+        """Write each row's new token (at seq_lens - 1, already counted) into the
+        cache and update its page's metadata, in one launch."""
+        B.append_token(self.shape, k_new, v_new, block_table, seq_lens, K, V, self.kmin,
+                       self.kmax, self.mean, self.var)
+
     # -- one decode step ----------------------------------------------------
     def score(self, q, block_table, seq_lens):
         B.score_pages(self.shape, q, self.scale, self.kmin, self.kmax, block_table, seq_lens,

@@ -234,3 +234,20 @@ def test_step_argument_errors(lib):
     assert call(kmin=FAKE_MIS) == INVALID
     assert call(ws=None) == WORKSPACE
     assert call(ws_bytes=need - 1) == WORKSPACE
+
+
+def test_append_argument_errors(lib):
+    d = desc()
+
+    def call(k_new=FAKE, v_new=FAKE, K=FAKE, mean=None, var=None, kmin=FAKE):
+        return lib.ekv_append_token(ctypes.byref(d), k_new, v_new, FAKE, FAKE, K, FAKE, kmin,
+                                    FAKE, mean, var, None)
+
+    assert call(k_new=None) == INVALID
+    assert call(v_new=FAKE_MIS) == INVALID
+    assert call(K=None) == INVALID
+    assert call(kmin=FAKE_MIS) == INVALID
+    assert call(mean=FAKE, var=None) == INVALID
+    assert call(mean=FAKE_MIS, var=FAKE) == INVALID
+    assert lib.ekv_append_token(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                None, None) == INVALID

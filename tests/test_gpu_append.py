@@ -1,0 +1,142 @@
+"""GPU tests of the decode-time append (ekv_append_token).
+
+Rows start shorter than the workload's lengths, with the missing key/value
+slots cleared; tokens are then appended one per step (crossing page
+boundaries).  Afterwards the K/V caches must equal the full inputs bit for bit,
+and the page metadata must equal a from-scratch ekv_build_page_meta over the
+full lengths bit for bit (box alone, and box + moments), and the oracle's
+metadata on sampled pages (kmin/kmax exact, mean/var within 1 ulp).
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_kv_cache_page_amd import binding as B
+from sparse_kv_cache_page_amd import workloads as wl
+
+from gpu_util import cache_shape, ulp_dist
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def same_bits(a, b):
+    # bitwise equality (value padding slots hold a NaN sentinel)
+    it = torch.int16 if a.element_size() == 2 else torch.int32
+    return torch.equal(a.view(it), b.view(it))
+
+
+def small(seed, **kw):
+    base = dict(name="small", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                page_size=16, lens_range=(60, 900), kv_dtype="bf16",
+                q_std=2.0 / np.sqrt(128), scale=1.0, alpha=1.5, policy="topk", top_k=9,
+                planted_per_kv_head=0, permute_pool=True, seed=seed)
+    base.update(kw)
+    return wl.Workload(**base)
+
+
+@pytest.mark.parametrize("moments", [False, True])
+@pytest.mark.parametrize("kw", [
+    dict(), dict(num_q_heads=16, num_kv_heads=2), dict(kv_dtype="f32", head_dim=64),
+    dict(page_size=1, lens_range=(5, 200)), dict(page_size=64, lens_range=(70, 1500)),
+    dict(num_q_heads=4, num_kv_heads=4, page_size=32),
+])
+def test_append_matches_full_build(kw, moments):
+    w = small(701 + len(kw), **kw)
+    inp = wl.make_inputs(w, device=DEV)
+    s = cache_shape(inp)
+    P = w.page_size
+    steps = P + 3                       # every row crosses at least one page boundary
+    lens = torch.tensor(inp["lens"], dtype=torch.int32, device=DEV)
+    start = (lens - steps).clamp(min=1)
+    K0, V0 = inp["K"], inp["V"]
+    bt = inp["block_table"]
+    K, V = K0.clone(), V0.clone()
+    # clear the slots of the tokens still to be appended
+    btc = bt.cpu()
+    for b in range(w.batch):
+        for t in range(int(start[b]), int(lens[b])):
+            pi = int(btc[b, t // P])
+            K[pi, :, t % P] = 0
+            V[pi, :, t % P] = 0
+    mshape = (s.num_phys_pages, s.num_kv_heads, s.head_dim)
+    mk = lambda dt: torch.zeros(mshape, dtype=dt, device=DEV)
+    meta = [mk(s.kv_dtype), mk(s.kv_dtype)] + ([mk(torch.float32), mk(torch.float32)]
+                                               if moments else [None, None])
+    B.build_page_meta(s, K, bt, start, *meta)
+    cur = start.clone()
+    rows = torch.arange(w.batch, device=DEV)
+    for _ in range(steps):
+        grow = cur < lens
+        cur = torch.where(grow, cur + 1, cur)
+        # the token at position cur - 1 of each row (rows already complete
+        # re-append their last token, which leaves everything unchanged)
+        t = (cur - 1).long()
+        pi = bt[rows, t // P].long()
+        k_new = K0[pi, :, t % P].contiguous()     # [B][Hkv][d]
+        v_new = V0[pi, :, t % P].contiguous()
+        B.append_token(s, k_new, v_new, bt, cur, K, V, *meta)
+    torch.cuda.synchronize()
+    assert torch.equal(cur, lens)
+    assert same_bits(K, K0) and same_bits(V, V0)
+    ref = [mk(s.kv_dtype), mk(s.kv_dtype)] + ([mk(torch.float32), mk(torch.float32)]
+                                              if moments else [None, None])
+    B.build_page_meta(s, K0, bt, lens, *ref)
+    torch.cuda.synchronize()
+    for x, y in zip(meta, ref):
+        if x is not None:
+            assert torch.equal(x, y)
+    # the oracle on the last page of every row (the one the appends ended on)
+    from oracle import meta as ometa
+    from oracle import pipeline
+    Kc = pipeline.widen(K0)
+    for b in range(w.batch):
+        L = int(lens[b])
+        p = (L - 1) // P
+        pi = int(btc[b, p])
+        nv = L - p * P
+        for g in range(w.num_kv_heads):
+            kmin, kmax, mu, va = ometa.page_meta(Kc[pi, g, :nv])
+            np.testing.assert_array_equal(pipeline.widen(meta[0][pi, g]), kmin)
+            np.testing.assert_array_equal(pipeline.widen(meta[1][pi, g]), kmax)
+            if moments:
+                assert ulp_dist(meta[2][pi, g].cpu().numpy(), mu).max() <= 1
+                assert ulp_dist(meta[3][pi, g].cpu().numpy(), va).max() <= 1
+
+
+def test_append_then_step_equals_fresh_build():
+    # a decode step after appends equals one on metadata built from scratch
+    from sparse_kv_cache_page_amd.engine import PagedEntmaxDecoder
+    w = small(751, lens_range=(300, 2000), planted_per_kv_head=8)
+    inp = wl.make_inputs(w, device=DEV)
+    s = cache_shape(inp)
+    P = w.page_size
+    lens = torch.tensor(inp["lens"], dtype=torch.int32, device=DEV)
+    start = lens - 5
+    K, V = inp["K"].clone(), inp["V"].clone()
+    bt = inp["block_table"]
+    a = PagedEntmaxDecoder(s, policy="topk", top_k=w.top_k, alpha=w.alpha, scale=w.scale,
+                           fused=True)
+    f = PagedEntmaxDecoder(s, policy="topk", top_k=w.top_k, alpha=w.alpha, scale=w.scale,
+                           fused=True)
+    a.build_meta(K, bt, start)
+    rows = torch.arange(w.batch, device=DEV)
+    cur = start.clone()
+    for _ in range(5):
+        cur = cur + 1
+        t = (cur - 1).long()
+        pi = bt[rows, t // P].long()
+        a.append(inp["K"][pi, :, t % P].contiguous(), inp["V"][pi, :, t % P].contiguous(),
+                 K, V, bt, cur)
+    f.build_meta(inp["K"], bt, lens)
+    a.fused_step(inp["q"], K, V, bt, lens)
+    f.fused_step(inp["q"], inp["K"], inp["V"], bt, lens)
+    torch.cuda.synchronize()
+    for k in ("kmin", "kmax", "ubg", "n_sel", "out", "tau", "n_support"):
+        x, y = getattr(a, k), getattr(f, k)
+        if k == "ubg":
+            for b in range(w.batch):
+                n = inp["npages"][b]
+                assert torch.equal(x[b, :, :n], y[b, :, :n])
+        else:
+            assert torch.equal(x, y), k
