@@ -26,7 +26,7 @@ class PagedEntmaxDecoder:
     def __init__(self, shape: CacheShape, *, policy: str = "topk", top_k: int = 256,
                  alpha: float = 1.5, scale: float = 1.0, delta: float = 0.1,
                  device: Optional[torch.device] = None, fused: bool = False,
-                 prune: bool = True):
+                 prune: Optional[bool] = None):
         if policy not in ("topk", "gauss", "gauss_est", "dense"):
             raise ValueError("policy must be 'topk', 'gauss', 'gauss_est' or 'dense'")
         self.shape = s = shape
@@ -46,7 +46,13 @@ class PagedEntmaxDecoder:
         self.var = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
         self.ubg = torch.empty(Bt, Hkv, mp, dtype=torch.float32, device=dev)
         # per-head page bounds: read by the box-bound Gaussian rule, and by the
-        # decode's page pruning (prune=True) for every selecting policy
+        # decode's page pruning.  Pruning is on by default for top-k only: the
+        # Gaussian rules keep a page only if its estimated maximum reaches
+        # tau_hat - delta, and tau_hat tracks tau >= z_max - 1, so the pages
+        # they keep already lie near z_max - 1 and the probe launch would find
+        # nothing to skip (prune=True still forces it)
+        if prune is None:
+            prune = policy == "topk"
         self.prune = bool(prune) and policy != "dense"
         self.ub = (torch.empty(Bt, Hkv, mp, Hq // Hkv, dtype=torch.float32, device=dev)
                    if policy == "gauss" or self.prune else None)

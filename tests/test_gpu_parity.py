@@ -235,6 +235,43 @@ def test_page_pruning_is_exact(case):
         check_pair(inp, pruned, b, g, pol)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(num_q_heads=16, num_kv_heads=2), dict(num_q_heads=4, num_kv_heads=4),
+    dict(kv_dtype="f32", head_dim=64, q_std=2.0 / 8.0), dict(page_size=64, top_k=40),
+    dict(page_size=1, lens_range=(300, 3000), top_k=600), dict(alpha=1.25), dict(alpha=2.0),
+    dict(alpha=3.0, q_std=4.0 / np.sqrt(128)),
+])
+def test_page_pruning_is_exact_shapes(kw):
+    # the pruned decode equals the unpruned one bit for bit across group sizes,
+    # dtypes, head dims, page sizes and alpha (planted keys, so pages get pruned)
+    base = dict(lens_range=(2000, 6000), top_k=200, planted_per_kv_head=8)
+    base.update(kw)
+    w = small(181 + len(kw) + int(10 * base.get("alpha", 0)), **base)
+    inp = wl.make_inputs(w, device=DEV)
+    plain = run_gpu(inp, "topk", prune=False)
+    pruned = run_gpu(inp, "topk", prune=True)
+    for k in ("out", "tau", "n_support"):
+        assert torch.equal(plain[k], pruned[k]), k
+    skipped, total = _skipped_pages(pruned, w, w.alpha)
+    print(f"pruned {skipped} of {total} selected pages")
+    check_pair(inp, pruned, w.batch - 1, w.num_kv_heads - 1, "topk")
+
+
+@pytest.mark.parametrize("policy", ["gauss", "gauss_est"])
+def test_page_pruning_is_exact_gaussian(policy):
+    # pruning over the Gaussian policies' selections (clustered keys, alpha 2)
+    w = small(191, lens_range=(1500, 4000), alpha=2.0, policy=policy, delta=0.1,
+              planted_per_kv_head=0, clusters=64, cluster_sigma=0.5)
+    inp = wl.make_inputs(w, device=DEV)
+    plain = run_gpu(inp, policy, prune=False)
+    pruned = run_gpu(inp, policy, prune=True)
+    for k in ("sel", "n_sel", "out", "tau", "n_support"):
+        assert torch.equal(plain[k], pruned[k]), k
+    skipped, total = _skipped_pages(pruned, w, w.alpha)
+    print(f"{policy}: pruned {skipped} of {total} selected pages")
+    check_pair(inp, pruned, 0, 0, policy)
+
+
 def test_edge_single_token_rows():
     w = small(91, lens_range=None, seq_len=1, batch=2, top_k=3)
     inp = wl.make_inputs(w, device=DEV)
