@@ -22,10 +22,14 @@
  *    error nothing is launched and a negative ekv_status is returned.  Values
  *    that live in device memory (seq_lens, block_table, sel, n_sel) cannot be
  *    checked without a synchronisation: they must satisfy
- *        1 <= seq_lens[b] <= max_pages_per_seq * page_size,
+ *        0 <= seq_lens[b] <= max_pages_per_seq * page_size,
  *        0 <= block_table[b][p] < num_phys_pages  for p < ceil(seq_lens[b]/P),
  *    and a physical page referenced by several rows must hold the same number
  *    of valid tokens in each of them.
+ *  * An empty row (seq_lens[b] = 0, an idle batch slot) has no pages: the
+ *    selections give it n_sel = 0 (and tau_hat NaN), the decode writes a zero
+ *    output, tau NaN and n_support 0 for its heads, and the metadata calls
+ *    and the append skip it.  Its block-table entries are not used.
  *  * Alignment: K, V, q, out, kmin, kmax, mean and var 16 bytes; int32 and
  *    fp32 arrays 4 bytes; fp64 arrays 8 bytes; workspaces 256 bytes.
  *  * Layouts (row-major, innermost last):

@@ -46,7 +46,19 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QkArgs<T> a, long long n_ite
   __shared__ int s_last;
   for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
     const QkItemInfo it = qk_item<T, D, G, kFused>(a, item, sm);
-    if (!it.ran) continue;  // uniform over the block
+    if (!it.ran) {  // uniform over the block
+      if constexpr (kFused) {
+        // an empty row has no item to arrive: its first split writes the
+        // outputs of the group's heads
+        const int pair = (int)(item / a.splits);
+        if (item % a.splits == 0 && a.lens[pair / a.Hkv] < 1) {
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            empty_row_head(ta.out, ta.tau_out, ta.n_support, pair * G + h, D);
+        }
+      }
+      continue;
+    }
     if constexpr (kFused) {
       // arrival: this item's device-coherent stores drain, the block counts
       // itself once, and the last item of the pair runs the tau / PV tail

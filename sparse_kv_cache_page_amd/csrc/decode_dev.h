@@ -858,6 +858,15 @@ __device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
   }
 }
 
+// Outputs of one query head of an empty row (no token to attend to): a zero
+// output, tau NaN, support 0.  Called by all threads of a workgroup.
+__device__ inline void empty_row_head(float* __restrict__ out, float* __restrict__ tau_out,
+                                      int32_t* __restrict__ n_support, int bh, int D) {
+  for (int t = threadIdx.x; t < D; t += kBlock) out[(size_t)bh * D + t] = 0.0f;
+  if (tau_out && threadIdx.x == 0) tau_out[bh] = __builtin_nanf("");
+  if (n_support && threadIdx.x == 0) n_support[bh] = 0;
+}
+
 // Arguments of the tau / PV stage (one (row, query head) each).
 template <typename T>
 struct TauArgs {
@@ -931,6 +940,11 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
   const int nsel = has_sel ? n_sel[pair] : np;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
+  if (np == 0) {
+    // empty row: no token to attend to
+    empty_row_head(out, tau_out, n_support, bh, D);
+    return;
+  }
   if (nsel > max_sel || nsel < 1) {
     // outside the launch's bound: flag the row instead of reading past the workspace
     for (int t = threadIdx.x; t < D; t += kBlock) out[(size_t)bh * D + t] = __builtin_nanf("");

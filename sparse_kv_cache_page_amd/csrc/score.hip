@@ -340,7 +340,12 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
     s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
   const int L = lens[b];
   const int np = (L + P - 1) / P;
-  if (p_begin >= np) return;
+  if (p_begin >= np) {
+    // an empty row has no slice to count: its first workgroup records the
+    // empty selection
+    if (np == 0 && p_begin == 0 && threadIdx.x == 0) n_sel[pair] = 0;
+    return;
+  }
   const int p_end = min(np, p_begin + pages_per_block);
   if (refresh && p_end == np && threadIdx.x < kWave) {
     // only this workgroup reads the refreshed page's box: the barrier below

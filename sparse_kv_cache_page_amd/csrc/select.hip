@@ -179,6 +179,10 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
   const int b = bh / Hq;
   const int L = lens[b];
   const int n = (L + P - 1) / P;
+  if (n == 0) {  // empty row: no pages, no threshold
+    if (threadIdx.x == 0) tau_hat[bh] = __builtin_nan("");
+    return;
+  }
   const double* M = gm + (size_t)bh * maxP;
   const double* V = gv + (size_t)bh * maxP;
 
@@ -342,6 +346,10 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
   const int Hq = Hkv * G;
   const int L = lens[b];
   const int n = (L + P - 1) / P;
+  if (n == 0) {  // empty row: nothing to select (the guard needs a page)
+    if (threadIdx.x == 0) n_sel[pair] = 0;
+    return;
+  }
   const size_t head0 = ((size_t)b * Hq + g * G) * maxP;
   const double* th = tau_hat + (size_t)b * Hq + g * G;
   int32_t* out = sel + (size_t)pair * maxP;

@@ -142,7 +142,8 @@ def make_inputs(w: Workload, device="cpu", lens: Optional[List[int]] = None) -> 
     assert Hq % Hkv == 0
     G = Hq // Hkv
     lens = list(lens) if lens is not None else draw_lengths(w)
-    assert len(lens) == B and all(L >= 1 for L in lens)
+    # a row may be empty (an idle batch slot); at least one row holds tokens
+    assert len(lens) == B and all(L >= 0 for L in lens) and max(lens) >= 1
     npages = [(L + P - 1) // P for L in lens]
     maxP = max(npages)
     Np = sum(npages)
@@ -193,6 +194,8 @@ def make_inputs(w: Workload, device="cpu", lens: Optional[List[int]] = None) -> 
         for b in range(B):
             L = lens[b]
             m = min(n_pl, L)
+            if m == 0:
+                continue
             # distinct uniform positions per KV head
             pos = torch.stack([torch.randperm(L, generator=gcpu)[:m] for _ in range(Hkv)])  # [Hkv][m]
             heads = (torch.arange(Hkv)[:, None] * G + (torch.arange(m)[None, :] % G))  # [Hkv][m]

@@ -386,3 +386,62 @@ def test_topk_long_rows(lens):
     gpu = run_gpu(inp, "topk")
     for b, g in [(0, 0), (w.batch - 1, 1)]:
         check_pair(inp, gpu, b, g, "topk")
+
+
+@pytest.mark.parametrize("policy,prune", [("topk", True), ("topk", False), ("gauss", False),
+                                          ("gauss_est", True), ("dense", False)])
+def test_edge_empty_rows(policy, prune):
+    # idle batch slots (seq_len 0) next to rows with tokens: the empty rows get
+    # n_sel = 0, a zero output, tau NaN and support 0; the other rows are those
+    # of the oracle
+    gauss = policy in ("gauss", "gauss_est")
+    w = small(211, batch=5, lens_range=None, alpha=2.0 if gauss else 1.5, policy=policy,
+              planted_per_kv_head=0 if gauss else 8, clusters=64 if gauss else 0)
+    inp = wl.make_inputs(w, device=DEV, lens=[0, 700, 0, 33, 1500])
+    gpu = run_gpu(inp, policy, prune=prune)
+    G = w.group
+    for b in (0, 2):
+        for g in range(w.num_kv_heads):
+            if policy != "dense":
+                assert int(gpu["n_sel"][b, g]) == 0
+        assert torch.equal(gpu["out"][b], torch.zeros_like(gpu["out"][b]))
+        assert torch.isnan(gpu["tau"][b]).all()
+        assert int(gpu["n_support"][b].abs().sum()) == 0
+        if gauss:
+            assert torch.isnan(gpu["tau_hat"][b]).all()
+    for b in (1, 3, 4):
+        for g in range(w.num_kv_heads):
+            check_pair(inp, gpu, b, g, policy)
+
+
+def test_edge_empty_rows_fused_paths():
+    # the fused step and the fused decode on a batch with idle slots
+    from sparse_kv_cache_page_amd.engine import PagedEntmaxDecoder
+    w = small(221, batch=4, lens_range=None, top_k=20)
+    inp = wl.make_inputs(w, device=DEV, lens=[900, 0, 2000, 0])
+    s = cache_shape(inp)
+    f = PagedEntmaxDecoder(s, policy="topk", top_k=w.top_k, alpha=w.alpha, scale=w.scale,
+                           fused=True)
+    f.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
+    f.out.fill_(float("nan"))
+    f.fused_step(inp["q"], inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
+    ws = torch.zeros(B.decode_fused_workspace_bytes(s, w.top_k), dtype=torch.uint8, device=DEV)
+    out2 = torch.full_like(f.out, float("nan"))
+    tau2 = torch.full_like(f.tau, 0.0)
+    sup2 = torch.full_like(f.n_support, 7)
+    torch.cuda.synchronize()
+    B.entmax_decode(s, inp["q"], w.scale, w.alpha, inp["K"], inp["V"], inp["block_table"],
+                    inp["seq_lens"], out2, ws, sel=f.sel, n_sel=f.n_sel, max_sel=w.top_k,
+                    tau=tau2, n_support=sup2, fused=True)
+    torch.cuda.synchronize()
+    for out, tau, sup in ((f.out, f.tau, f.n_support), (out2, tau2, sup2)):
+        for b in (1, 3):
+            assert torch.equal(out[b], torch.zeros_like(out[b]))
+            assert torch.isnan(tau[b]).all()
+            assert int(sup[b].abs().sum()) == 0
+        assert not torch.isnan(out[0]).any() and not torch.isnan(out[2]).any()
+    assert int(f.n_sel[1].abs().sum()) == 0 and int(f.n_sel[3].abs().sum()) == 0
+    gpu = dict(kmin=f.kmin, kmax=f.kmax, ubg=f.ubg, sel=f.sel, n_sel=f.n_sel, out=f.out,
+               tau=f.tau)
+    for b, g in [(0, 0), (2, 1)]:
+        check_pair(inp, gpu, b, g, "topk", check_meta=False)
