@@ -63,7 +63,7 @@ def test_topk_page_sizes(page_size):
         check_pair(inp, gpu, b, g, "topk")
 
 
-@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0, 1.1])
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0, 1.1, 1.05, 1.02, 5.0, 8.0])
 def test_alpha_values(alpha):
     w = small(41, alpha=alpha, planted_per_kv_head=4)
     inp = wl.make_inputs(w, device=DEV)
