@@ -91,7 +91,8 @@ def decode_heads(q_heads, keys_sel, vals_sel, scale: float, alpha: float):
 def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=None,
              delta=None, scale=None, q=None, exact_meta=False, with_full=False,
              sel_override=None, timings=None):
-    """One decode step of (row b, KV head g) under `policy` ('topk', 'gauss', 'gauss_est', 'dense').
+    """One decode step of (row b, KV head g) under `policy` ('topk', 'gauss', 'gauss_est',
+    'gauss_mass', 'dense').
 
     alpha, scale and delta are the fp32 values handed to the library (widened).
     Returns a dict with the metadata, bounds, selection and entmax outputs.
@@ -134,13 +135,15 @@ def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=Non
         sel = select.topk_pages(U, top_k)
     elif policy == "dense":
         sel = list(range(n))
-    elif policy in ("gauss", "gauss_est"):
+    elif policy in ("gauss", "gauss_est", "gauss_mass"):
         m = np.empty((G, n))
         v = np.empty((G, n))
         for h in range(G):
             for p in range(n):
                 m[h, p], v[h, p] = scores.gauss_moments(qq[h], mu[p], var[p], scale)
-        rule = select.gauss_select if policy == "gauss" else select.gauss_est_select
+        rule = {"gauss": select.gauss_select, "gauss_est": select.gauss_est_select,
+                "gauss_mass": select.gauss_mass_select}[policy]
+        # delta: the margin of the maximum-score rules, the mass threshold of G-mass
         sel, tau_hat = rule(u, m, v, counts, alpha, delta)
         out.update(m=m, v=v, tau_hat=tau_hat)
     else:

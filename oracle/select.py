@@ -30,6 +30,15 @@ EntmaxKV page, §2.B "Politiques de Sélection des Candidats", two policies:
    and keeps p when (alpha-1) est_{h,p} >= tau-hat_h - Delta for some head h
    of the group, with the same tau-hat and the same empty-set guard.
 
+A third reading (policy G-mass) tests each page's expected mass instead of
+its maximum: under the same model the tokens of page p carry, for head h, the
+expected entmax mass
+      M_{h,p} = n_p * E[(X_{h,p} - tau-hat_h)_+^gamma],
+and these masses sum to F_h(tau-hat_h) = 1 over the pages.  Dropping a page
+drops its mass, and the output error is at most 2 B times the dropped mass
+(§3), so page p is kept when M_{h,p} >= eps for some head h of the group
+(eps is the policy's threshold; same tau-hat, same empty-set guard).
+
 Gaussian partial moments, I_g(h) = E[(Z + h)_+^g] for Z ~ N(0, 1):
    I_0 = Phi(h),  I_1 = h Phi(h) + phi(h),  I_g = h I_{g-1} + (g-1) I_{g-2}
 (the last by Stein's identity E[Z f(Z)] = E[f'(Z)]), and for X ~ N(mu, s^2),
@@ -42,7 +51,9 @@ hand-built tie cases; e_n against the closed forms known for n <= 5 and a
 Monte Carlo estimate; I_g against numerical quadrature (scipy.integrate.quad);
 tau-hat for zero-variance pages equals the exact entmax threshold of the
 expanded token multiset (checked against the sort-based sparsemax closed form);
-F(tau-hat) = 1.
+F(tau-hat) = 1; page masses: for zero-variance pages they are the exact entmax
+masses of the pages' tokens, and one page's expected mass matches a Monte
+Carlo estimate.
 """
 from __future__ import annotations
 
@@ -186,6 +197,45 @@ def gauss_est_select(u_heads, m_heads, v_heads, counts, alpha: float, delta: flo
         taus[h] = t
         est = m + e * np.sqrt(v)
         keep |= a1 * est >= t - float(delta)
+    if not keep.any():
+        U = u_heads.max(axis=0)
+        best = max(range(n), key=lambda p: (float(U[p]), -p))
+        return [best], taus
+    return [int(p) for p in np.nonzero(keep)[0]], taus
+
+
+def gauss_page_masses(mu_z, sig_z, counts, g: int, tau: float) -> np.ndarray:
+    """M_p = n_p E[(X_p - tau)_+^g], X_p ~ N(mu_z[p], sig_z[p]^2) (zero sig: a point mass)."""
+    mu_z = np.asarray(mu_z, dtype=np.float64)
+    sig_z = np.asarray(sig_z, dtype=np.float64)
+    counts = np.asarray(counts, dtype=np.float64)
+    pos = sig_z > 0.0
+    terms = np.empty_like(mu_z)
+    sp = sig_z[pos]
+    terms[pos] = sp ** g * partial_moment((mu_z[pos] - tau) / sp, g)
+    terms[~pos] = np.maximum(mu_z[~pos] - tau, 0.0) ** g
+    return counts * terms
+
+
+def gauss_mass_select(u_heads, m_heads, v_heads, counts, alpha: float, eps: float):
+    """Gaussian selection by expected page mass (G-mass), one (row, KV head).
+
+    Same arguments and results as gauss_select, with eps in place of delta:
+    page p is kept when n_p E[(X_{h,p} - tau_hat_h)_+^gamma] >= eps for a head
+    h of the group.
+    """
+    g = integer_gamma(alpha)
+    a1 = float(alpha) - 1.0
+    u_heads = np.asarray(u_heads, dtype=np.float32)
+    G, n = u_heads.shape
+    keep = np.zeros(n, dtype=bool)
+    taus = np.empty(G)
+    for h in range(G):
+        mu_z = a1 * np.asarray(m_heads[h], dtype=np.float64)
+        sig_z = a1 * np.sqrt(np.asarray(v_heads[h], dtype=np.float64))
+        t = gauss_tau_hat(mu_z, sig_z, counts, g)
+        taus[h] = t
+        keep |= gauss_page_masses(mu_z, sig_z, counts, g, t) >= float(eps)
     if not keep.any():
         U = u_heads.max(axis=0)
         best = max(range(n), key=lambda p: (float(U[p]), -p))

@@ -192,3 +192,70 @@ def test_gauss_est_select_rule_and_guard():
     v2 = np.full((1, 3), 4.0)
     sel2, t2 = select.gauss_est_select(u2, m2, v2, [1, 1, 1], 2.0, 0.1)
     assert t2[0] - 0.1 > 0.0 and sel2 == [1]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_page_masses_zero_variance_are_exact_entmax_masses(seed):
+    # zero variance: each page's tokens all score mu_z[p]; the exact entmax
+    # weights of the expanded multiset come from the sort-based closed forms,
+    # and a page's mass is the sum of its tokens' weights
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(2, 40))
+    mu_z = rng.normal(0, 1.5, n)
+    counts = rng.integers(1, 17, n)
+    sig = np.zeros(n)
+    for g, closed in ((1, sparsemax_sort), (2, entmax15_sort)):
+        tau_exact = closed(_expand(mu_z, counts))
+        w = np.maximum(_expand(mu_z, counts) - tau_exact, 0.0) ** g
+        per_page = np.add.reduceat(w, np.concatenate([[0], np.cumsum(counts)[:-1]]))
+        t = select.gauss_tau_hat(mu_z, sig, counts, g)
+        M = select.gauss_page_masses(mu_z, sig, counts, g, t)
+        np.testing.assert_allclose(M, per_page, rtol=1e-9, atol=1e-12)
+        assert abs(math.fsum(M) - 1.0) < 1e-12
+
+
+def test_page_masses_monte_carlo_and_sum():
+    rng = np.random.default_rng(11)
+    mu, s, tau, cnt = -0.3, 0.9, 0.2, 16
+    x = rng.normal(mu, s, 2_000_000)
+    for g in (1, 2, 3):
+        mc = cnt * np.mean(np.maximum(x - tau, 0.0) ** g)
+        val = select.gauss_page_masses([mu], [s], [cnt], g, tau)[0]
+        assert abs(mc - val) < 0.01 * val
+    # at tau-hat the masses of all pages sum to 1
+    n = 300
+    mu_z = rng.normal(0, 1, n)
+    sig = rng.uniform(0.0, 1.2, n)
+    sig[::5] = 0.0
+    counts = rng.integers(1, 17, n)
+    for g in (1, 2, 4):
+        t = select.gauss_tau_hat(mu_z, sig, counts, g)
+        assert abs(math.fsum(select.gauss_page_masses(mu_z, sig, counts, g, t)) - 1.0) < 1e-12
+
+
+def test_gauss_mass_select_rule_and_guard():
+    # keep p iff n_p E[(X - tau_hat)_+^g] >= eps for some head; a page whose mean
+    # lies below tau-hat can still carry mass through its spread
+    alpha, eps = 1.5, 0.02
+    a1, g = alpha - 1.0, 2
+    u = np.array([[4.0, 3.0, 2.0, 1.0], [1.0, 2.0, 3.0, 4.0]], np.float32)
+    m = np.array([[6.0, 0.2, -0.5, 4.23], [0.1, 5.5, 3.0, -1.0]])
+    v = np.array([[0.5, 2.0, 0.1, 1.0], [1.0, 0.3, 9.0, 0.2]])
+    counts = [4, 4, 4, 3]
+    sel, taus = select.gauss_mass_select(u, m, v, counts, alpha, eps)
+    M = np.array([select.gauss_page_masses(a1 * m[h], a1 * np.sqrt(v[h]), counts, g, taus[h])
+                  for h in range(2)])
+    expect = [p for p in range(4) if (M[:, p] >= eps).any()]
+    assert sel == expect and len(sel) >= 2
+    assert a1 * m[1, 2] < taus[1] and M[1, 2] >= eps        # kept through its spread
+    # the threshold is the Gaussian policy's own tau-hat
+    _, taus_b = select.gauss_select(u, m, v, counts, alpha, eps)
+    assert np.array_equal(taus, taus_b)
+    # a larger threshold keeps a subset
+    sel_hi, _ = select.gauss_mass_select(u, m, v, counts, alpha, 0.3)
+    assert set(sel_hi) <= set(sel)
+    # guard: no page holds more than mass 1, so eps > 1 keeps only argmax U
+    # (lowest index on ties)
+    u2 = np.array([[1.0, 7.0, 7.0]], np.float32)
+    sel2, _ = select.gauss_mass_select(u2, np.zeros((1, 3)), np.ones((1, 3)), [4, 4, 4], 2.0, 1.5)
+    assert sel2 == [1]
