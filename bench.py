@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="gqa",
-                    help="tiny | gqa | gauss | gauss_est | ragged | stress")
+                    help="tiny | gqa | gauss | gauss_est | gauss_mass | ragged | stress")
     ap.add_argument("--layers", type=int, default=0, help="layers cycled (0 = auto)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -152,7 +152,7 @@ def stage_bytes(layer):
     w, inp, dec = layer.w, layer.inp, layer.dec
     e = 2 if w.kv_dtype == "bf16" else 4
     d, P, Hkv = w.head_dim, w.page_size, w.num_kv_heads
-    gauss = w.policy in ("gauss", "gauss_est")
+    gauss = w.policy in ("gauss", "gauss_est", "gauss_mass")
     lens = inp["lens"]
     npg = inp["npages"]
     last_valid = [L - (n - 1) * P for L, n in zip(lens, npg)]
@@ -360,7 +360,7 @@ def workload_config(w, R, graph, inp):
             "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": ctx,
             "page_size": w.page_size, "kv_dtype": w.kv_dtype, "alpha": w.alpha,
             "policy": w.policy, "top_k": w.top_k if w.policy == "topk" else None,
-            "delta": w.delta if w.policy in ("gauss", "gauss_est") else None,
+            "delta": w.delta if w.policy in ("gauss", "gauss_est", "gauss_mass") else None,
             "q_std_x_sqrt_d": round(w.q_std * math.sqrt(w.head_dim), 6),
             "layers_rotated": R, "hip_graph": graph,
             "graph_scope": "one graph per pass over the rotated layers" if graph else None}

@@ -71,8 +71,10 @@ typedef enum {
   EKV_SELECT_TOPK = 0,  /* fixed budget: k pages with the largest bound     */
   EKV_SELECT_GAUSS = 1,     /* Gaussian estimate tau-hat of the threshold, margin Delta;
                                a page's maximum score estimated by its box bound     */
-  EKV_SELECT_GAUSS_EST = 2  /* same tau-hat and Delta; maximum score estimated as the
+  EKV_SELECT_GAUSS_EST = 2, /* same tau-hat and Delta; maximum score estimated as the
                                expected maximum of its tokens' Gaussian scores       */
+  EKV_SELECT_GAUSS_MASS = 3 /* same tau-hat; a page is kept when its expected entmax
+                               mass reaches the threshold passed as delta            */
 } ekv_policy;
 
 typedef struct {
@@ -180,6 +182,13 @@ ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float sca
  *   (fp64, each operation rounded separately), with e_n = E[max of n iid
  *   N(0,1)] (e_1 = 0, e_16 = 1.76599...).  ub is not read and may be NULL.
  *   The empty-set guard and every other rule are those of EKV_SELECT_GAUSS.
+ * EKV_SELECT_GAUSS_MASS: same tau_hat; instead of a maximum score, the
+ *   expected entmax mass of the page's tokens under the same Gaussian model,
+ *   M = n_p * E[(X_p - tau_hat[b][h])_+^gamma] (these sum to 1 over the pages
+ *   at tau_hat; dropping a page drops its mass, and the output error is at
+ *   most 2 B times the dropped mass, §3).  Page p is kept when M >= delta for
+ *   some head of the group (fp64); delta is here the mass threshold (>= 0).
+ *   ub is not read and may be NULL; guard and other rules as EKV_SELECT_GAUSS.
  * Arrays: sel [B][Hkv][maxP] int32; n_sel [B][Hkv] int32; tau_hat [B][Hq] fp64.
  */
 ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libentmaxkv
 
 EKV_OK = 0
 EKV_BF16, EKV_F32 = 0, 1
-EKV_SELECT_TOPK, EKV_SELECT_GAUSS, EKV_SELECT_GAUSS_EST = 0, 1, 2
+EKV_SELECT_TOPK, EKV_SELECT_GAUSS, EKV_SELECT_GAUSS_EST, EKV_SELECT_GAUSS_MASS = 0, 1, 2, 3
 
 EXPORTED = (
     "ekv_build_page_meta",
@@ -237,7 +237,8 @@ def score_pages(s: CacheShape, q, scale: float, kmin, kmax, block_table, seq_len
 def select_pages(s: CacheShape, seq_lens, policy: int, top_k: int, alpha: float, delta: float,
                  ubg, sel, n_sel, ub=None, gm=None, gv=None, tau_hat=None):
     """ekv_select_pages: top-k (policy 0) or Gaussian-aware selection with the box
-    bound (policy 1) or the expected maximum (policy 2) as a page's estimated maximum."""
+    bound (policy 1) or the expected maximum (policy 2) as a page's estimated maximum, or
+    the page's expected entmax mass against delta (policy 3)."""
     B, Hq, Hkv, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.max_pages_per_seq
     _need(seq_lens, "seq_lens", torch.int32, (B,))
     _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
@@ -245,7 +246,7 @@ def select_pages(s: CacheShape, seq_lens, policy: int, top_k: int, alpha: float,
     _need(n_sel, "n_sel", torch.int32, (B, Hkv))
     if policy == EKV_SELECT_GAUSS:
         _need(ub, "ub", torch.float32, (B, Hkv, mp, Hq // Hkv))
-    if policy in (EKV_SELECT_GAUSS, EKV_SELECT_GAUSS_EST):
+    if policy in (EKV_SELECT_GAUSS, EKV_SELECT_GAUSS_EST, EKV_SELECT_GAUSS_MASS):
         _need(gm, "gm", torch.float64, (B, Hq, mp))
         _need(gv, "gv", torch.float64, (B, Hq, mp))
         _need(tau_hat, "tau_hat", torch.float64, (B, Hq))

@@ -137,16 +137,18 @@ ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
     if (top_k < 1) return EKV_ERR_INVALID_ARG;
     return from_hip(ekv::launch_topk(s, seq_lens, top_k, ubg, sel, n_sel, stream));
   }
-  if (policy != EKV_SELECT_GAUSS && policy != EKV_SELECT_GAUSS_EST) return EKV_ERR_INVALID_ARG;
-  const bool est = policy == EKV_SELECT_GAUSS_EST;
-  if ((!est && !ok_i32(ub)) || !ok_f64(gm) || !ok_f64(gv) || !ok_f64(tau_hat))
+  if (policy != EKV_SELECT_GAUSS && policy != EKV_SELECT_GAUSS_EST &&
+      policy != EKV_SELECT_GAUSS_MASS)
+    return EKV_ERR_INVALID_ARG;
+  const int rule = policy == EKV_SELECT_GAUSS ? 0 : (policy == EKV_SELECT_GAUSS_EST ? 1 : 2);
+  if ((rule == 0 && !ok_i32(ub)) || !ok_f64(gm) || !ok_f64(gv) || !ok_f64(tau_hat))
     return EKV_ERR_INVALID_ARG;
   if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
   if (!(delta >= 0.0f) || !isfinite(delta)) return EKV_ERR_INVALID_ARG;
   const double gamma = 1.0 / ((double)alpha - 1.0);
   const double gr = rint(gamma);
   if (gr < 1.0 || gr > 4.0 || fabs(gamma - gr) > 1e-6 * gr) return EKV_ERR_UNSUPPORTED;
-  return from_hip(ekv::launch_gauss(s, seq_lens, alpha, (int)gr, delta, est, ub, ubg, gm, gv,
+  return from_hip(ekv::launch_gauss(s, seq_lens, alpha, (int)gr, delta, rule, ub, ubg, gm, gv,
                                     sel, n_sel, tau_hat, stream));
 }
 

@@ -48,10 +48,11 @@ hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const flo
 // (NaN outside 1 <= n <= kMaxPageSize).
 double expected_max_std_normal(int n);
 
-// Gaussian-aware selection; `est` picks the expected-maximum estimate
-// m + e_n sqrt(v) of a page's maximum score instead of its box bound ub.
+// Gaussian-aware selection; `rule` 0 compares the box bound ub, 1 the
+// expected maximum m + e_n sqrt(v) of the page's scores, 2 the page's
+// expected entmax mass (against delta).
 hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int gamma,
-                        float delta, bool est, const float* ub, const float* ubg,
+                        float delta, int rule, const float* ub, const float* ubg,
                         const double* gm, const double* gv, int32_t* sel, int32_t* n_sel,
                         double* tau_hat, hipStream_t stream);
 

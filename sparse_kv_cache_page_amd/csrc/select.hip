@@ -330,7 +330,11 @@ __device__ int compact_ascending(int n, Flag flag, int32_t* out, uint8_t* s_flag
   return total;
 }
 
-template <bool kEst, int G>
+// Which estimate a Gaussian rule compares: the box bound, the expected
+// maximum of the page's tokens, or the page's expected entmax mass.
+enum MarkRule { kRuleBound = 0, kRuleEstMax = 1, kRuleMass = 2 };
+
+template <int kRule, int G, int kG>
 __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
     const float* __restrict__ ub, const float* __restrict__ ubg, const double* __restrict__ gm,
     const double* __restrict__ gv, const double* __restrict__ tau_hat,
@@ -354,15 +358,34 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
   const double* th = tau_hat + (size_t)b * Hq + g * G;
   int32_t* out = sel + (size_t)pair * maxP;
   // every page but the last holds P tokens
+  const int n_last = page_valid(L, n - 1, P);
   const double e_full = et.e[P];
-  const double e_last = et.e[page_valid(L, n - 1, P)];
+  const double e_last = et.e[n_last];
   auto keep = [&](int p) -> bool {
     bool any = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const size_t i = head0 + (size_t)h * maxP + p;
+      if constexpr (kRule == kRuleMass) {
+        // n_p E[(X - tau_hat)_+^gamma], X ~ N((alpha-1) m, (alpha-1)^2 v):
+        // the expected entmax mass of the page's tokens, against delta
+        const double mz = a1 * gm[i];
+        const double sd = a1 * sqrt(gv[i]);
+        const double cnt = p == n - 1 ? (double)n_last : (double)P;
+        double mass;
+        if (sd > 0.0) {
+          double ig, igm1, jdd;
+          partial_moments<kG>((mz - th[h]) / sd, ig, igm1, jdd);
+          mass = cnt * (ipow<kG>(sd) * ig);
+        } else {
+          const double x = mz - th[h];
+          mass = x > 0.0 ? cnt * ipow<kG>(x) : 0.0;
+        }
+        any |= mass >= delta;
+        continue;
+      }
       double est;
-      if constexpr (kEst) {
+      if constexpr (kRule == kRuleEstMax) {
         // m + e_n sqrt(v), each operation rounded on its own (no contraction)
         const double e = p == n - 1 ? e_last : e_full;
         est = __dadd_rn(gm[i], __dmul_rn(e, sqrt(gv[i])));
@@ -460,19 +483,38 @@ const ExpMaxTable& exp_max_table() {
   return table;
 }
 
+template <int kRule, int G, int kG>
+void launch_mark_t(const Shape& s, const float* ub, const float* ubg, const double* gm,
+                   const double* gv, const double* tau_hat, const int32_t* lens, double a1,
+                   double delta, const ExpMaxTable& et, int32_t* sel, int32_t* n_sel,
+                   hipStream_t stream) {
+  hipLaunchKernelGGL((gauss_mark_kernel<kRule, G, kG>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
+                     stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, a1, delta, et,
+                     sel, n_sel);
+}
+
 template <int G>
-void launch_mark(const Shape& s, bool est, const float* ub, const float* ubg, const double* gm,
-                 const double* gv, const double* tau_hat, const int32_t* lens, double a1,
-                 double delta, const ExpMaxTable& et, int32_t* sel, int32_t* n_sel,
-                 hipStream_t stream) {
-  if (est)
-    hipLaunchKernelGGL((gauss_mark_kernel<true, G>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
-                       stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, a1, delta, et,
-                       sel, n_sel);
-  else
-    hipLaunchKernelGGL((gauss_mark_kernel<false, G>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
-                       stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, a1, delta, et,
-                       sel, n_sel);
+hipError_t launch_mark(const Shape& s, int rule, int gamma, const float* ub, const float* ubg,
+                       const double* gm, const double* gv, const double* tau_hat,
+                       const int32_t* lens, double a1, double delta, const ExpMaxTable& et,
+                       int32_t* sel, int32_t* n_sel, hipStream_t stream) {
+#define EKV_MARK(R, KG) \
+  launch_mark_t<R, G, KG>(s, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream)
+  if (rule == kRuleBound) {
+    EKV_MARK(kRuleBound, 1);
+  } else if (rule == kRuleEstMax) {
+    EKV_MARK(kRuleEstMax, 1);
+  } else {
+    switch (gamma) {
+      case 1: EKV_MARK(kRuleMass, 1); break;
+      case 2: EKV_MARK(kRuleMass, 2); break;
+      case 3: EKV_MARK(kRuleMass, 3); break;
+      case 4: EKV_MARK(kRuleMass, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef EKV_MARK
+  return hipSuccess;
 }
 
 }  // namespace
@@ -494,7 +536,7 @@ hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const flo
 }
 
 hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int gamma, float delta,
-                        bool est, const float* ub, const float* ubg, const double* gm,
+                        int rule, const float* ub, const float* ubg, const double* gm,
                         const double* gv, int32_t* sel, int32_t* n_sel, double* tau_hat,
                         hipStream_t stream) {
   const double a1 = (double)alpha - 1.0;
@@ -508,12 +550,13 @@ hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int ga
   if (e != hipSuccess) return e;
   const ExpMaxTable& et = exp_max_table();
   switch (s.G) {
-    case 1: launch_mark<1>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
-    case 2: launch_mark<2>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
-    case 4: launch_mark<4>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
-    case 8: launch_mark<8>(s, est, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 1: e = launch_mark<1>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 2: e = launch_mark<2>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 4: e = launch_mark<4>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 8: e = launch_mark<8>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

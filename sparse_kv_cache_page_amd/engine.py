@@ -27,8 +27,9 @@ class PagedEntmaxDecoder:
                  alpha: float = 1.5, scale: float = 1.0, delta: float = 0.1,
                  device: Optional[torch.device] = None, fused: bool = False,
                  prune: Optional[bool] = None):
-        if policy not in ("topk", "gauss", "gauss_est", "dense"):
-            raise ValueError("policy must be 'topk', 'gauss', 'gauss_est' or 'dense'")
+        if policy not in ("topk", "gauss", "gauss_est", "gauss_mass", "dense"):
+            raise ValueError("policy must be 'topk', 'gauss', 'gauss_est', 'gauss_mass' or "
+                             "'dense'")
         self.shape = s = shape
         self.policy = policy
         self.top_k = int(top_k)
@@ -39,7 +40,7 @@ class PagedEntmaxDecoder:
         self.device = dev
         Bt, Hq, Hkv, d, mp, Np = (s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim,
                                   s.max_pages_per_seq, s.num_phys_pages)
-        gauss = policy in ("gauss", "gauss_est")
+        gauss = policy in ("gauss", "gauss_est", "gauss_mass")
         self.kmin = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
         self.kmax = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
         self.mean = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
@@ -97,8 +98,9 @@ class PagedEntmaxDecoder:
         if self.policy == "topk":
             B.select_pages(self.shape, seq_lens, B.EKV_SELECT_TOPK, self.top_k, self.alpha,
                            self.delta, self.ubg, self.sel, self.n_sel)
-        elif self.policy in ("gauss", "gauss_est"):
-            pol = B.EKV_SELECT_GAUSS if self.policy == "gauss" else B.EKV_SELECT_GAUSS_EST
+        elif self.policy in ("gauss", "gauss_est", "gauss_mass"):
+            pol = {"gauss": B.EKV_SELECT_GAUSS, "gauss_est": B.EKV_SELECT_GAUSS_EST,
+                   "gauss_mass": B.EKV_SELECT_GAUSS_MASS}[self.policy]
             B.select_pages(self.shape, seq_lens, pol, self.top_k, self.alpha, self.delta,
                            self.ubg, self.sel, self.n_sel, ub=self.ub, gm=self.gm, gv=self.gv,
                            tau_hat=self.tau_hat)

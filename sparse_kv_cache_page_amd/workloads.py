@@ -49,7 +49,7 @@ class Workload:
     q_std: float = 1.0               # per-coordinate std of q
     scale: float = 1.0               # score scale passed to the library
     alpha: float = 1.5
-    policy: str = "topk"             # "topk" | "gauss" | "gauss_est" | "dense"
+    policy: str = "topk"             # "topk" | "gauss" | "gauss_est" | "gauss_mass" | "dense"
     top_k: int = 256
     delta: float = 0.1
     planted_per_kv_head: int = 0     # planted high-score keys per (row, KV head)
@@ -93,6 +93,11 @@ CONFIGS = {
                       page_size=16, seq_len=32768, kv_dtype="bf16",
                       q_std=2.0 / math.sqrt(128), scale=1.0, alpha=2.0, policy="gauss_est",
                       delta=0.1, clusters=64, cluster_sigma=0.5, seed=3003),
+    # gauss shapes, the expected-mass rule (delta is the mass threshold)
+    "gauss_mass": _cfg(name="gauss_mass", batch=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                       page_size=16, seq_len=32768, kv_dtype="bf16",
+                       q_std=2.0 / math.sqrt(128), scale=1.0, alpha=2.0, policy="gauss_mass",
+                       delta=1e-4, clusters=64, cluster_sigma=0.5, seed=3003),
     "ragged": _cfg(name="ragged", batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
                    page_size=16, lens_range=(4096, 65536), kv_dtype="bf16",
                    q_std=2.0 / math.sqrt(128), scale=1.0, alpha=1.5, policy="topk",

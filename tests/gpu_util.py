@@ -62,7 +62,7 @@ def run_gpu(inp, policy, *, alpha=None, top_k=None, delta=None, scale=None, q=No
     o["ub"] = torch.full((Bt, w.num_kv_heads, mp, w.group), float("nan"), dtype=torch.float32,
                          device=dev)
     o["ubg"] = torch.full((Bt, Hkv, mp), float("nan"), dtype=torch.float32, device=dev)
-    gauss = policy in ("gauss", "gauss_est")
+    gauss = policy in ("gauss", "gauss_est", "gauss_mass")
     if gauss:
         o["gm"] = torch.full((Bt, Hq, mp), float("nan"), dtype=torch.float64, device=dev)
         o["gv"] = torch.full((Bt, Hq, mp), float("nan"), dtype=torch.float64, device=dev)
@@ -74,7 +74,7 @@ def run_gpu(inp, policy, *, alpha=None, top_k=None, delta=None, scale=None, q=No
         o["sel"] = torch.full((Bt, Hkv, mp), -7, dtype=torch.int32, device=dev)
         o["n_sel"] = torch.full((Bt, Hkv), -7, dtype=torch.int32, device=dev)
         pol = {"topk": B.EKV_SELECT_TOPK, "gauss": B.EKV_SELECT_GAUSS,
-               "gauss_est": B.EKV_SELECT_GAUSS_EST}[policy]
+               "gauss_est": B.EKV_SELECT_GAUSS_EST, "gauss_mass": B.EKV_SELECT_GAUSS_MASS}[policy]
         B.select_pages(s, inp["seq_lens"], pol, top_k, alpha, delta, o["ubg"], o["sel"],
                        o["n_sel"], ub=o["ub"] if policy == "gauss" else None, gm=o.get("gm"),
                        gv=o.get("gv"), tau_hat=o.get("tau_hat"))
@@ -124,7 +124,7 @@ def check_pair(inp, gpu, b, g, policy, *, alpha=None, top_k=None, delta=None, sc
         kmax = _np(gpu["kmax"][idx, g])
         np.testing.assert_array_equal(kmin, np.stack(ref["kmin"]), err_msg=f"kmin b{b} g{g}")
         np.testing.assert_array_equal(kmax, np.stack(ref["kmax"]), err_msg=f"kmax b{b} g{g}")
-        if policy in ("gauss", "gauss_est"):
+        if policy in ("gauss", "gauss_est", "gauss_mass"):
             mu = gpu["mean"][idx, g].cpu().numpy()
             va = gpu["var"][idx, g].cpu().numpy()
             assert ulp_dist(mu, np.stack(ref["mean"])).max() <= 1, f"mean b{b} g{g}"
@@ -134,7 +134,7 @@ def check_pair(inp, gpu, b, g, policy, *, alpha=None, top_k=None, delta=None, sc
         assert ulp_dist(ub, ref["u"]).max() <= 1, f"u b{b} g{g}"
     ubg = gpu["ubg"][b, g, :n].cpu().numpy()
     assert ulp_dist(ubg, ref["U"]).max() <= 1, f"U b{b} g{g}"
-    if policy in ("gauss", "gauss_est"):
+    if policy in ("gauss", "gauss_est", "gauss_mass"):
         th = gpu["tau_hat"][b, g * G:(g + 1) * G].cpu().numpy()
         np.testing.assert_allclose(th, ref["tau_hat"], rtol=TAU_HAT_RTOL, atol=1e-300,
                                    err_msg=f"tau_hat b{b} g{g}")

@@ -158,7 +158,13 @@ def test_select_argument_errors(lib):
     assert call(policy=2, alpha=1.7, ub=None) == UNSUPPORTED
     assert call(policy=2, gv=None, ub=None) == INVALID
     assert call(policy=2, tau=None, ub=None) == INVALID
-    assert call(policy=3) == INVALID
+    # the expected-mass policy (delta is the mass threshold): same checks
+    assert call(policy=3, alpha=1.0, ub=None) == INVALID
+    assert call(policy=3, delta=-0.1, ub=None) == INVALID
+    assert call(policy=3, alpha=1.7, ub=None) == UNSUPPORTED
+    assert call(policy=3, gm=None, ub=None) == INVALID
+    assert call(policy=3, tau=None, ub=None) == INVALID
+    assert call(policy=4) == INVALID
 
 
 def test_library_expected_max_table(lib):

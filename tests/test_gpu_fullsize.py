@@ -90,6 +90,19 @@ def test_fullsize_gauss_est():
     decoder_matches(inp, gpu, "gauss_est", w.alpha, w.top_k, w.delta, w.scale, inp["q"])
 
 
+def test_fullsize_gauss_mass():
+    # gauss shapes with the expected-mass rule (mass threshold 1e-4)
+    w = wl.CONFIGS["gauss_mass"]
+    print("[fullsize] gauss_mass: generating", flush=True)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "gauss_mass")
+    check_properties(inp, gpu, "gauss_mass", w.top_k)
+    for b, g in [(0, 0), (6, 2)]:
+        print(f"[fullsize] gauss_mass: oracle pair b{b} g{g}", flush=True)
+        check_pair(inp, gpu, b, g, "gauss_mass")
+    decoder_matches(inp, gpu, "gauss_mass", w.alpha, w.top_k, w.delta, w.scale, inp["q"])
+
+
 @pytest.fixture(scope="module")
 def stress_inputs():
     w = wl.CONFIGS["stress"]

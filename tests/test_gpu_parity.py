@@ -144,6 +144,30 @@ def test_gauss_est_policy(alpha, page_size):
         check_pair(inp, gpu, b, g, "gauss_est")
 
 
+@pytest.mark.parametrize("alpha,page_size,eps", [(2.0, 16, 1e-4), (1.5, 8, 1e-3),
+                                                 (1.25, 32, 1e-2), (4.0 / 3.0, 64, 3e-4)])
+def test_gauss_mass_policy(alpha, page_size, eps):
+    # expected page mass n_p E[(X - tau_hat)_+^gamma] against eps (ragged last
+    # pages use their own token counts)
+    w = small(77, alpha=alpha, policy="gauss_mass", clusters=16, planted_per_kv_head=0,
+              page_size=page_size, lens_range=(100, 1200), delta=eps)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "gauss_mass")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "gauss_mass")
+
+
+def test_gauss_mass_guard_keeps_argmax():
+    # no page can hold a mass above 1: eps = 1.5 leaves only the guard's page
+    w = small(83, alpha=2.0, policy="gauss_mass", clusters=16, planted_per_kv_head=0,
+              lens_range=(300, 900), delta=1.5)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "gauss_mass")
+    for b, g in all_pairs(w):
+        check_pair(inp, gpu, b, g, "gauss_mass")
+        assert int(gpu["n_sel"][b, g]) == 1
+
+
 def test_gauss_est_guard_keeps_argmax():
     # the guard case of the box-bound reading, with tau-hat also above
     # m + e_16 sigma: F(m + e_16 sigma) = 16 * 40 * sigma * I_1(-e_16) ~ 2.5 > 1
@@ -160,14 +184,14 @@ def test_gauss_est_guard_keeps_argmax():
         assert int(gpu["n_sel"][b, g]) == 1 and int(gpu["sel"][b, g, 0]) == 0
 
 
-@pytest.mark.parametrize("policy,alpha", [("gauss", 2.0), ("gauss_est", 1.5)])
+@pytest.mark.parametrize("policy,alpha", [("gauss", 2.0), ("gauss_est", 1.5), ("gauss_mass", 2.0)])
 def test_gauss_long_rows(policy, alpha):
     # pages of 2 tokens, rows of 4500-6000 pages: the tau-hat kernel's variant
     # that reads the moments from global memory (> 4096 pages) and the marking
     # kernel's compaction over several 4096-page chunks
     w = small(161, page_size=2, lens_range=(9000, 12000), num_q_heads=4, num_kv_heads=2,
               head_dim=64, q_std=2.0 / 8.0, alpha=alpha, policy=policy, clusters=16,
-              planted_per_kv_head=0, delta=0.1, batch=2)
+              planted_per_kv_head=0, delta=1e-5 if policy == "gauss_mass" else 0.1, batch=2)
     inp = wl.make_inputs(w, device=DEV)
     assert min(inp["npages"]) > 4096
     gpu = run_gpu(inp, policy)
@@ -257,10 +281,11 @@ def test_page_pruning_is_exact_shapes(kw):
     check_pair(inp, pruned, w.batch - 1, w.num_kv_heads - 1, "topk")
 
 
-@pytest.mark.parametrize("policy", ["gauss", "gauss_est"])
+@pytest.mark.parametrize("policy", ["gauss", "gauss_est", "gauss_mass"])
 def test_page_pruning_is_exact_gaussian(policy):
     # pruning over the Gaussian policies' selections (clustered keys, alpha 2)
-    w = small(191, lens_range=(1500, 4000), alpha=2.0, policy=policy, delta=0.1,
+    w = small(191, lens_range=(1500, 4000), alpha=2.0, policy=policy,
+              delta=1e-4 if policy == "gauss_mass" else 0.1,
               planted_per_kv_head=0, clusters=64, cluster_sigma=0.5)
     inp = wl.make_inputs(w, device=DEV)
     plain = run_gpu(inp, policy, prune=False)
@@ -389,13 +414,15 @@ def test_topk_long_rows(lens):
 
 
 @pytest.mark.parametrize("policy,prune", [("topk", True), ("topk", False), ("gauss", False),
-                                          ("gauss_est", True), ("dense", False)])
+                                          ("gauss_est", True), ("gauss_mass", False),
+                                          ("dense", False)])
 def test_edge_empty_rows(policy, prune):
     # idle batch slots (seq_len 0) next to rows with tokens: the empty rows get
     # n_sel = 0, a zero output, tau NaN and support 0; the other rows are those
     # of the oracle
-    gauss = policy in ("gauss", "gauss_est")
+    gauss = policy in ("gauss", "gauss_est", "gauss_mass")
     w = small(211, batch=5, lens_range=None, alpha=2.0 if gauss else 1.5, policy=policy,
+              delta=1e-3 if policy == "gauss_mass" else 0.1,
               planted_per_kv_head=0 if gauss else 8, clusters=64 if gauss else 0)
     inp = wl.make_inputs(w, device=DEV, lens=[0, 700, 0, 33, 1500])
     gpu = run_gpu(inp, policy, prune=prune)
