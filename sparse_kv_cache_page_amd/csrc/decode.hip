@@ -44,14 +44,41 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QkArgs<T> a, long long n_ite
   struct NoTail {};
   __shared__ std::conditional_t<kFused, TailLds, NoTail> tl;
   __shared__ int s_last;
-  for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
+  __shared__ int s_wmax[kBlock / kWave];
+  // the largest selection any pair uses, requested with the first item's loads
+  // and reduced before the second item: items past its split count
+  // (split-major numbering) are empty for every pair, so the loop stops there
+  // instead of paying a round trip per empty item when selections are far
+  // below max_sel
+  int mx = 0;
+  for (int p = threadIdx.x; p < a.npairs; p += kBlock) {
+    const int np = (a.lens[p / a.Hkv] + a.P - 1) / a.P;
+    mx = max(mx, min(a.sel ? a.n_sel[p] : np, a.max_sel));
+  }
+  long long n_used = n_items;
+  bool bounded = false;
+  for (long long item = blockIdx.x; item < n_used; item += gridDim.x) {
+    if (!bounded && item != (long long)blockIdx.x) {  // uniform over the block
+      bounded = true;
+      const int wm = (int)wave_max_u32((uint32_t)mx);  // mx >= 0
+      if (threadIdx.x % kWave == 0) s_wmax[threadIdx.x / kWave] = wm;
+      __syncthreads();
+      int m = s_wmax[0];
+#pragma unroll
+      for (int w = 1; w < kBlock / kWave; ++w) m = max(m, s_wmax[w]);
+      // split 0 of every pair is always visited: the fused variant writes
+      // the outputs of empty rows there
+      const long long used = max(1LL, (((long long)m << a.log2P) + kR - 1) / kR);
+      n_used = min(n_items, used * a.npairs);
+      if (item >= n_used) break;
+    }
     const QkItemInfo it = qk_item<T, D, G, kFused>(a, item, sm);
     if (!it.ran) {  // uniform over the block
       if constexpr (kFused) {
         // an empty row has no item to arrive: its first split writes the
         // outputs of the group's heads
-        const int pair = (int)(item / a.splits);
-        if (item % a.splits == 0 && a.lens[pair / a.Hkv] < 1) {
+        const int pair = (int)(item % a.npairs);
+        if (item / a.npairs == 0 && a.lens[pair / a.Hkv] < 1) {
 #pragma unroll
           for (int h = 0; h < G; ++h)
             empty_row_head(ta.out, ta.tau_out, ta.n_support, pair * G + h, D);
@@ -114,7 +141,8 @@ hipError_t launch_qk_t(const Shape& s, const DecodePlan& pl, const float* q, flo
   const long long grid = items < cap ? items : cap;
   const QkArgs<T> a{q,      zscale,  (const T*)K, bt,       lens,      sel,  n_sel,
                     pl.max_sel, s.Hkv, s.P,    s.log2P,  s.maxP,    pl.splits,
-                    cand,   cnt,     smax,        ub,       zlb,       a1};
+                    cand,   cnt,     smax,        ub,       zlb,       a1,
+                    (int)(s.B * s.Hkv)};
   hipLaunchKernelGGL((qk_kernel<T, D, G, kFused>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
                      a, items, ta);
   return hipGetLastError();

@@ -434,6 +434,7 @@ struct QkArgs {
   const float* ub;
   const float* zlb;
   float a1;  // alpha - 1
+  int npairs;  // B * Hkv
 };
 
 // A selected page whose tokens cannot reach z_max - 1 for any head of the
@@ -500,8 +501,12 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   (void)rg;
   (void)kRowsPerPass;
   QkItemInfo info{false, 0, 0, 0, 0, 0, 0};
-  const int pair = (int)(item / splits);
-  const int s = (int)(item % splits);
+  // split-major numbering: consecutive items are the same split of
+  // consecutive pairs, so a workgroup striding over the items visits many
+  // splits, and the low splits that short selections use spread over all
+  // workgroups (pair-major numbering gave workgroup i only split i % splits)
+  const int pair = (int)(item % a.npairs);
+  const int s = (int)(item / a.npairs);
   const int b = pair / Hkv;
   const int g = pair % Hkv;
   const int r_begin = s * kR;
