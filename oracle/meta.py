@@ -11,12 +11,16 @@ Readings taken where the page is silent:
   * moments are per coordinate (diagonal), the variance is the population
     variance (divide by n), over the page's valid tokens only;
   * k_min/k_max are exact (same dtype as the keys), mean/variance are stored
-    as fp32, rounded to nearest from the fp64 value.
+    as fp32, rounded to nearest from the fp64 value -- or, in the compact
+    format, as bf16, rounded once to nearest (ties to an even last bit) from
+    the fp64 value.
 
-Pins (tests/test_oracle_meta.py): bounding box by brute force (every key lies
+Pins (tests/test_oracle_meta_scores.py): bounding box by brute force (every key lies
 inside, every face is attained); moments of constructed pages with known
 closed-form mean and variance; a one-token page has k_min = k_max = k and zero
-variance.
+variance; the bf16 rounding against hand-worked ties and a value that rounding
+through fp32 first would get wrong, and on random values against both of its
+bf16 neighbours.
 """
 from __future__ import annotations
 
@@ -25,12 +29,36 @@ import math
 import numpy as np
 
 
-def page_meta(keys):
+def round_bf16(x):
+    """The bf16 value nearest to each fp64 x (ties to an even last bit), in fp64.
+
+    A bf16 number has 8 significant bits and the exponent range of fp32; below
+    2^-126 its spacing stays 2^-133.  With x = m 2^e, 0.5 <= m < 1, the
+    spacing at x is 2^(e-8): x / spacing is exact in fp64, rounded half-even
+    to an integer, and scaled back exactly.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(np.abs(x))
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    return np.round(x / q) * q                      # numpy rounds halves to even
+
+
+def store_moments(mean64, var64, moments: str = "f32"):
+    """Storage rounding of fp64 moments: 'f32' (nearest fp32) or 'bf16' (round_bf16)."""
+    if moments == "bf16":
+        return round_bf16(mean64).astype(np.float32), round_bf16(var64).astype(np.float32)
+    if moments != "f32":
+        raise ValueError(moments)
+    return np.asarray(mean64).astype(np.float32), np.asarray(var64).astype(np.float32)
+
+
+def page_meta(keys, moments: str = "f32"):
     """Metadata of one page from its valid keys.
 
     keys: array [n][d] (n >= 1) of the exact key values (fp64).
-    Returns (kmin, kmax, mean32, var32): kmin/kmax fp64 holding exact key
-    values, mean32/var32 float32 arrays.
+    Returns (kmin, kmax, mean, var): kmin/kmax fp64 holding exact key values,
+    mean/var float32 arrays holding the stored values (fp32, or bf16 values
+    with moments='bf16').
     """
     k = np.asarray(keys, dtype=np.float64)
     n, d = k.shape
@@ -54,10 +82,10 @@ def page_meta(keys):
         mu = math.fsum(col) / n
         mean64[j] = mu
         var64[j] = math.fsum((col - mu) ** 2) / n
-    return kmin, kmax, mean64.astype(np.float32), var64.astype(np.float32)
+    return (kmin, kmax) + store_moments(mean64, var64, moments)
 
 
-def page_meta_fast(keys):
+def page_meta_fast(keys, moments: str = "f32"):
     """Same quantities as page_meta, vectorised over pages.
 
     keys: [npages][n][d] with the same n valid tokens in every page.  Uses
@@ -71,4 +99,4 @@ def page_meta_fast(keys):
     kmax = k.max(axis=1)
     mu = k.sum(axis=1) / n
     var = ((k - mu[:, None, :]) ** 2).sum(axis=1) / n
-    return kmin, kmax, mu.astype(np.float32), var.astype(np.float32)
+    return (kmin, kmax) + store_moments(mu, var, moments)

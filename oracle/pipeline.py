@@ -51,21 +51,21 @@ def pair_keys_values(inputs: dict, b: int, g: int):
     return phys, counts, keys, vals
 
 
-def pair_meta(keys, exact: bool = False):
-    """Metadata of every page of a pair (lists of kmin, kmax, mean32, var32)."""
+def pair_meta(keys, exact: bool = False, moments: str = "f32"):
+    """Metadata of every page of a pair (lists of kmin, kmax, mean, var)."""
     if exact:
-        out = [meta.page_meta(k) for k in keys]
+        out = [meta.page_meta(k, moments) for k in keys]
         return ([o[0] for o in out], [o[1] for o in out],
                 [o[2] for o in out], [o[3] for o in out])
     n_full = [i for i, k in enumerate(keys) if k.shape[0] == keys[0].shape[0]]
     res = [None] * len(keys)
     if n_full:
-        kmin, kmax, mu, var = meta.page_meta_fast(np.stack([keys[i] for i in n_full]))
+        kmin, kmax, mu, var = meta.page_meta_fast(np.stack([keys[i] for i in n_full]), moments)
         for j, i in enumerate(n_full):
             res[i] = (kmin[j], kmax[j], mu[j], var[j])
     for i, k in enumerate(keys):
         if res[i] is None:
-            res[i] = meta.page_meta(k)
+            res[i] = meta.page_meta(k, moments)
     return ([r[0] for r in res], [r[1] for r in res], [r[2] for r in res], [r[3] for r in res])
 
 
@@ -119,7 +119,8 @@ def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=Non
     phys, counts, keys, vals = pair_keys_values(inputs, b, g)
     n = len(phys)
     lap("read")
-    kmin, kmax, mu, var = pair_meta(keys, exact=exact_meta)
+    kmin, kmax, mu, var = pair_meta(keys, exact=exact_meta,
+                                    moments="bf16" if w.moments_bf16 else "f32")
     lap("meta")
 
     u = np.array([scores.box_bounds(qq[h], kmin, kmax, scale) for h in range(G)],

@@ -55,6 +55,7 @@ class Workload:
     planted_per_kv_head: int = 0     # planted high-score keys per (row, KV head)
     planted_literal: bool = False    # True: k = 3 q + noise; False: k = 3 q / q_std + noise
     planted_noise: float = 0.1
+    moments_bf16: bool = False       # page mean/variance stored as bf16 (else fp32)
     clusters: int = 0                # >0: clustered keys (centroids per KV head)
     cluster_sigma: float = 0.5
     permute_pool: bool = False

@@ -124,3 +124,59 @@ def test_gauss_moments_match_sampling():
     assert abs(sc.var() - v) < 0.02 * v
     m2, v2 = scores.gauss_moments(q, mu, s2, 0.5)
     assert abs(m2 - 0.5 * m) < 1e-12 * (1 + abs(m)) and abs(v2 - 0.25 * v) < 1e-12 * v
+
+
+def _bf16_values(x32):
+    # a float32 holds a bf16 value iff its low 16 bits are zero
+    return (np.asarray(x32, np.float32).view(np.uint32) & 0xFFFF) == 0
+
+
+def test_round_bf16_hand_cases():
+    r = meta.round_bf16
+    e = 2.0 ** -7                        # bf16 spacing in [1, 2)
+    assert r(1.0) == 1.0 and r(0.0) == 0.0 and r(-2.5) == -2.5
+    assert r(1 + e / 2) == 1.0           # tie between 1 and 1 + e -> even (1)
+    assert r(1 + 3 * e / 2) == 1 + 2 * e  # tie between 1 + e (odd) and 1 + 2e (even)
+    assert r(1 + e / 2 + 2.0 ** -40) == 1 + e   # just above the tie
+    # rounding through fp32 first would land on the tie and then go to 1.0
+    x = 1 + e / 2 + 2.0 ** -30
+    assert float(np.float32(x)) == 1 + e / 2
+    assert r(x) == 1 + e
+    assert r(-(1 + e / 2 + 2.0 ** -30)) == -(1 + e)
+    # the spacing below 2^-126 stays 2^-133
+    assert r(2.0 ** -133 * 5.5) == 2.0 ** -133 * 6
+    assert r(2.0 ** -133 * 0.5) == 0.0
+    assert r(255.5 * 2.0 ** -7) == 2.0          # carries into the next binade
+
+
+def test_round_bf16_is_nearest_on_random_values():
+    rng = np.random.default_rng(7)
+    x = rng.normal(0, 1, 20000) * np.exp2(rng.integers(-40, 40, 20000))
+    r = meta.round_bf16(x)
+    assert np.all(_bf16_values(r.astype(np.float32)))
+    assert np.array_equal(r.astype(np.float32).astype(np.float64), r)
+    # no bf16 value lies closer: compare with both neighbours of r
+    _, ex = np.frexp(np.abs(r))
+    sp = np.ldexp(1.0, np.maximum(ex - 8, -133))    # spacing above |r| ...
+    sp_lo = np.where(np.abs(r) == np.ldexp(0.5, ex), sp / 2, sp)   # ... and below at a power of 2
+    d = np.abs(x - r)
+    up = np.abs(x - (r + np.sign(x) * sp))
+    dn = np.abs(x - (r - np.sign(x) * sp_lo))
+    assert np.all(d <= up) and np.all(d <= dn)
+
+
+def test_bf16_moments_are_rounded_fp64_moments():
+    rng = np.random.default_rng(8)
+    keys = rng.normal(0, 1, (16, 64)).astype(np.float32).astype(np.float64)
+    kmin, kmax, mu32, var32 = meta.page_meta(keys, "f32")
+    kmin2, kmax2, mu16, var16 = meta.page_meta(keys, "bf16")
+    assert np.array_equal(kmin, kmin2) and np.array_equal(kmax, kmax2)
+    assert np.all(_bf16_values(mu16)) and np.all(_bf16_values(var16))
+    mu64 = keys.mean(axis=0)
+    var64 = ((keys - mu64) ** 2).mean(axis=0)
+    # within half a bf16 spacing of the fp64 moments
+    for a, b in ((mu16, mu64), (var16, var64)):
+        _, ex = np.frexp(np.abs(b))
+        assert np.all(np.abs(a - b) <= np.ldexp(1.0, ex - 9) * (1 + 1e-12))
+    kminf, kmaxf, muf, varf = meta.page_meta_fast(keys[None], "bf16")
+    assert np.array_equal(muf[0], mu16) and np.array_equal(varf[0], var16)
