@@ -85,7 +85,8 @@ class Layer:
         inp = self.inp
         self.shape = CacheShape(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
                                 inp["max_pages"], inp["num_phys_pages"],
-                                torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32)
+                                torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32,
+                                torch.bfloat16 if w.moments_bf16 else torch.float32)
         self.dec = PagedEntmaxDecoder(self.shape, policy=w.policy, top_k=w.top_k,
                                       alpha=w.alpha, scale=w.scale, delta=w.delta, device=dev,
                                       fused=w.policy == "topk")
@@ -156,7 +157,8 @@ def stage_bytes(layer):
     lens = inp["lens"]
     npg = inp["npages"]
     last_valid = [L - (n - 1) * P for L, n in zip(lens, npg)]
-    meta_pp = 2 * d * e + (2 * d * 4 if gauss else 0)
+    mom_e = 2 if w.moments_bf16 else 4          # bytes per stored mean / variance value
+    meta_pp = 2 * d * e + (2 * d * mom_e if gauss else 0)
     refresh = sum(Hkv * (v * d * e + meta_pp) for v in last_valid)
     pages = sum(npg) * Hkv
     # per query head: ub (box-bound reading only) and the fp64 moments

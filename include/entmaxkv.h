@@ -38,7 +38,8 @@
  *        block_table   [B][max_pages_per_seq]        int32
  *        seq_lens      [B]                           int32
  *        kmin, kmax    [num_phys_pages][Hkv][d]      same dtype as K
- *        mean, var     [num_phys_pages][Hkv][d]      fp32
+ *        mean, var     [num_phys_pages][Hkv][d]      fp32, or bf16 with
+ *                                                    compact_moments
  *    Query head h reads KV head h / (Hq/Hkv) (contiguous query groups).
  *    Token t of logical page p of row b is valid when p*P + t < seq_lens[b];
  *    invalid slots of a row's last page are never read.
@@ -86,6 +87,8 @@ typedef struct {
   int32_t max_pages_per_seq; /* maxP, row stride of block_table and scores  */
   int32_t num_phys_pages;    /* Np, pages in the K/V pool                   */
   int32_t kv_dtype;          /* ekv_dtype of K, V, kmin, kmax               */
+  int32_t compact_moments;   /* 0: page mean/var fp32; 1: bf16 (each rounded
+                                once, to nearest even, from its fp64 value) */
 } ekv_cache_desc;
 
 /*
@@ -97,9 +100,12 @@ typedef struct {
  * first_page[b] + span (and p < ceil(seq_lens[b]/P)), over the page's valid
  * tokens, writes to physical page pi = block_table[b][p], KV head g:
  *   kmin[pi][g][j], kmax[pi][g][j]  exact per-coordinate min / max;
- *   mean[pi][g][j]                  (sum_t k_tj) / n, fp64 then rounded to fp32;
+ *   mean[pi][g][j]                  (sum_t k_tj) / n in fp64, rounded to fp32;
  *   var[pi][g][j]                   population variance (1/n) sum_t (k_tj - mean)^2,
- *                                   two-pass in fp64, rounded to fp32.
+ *                                   two-pass in fp64, rounded to fp32;
+ *   with desc->compact_moments = 1 both are rounded once from fp64 to the
+ *   nearest bf16 instead (ties to an even last bit; half the bytes the
+ *   Gaussian scorer reads for them).
  * first_page: device int32 [B] or NULL (= 0 for every row).
  * span: pages per row to (re)build; span <= 0 means max_pages_per_seq.
  *       span = 1 with first_page[b] = last page refreshes the page a decode
@@ -109,7 +115,7 @@ typedef struct {
 ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
                                const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* first_page, int32_t span,
-                               void* kmin, void* kmax, float* mean, float* var,
+                               void* kmin, void* kmax, void* mean, void* var,
                                hipStream_t stream);
 
 /*
@@ -132,7 +138,7 @@ ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
  */
 ekv_status ekv_append_token(const ekv_cache_desc* desc, const void* k_new, const void* v_new,
                             const int32_t* block_table, const int32_t* seq_lens, void* K,
-                            void* V, void* kmin, void* kmax, float* mean, float* var,
+                            void* V, void* kmin, void* kmax, void* mean, void* var,
                             hipStream_t stream);
 
 /*
@@ -153,7 +159,7 @@ ekv_status ekv_append_token(const ekv_cache_desc* desc, const void* k_new, const
  */
 ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float scale,
                            const void* kmin, const void* kmax,
-                           const float* mean, const float* var,
+                           const void* mean, const void* var,
                            const int32_t* block_table, const int32_t* seq_lens,
                            float* ub, float* ubg, double* gm, double* gv,
                            hipStream_t stream);

@@ -49,6 +49,7 @@ class CacheDesc(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("num_phys_pages", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
+        ("compact_moments", ctypes.c_int32),
     ]
 
 
@@ -137,6 +138,7 @@ class CacheShape:
     max_pages_per_seq: int
     num_phys_pages: int
     kv_dtype: torch.dtype = torch.bfloat16
+    moments_dtype: torch.dtype = torch.float32   # page mean/var: float32 or bfloat16
 
     @property
     def group(self) -> int:
@@ -145,9 +147,12 @@ class CacheShape:
     def desc(self) -> CacheDesc:
         if self.kv_dtype not in (torch.bfloat16, torch.float32):
             raise TypeError("K/V must be bfloat16 or float32")
+        if self.moments_dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("page moments must be float32 or bfloat16")
         return CacheDesc(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
                          self.page_size, self.max_pages_per_seq, self.num_phys_pages,
-                         EKV_BF16 if self.kv_dtype == torch.bfloat16 else EKV_F32)
+                         EKV_BF16 if self.kv_dtype == torch.bfloat16 else EKV_F32,
+                         1 if self.moments_dtype == torch.bfloat16 else 0)
 
 
 def _need(t: torch.Tensor, name: str, dtype, shape):
@@ -177,8 +182,8 @@ def build_page_meta(s: CacheShape, K, block_table, seq_lens, kmin, kmax, mean=No
     _need(kmin, "kmin", s.kv_dtype, mshape)
     _need(kmax, "kmax", s.kv_dtype, mshape)
     if mean is not None or var is not None:
-        _need(mean, "mean", torch.float32, mshape)
-        _need(var, "var", torch.float32, mshape)
+        _need(mean, "mean", s.moments_dtype, mshape)
+        _need(var, "var", s.moments_dtype, mshape)
     if first_page is not None:
         _need(first_page, "first_page", torch.int32, (s.batch,))
     d = s.desc()
@@ -202,8 +207,8 @@ def append_token(s: CacheShape, k_new, v_new, block_table, seq_lens, K, V, kmin,
     _need(kmin, "kmin", s.kv_dtype, mshape)
     _need(kmax, "kmax", s.kv_dtype, mshape)
     if mean is not None or var is not None:
-        _need(mean, "mean", torch.float32, mshape)
-        _need(var, "var", torch.float32, mshape)
+        _need(mean, "mean", s.moments_dtype, mshape)
+        _need(var, "var", s.moments_dtype, mshape)
     d = s.desc()
     _check("ekv_append_token", load_library().ekv_append_token(
         ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(seq_lens), _ptr(K),
@@ -226,8 +231,8 @@ def score_pages(s: CacheShape, q, scale: float, kmin, kmax, block_table, seq_len
     if gm is not None or gv is not None:
         _need(gm, "gm", torch.float64, (B, Hq, mp))
         _need(gv, "gv", torch.float64, (B, Hq, mp))
-        _need(mean, "mean", torch.float32, mshape)
-        _need(var, "var", torch.float32, mshape)
+        _need(mean, "mean", s.moments_dtype, mshape)
+        _need(var, "var", s.moments_dtype, mshape)
     d_ = s.desc()
     _check("ekv_score_pages", load_library().ekv_score_pages(
         ctypes.byref(d_), _ptr(q), float(scale), _ptr(kmin), _ptr(kmax), _ptr(mean), _ptr(var),

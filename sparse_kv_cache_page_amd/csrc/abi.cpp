@@ -26,6 +26,7 @@ ekv_status make_shape(const ekv_cache_desc* d, Shape* s) {
     return EKV_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return EKV_ERR_INVALID_ARG;
   if (d->kv_dtype != EKV_BF16 && d->kv_dtype != EKV_F32) return EKV_ERR_INVALID_ARG;
+  if (d->compact_moments != 0 && d->compact_moments != 1) return EKV_ERR_INVALID_ARG;
   const int G = d->num_q_heads / d->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return EKV_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return EKV_ERR_UNSUPPORTED;
@@ -43,6 +44,7 @@ ekv_status make_shape(const ekv_cache_desc* d, Shape* s) {
   s->maxP = d->max_pages_per_seq;
   s->Np = d->num_phys_pages;
   s->bf16 = d->kv_dtype == EKV_BF16;
+  s->mom16 = d->compact_moments == 1;
   return EKV_OK;
 }
 
@@ -72,7 +74,7 @@ double ekv_gauss_expected_max(int32_t n) { return ekv::expected_max_std_normal(n
 ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
                                const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* first_page, int32_t span, void* kmin, void* kmax,
-                               float* mean, float* var, hipStream_t stream) {
+                               void* mean, void* var, hipStream_t stream) {
   Shape s;
   ekv_status st = make_shape(desc, &s);
   if (st != EKV_OK) return st;
@@ -88,7 +90,7 @@ ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
 
 ekv_status ekv_append_token(const ekv_cache_desc* desc, const void* k_new, const void* v_new,
                             const int32_t* block_table, const int32_t* seq_lens, void* K,
-                            void* V, void* kmin, void* kmax, float* mean, float* var,
+                            void* V, void* kmin, void* kmax, void* mean, void* var,
                             hipStream_t stream) {
   Shape s;
   ekv_status st = make_shape(desc, &s);
@@ -103,8 +105,8 @@ ekv_status ekv_append_token(const ekv_cache_desc* desc, const void* k_new, const
 }
 
 ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float scale,
-                           const void* kmin, const void* kmax, const float* mean,
-                           const float* var, const int32_t* block_table,
+                           const void* kmin, const void* kmax, const void* mean,
+                           const void* var, const int32_t* block_table,
                            const int32_t* seq_lens, float* ub, float* ubg, double* gm,
                            double* gv, hipStream_t stream) {
   Shape s;

@@ -301,10 +301,10 @@ __device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int 
 // Metadata of one (physical page pi, KV head g) tile with nv valid tokens,
 // computed by one wave (all 64 lanes call it): exact per-coordinate min/max,
 // mean and population variance (two passes, fp64 sums, one rounding to fp32).
-template <typename T, int D>
+template <typename T, int D, typename M = float>
 __device__ __forceinline__ void meta_tile(const T* __restrict__ K, int Hkv, int P, int pi, int g,
                                           int nv, T* __restrict__ kmin, T* __restrict__ kmax,
-                                          float* __restrict__ mean, float* __restrict__ var) {
+                                          M* __restrict__ mean, M* __restrict__ var) {
   constexpr int kVec = Elem<T>::kVec;
   constexpr int kLpr = D / kVec;      // lanes per key row
   constexpr int kRows = kWave / kLpr; // rows per wave instruction
@@ -401,13 +401,30 @@ __device__ __forceinline__ void meta_tile(const T* __restrict__ K, int Hkv, int 
     *reinterpret_cast<float4*>(kmax + m_off) = make_float4(mx[0], mx[1], mx[2], mx[3]);
   }
   if (mean != nullptr) {
+    if constexpr (sizeof(M) == 2) {
+      // compact moments: each fp64 value rounded once to bf16, two per word
+      uint32_t wm[kVec / 2], wv[kVec / 2];
 #pragma unroll
-    for (int v = 0; v < kVec; v += 4) {
-      *reinterpret_cast<float4*>(mean + m_off + v) =
-          make_float4((float)mu[v], (float)mu[v + 1], (float)mu[v + 2], (float)mu[v + 3]);
-      *reinterpret_cast<float4*>(var + m_off + v) = make_float4(
-          (float)(sq[v] / nv), (float)(sq[v + 1] / nv), (float)(sq[v + 2] / nv),
-          (float)(sq[v + 3] / nv));
+      for (int i = 0; i < kVec / 2; ++i) {
+        wm[i] = bf16_bits_rn(mu[2 * i]) | (bf16_bits_rn(mu[2 * i + 1]) << 16);
+        wv[i] = bf16_bits_rn(sq[2 * i] / nv) | (bf16_bits_rn(sq[2 * i + 1] / nv) << 16);
+      }
+      if constexpr (kVec == 8) {
+        *reinterpret_cast<uint4*>(mean + m_off) = make_uint4(wm[0], wm[1], wm[2], wm[3]);
+        *reinterpret_cast<uint4*>(var + m_off) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      } else {
+        *reinterpret_cast<uint2*>(mean + m_off) = make_uint2(wm[0], wm[1]);
+        *reinterpret_cast<uint2*>(var + m_off) = make_uint2(wv[0], wv[1]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < kVec; v += 4) {
+        *reinterpret_cast<float4*>(mean + m_off + v) =
+            make_float4((float)mu[v], (float)mu[v + 1], (float)mu[v + 2], (float)mu[v + 3]);
+        *reinterpret_cast<float4*>(var + m_off + v) = make_float4(
+            (float)(sq[v] / nv), (float)(sq[v + 1] / nv), (float)(sq[v + 2] / nv),
+            (float)(sq[v + 3] / nv));
+      }
     }
   }
 }

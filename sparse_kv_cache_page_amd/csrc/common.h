@@ -236,6 +236,20 @@ __device__ inline int wave_sum_i32(int x) {
   return wave_reduce_b32(x, [](int a, int b) { return a + b; });
 }
 
+// The bf16 value nearest to an fp64 value (ties to an even last bit), as its
+// 16-bit pattern, rounded once: the value is first truncated to fp32 with
+// the last bit set when anything was dropped (round to odd), which keeps 16
+// more bits than bf16 and marks inexact values, so the round to nearest even
+// that follows sees the true position of x and cannot land on a false tie.
+// For finite x within the fp32 range.
+__device__ inline uint32_t bf16_bits_rn(double x) {
+  const float f = __double2float_rz(x);
+  uint32_t u = __float_as_uint(f);
+  u |= (double)f != x ? 1u : 0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
 // Number of valid tokens of logical page p in a row of length L.
 __device__ inline int page_valid(int L, int p, int P) {
   const int r = L - p * P;

@@ -13,7 +13,8 @@ constexpr int kMaxPageSize = 64;  // largest supported tokens per page
 
 struct Shape {
   int B, Hq, Hkv, G, D, P, log2P, maxP, Np;
-  bool bf16;
+  bool bf16;   // K, V, kmin, kmax in bf16 (else fp32)
+  bool mom16;  // page mean/var in bf16 (else fp32)
 };
 
 // Decode-time append of the token at position lens[b] - 1 of every row: K/V
@@ -21,15 +22,15 @@ struct Shape {
 // are given).
 hipError_t launch_append(const Shape& s, const void* k_new, const void* v_new,
                          const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,
-                         void* kmax, float* mean, float* var, hipStream_t stream);
+                         void* kmax, void* mean, void* var, hipStream_t stream);
 
 hipError_t launch_build_meta(const Shape& s, const void* K, const int32_t* bt,
                              const int32_t* lens, const int32_t* first_page, int span,
-                             void* kmin, void* kmax, float* mean, float* var,
+                             void* kmin, void* kmax, void* mean, void* var,
                              hipStream_t stream);
 
 hipError_t launch_score(const Shape& s, const float* q, float scale, const void* kmin,
-                        const void* kmax, const float* mean, const float* var,
+                        const void* kmax, const void* mean, const void* var,
                         const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
                         double* gm, double* gv, hipStream_t stream);
 

@@ -14,12 +14,11 @@
 namespace ekv {
 namespace {
 
-template <typename T, int D>
+template <typename T, int D, typename M>
 __global__ __launch_bounds__(256) void build_meta_kernel(
     const T* __restrict__ K, const int32_t* __restrict__ bt, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ first_page, int span, int B, int Hkv, int P, int maxP,
-    T* __restrict__ kmin, T* __restrict__ kmax, float* __restrict__ mean,
-    float* __restrict__ var) {
+    T* __restrict__ kmin, T* __restrict__ kmax, M* __restrict__ mean, M* __restrict__ var) {
   const int wave = threadIdx.x / kWave;
   const long long tile = (long long)blockIdx.x * 4 + wave;
   const int g = (int)(tile % Hkv);
@@ -31,19 +30,20 @@ __global__ __launch_bounds__(256) void build_meta_kernel(
   const int np = (L + P - 1) / P;
   const int p = (first_page ? first_page[b] : 0) + pr;
   if (p < 0 || p >= np) return;
-  meta_tile<T, D>(K, Hkv, P, bt[(size_t)b * maxP + p], g, page_valid(L, p, P), kmin, kmax, mean, var);
+  meta_tile<T, D, M>(K, Hkv, P, bt[(size_t)b * maxP + p], g, page_valid(L, p, P), kmin, kmax,
+                     mean, var);
 }
 
-template <typename T, int D>
+template <typename T, int D, typename M>
 hipError_t launch_meta_t(const Shape& s, const void* K, const int32_t* bt, const int32_t* lens,
                          const int32_t* first_page, int span, void* kmin, void* kmax,
-                         float* mean, float* var, hipStream_t stream) {
+                         void* mean, void* var, hipStream_t stream) {
   const long long tiles = (long long)s.B * span * s.Hkv;
   const long long blocks = (tiles + 3) / 4;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((build_meta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((build_meta_kernel<T, D, M>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const T*)K, bt, lens, first_page, span, s.B, s.Hkv, s.P, s.maxP, (T*)kmin,
-                     (T*)kmax, mean, var);
+                     (T*)kmax, (M*)mean, (M*)var);
   return hipGetLastError();
 }
 
@@ -56,12 +56,12 @@ hipError_t launch_meta_t(const Shape& s, const void* K, const int32_t* bt, const
 // as ekv_build_page_meta does; a workgroup-scope release/acquire pair makes
 // the new row, stored by this wave's lanes, visible to the lanes that read it
 // back (all lanes of a workgroup share one CU's vector L1).
-template <typename T, int D>
+template <typename T, int D, typename M>
 __global__ __launch_bounds__(256) void append_kernel(
     const T* __restrict__ k_new, const T* __restrict__ v_new, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ lens, int B, int Hkv, int P, int maxP, T* __restrict__ K,
-    T* __restrict__ V, T* __restrict__ kmin, T* __restrict__ kmax, float* __restrict__ mean,
-    float* __restrict__ var) {
+    T* __restrict__ V, T* __restrict__ kmin, T* __restrict__ kmax, M* __restrict__ mean,
+    M* __restrict__ var) {
   constexpr int kVec = Elem<T>::kVec;
   constexpr int kLpr = D / kVec;
   const int lane = threadIdx.x % kWave;
@@ -118,49 +118,59 @@ __global__ __launch_bounds__(256) void append_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __builtin_amdgcn_wave_barrier();
-    meta_tile<T, D>(K, Hkv, P, pi, g, slot + 1, kmin, kmax, mean, var);
+    meta_tile<T, D, M>(K, Hkv, P, pi, g, slot + 1, kmin, kmax, mean, var);
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, typename M>
 hipError_t launch_append_t(const Shape& s, const void* k_new, const void* v_new,
                            const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,
-                           void* kmax, float* mean, float* var, hipStream_t stream) {
+                           void* kmax, void* mean, void* var, hipStream_t stream) {
   const long long units = (long long)s.B * s.Hkv;
   const long long blocks = (units + 3) / 4;
-  hipLaunchKernelGGL((append_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((append_kernel<T, D, M>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const T*)k_new, (const T*)v_new, bt, lens, s.B, s.Hkv, s.P, s.maxP, (T*)K,
-                     (T*)V, (T*)kmin, (T*)kmax, mean, var);
+                     (T*)V, (T*)kmin, (T*)kmax, (M*)mean, (M*)var);
   return hipGetLastError();
 }
+
+// K dtype x head dim x moment dtype
+template <template <typename, int, typename> class F, typename... A>
+hipError_t dispatch_meta(const Shape& s, A... args) {
+  if (s.bf16) {
+    if (s.D == 128)
+      return s.mom16 ? F<bf16_t, 128, bf16_t>::run(s, args...) : F<bf16_t, 128, float>::run(s, args...);
+    return s.mom16 ? F<bf16_t, 64, bf16_t>::run(s, args...) : F<bf16_t, 64, float>::run(s, args...);
+  }
+  if (s.D == 128)
+    return s.mom16 ? F<float, 128, bf16_t>::run(s, args...) : F<float, 128, float>::run(s, args...);
+  return s.mom16 ? F<float, 64, bf16_t>::run(s, args...) : F<float, 64, float>::run(s, args...);
+}
+
+template <typename T, int D, typename M>
+struct AppendOp {
+  template <typename... A>
+  static hipError_t run(const Shape& s, A... args) { return launch_append_t<T, D, M>(s, args...); }
+};
+template <typename T, int D, typename M>
+struct MetaOp {
+  template <typename... A>
+  static hipError_t run(const Shape& s, A... args) { return launch_meta_t<T, D, M>(s, args...); }
+};
 
 }  // namespace
 
 hipError_t launch_append(const Shape& s, const void* k_new, const void* v_new,
                          const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,
-                         void* kmax, float* mean, float* var, hipStream_t stream) {
-  if (s.bf16) {
-    if (s.D == 128)
-      return launch_append_t<bf16_t, 128>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
-    return launch_append_t<bf16_t, 64>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
-  }
-  if (s.D == 128)
-    return launch_append_t<float, 128>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
-  return launch_append_t<float, 64>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
+                         void* kmax, void* mean, void* var, hipStream_t stream) {
+  return dispatch_meta<AppendOp>(s, k_new, v_new, bt, lens, K, V, kmin, kmax, mean, var, stream);
 }
 
 hipError_t launch_build_meta(const Shape& s, const void* K, const int32_t* bt,
                              const int32_t* lens, const int32_t* first_page, int span,
-                             void* kmin, void* kmax, float* mean, float* var,
+                             void* kmin, void* kmax, void* mean, void* var,
                              hipStream_t stream) {
-  if (s.bf16) {
-    if (s.D == 128)
-      return launch_meta_t<bf16_t, 128>(s, K, bt, lens, first_page, span, kmin, kmax, mean, var, stream);
-    return launch_meta_t<bf16_t, 64>(s, K, bt, lens, first_page, span, kmin, kmax, mean, var, stream);
-  }
-  if (s.D == 128)
-    return launch_meta_t<float, 128>(s, K, bt, lens, first_page, span, kmin, kmax, mean, var, stream);
-  return launch_meta_t<float, 64>(s, K, bt, lens, first_page, span, kmin, kmax, mean, var, stream);
+  return dispatch_meta<MetaOp>(s, K, bt, lens, first_page, span, kmin, kmax, mean, var, stream);
 }
 
 }  // namespace ekv

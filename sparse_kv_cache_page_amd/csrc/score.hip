@@ -104,10 +104,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (slot, c) adds column c of the kLpr rows of its page slot in a fixed order,
 // so every (page, head) total is finished by one lane, and the group maximum
 // is taken over the G lanes that hold one page's heads.
-template <typename T, int D, int G, int kVec, bool kGauss, bool kCoherentU = false>
+template <typename T, int D, int G, int kVec, bool kGauss, bool kCoherentU = false,
+          typename M = float>
 __device__ __forceinline__ void score_range(
     const float* __restrict__ q, float scale, const T* __restrict__ kmin,
-    const T* __restrict__ kmax, const float* __restrict__ mean, const float* __restrict__ var,
+    const T* __restrict__ kmax, const M* __restrict__ mean, const M* __restrict__ var,
     const int* s_pi, int b, int g, int pair, int Hkv, int maxP, int p_begin, int p_end,
     float* __restrict__ ub, float* __restrict__ ubg, double* __restrict__ gm,
     double* __restrict__ gv, double (*red)[ScoreGeo<D, G, kVec, kGauss>::kPitch]) {
@@ -119,7 +120,7 @@ __device__ __forceinline__ void score_range(
   constexpr int kKinds = Geo::kKinds;
   constexpr int kM = Geo::kM;
   constexpr int kRawBytes = kVec * (int)sizeof(T);
-  constexpr int kMomRaw = kVec * 4;   // bytes of fp32 mean (or var) per lane
+  constexpr int kMomRaw = kVec * (int)sizeof(M);   // bytes of mean (or var) per lane
   using Raw = RawT<kRawBytes>;
   static_assert(kLpr % G == 0, "a page's heads sit in aligned lane groups");
   const int Hq = Hkv * G;
@@ -155,7 +156,23 @@ __device__ __forceinline__ void score_range(
       const size_t off = ((size_t)s_pi[pl] * Hkv + g) * D + c * kVec;
       bt_.lo[u] = Raw::load(kmin + off);
       bt_.hi[u] = Raw::load(kmax + off);
-      if constexpr (kGauss) {
+      if constexpr (kGauss && sizeof(M) == 2) {
+        // compact (bf16) moments: kVec values in 2 kVec bytes
+        if constexpr (kMomRaw == 16) {
+          Elem<bf16_t>::unpack(load16_stream(mean + off), bt_.mu[u]);
+          Elem<bf16_t>::unpack(load16_stream(var + off), bt_.s2[u]);
+        } else if constexpr (kMomRaw == 8) {
+          Unpack<bf16_t, 4>::run(load8_stream(mean + off), bt_.mu[u]);
+          Unpack<bf16_t, 4>::run(load8_stream(var + off), bt_.s2[u]);
+        } else {
+          const uint32_t wm = *reinterpret_cast<const uint32_t*>(mean + off);
+          const uint32_t wv = *reinterpret_cast<const uint32_t*>(var + off);
+          bt_.mu[u][0] = __uint_as_float(wm << 16);
+          bt_.mu[u][1] = __uint_as_float(wm & 0xffff0000u);
+          bt_.s2[u][0] = __uint_as_float(wv << 16);
+          bt_.s2[u][1] = __uint_as_float(wv & 0xffff0000u);
+        }
+      } else if constexpr (kGauss) {
         if constexpr (kMomRaw == 32) {
           Elem<float>::unpack(load16_stream(mean + off), bt_.mu[u]);
           Elem<float>::unpack(load16_stream(mean + off + 4), bt_.mu[u] + 4);
@@ -279,10 +296,10 @@ int slice_pages(const Shape& s, int per_iter) {
   return per_iter * iters;
 }
 
-template <typename T, int D, int G, int kVec, bool kGauss>
+template <typename T, int D, int G, int kVec, bool kGauss, typename M = float>
 __global__ __launch_bounds__(kScoreBlock) void score_kernel(
     const float* __restrict__ q, float scale, const T* __restrict__ kmin,
-    const T* __restrict__ kmax, const float* __restrict__ mean, const float* __restrict__ var,
+    const T* __restrict__ kmax, const M* __restrict__ mean, const M* __restrict__ var,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens, int Hkv, int P, int maxP,
     int pages_per_block, int npairs, float* __restrict__ ub, float* __restrict__ ubg,
     double* __restrict__ gm, double* __restrict__ gv) {
@@ -302,7 +319,8 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
   if (p_begin >= np) return;
   const int p_end = min(np, p_begin + pages_per_block);
   __syncthreads();
-  score_range<T, D, G, kVec, kGauss>(q, scale, kmin, kmax, mean, var, s_pi, b, g, pair, Hkv, maxP,
+  score_range<T, D, G, kVec, kGauss, false, M>(q, scale, kmin, kmax, mean, var, s_pi, b, g, pair,
+                                               Hkv, maxP,
                                      p_begin, p_end, ub, ubg, gm, gv,
                                      red.v[threadIdx.x / kWave]);
 }
@@ -350,11 +368,12 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   if (refresh && p_end == np && threadIdx.x < kWave) {
     // only this workgroup reads the refreshed page's box: the barrier below
     // (which waits for the stores) is enough to publish it
-    meta_tile<T, D>(K, Hkv, P, bt[(size_t)b * maxP + np - 1], g, page_valid(L, np - 1, P), kmin,
-                    kmax, nullptr, nullptr);
+    meta_tile<T, D, float>(K, Hkv, P, bt[(size_t)b * maxP + np - 1], g,
+                           page_valid(L, np - 1, P), kmin, kmax, nullptr, nullptr);
   }
   __syncthreads();
-  score_range<T, D, G, kVec, false, true>(q, scale, kmin, kmax, nullptr, nullptr, s_pi, b, g, pair,
+  score_range<T, D, G, kVec, false, true, float>(q, scale, kmin, kmax, nullptr, nullptr, s_pi, b,
+                                                 g, pair,
                                           Hkv, maxP, p_begin, p_end, ub, ubg, nullptr,
                                           nullptr, sm.red.v[threadIdx.x / kWave]);
   // arrival: every wave waits until its device-coherent bound stores have
@@ -390,7 +409,7 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
 
 template <typename T, int D, int G, int kVec>
 hipError_t launch_score_t(const Shape& s, const float* q, float scale, const void* kmin,
-                          const void* kmax, const float* mean, const float* var,
+                          const void* kmax, const void* mean, const void* var,
                           const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
                           double* gm, double* gv, hipStream_t stream) {
   constexpr int kLpr = D / kVec;
@@ -406,31 +425,44 @@ hipError_t launch_score_t(const Shape& s, const float* q, float scale, const voi
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)nblocks);
   const int npairs = (int)pairs;
-  if (gauss) {
+  if (gauss && s.mom16) {
+    hipLaunchKernelGGL((score_kernel<T, D, G, kVec, true, bf16_t>), grid, dim3(kScoreBlock), 0,
+                       stream, q, scale, (const T*)kmin, (const T*)kmax, (const bf16_t*)mean,
+                       (const bf16_t*)var, bt, lens, s.Hkv, s.P, s.maxP, ppb, npairs, ub, ubg, gm,
+                       gv);
+  } else if (gauss) {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0, stream, q,
-                       scale, (const T*)kmin, (const T*)kmax, mean, var, bt, lens, s.Hkv, s.P,
-                       s.maxP, ppb, npairs, ub, ubg, gm, gv);
+                       scale, (const T*)kmin, (const T*)kmax, (const float*)mean,
+                       (const float*)var, bt, lens, s.Hkv, s.P, s.maxP, ppb, npairs, ub, ubg, gm,
+                       gv);
   } else {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, false>), grid, dim3(kScoreBlock), 0, stream,
-                       q, scale, (const T*)kmin, (const T*)kmax, mean, var, bt, lens, s.Hkv,
-                       s.P, s.maxP, ppb, npairs, ub, ubg, gm, gv);
+                       q, scale, (const T*)kmin, (const T*)kmax, (const float*)nullptr,
+                       (const float*)nullptr, bt, lens, s.Hkv, s.P, s.maxP, ppb, npairs, ub, ubg,
+                       gm, gv);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_score_d(const Shape& s, const float* q, float scale, const void* kmin,
-                          const void* kmax, const float* mean, const float* var,
+                          const void* kmax, const void* mean, const void* var,
                           const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
                           double* gm, double* gv, hipStream_t stream) {
   // 16-byte loads while q+/q- fit comfortably in registers, 8-byte loads for
-  // the 8-head group (halves the per-lane coordinates, hence the registers)
+  // the 8-head group (halves the per-lane coordinates, hence the registers),
+  // and for the 4-head group when the Gaussian moments are summed too: with
+  // 16-byte loads that kernel needed 256 VGPRs + 104 AGPRs (one wave per
+  // SIMD); with 8-byte loads 234 VGPRs (two)
   constexpr int kV16 = 16 / sizeof(T);
   constexpr int kV8 = 8 / sizeof(T);
   switch (s.G) {
     case 1: return launch_score_t<T, D, 1, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
     case 2: return launch_score_t<T, D, 2, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
-    case 4: return launch_score_t<T, D, 4, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
+    case 4:
+      if (gm != nullptr)
+        return launch_score_t<T, D, 4, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
+      return launch_score_t<T, D, 4, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
     case 8: return launch_score_t<T, D, 8, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
   }
   return hipErrorInvalidValue;
@@ -480,7 +512,7 @@ hipError_t launch_score_select_d(const Shape& s, const float* q, float scale, co
 }  // namespace
 
 hipError_t launch_score(const Shape& s, const float* q, float scale, const void* kmin,
-                        const void* kmax, const float* mean, const float* var,
+                        const void* kmax, const void* mean, const void* var,
                         const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
                         double* gm, double* gv, hipStream_t stream) {
   if (s.bf16) {

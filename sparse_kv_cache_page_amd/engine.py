@@ -43,8 +43,9 @@ class PagedEntmaxDecoder:
         gauss = policy in ("gauss", "gauss_est", "gauss_mass")
         self.kmin = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
         self.kmax = torch.empty(Np, Hkv, d, dtype=s.kv_dtype, device=dev)
-        self.mean = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
-        self.var = torch.empty(Np, Hkv, d, dtype=torch.float32, device=dev) if gauss else None
+        md = s.moments_dtype
+        self.mean = torch.empty(Np, Hkv, d, dtype=md, device=dev) if gauss else None
+        self.var = torch.empty(Np, Hkv, d, dtype=md, device=dev) if gauss else None
         self.ubg = torch.empty(Bt, Hkv, mp, dtype=torch.float32, device=dev)
         # per-head page bounds: read by the box-bound Gaussian rule, and by the
         # decode's page pruning.  Pruning is on by default for top-k only: the

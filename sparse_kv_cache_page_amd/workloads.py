@@ -99,6 +99,12 @@ CONFIGS = {
                        page_size=16, seq_len=32768, kv_dtype="bf16",
                        q_std=2.0 / math.sqrt(128), scale=1.0, alpha=2.0, policy="gauss_mass",
                        delta=1e-4, clusters=64, cluster_sigma=0.5, seed=3003),
+    # the same with the compact metadata format (bf16 page mean / variance)
+    "gauss_mass_m16": _cfg(name="gauss_mass_m16", batch=8, num_q_heads=32, num_kv_heads=8,
+                           head_dim=128, page_size=16, seq_len=32768, kv_dtype="bf16",
+                           q_std=2.0 / math.sqrt(128), scale=1.0, alpha=2.0,
+                           policy="gauss_mass", delta=1e-4, clusters=64, cluster_sigma=0.5,
+                           moments_bf16=True, seed=3003),
     "ragged": _cfg(name="ragged", batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
                    page_size=16, lens_range=(4096, 65536), kv_dtype="bf16",
                    q_std=2.0 / math.sqrt(128), scale=1.0, alpha=1.5, policy="topk",

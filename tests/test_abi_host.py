@@ -221,6 +221,15 @@ def test_binding_rejects_cpu_tensors(lib):
                           torch.zeros(4, 1, 64))
 
 
+def test_compact_moments_flag(lib):
+    # compact_moments selects the moments' storage (0 fp32, 1 bf16); other values are invalid
+    d = desc(compact_moments=2)
+    assert lib.ekv_build_page_meta(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None,
+                                   None, None) == INVALID
+    assert lib.ekv_score_select_workspace_bytes(ctypes.byref(d)) == 0
+    assert lib.ekv_score_select_workspace_bytes(ctypes.byref(desc(compact_moments=1))) > 0
+
+
 def test_step_argument_errors(lib):
     d = desc()
     need = lib.ekv_step_workspace_bytes(ctypes.byref(d), 4)

@@ -39,7 +39,7 @@ def small(seed, **kw):
 @pytest.mark.parametrize("kw", [
     dict(), dict(num_q_heads=16, num_kv_heads=2), dict(kv_dtype="f32", head_dim=64),
     dict(page_size=1, lens_range=(5, 200)), dict(page_size=64, lens_range=(70, 1500)),
-    dict(num_q_heads=4, num_kv_heads=4, page_size=32),
+    dict(num_q_heads=4, num_kv_heads=4, page_size=32), dict(moments_bf16=True),
 ])
 def test_append_matches_full_build(kw, moments):
     w = small(701 + len(kw), **kw)
@@ -61,7 +61,7 @@ def test_append_matches_full_build(kw, moments):
             V[pi, :, t % P] = 0
     mshape = (s.num_phys_pages, s.num_kv_heads, s.head_dim)
     mk = lambda dt: torch.zeros(mshape, dtype=dt, device=DEV)
-    meta = [mk(s.kv_dtype), mk(s.kv_dtype)] + ([mk(torch.float32), mk(torch.float32)]
+    meta = [mk(s.kv_dtype), mk(s.kv_dtype)] + ([mk(s.moments_dtype), mk(s.moments_dtype)]
                                                if moments else [None, None])
     B.build_page_meta(s, K, bt, start, *meta)
     cur = start.clone()
@@ -79,7 +79,7 @@ def test_append_matches_full_build(kw, moments):
     torch.cuda.synchronize()
     assert torch.equal(cur, lens)
     assert same_bits(K, K0) and same_bits(V, V0)
-    ref = [mk(s.kv_dtype), mk(s.kv_dtype)] + ([mk(torch.float32), mk(torch.float32)]
+    ref = [mk(s.kv_dtype), mk(s.kv_dtype)] + ([mk(s.moments_dtype), mk(s.moments_dtype)]
                                               if moments else [None, None])
     B.build_page_meta(s, K0, bt, lens, *ref)
     torch.cuda.synchronize()
@@ -96,12 +96,14 @@ def test_append_matches_full_build(kw, moments):
         pi = int(btc[b, p])
         nv = L - p * P
         for g in range(w.num_kv_heads):
-            kmin, kmax, mu, va = ometa.page_meta(Kc[pi, g, :nv])
+            kmin, kmax, mu, va = ometa.page_meta(Kc[pi, g, :nv],
+                                                 "bf16" if w.moments_bf16 else "f32")
             np.testing.assert_array_equal(pipeline.widen(meta[0][pi, g]), kmin)
             np.testing.assert_array_equal(pipeline.widen(meta[1][pi, g]), kmax)
             if moments:
-                assert ulp_dist(meta[2][pi, g].cpu().numpy(), mu).max() <= 1
-                assert ulp_dist(meta[3][pi, g].cpu().numpy(), va).max() <= 1
+                unit = 1 << 16 if w.moments_bf16 else 1     # one unit of the storage format
+                assert ulp_dist(meta[2][pi, g].float().cpu().numpy(), mu).max() <= unit
+                assert ulp_dist(meta[3][pi, g].float().cpu().numpy(), va).max() <= unit
 
 
 def test_append_then_step_equals_fresh_build():

@@ -103,6 +103,18 @@ def test_fullsize_gauss_mass():
     decoder_matches(inp, gpu, "gauss_mass", w.alpha, w.top_k, w.delta, w.scale, inp["q"])
 
 
+def test_fullsize_gauss_mass_compact_moments():
+    # the expected-mass rule on bf16 page moments (the compact metadata format)
+    w = wl.CONFIGS["gauss_mass_m16"]
+    print("[fullsize] gauss_mass_m16: generating", flush=True)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, "gauss_mass")
+    check_properties(inp, gpu, "gauss_mass", w.top_k)
+    for b, g in [(1, 1), (7, 6)]:
+        print(f"[fullsize] gauss_mass_m16: oracle pair b{b} g{g}", flush=True)
+        check_pair(inp, gpu, b, g, "gauss_mass")
+
+
 @pytest.fixture(scope="module")
 def stress_inputs():
     w = wl.CONFIGS["stress"]

@@ -102,10 +102,10 @@ def test_caller_page_list():
         check_pair(inp, gpu, b, g, "topk", sel_override=lists[(b, g)])
 
 
-@pytest.mark.parametrize("alpha", [2.0, 1.5, 1.25])
-def test_gauss_policy(alpha):
+@pytest.mark.parametrize("alpha,m16", [(2.0, False), (1.5, False), (1.25, False), (1.5, True)])
+def test_gauss_policy(alpha, m16):
     w = small(71, alpha=alpha, policy="gauss", clusters=16, planted_per_kv_head=0,
-              lens_range=(100, 1200), delta=0.1)
+              lens_range=(100, 1200), delta=0.1, moments_bf16=m16)
     inp = wl.make_inputs(w, device=DEV)
     gpu = run_gpu(inp, "gauss")
     for b, g in all_pairs(w):
@@ -132,25 +132,29 @@ def test_gauss_guard_keeps_argmax():
         assert int(gpu["n_sel"][b, g]) == 1 and int(gpu["sel"][b, g, 0]) == 0
 
 
-@pytest.mark.parametrize("alpha,page_size", [(2.0, 16), (1.5, 8), (1.25, 32), (4.0 / 3.0, 64)])
-def test_gauss_est_policy(alpha, page_size):
+@pytest.mark.parametrize("alpha,page_size,m16", [(2.0, 16, False), (1.5, 8, False),
+                                                 (1.25, 32, False), (4.0 / 3.0, 64, False),
+                                                 (2.0, 16, True)])
+def test_gauss_est_policy(alpha, page_size, m16):
     # expected-maximum estimate m + e_n sqrt(v): e_P on full pages, e_n on the
     # ragged last page of each row
     w = small(73, alpha=alpha, policy="gauss_est", clusters=16, planted_per_kv_head=0,
-              page_size=page_size, lens_range=(100, 1200), delta=0.1)
+              page_size=page_size, lens_range=(100, 1200), delta=0.1, moments_bf16=m16)
     inp = wl.make_inputs(w, device=DEV)
     gpu = run_gpu(inp, "gauss_est")
     for b, g in all_pairs(w):
         check_pair(inp, gpu, b, g, "gauss_est")
 
 
+@pytest.mark.parametrize("m16", [False, True])
 @pytest.mark.parametrize("alpha,page_size,eps", [(2.0, 16, 1e-4), (1.5, 8, 1e-3),
                                                  (1.25, 32, 1e-2), (4.0 / 3.0, 64, 3e-4)])
-def test_gauss_mass_policy(alpha, page_size, eps):
+def test_gauss_mass_policy(alpha, page_size, eps, m16):
     # expected page mass n_p E[(X - tau_hat)_+^gamma] against eps (ragged last
     # pages use their own token counts)
+    # (m16: the compact metadata format, bf16 page mean / variance)
     w = small(77, alpha=alpha, policy="gauss_mass", clusters=16, planted_per_kv_head=0,
-              page_size=page_size, lens_range=(100, 1200), delta=eps)
+              page_size=page_size, lens_range=(100, 1200), delta=eps, moments_bf16=m16)
     inp = wl.make_inputs(w, device=DEV)
     gpu = run_gpu(inp, "gauss_mass")
     for b, g in all_pairs(w):
