@@ -227,9 +227,10 @@ ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
  *   (fp32, [B][Hq]): the largest z over the valid tokens of the selected page
  *   with the largest bound for head h, lowest page on ties (a lower bound of
  *   z_max over the selected tokens; -inf if none).  The keys of a selected
- *   page are then not read when, for every head h of its group, (alpha-1)
- *   times its bound plus a rounding slack is below
- *   zlb[b][h] - 1 minus a rounding slack: since tau >= z_max - 1 (the largest
+ *   page are then not read when, for every head h of its group,
+ *   x + 1e-3 (1 + |x|) < zlb[b][h] - 1 - 1e-4 (1 + |zlb[b][h]|) with x =
+ *   (alpha-1) times its bound (fp32; the slacks exceed the rounding of the
+ *   bound and of the fp32 scores): since tau >= z_max - 1 (the largest
  *   weight is at most 1), none of its tokens can carry weight, so tau, out
  *   and n_support are those of the unpruned call (§2.C, §3: only support
  *   tokens matter).  How many pages this skips depends on the data.
