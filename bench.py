@@ -419,9 +419,11 @@ def run(w, args, dev, emit_cpu=True):
 
 
 def kernel_source_files(entry):
-    """The HIP file of an entry point and every local header it includes."""
+    """The HIP file of an entry point and every device-code header it includes (the
+    library's own sources; the public C header, which declares the host interface
+    and holds no device code, is left out)."""
     import re
-    dirs = [os.path.join(HERE, "sparse_kv_cache_page_amd", "csrc"), os.path.join(HERE, "include")]
+    dirs = [os.path.join(HERE, "sparse_kv_cache_page_amd", "csrc")]
     todo, seen = [KERNEL_SOURCES[entry]], []
     while todo:
         name = todo.pop(0)
