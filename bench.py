@@ -532,9 +532,9 @@ def main():
         counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this library has no multi-GPU path "
-              "(every (row, KV head) pair is independent; see DESIGN.md for how it would "
-              "shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path (every "
+              "(row, KV head) pair is independent, so rows or KV heads would be split across "
+              "GPUs with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
