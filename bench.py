@@ -383,6 +383,7 @@ def run(w, args, dev, emit_cpu=True):
     stages = time_stages(layers, max(20, min(args.steps, 400)), graph)
     refresh_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["refresh"])["refresh"]
     append_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["append"])["append"]
+    copy_gbps = measured_copy_gbps(dev)
     nb = stage_bytes(layers[0])
     eff = nb["kv_bytes"] / (ms * 1e-3) / 1e9
     dom = max(stages, key=lambda n: stages[n])
@@ -394,6 +395,7 @@ def run(w, args, dev, emit_cpu=True):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
         "data": "synthetic", "config": workload_config(w, R, graph, layers[0].inp),
         "effective_kv_gbps": eff, "hbm_frac": eff / HBM_PEAK_GBPS,
+        "measured_copy_gbps": copy_gbps, "frac_of_measured_copy": eff / copy_gbps,
         "kv_bytes_per_step": nb["kv_bytes"], "full_cache_bytes": nb["full_cache"],
         "read_fraction_of_full_cache": nb["kv_bytes"] / nb["full_cache"],
         "stage_ms": stages, "stage_bytes": {k: nb[k] for k in stages},
@@ -416,6 +418,25 @@ def run(w, args, dev, emit_cpu=True):
     del layers
     torch.cuda.empty_cache()
     return rec
+
+
+def measured_copy_gbps(dev, mib=1024, reps=5):
+    """HBM rate of a plain device-to-device copy on this GPU (bytes read + written per second)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    return 2 * n / sec / 1e9
 
 
 def kernel_source_files(entry):
