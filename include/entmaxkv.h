@@ -119,6 +119,20 @@ ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
                                hipStream_t stream);
 
 /*
+ * Device-side check of the values the other entry points cannot validate on
+ * the host without a synchronisation (see the conventions above): writes
+ *   bad[0] = number of rows b with seq_lens[b] outside [0, max_pages_per_seq * P],
+ *   bad[1] = number of entries block_table[b][p], p < ceil(seq_lens[b]/P) of a
+ *            row with a valid length, outside [0, num_phys_pages).
+ * bad: device int32 [2], overwritten (cleared by a kernel, so the call can be
+ * captured in a graph).  Nothing is synchronised: read bad after the stream
+ * has reached this call.  Meant for debugging and admission checks; the
+ * decode path itself never reads it.
+ */
+ekv_status ekv_validate_cache(const ekv_cache_desc* desc, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t* bad, hipStream_t stream);
+
+/*
  * Decode-time append of one token per row (§2.A: the page metadata is stored
  * per page, so a new token changes only its own page's record).  For every
  * row b, with t = seq_lens[b] - 1 (seq_lens already counts the new token),

@@ -31,6 +31,7 @@ EXPORTED = (
     "ekv_decode_fused_workspace_bytes",
     "ekv_score_select_pages",
     "ekv_append_token",
+    "ekv_validate_cache",
     "ekv_score_select_workspace_bytes",
     "ekv_decode_step",
     "ekv_step_workspace_bytes",
@@ -85,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            vp, vp, sz, vp]
     lib.ekv_score_select_workspace_bytes.argtypes = [dp]
     lib.ekv_append_token.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ekv_validate_cache.argtypes = [dp, vp, vp, vp, vp]
     lib.ekv_score_select_workspace_bytes.restype = sz
     lib.ekv_step_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_step_workspace_bytes.restype = sz
@@ -100,7 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
                  "ekv_entmax_decode", "ekv_decode_step", "ekv_score_select_pages",
-                 "ekv_entmax_decode_fused", "ekv_append_token"):
+                 "ekv_entmax_decode_fused", "ekv_append_token", "ekv_validate_cache"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -190,6 +192,19 @@ def build_page_meta(s: CacheShape, K, block_table, seq_lens, kmin, kmax, mean=No
     _check("ekv_build_page_meta", load_library().ekv_build_page_meta(
         ctypes.byref(d), _ptr(K), _ptr(block_table), _ptr(seq_lens), _ptr(first_page),
         int(span), _ptr(kmin), _ptr(kmax), _ptr(mean), _ptr(var), _stream()))
+
+
+def validate_cache(s: CacheShape, block_table, seq_lens):
+    """ekv_validate_cache: (#rows with an invalid length, #invalid block-table entries),
+    counted on the device; synchronises to read the two counts."""
+    _need(block_table, "block_table", torch.int32, (s.batch, s.max_pages_per_seq))
+    _need(seq_lens, "seq_lens", torch.int32, (s.batch,))
+    bad = torch.empty(2, dtype=torch.int32, device=seq_lens.device)
+    d = s.desc()
+    _check("ekv_validate_cache", load_library().ekv_validate_cache(
+        ctypes.byref(d), _ptr(block_table), _ptr(seq_lens), _ptr(bad), _stream()))
+    b = bad.cpu()
+    return int(b[0]), int(b[1])
 
 
 def append_token(s: CacheShape, k_new, v_new, block_table, seq_lens, K, V, kmin, kmax,

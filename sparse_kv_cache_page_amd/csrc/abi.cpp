@@ -88,6 +88,15 @@ ekv_status ekv_build_page_meta(const ekv_cache_desc* desc, const void* K,
                                          kmax, mean, var, stream));
 }
 
+ekv_status ekv_validate_cache(const ekv_cache_desc* desc, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t* bad, hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_i32(block_table) || !ok_i32(seq_lens) || !ok_i32(bad)) return EKV_ERR_INVALID_ARG;
+  return from_hip(ekv::launch_validate(s, block_table, seq_lens, bad, stream));
+}
+
 ekv_status ekv_append_token(const ekv_cache_desc* desc, const void* k_new, const void* v_new,
                             const int32_t* block_table, const int32_t* seq_lens, void* K,
                             void* V, void* kmin, void* kmax, void* mean, void* var,

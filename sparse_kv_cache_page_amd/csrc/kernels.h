@@ -24,6 +24,10 @@ hipError_t launch_append(const Shape& s, const void* k_new, const void* v_new,
                          const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,
                          void* kmax, void* mean, void* var, hipStream_t stream);
 
+// Counts of invalid row lengths and block-table entries into bad[0], bad[1].
+hipError_t launch_validate(const Shape& s, const int32_t* bt, const int32_t* lens, int32_t* bad,
+                           hipStream_t stream);
+
 hipError_t launch_build_meta(const Shape& s, const void* K, const int32_t* bt,
                              const int32_t* lens, const int32_t* first_page, int span,
                              void* kmin, void* kmax, void* mean, void* var,

@@ -134,6 +134,31 @@ hipError_t launch_append_t(const Shape& s, const void* k_new, const void* v_new,
   return hipGetLastError();
 }
 
+// Device-side check of the cache description: one thread per (row, page
+// slot); counts rows whose length is outside [0, maxP * P] (bad[0]) and
+// block-table entries of a row's valid pages outside [0, Np) (bad[1]).
+__global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict__ bt,
+                                                       const int32_t* __restrict__ lens, int B,
+                                                       int P, int maxP, int Np,
+                                                       int32_t* __restrict__ bad) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)B * maxP) return;
+  const int b = (int)(i / maxP);
+  const int p = (int)(i % maxP);
+  const int L = lens[b];
+  const bool len_ok = L >= 0 && (long long)L <= (long long)maxP * P;
+  if (p == 0 && !len_ok) atomicAdd(&bad[0], 1);
+  if (!len_ok) return;  // the row's page count is not defined
+  if (p < (L + P - 1) / P) {
+    const int pi = bt[i];
+    if (pi < 0 || pi >= Np) atomicAdd(&bad[1], 1);
+  }
+}
+
+__global__ void clear2_kernel(int32_t* bad) {
+  if (threadIdx.x < 2) bad[threadIdx.x] = 0;
+}
+
 // K dtype x head dim x moment dtype
 template <template <typename, int, typename> class F, typename... A>
 hipError_t dispatch_meta(const Shape& s, A... args) {
@@ -159,6 +184,19 @@ struct MetaOp {
 };
 
 }  // namespace
+
+hipError_t launch_validate(const Shape& s, const int32_t* bt, const int32_t* lens, int32_t* bad,
+                           hipStream_t stream) {
+  // the counters are cleared by a one-block kernel (no memset node in a
+  // captured graph)
+  hipLaunchKernelGGL(clear2_kernel, dim3(1), dim3(64), 0, stream, bad);
+  const long long n = (long long)s.B * s.maxP;
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(validate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, bt, lens, s.B,
+                     s.P, s.maxP, s.Np, bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const Shape& s, const void* k_new, const void* v_new,
                          const int32_t* bt, const int32_t* lens, void* K, void* V, void* kmin,

@@ -266,3 +266,13 @@ def test_append_argument_errors(lib):
     assert call(mean=FAKE_MIS, var=FAKE) == INVALID
     assert lib.ekv_append_token(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                 None, None) == INVALID
+
+
+def test_validate_argument_errors(lib):
+    d = desc()
+    assert lib.ekv_validate_cache(ctypes.byref(d), None, FAKE, FAKE, None) == INVALID
+    assert lib.ekv_validate_cache(ctypes.byref(d), FAKE, None, FAKE, None) == INVALID
+    assert lib.ekv_validate_cache(ctypes.byref(d), FAKE, FAKE, None, None) == INVALID
+    assert lib.ekv_validate_cache(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x10002),
+                                  None) == INVALID
+    assert lib.ekv_validate_cache(None, FAKE, FAKE, FAKE, None) == INVALID

@@ -476,3 +476,25 @@ def test_edge_empty_rows_fused_paths():
                tau=f.tau)
     for b, g in [(0, 0), (2, 1)]:
         check_pair(inp, gpu, b, g, "topk", check_meta=False)
+
+
+def test_validate_cache_counts_planted_errors():
+    # device-side check of seq_lens and the block table: valid inputs give
+    # (0, 0); planted bad lengths and out-of-pool pages are counted, slots past
+    # a row's pages are not looked at
+    w = small(231, batch=5, lens_range=None)
+    inp = wl.make_inputs(w, device=DEV, lens=[900, 0, 2000, 40, 333])
+    s = cache_shape(inp)
+    assert B.validate_cache(s, inp["block_table"], inp["seq_lens"]) == (0, 0)
+    bt = inp["block_table"].clone()
+    lens = inp["seq_lens"].clone()
+    P, mp = w.page_size, inp["max_pages"]
+    lens[1] = mp * P + 1            # too long
+    lens[4] = -3                    # negative
+    bt[0, 0] = s.num_phys_pages     # outside the pool
+    bt[3, 2] = -1                   # row 3 has 3 pages: its last one
+    bt[2, mp - 1] = 12345678        # row 2 (2000 tokens) ends before this slot if mp > 125
+    expect_bt = 2 + (1 if (2000 + P - 1) // P == mp else 0)
+    assert B.validate_cache(s, bt, lens) == (2, expect_bt)
+    lens[1] = mp * P                # exactly full is valid
+    assert B.validate_cache(s, bt, lens)[0] == 1
