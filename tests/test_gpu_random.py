@@ -55,3 +55,18 @@ def test_random_configuration(seed):
             continue
         for g in range(w.num_kv_heads):
             check_pair(inp, gpu, b, g, w.policy)
+    if w.policy == "topk":
+        # the fused step (scores + top-k in one launch, then the pruned
+        # decode) equals the separate calls bit for bit
+        import torch
+        from sparse_kv_cache_page_amd.engine import PagedEntmaxDecoder
+        from gpu_util import cache_shape
+        f = PagedEntmaxDecoder(cache_shape(inp), policy="topk", top_k=w.top_k, alpha=w.alpha,
+                               scale=w.scale, fused=True)
+        f.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
+        f.fused_step(inp["q"], inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
+        torch.cuda.synchronize()
+        assert torch.equal(f.n_sel, gpu["n_sel"])
+        for k in ("out", "tau", "n_support"):
+            assert torch.equal(torch.nan_to_num(f.__dict__[k], nan=-9.0),
+                               torch.nan_to_num(gpu[k], nan=-9.0)), k
