@@ -57,7 +57,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
-    ap.add_argument("--sweep", default="", help="also run the batch x ctx sweep, JSON lines to FILE")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the batch x ctx sweep that the gqa run reports with its line")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--policy", default=None)
     ap.add_argument("--top-k", type=int, default=None)
@@ -530,21 +531,35 @@ def build_workload(args):
     return wl.variant(w, **kw) if kw else w
 
 
-def sweep(args, dev, path):
-    """batch x ctx sweep with the GQA decode heads, top-k = 1/8 of the pages, alpha 1.5."""
+def sweep(dev, steps=100, warmup=10):
+    """batch x ctx sweep on the gqa decode heads (32 query / 8 KV heads, d 128, page 16,
+    bf16, alpha 1.5), top-k = 1/8 of the pages: one graph-replayed step per point,
+    with its algorithmic bytes (the same accounting as the main line)."""
+    import gc
+    import torch
     from sparse_kv_cache_page_amd import workloads as wl
-    with open(path, "w") as f:
-        for B in (1, 8, 32, 64):
-            for ctx in (8192, 32768, 131072):
-                w = wl.variant("gqa", batch=B, seq_len=ctx, top_k=ctx // 16 // 8,
-                               name=f"gqa_b{B}_ctx{ctx}")
-                a = argparse.Namespace(**vars(args))
-                a.steps, a.warmup, a.layers = min(args.steps, 200), 10, 0
-                rec = run(w, a, dev, emit_cpu=False)
-                f.write(json.dumps(rec) + "\n")
-                f.flush()
-                print(f"[sweep] B={B} ctx={ctx}: {rec['value']:.1f} steps/s, "
-                      f"{rec['effective_kv_gbps']:.0f} GB/s", file=sys.stderr, flush=True)
+    out = []
+    for B in (1, 8, 32):
+        for ctx in (8192, 32768, 131072):
+            w = wl.variant("gqa", batch=B, seq_len=ctx, top_k=ctx // 16 // 8,
+                           name=f"gqa_b{B}_ctx{ctx}")
+            probe = Layer(w, 0, dev)
+            per_layer = stage_bytes_after_step(probe)["kv_bytes"]
+            R = max(2, min(16, math.ceil((1 << 30) / max(per_layer, 1))))
+            layers = [probe] + [Layer(w, 7919 * (i + 1), dev) for i in range(R - 1)]
+            ms, _ = time_steps(layers, steps, warmup, True)
+            nb = stage_bytes(layers[0])
+            eff = nb["kv_bytes"] / (ms * 1e-3) / 1e9
+            out.append({"batch": B, "context": ctx, "top_k": w.top_k, "ms_per_step": ms,
+                        "steps_per_s": 1000.0 / ms, "effective_kv_gbps": eff,
+                        "hbm_frac": eff / HBM_PEAK_GBPS,
+                        "read_fraction_of_full_cache": nb["kv_bytes"] / nb["full_cache"]})
+            print(f"[sweep] B={B} ctx={ctx}: {1000.0 / ms:.1f} steps/s, {eff:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+            del layers, probe
+            gc.collect()
+            torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -575,9 +590,9 @@ def main():
     dev = torch.device("cuda:0")
     w = build_workload(args)
     rec = run(w, args, dev)
+    if w.name == "gqa" and not args.no_sweep:
+        rec["sweep"] = sweep(dev)
     print(json.dumps(rec), flush=True)
-    if args.sweep:
-        sweep(args, dev, args.sweep)
 
 
 if __name__ == "__main__":
