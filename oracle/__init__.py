@@ -17,6 +17,8 @@ Modules:
   meta     -- per-page key metadata (bounding box, mean, variance)
   scores   -- box upper bound and Gaussian score moments per page
   select   -- top-k page selection and Gaussian-aware selection (tau-hat)
+  softmax  -- softmax decode over a kept set and its dropped mass (the
+              comparison side of the method)
   pipeline -- the per-(row, KV head) composition used by the tests
 
 Every function is pinned by tests under tests/ (marked "not gpu") against
@@ -25,4 +27,4 @@ docstring.  The one approximation with no such pin is how well tau-hat - Delta
 recovers the true support (the pages print no numbers for it): parity unpinned
 for that property, only reported.
 """
-from . import entmax, meta, scores, select, pipeline  # noqa: F401
+from . import entmax, meta, scores, select, softmax, pipeline  # noqa: F401

@@ -173,3 +173,29 @@ def run_pair(inputs: dict, b: int, g: int, policy: str, *, alpha=None, top_k=Non
         out.update(tau_full=tau_f, p_full=p_f, o_full=o_f, dropped_mass=delta_mass,
                    support_recovered=support_in, value_norm_bound=B, kept_mask=kept)
     return out
+
+
+def softmax_pair(inputs: dict, b: int, g: int, sel, *, scale=None, q=None):
+    """Softmax decode of (row b, KV head g) over the pages `sel` (None: every page),
+    and over the full cache: the comparison of §3-§4 of the EntmaxKV page.
+
+    Returns dict(lse, o) of the kept set, (lse_full, o_full), the dropped softmax
+    mass delta per head and the largest value-row norm B of the row.
+    """
+    from . import softmax
+    w = inputs["workload"]
+    scale = float(np.float32(w.scale if scale is None else scale))
+    G = w.group
+    qq = widen(inputs["q"] if q is None else q)[b, g * G:(g + 1) * G]
+    phys, counts, keys, vals = pair_keys_values(inputs, b, g)
+    kf = np.concatenate(keys)
+    vf = np.concatenate(vals)
+    lse_f, _, o_f = softmax.softmax_decode_heads(qq, kf, vf, scale)
+    if sel is None:
+        sel = list(range(len(phys)))
+    ks = np.concatenate([keys[p] for p in sel])
+    vs = np.concatenate([vals[p] for p in sel])
+    lse, _, o = softmax.softmax_decode_heads(qq, ks, vs, scale)
+    return dict(lse=lse, o=o, lse_full=lse_f, o_full=o_f,
+                dropped_mass=softmax.dropped_mass(lse, lse_f),
+                value_norm_bound=np.sqrt((vf * vf).sum(axis=1)).max())
