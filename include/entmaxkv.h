@@ -9,6 +9,7 @@
  *   ekv_score_pages      -- query-aware page upper bounds     (§2.A)
  *   ekv_select_pages     -- top-k or Gaussian-aware selection (§2.B)
  *   ekv_entmax_decode    -- alpha-entmax over selected pages  (§2.C)
+ *   ekv_softmax_decode   -- softmax over the same pages (comparison, §3-§4)
  * The alpha-entmax mapping itself is the standard one: with
  * z_i = (alpha-1) * s_i, p_i = [z_i - tau]_+^(1/(alpha-1)) and tau chosen so
  * that sum_i p_i = 1.  tau is always reported in that z-space.
@@ -337,6 +338,38 @@ size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k);
 /* Scratch bytes ekv_entmax_decode needs for this cache shape and max_sel
  * (0 if desc is invalid). */
 size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);
+
+/*
+ * Softmax decode over the selected pages, or over every page of each row
+ * (sel NULL): the comparison path of the EntmaxKV summary page (§3: under
+ * softmax every token keeps positive weight, so dropping pages drops mass
+ * delta > 0 and the output error is only bounded by 2 B delta; §4: the
+ * method's speed is compared with a full-cache softmax decode of the
+ * FlashDecoding kind).  For each row b and query head h (KV head g), over the
+ * valid tokens i of the pages sel[b][g][0 .. n_sel[b][g]) (all pages
+ * 0 .. n_b-1 when sel is NULL):
+ *   s_i = scale * <q[b][h], k_i>                         (fp32 accumulation)
+ *   out[b][h] = sum_i exp(s_i) v_i / sum_i exp(s_i)      (fp32, every value
+ *                                                          row is read)
+ *   lse[b][h] = ln sum_i exp(s_i)  (fp32, [B][Hq]), if lse is not NULL.
+ * The dropped softmax mass of a selection is 1 - exp(lse_sel - lse_all),
+ * with lse_all from the call with sel NULL.  An empty row (or n_sel 0) gets a
+ * zero output and lse = -inf; a row whose n_sel exceeds max_sel gets NaN.
+ * max_sel: host upper bound on every n_sel[b][g] (<= 0, or sel NULL: the
+ *   row capacity max_pages_per_seq); it sizes the launch and the workspace.
+ * ws / ws_bytes: device scratch of at least ekv_softmax_workspace_bytes(desc,
+ *   max_sel) bytes, 256-byte aligned; no initialisation needed, garbage
+ *   afterwards.  scale > 0 and finite.  Two launches (split partials, merge).
+ */
+ekv_status ekv_softmax_decode(const ekv_cache_desc* desc, const float* q, float scale,
+                              const void* K, const void* V, const int32_t* block_table,
+                              const int32_t* seq_lens, const int32_t* sel,
+                              const int32_t* n_sel, int32_t max_sel, float* out, float* lse,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Scratch bytes ekv_softmax_decode needs for this cache shape and max_sel
+ * (0 if desc is invalid; pass max_sel <= 0 for the full-cache call). */
+size_t ekv_softmax_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);
 
 /* e_n = E[max of n iid N(0,1)] as used by EKV_SELECT_GAUSS_EST for a page of
  * n valid tokens (tabulated once on the host by quadrature); NaN unless

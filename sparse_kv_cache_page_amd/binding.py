@@ -32,6 +32,8 @@ EXPORTED = (
     "ekv_score_select_pages",
     "ekv_append_token",
     "ekv_validate_cache",
+    "ekv_softmax_decode",
+    "ekv_softmax_workspace_bytes",
     "ekv_score_select_workspace_bytes",
     "ekv_decode_step",
     "ekv_step_workspace_bytes",
@@ -96,13 +98,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_decode_fused_workspace_bytes.restype = sz
     lib.ekv_decode_workspace_bytes.argtypes = [dp, i32]
     lib.ekv_decode_workspace_bytes.restype = sz
+    lib.ekv_softmax_decode.argtypes = [dp, vp, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz,
+                                       vp]
+    lib.ekv_softmax_workspace_bytes.argtypes = [dp, i32]
+    lib.ekv_softmax_workspace_bytes.restype = sz
     lib.ekv_gauss_expected_max.argtypes = [i32]
     lib.ekv_gauss_expected_max.restype = ctypes.c_double
     lib.ekv_status_string.argtypes = [ctypes.c_int]
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
                  "ekv_entmax_decode", "ekv_decode_step", "ekv_score_select_pages",
-                 "ekv_entmax_decode_fused", "ekv_append_token", "ekv_validate_cache"):
+                 "ekv_entmax_decode_fused", "ekv_append_token", "ekv_validate_cache",
+                 "ekv_softmax_decode"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -321,6 +328,37 @@ def entmax_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_tabl
         ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
         _ptr(block_table), _ptr(seq_lens), _ptr(sel), _ptr(n_sel), int(max_sel), _ptr(ub),
         _ptr(zlb), _ptr(out), _ptr(tau), _ptr(n_support), _ptr(ws),
+        ctypes.c_size_t(ws.numel()), _stream()))
+
+
+def softmax_workspace_bytes(s: CacheShape, max_sel: int = 0) -> int:
+    d = s.desc()
+    return int(load_library().ekv_softmax_workspace_bytes(ctypes.byref(d), int(max_sel)))
+
+
+def softmax_decode(s: CacheShape, q, scale: float, K, V, block_table, seq_lens, out, ws,
+                   sel=None, n_sel=None, max_sel: int = 0, lse=None):
+    """ekv_softmax_decode: softmax attention over the selected pages (every page
+    of each row if sel is None); lse [B, Hq] receives ln sum exp(scores)."""
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(V, "V", s.kv_dtype, _kv_shape(s))
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(out, "out", torch.float32, (B, Hq, d))
+    if sel is not None or n_sel is not None:
+        _need(sel, "sel", torch.int32, (B, Hkv, mp))
+        _need(n_sel, "n_sel", torch.int32, (B, Hkv))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq))
+    if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.dtype == torch.uint8
+            and ws.is_contiguous()):
+        raise TypeError("ws must be a contiguous uint8 GPU tensor")
+    d_ = s.desc()
+    _check("ekv_softmax_decode", load_library().ekv_softmax_decode(
+        ctypes.byref(d_), _ptr(q), float(scale), _ptr(K), _ptr(V), _ptr(block_table),
+        _ptr(seq_lens), _ptr(sel), _ptr(n_sel), int(max_sel), _ptr(out), _ptr(lse), _ptr(ws),
         ctypes.c_size_t(ws.numel()), _stream()))
 
 

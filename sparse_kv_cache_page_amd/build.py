@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libentmaxkv.so")
 ARCH = os.environ.get("EKV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "meta.hip", "score.hip", "select.hip", "decode.hip"]
+SOURCES = ["abi.cpp", "meta.hip", "score.hip", "select.hip", "decode.hip", "softmax.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

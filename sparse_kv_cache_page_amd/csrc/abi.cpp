@@ -319,3 +319,37 @@ ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float sca
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t ekv_softmax_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK) return 0;
+  if (max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
+  return ekv::make_softmax_plan(s, max_sel).total;
+}
+
+ekv_status ekv_softmax_decode(const ekv_cache_desc* desc, const float* q, float scale,
+                              const void* K, const void* V, const int32_t* block_table,
+                              const int32_t* seq_lens, const int32_t* sel,
+                              const int32_t* n_sel, int32_t max_sel, float* out, float* lse,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(q) || !ok_vec(K) || !ok_vec(V) || !ok_i32(block_table) || !ok_i32(seq_lens) ||
+      !ok_vec(out))
+    return EKV_ERR_INVALID_ARG;
+  if ((sel == nullptr) != (n_sel == nullptr)) return EKV_ERR_INVALID_ARG;
+  if (sel != nullptr && (!aligned(sel, 4) || !aligned(n_sel, 4))) return EKV_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return EKV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
+  if (sel == nullptr || max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
+  if ((long long)s.Np * s.Hkv * s.P * s.D >= (1LL << 40)) return EKV_ERR_UNSUPPORTED;
+  const ekv::SoftmaxPlan plan = ekv::make_softmax_plan(s, max_sel);
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < plan.total) return EKV_ERR_WORKSPACE;
+  return from_hip(ekv::launch_softmax(s, plan, q, scale, K, V, block_table, seq_lens, sel,
+                                      n_sel, out, lse, ws, stream));
+}
+
+}  // extern "C"

@@ -88,4 +88,22 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& plan, const float* q,
                          const float* ub, float* zlb, float* out, float* tau_out,
                          int32_t* n_support, void* ws, bool fused, hipStream_t stream);
 
+// Softmax decode (the comparison path): split-page partials (m, l, o) of
+// `slots` token slots each, merged per query head.
+struct SoftmaxPlan {
+  int max_sel;   // upper bound on selected pages per pair
+  int slots;     // token slots per split (a multiple of the page size)
+  int splits;    // ceil(max_sel * P / slots)
+  size_t ml_off;  // float2 [B*Hq][splits]
+  size_t o_off;   // float  [B*Hq][splits][D]
+  size_t total;
+};
+
+SoftmaxPlan make_softmax_plan(const Shape& s, int max_sel);
+
+hipError_t launch_softmax(const Shape& s, const SoftmaxPlan& plan, const float* q, float scale,
+                          const void* K, const void* V, const int32_t* bt, const int32_t* lens,
+                          const int32_t* sel, const int32_t* n_sel, float* out, float* lse,
+                          void* ws, hipStream_t stream);
+
 }  // namespace ekv

@@ -276,3 +276,33 @@ def test_validate_argument_errors(lib):
     assert lib.ekv_validate_cache(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x10002),
                                   None) == INVALID
     assert lib.ekv_validate_cache(None, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_softmax_argument_errors(lib):
+    d = desc()
+    need = lib.ekv_softmax_workspace_bytes(ctypes.byref(d), 0)
+    assert need > 0
+    assert lib.ekv_softmax_workspace_bytes(ctypes.byref(d), 3) <= need
+    assert lib.ekv_softmax_workspace_bytes(None, 0) == 0
+
+    def call(q=FAKE, scale=1.0, K=FAKE, V=FAKE, sel=None, n_sel=None, out=FAKE, lse=None,
+             ws=ctypes.c_void_p(0x10000), ws_bytes=need, dd=d):
+        return lib.ekv_softmax_decode(ctypes.byref(dd) if dd is not None else None, q, scale,
+                                      K, V, FAKE, FAKE, sel, n_sel, 0, out, lse, ws,
+                                      ws_bytes, None)
+
+    assert call(q=None) == INVALID
+    assert call(K=FAKE_MIS) == INVALID
+    assert call(V=None) == INVALID
+    assert call(out=FAKE_MIS) == INVALID
+    assert call(sel=FAKE, n_sel=None) == INVALID
+    assert call(sel=None, n_sel=FAKE) == INVALID
+    assert call(sel=ctypes.c_void_p(0x10002), n_sel=FAKE) == INVALID
+    assert call(lse=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE
+    assert call(dd=None) == INVALID
+    assert call(dd=desc(head_dim=96)) == UNSUPPORTED
