@@ -17,7 +17,7 @@ the 8 TB/s HBM peak, the roofline of the dominant entry point, and the CPU
 oracle timed on a bounded sample of the same step.
 
     python bench.py [--steps K] [--warmup W] [--config gqa] [--layers R]
-                    [--no-graph] [--cpu-seconds S] [--sweep FILE]
+                    [--no-graph] [--cpu-seconds S] [--no-sweep] [--no-comparison]
 """
 from __future__ import annotations
 
@@ -59,6 +59,8 @@ def parse():
                     help="CPU oracle sample budget (0 disables the cpu_baseline leg)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the batch x ctx sweep that the gqa run reports with its line")
+    ap.add_argument("--no-comparison", action="store_true",
+                    help="skip the softmax / full-cache comparison of the gqa run")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--policy", default=None)
     ap.add_argument("--top-k", type=int, default=None)
@@ -138,6 +140,49 @@ class Layer:
     def step(self):
         for n in self.stages:
             getattr(self, n)()
+
+    # the comparison of §3-§4 of the EntmaxKV page: softmax decode over the
+    # step's selected pages and over the full cache, and the full-cache entmax
+    # decode (buffers made on first use)
+    def _cmp_buffers(self):
+        if hasattr(self, "cmp"):
+            return self.cmp
+        import torch
+        from sparse_kv_cache_page_amd import binding as Bd
+        s, dev = self.shape, self.inp["K"].device
+        B, Hq, d = s.batch, s.num_q_heads, s.head_dim
+        c = {"o_sm_sel": torch.empty(B, Hq, d, device=dev),
+             "o_sm_full": torch.empty(B, Hq, d, device=dev),
+             "o_ent_full": torch.empty(B, Hq, d, device=dev),
+             "lse_sel": torch.empty(B, Hq, device=dev),
+             "lse_full": torch.empty(B, Hq, device=dev),
+             "ws_sm_sel": torch.empty(Bd.softmax_workspace_bytes(s, self.dec.max_sel),
+                                      dtype=torch.uint8, device=dev),
+             "ws_sm_full": torch.empty(Bd.softmax_workspace_bytes(s, 0), dtype=torch.uint8,
+                                       device=dev),
+             "ws_ent_full": torch.empty(Bd.decode_workspace_bytes(s, 0), dtype=torch.uint8,
+                                        device=dev)}
+        self.cmp = c
+        return c
+
+    def softmax_sel(self):
+        from sparse_kv_cache_page_amd import binding as Bd
+        c, i = self._cmp_buffers(), self.inp
+        Bd.softmax_decode(self.shape, i["q"], self.w.scale, i["K"], i["V"], i["block_table"],
+                          i["seq_lens"], c["o_sm_sel"], c["ws_sm_sel"], sel=self.dec.sel,
+                          n_sel=self.dec.n_sel, max_sel=self.dec.max_sel, lse=c["lse_sel"])
+
+    def softmax_full(self):
+        from sparse_kv_cache_page_amd import binding as Bd
+        c, i = self._cmp_buffers(), self.inp
+        Bd.softmax_decode(self.shape, i["q"], self.w.scale, i["K"], i["V"], i["block_table"],
+                          i["seq_lens"], c["o_sm_full"], c["ws_sm_full"], lse=c["lse_full"])
+
+    def entmax_full(self):
+        from sparse_kv_cache_page_amd import binding as Bd
+        c, i = self._cmp_buffers(), self.inp
+        Bd.entmax_decode(self.shape, i["q"], self.w.scale, self.w.alpha, i["K"], i["V"],
+                         i["block_table"], i["seq_lens"], c["o_ent_full"], c["ws_ent_full"])
 
 
 def stage_bytes(layer):
@@ -562,6 +607,61 @@ def sweep(dev, steps=100, warmup=10):
     return out
 
 
+def comparison(w, args, dev, step_ms, copy_gbps):
+    """Softmax decode over the same selected pages and over the full cache, and the
+    full-cache entmax decode, on the same layers (graph-replayed launches); the
+    dropped softmax mass and the sparse-vs-full output error of both mappings on
+    the first layer."""
+    import gc
+    import torch
+    R = max(2, args.layers) if args.layers > 0 else 4
+    layers = [Layer(w, 7919 * i, dev) for i in range(R)]
+    for L in layers:
+        L.step()
+        L._cmp_buffers()
+    names = ["softmax_sel", "softmax_full", "entmax_full"]
+    t = time_stages(layers, 40, not args.no_graph, names)
+    L0 = layers[0]
+    L0.step()
+    for n in names:
+        getattr(L0, n)()
+    torch.cuda.synchronize()
+    c = L0.cmp
+    delta = (1.0 - torch.exp(c["lse_sel"].double() - c["lse_full"].double())).flatten()
+
+    def rel(a, b):
+        return ((a - b).norm(dim=-1) / b.norm(dim=-1).clamp_min(1e-30)).flatten()
+
+    e_ent = rel(L0.dec.out, c["o_ent_full"])
+    e_sm = rel(c["o_sm_sel"], c["o_sm_full"])
+    nb = stage_bytes(L0)
+    full_kv = nb["full_cache"]
+    res = {
+        "ms": t,
+        "entmax_step_ms": step_ms,
+        "speedup_vs_softmax_full_cache": t["softmax_full"] / step_ms,
+        "speedup_vs_entmax_full_cache": t["entmax_full"] / step_ms,
+        "softmax_full_cache_gbps": full_kv / (t["softmax_full"] * 1e-3) / 1e9,
+        # against a softmax decode that streamed the full cache at the measured
+        # device-copy rate (an upper bound for any full-cache decode here)
+        "speedup_vs_full_cache_read_at_copy_rate":
+            full_kv / (copy_gbps * 1e9) / (step_ms * 1e-3),
+        "softmax_full_cache_hbm_frac": full_kv / (t["softmax_full"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "softmax_dropped_mass": {"mean": float(delta.mean()), "max": float(delta.max())},
+        "sparse_vs_full_output_rel_err": {
+            "entmax": {"median": float(e_ent.median()), "max": float(e_ent.max())},
+            "softmax": {"median": float(e_sm.median()), "max": float(e_sm.max())}},
+        "note": "same layers and selected pages; full-cache bytes = every valid K and V row",
+    }
+    print(f"[comparison] step {step_ms * 1000:.1f} us; softmax same pages "
+          f"{t['softmax_sel'] * 1000:.1f} us, softmax full {t['softmax_full'] * 1000:.1f} us, "
+          f"entmax full {t['entmax_full'] * 1000:.1f} us", file=sys.stderr, flush=True)
+    del layers
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.counter_summary:
@@ -590,6 +690,9 @@ def main():
     dev = torch.device("cuda:0")
     w = build_workload(args)
     rec = run(w, args, dev)
+    if w.name == "gqa" and not args.no_comparison:
+        rec["comparison"] = comparison(w, args, dev, rec["ms_per_step"],
+                                       rec["measured_copy_gbps"])
     if w.name == "gqa" and not args.no_sweep:
         rec["sweep"] = sweep(dev)
     print(json.dumps(rec), flush=True)

@@ -8,9 +8,11 @@
 // exp(s - m) and o the sum of exp(s - m) v, combine by rescaling each to the
 // common maximum.  So the decode is a split-page pass and a merge:
 //
-//  1. softmax_split_kernel -- work items (row, KV head, split of kSlots token
+//  1. softmax_split_kernel -- work items (row, KV head, split of `slots` token
 //     slots of the selected pages), split-major so consecutive items fall on
-//     different pairs (and XCDs).  Each lane owns one 16-byte chunk of a key
+//     different pairs (and XCDs).  The workgroup first resolves the split's
+//     pages (selection list, then block table) into an LDS page map, so that
+//     no key or value load waits on another global load.  Each lane owns one 16-byte chunk of a key
 //     row and of the matching value row; a wave covers kRows token rows per
 //     load and keeps kU loads in flight.  The scores of all G query heads of
 //     the group come from that one key read (fp32 FMA, DPP row reduction), in
@@ -31,6 +33,7 @@ namespace ekv {
 namespace {
 
 constexpr int kSmBlock = 256;
+constexpr int kSmMaxPages = 1024;  // pages per split (the page map staged in LDS)
 constexpr int kSmWaves = kSmBlock / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -67,6 +70,7 @@ __global__ __launch_bounds__(kSmBlock) void softmax_split_kernel(SmArgs<T> a) {
   __shared__ float sm_o[kSmWaves][G][D];
   __shared__ float sm_m[kSmWaves][G];
   __shared__ float sm_l[kSmWaves][G];
+  __shared__ int2 sm_page[kSmMaxPages];  // (physical page, valid tokens) of the split
 
   const int item = blockIdx.x;
   const int pair = item % a.npairs;
@@ -78,6 +82,20 @@ __global__ __launch_bounds__(kSmBlock) void softmax_split_kernel(SmArgs<T> a) {
   const int s0 = split * a.slots;
   if (s0 >= n_slots) return;  // workgroup-uniform: nothing of this pair here
   const int s1 = min(n_slots, s0 + a.slots);
+
+  // the split's page map, resolved once (sel -> block table) so the K/V
+  // loads below depend on no other global load
+  const int p0 = s0 >> a.log2P;
+  const int np = ((s1 - 1) >> a.log2P) - p0 + 1;
+  {
+    const int32_t* selp = a.sel ? a.sel + (size_t)pair * a.maxP : nullptr;
+    const int32_t* btp = a.bt + (size_t)b * a.maxP;
+    for (int k = threadIdx.x; k < np; k += kSmBlock) {
+      const int lp = selp ? selp[p0 + k] : p0 + k;
+      sm_page[k] = make_int2(btp[lp], page_valid(L, lp, a.P));
+    }
+  }
+  __syncthreads();
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int c = lane % kC, r = lane / kC;
@@ -98,9 +116,6 @@ __global__ __launch_bounds__(kSmBlock) void softmax_split_kernel(SmArgs<T> a) {
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[h][e] = 0.f;
   }
-  const int32_t* selp = a.sel ? a.sel + (size_t)pair * a.maxP : nullptr;
-  const int32_t* btp = a.bt + (size_t)b * a.maxP;
-
   for (int base = s0 + wave * kRows * kU; base < s1; base += kSmWaves * kRows * kU) {
     uint4 kk[kU], vv[kU];
     bool valid[kU];
@@ -111,12 +126,12 @@ __global__ __launch_bounds__(kSmBlock) void softmax_split_kernel(SmArgs<T> a) {
       kk[u] = make_uint4(0, 0, 0, 0);
       vv[u] = make_uint4(0, 0, 0, 0);
       if (j < s1) {
-        const int idx = j >> a.log2P, t = j & (a.P - 1);
-        const int lp = selp ? selp[idx] : idx;
-        if (t < page_valid(L, lp, a.P)) {
+        const int t = j & (a.P - 1);
+        const int2 pg = sm_page[(j >> a.log2P) - p0];
+        if (t < pg.y) {
           valid[u] = true;
           const size_t off =
-              ((((size_t)btp[lp] * a.Hkv + g) << a.log2P) + t) * D + (size_t)c * kVec;
+              ((((size_t)pg.x * a.Hkv + g) << a.log2P) + t) * D + (size_t)c * kVec;
           kk[u] = load16_stream(a.K + off);
           vv[u] = load16_stream(a.V + off);
         }
@@ -292,8 +307,9 @@ SoftmaxPlan make_softmax_plan(const Shape& s, int max_sel) {
   const long long slots = (long long)max_sel * s.P;
   const long long pairs = (long long)s.B * s.Hkv;
   // the largest split (a multiple of the page size) that still gives about
-  // 2048 work items, between 256 and 4096 token slots
-  int sps = 4096;
+  // 2048 work items, between 256 and 4096 token slots and at most
+  // kSmMaxPages pages
+  int sps = s.P * kSmMaxPages < 4096 ? s.P * kSmMaxPages : 4096;
   while (sps > 256 && pairs * ((slots + sps - 1) / sps) < 2048) sps >>= 1;
   if (sps < s.P) sps = s.P;
   pl.slots = sps;
