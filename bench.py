@@ -61,6 +61,9 @@ def parse():
                     help="skip the batch x ctx sweep that the gqa run reports with its line")
     ap.add_argument("--no-comparison", action="store_true",
                     help="skip the softmax / full-cache comparison of the gqa run")
+    ap.add_argument("--comparison", action="store_true",
+                    help="also run the softmax / full-cache comparison on a top-k workload "
+                         "other than gqa")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--policy", default=None)
     ap.add_argument("--top-k", type=int, default=None)
@@ -690,7 +693,7 @@ def main():
     dev = torch.device("cuda:0")
     w = build_workload(args)
     rec = run(w, args, dev)
-    if w.name == "gqa" and not args.no_comparison:
+    if (w.name == "gqa" or (args.comparison and w.policy == "topk")) and not args.no_comparison:
         rec["comparison"] = comparison(w, args, dev, rec["ms_per_step"],
                                        rec["measured_copy_gbps"])
     if w.name == "gqa" and not args.no_sweep:
