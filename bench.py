@@ -324,6 +324,39 @@ def time_steps(layers, steps, warmup, graph):
     return start.elapsed_time(end) / steps, wall
 
 
+def step_distribution(layers, n, graph):
+    """Median / p10 / p90 (ms) of n individually timed steps (HIP events around
+    each step; with graph=True each step is the replay of that layer's captured
+    step, so the figure includes one graph launch)."""
+    import torch
+    R = len(layers)
+    graphs = []
+    if graph:
+        for L in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                L.step()
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+    torch.cuda.synchronize()
+    marks = []
+    for i in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        if graph:
+            graphs[i % R].replay()
+        else:
+            layers[i % R].step()
+        b.record()
+        marks.append((a, b))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in marks)
+    pick = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+    del graphs
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "steps": n}
+
+
 def time_stages(layers, steps, graph, names=None):
     """Average duration (ms) of one launch of each entry point.
 
@@ -429,6 +462,8 @@ def run(w, args, dev, emit_cpu=True):
         layers = [Layer(w, 7919 * i, dev) for i in range(R)]
     graph = not args.no_graph
     ms, wall = time_steps(layers, args.steps, args.warmup, graph)
+    dist = {"graph": step_distribution(layers, 100, True),
+            "eager": step_distribution(layers, 100, False)}
     stages = time_stages(layers, max(20, min(args.steps, 400)), graph)
     refresh_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["refresh"])["refresh"]
     append_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["append"])["append"]
@@ -449,6 +484,9 @@ def run(w, args, dev, emit_cpu=True):
         "read_fraction_of_full_cache": nb["kv_bytes"] / nb["full_cache"],
         "stage_ms": stages, "stage_bytes": {k: nb[k] for k in stages},
         "host_wall_ms_per_step": wall * 1000.0 / args.steps,
+        "step_ms_distribution": dict(dist, note="100 steps each timed by its own HIP events: "
+                                     "graph = replay of the layer's captured step, eager = "
+                                     "the step's launches"),
         "last_page_refresh": {"ms": refresh_ms, "bytes": nb["refresh"],
                               "gbps": nb["refresh"] / (refresh_ms * 1e-3) / 1e9,
                               "note": "build_page_meta of each row's last page, timed "
