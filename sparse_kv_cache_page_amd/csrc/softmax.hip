@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kWave) void softmax_merge_kernel(SmArgs<T> a, float
 template <typename T, int D, int G>
 hipError_t launch_softmax_tg(const Shape& s, const SoftmaxPlan& pl, const SmArgs<T>& a,
                              float* out, float* lse, hipStream_t stream) {
-  constexpr int kU = G >= 8 ? 2 : 4;
+  constexpr int kU = 4;
   hipLaunchKernelGGL((softmax_split_kernel<T, D, G, kU>), dim3(a.npairs * pl.splits),
                      dim3(kSmBlock), 0, stream, a);
   const hipError_t e = hipGetLastError();
