@@ -253,12 +253,25 @@ __global__ __launch_bounds__(kWave) void softmax_merge_kernel(SmArgs<T> a, float
   float acc[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
-  for (int s = 0; s < used; ++s) {
-    const float2 v = ml[s];
-    const float f = v.x == -INFINITY ? 0.f : exp2f(v.x - mx);
-    lt = fmaf(f, v.y, lt);
+  // kB splits per round: all their loads are issued before any is used
+  constexpr int kB = 8;
+  for (int s0 = 0; s0 < used; s0 += kB) {
+    float2 v[kB];
+    float x[kB][kE];
 #pragma unroll
-    for (int e = 0; e < kE; ++e) acc[e] = fmaf(f, po[(size_t)s * D + lane + e * kWave], acc[e]);
+    for (int j = 0; j < kB; ++j) {
+      const int s = s0 + j < used ? s0 + j : used - 1;
+      v[j] = ml[s];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) x[j][e] = po[(size_t)s * D + lane + e * kWave];
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const float f = (s0 + j >= used || v[j].x == -INFINITY) ? 0.f : exp2f(v[j].x - mx);
+      lt = fmaf(f, v[j].y, lt);
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[e] = fmaf(f, x[j][e], acc[e]);
+    }
   }
   const float inv = 1.f / lt;
 #pragma unroll
