@@ -345,7 +345,6 @@ ekv_status ekv_softmax_decode(const ekv_cache_desc* desc, const float* q, float 
   if (lse != nullptr && !aligned(lse, 4)) return EKV_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
   if (sel == nullptr || max_sel <= 0 || max_sel > s.maxP) max_sel = s.maxP;
-  if ((long long)s.Np * s.Hkv * s.P * s.D >= (1LL << 40)) return EKV_ERR_UNSUPPORTED;
   const ekv::SoftmaxPlan plan = ekv::make_softmax_plan(s, max_sel);
   if (ws == nullptr || !aligned(ws, 256) || ws_bytes < plan.total) return EKV_ERR_WORKSPACE;
   return from_hip(ekv::launch_softmax(s, plan, q, scale, K, V, block_table, seq_lens, sel,
