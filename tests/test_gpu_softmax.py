@@ -161,3 +161,25 @@ def test_softmax_caller_page_list_any_order():
     o_f, l_f = run_softmax(inp)
     for (b, g) in lists:
         check_softmax(inp, o_s, l_s, o_f, l_f, sel, n_sel, b, g)
+
+
+@pytest.mark.parametrize("seed", range(0, 64, 2))
+def test_softmax_random_configurations(seed):
+    # the random small configurations of the entmax sweep (every policy's
+    # selection, dtypes, page sizes 1-64, ragged and empty rows): softmax over
+    # each selection and over the full cache against the oracle on every pair
+    from test_gpu_random import draw
+    w, lens = draw(seed)
+    print(f"[softmax random {seed}] {w}", flush=True)
+    inp = wl.make_inputs(w, device=DEV, lens=lens)
+    gpu = run_gpu(inp, w.policy)
+    sel, n_sel = gpu.get("sel"), gpu.get("n_sel")
+    max_sel = min(w.top_k, inp["max_pages"]) if w.policy == "topk" else 0
+    o_s, l_s = run_softmax(inp, sel, n_sel, max_sel=max_sel)
+    o_f, l_f = run_softmax(inp)
+    for b in range(w.batch):
+        if lens[b] == 0:
+            assert np.all(o_s[b] == 0) and np.all(np.isneginf(l_f[b]))
+            continue
+        for g in range(w.num_kv_heads):
+            check_softmax(inp, o_s, l_s, o_f, l_f, sel, n_sel, b, g)
