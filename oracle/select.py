@@ -51,6 +51,8 @@ hand-built tie cases; e_n against the closed forms known for n <= 5 and a
 Monte Carlo estimate; I_g against numerical quadrature (scipy.integrate.quad);
 tau-hat for zero-variance pages equals the exact entmax threshold of the
 expanded token multiset (checked against the sort-based sparsemax closed form);
+the box-bound keep rule on hand-worked pages at alpha = 1.5 and 1.25 (literal
+page lists; pages with u >= tau-hat - Delta > (alpha-1) u must be dropped);
 F(tau-hat) = 1; page masses: for zero-variance pages they are the exact entmax
 masses of the pages' tokens, and one page's expected mass matches a Monte
 Carlo estimate.

@@ -125,6 +125,38 @@ def test_gauss_select_threshold_rule_and_guard():
     assert sel2 == [1]
 
 
+# Hand-worked box-bound rule away from alpha = 2, where (alpha-1) != 1.  All
+# pages have zero variance and one valid token, so tau-hat is the exact entmax
+# threshold of the page means in z-space: z = (alpha-1) m = [5, 0, 0.5, -1.5 or
+# -1, 1]; only z = 5 lies above 4, and (5 - 4)^gamma = 1, so tau-hat = 4 for
+# every gamma.  With Delta = 0.1 a page is kept iff (alpha-1) u >= 3.9.  Pages 1
+# and 3 have u >= 3.9 but (alpha-1) u < 3.9 (dropped: an oracle that compared u
+# itself would keep them); page 4 clears the bar by 0.005 in z-space (an oracle
+# that scaled Delta by (alpha-1) would drop it).
+@pytest.mark.parametrize("alpha,u,m", [
+    (1.5, [10.5, 5.0, 8.0, 7.7, 7.81], [10.0, 0.0, 1.0, -3.0, 2.0]),
+    (1.25, [20.5, 10.0, 16.0, 15.5, 15.7], [20.0, 0.0, 2.0, -4.0, 4.0]),
+])
+def test_gauss_select_hand_worked_alpha_scaling(alpha, u, m):
+    u = np.array([u], np.float32)
+    m = np.array([m])
+    v = np.zeros_like(m)
+    sel, taus = select.gauss_select(u, m, v, [1] * 5, alpha, 0.1)
+    assert abs(taus[0] - 4.0) <= 1e-12
+    assert sel == [0, 2, 4]
+    # two heads: the union of the heads' kept pages.  The second head's means
+    # are those of the first head shifted so that its own tau-hat is 4 - 2 = 2
+    # and its bar 1.9; its bounds keep only page 1 ((alpha-1) * 4.0 / (alpha-1) = 4 >= 1.9)
+    a1 = alpha - 1.0
+    m2 = m[0] - 2.0 / a1
+    u2 = np.full(5, 1.0, np.float32)
+    u2[1] = np.float32(4.0 / a1)
+    sel2, taus2 = select.gauss_select(np.stack([u[0], u2]), np.stack([m[0], m2]),
+                                      np.zeros((2, 5)), [1] * 5, alpha, 0.1)
+    assert abs(taus2[0] - 4.0) <= 1e-12 and abs(taus2[1] - 2.0) <= 1e-12
+    assert sel2 == [0, 1, 2, 4]
+
+
 def test_integer_gamma_rule():
     assert select.integer_gamma(1.5) == 2
     assert select.integer_gamma(2.0) == 1
