@@ -7,6 +7,8 @@ Tolerances (GPU vs oracle, same input bits):
   u, U                 <= 1 ulp fp32 (fp64 accumulation of exact products,
                         rounded once; the oracle rounds the exact sum)
   sel, n_sel           bit-exact
+  gm, gv               <= 1e-12 of the sum of the terms' magnitudes (fp64
+                        sums of exact products; v: of v itself)
   tau-hat              <= 1e-12 relative (both fp64; different root finders)
   tau (entmax)         <= 1e-5 absolute, z-space (or 4 fp32 ulps of |tau|
                         when larger: above |tau| ~ 40 fp32 scores cannot
@@ -18,13 +20,14 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from oracle import pipeline
+from oracle import pipeline, scores, select
 from sparse_kv_cache_page_amd import binding as B
 
 TAU_TOL = 1e-5
 TAU_TOL_REL = 4.0 * 2.0 ** -24
 OUT_TOL = 1e-3
 TAU_HAT_RTOL = 1e-12
+MOM_RTOL = 1e-12
 
 
 def cache_shape(inp) -> B.CacheShape:
@@ -138,6 +141,29 @@ def check_pair(inp, gpu, b, g, policy, *, alpha=None, top_k=None, delta=None, sc
         assert ulp_dist(ub, ref["u"]).max() <= 1, f"u b{b} g{g}"
     ubg = gpu["ubg"][b, g, :n].cpu().numpy()
     assert ulp_dist(ubg, ref["U"]).max() <= 1, f"U b{b} g{g}"
+    if policy in ("gauss", "gauss_est", "gauss_mass") and gpu.get("gm") is not None:
+        # Gaussian score moments, element by element and stage-wise: the
+        # oracle's moment formula is fed the page mean/variance the GPU stored
+        # (so a one-ulp difference in a stored moment cannot hide or fake a
+        # scoring error).  Both sides sum exact fp64 products (fp32 q times an
+        # fp32 or bf16 moment), the oracle correctly rounded, the GPU with at
+        # most a dozen fp64 roundings per sum, so they agree to 1e-12 of the
+        # sum of the terms' magnitudes (for v, which has no cancellation, that
+        # is 1e-12 of v itself)
+        gm = gpu["gm"][b, g * G:(g + 1) * G, :n].cpu().numpy()
+        gv = gpu["gv"][b, g * G:(g + 1) * G, :n].cpu().numpy()
+        sc = float(np.float32(w.scale if scale is None else scale))
+        qq = _np(inp["q"] if q is None else q)[b, g * G:(g + 1) * G]      # [G][d]
+        mu_g = _np(gpu["mean"][idx, g])                                    # [n][d]
+        va_g = _np(gpu["var"][idx, g])
+        m_ref = np.empty((G, n))
+        v_ref = np.empty((G, n))
+        for h in range(G):
+            for p in range(n):
+                m_ref[h, p], v_ref[h, p] = scores.gauss_moments(qq[h], mu_g[p], va_g[p], sc)
+        mag = sc * (np.abs(qq) @ np.abs(mu_g).T)                           # [G][n]
+        assert np.all(np.abs(gm - m_ref) <= MOM_RTOL * mag + 1e-300), f"gm b{b} g{g}"
+        assert np.all(np.abs(gv - v_ref) <= MOM_RTOL * np.abs(v_ref) + 1e-300), f"gv b{b} g{g}"
     if policy in ("gauss", "gauss_est", "gauss_mass"):
         th = gpu["tau_hat"][b, g * G:(g + 1) * G].cpu().numpy()
         np.testing.assert_allclose(th, ref["tau_hat"], rtol=TAU_HAT_RTOL, atol=1e-300,
@@ -146,6 +172,26 @@ def check_pair(inp, gpu, b, g, policy, *, alpha=None, top_k=None, delta=None, sc
         ns = int(gpu["n_sel"][b, g])
         got = gpu["sel"][b, g, :ns].cpu().tolist()
         assert got == list(ref["sel"]), f"sel b{b} g{g}: gpu {got[:12]}.. vs {ref['sel'][:12]}.."
+        # stage-wise: the oracle's selection fed the GPU's own bounds (and
+        # moments), so a scoring difference cannot mask a selection error
+        k_eff = w.top_k if top_k is None else top_k
+        if policy == "topk":
+            st = select.topk_pages(ubg, k_eff)
+            if st != got:
+                srt = np.sort(ubg.astype(np.float64))[::-1]
+                gap = (srt[k_eff - 1] - srt[k_eff]) / abs(srt[k_eff - 1]) if k_eff < n else None
+                raise AssertionError(f"stage-wise top-k b{b} g{g} differs (k-th gap {gap})")
+        elif gpu.get("gm") is not None:
+            a_ = float(np.float32(w.alpha if alpha is None else alpha))
+            d_ = float(np.float32(w.delta if delta is None else delta))
+            rule = {"gauss": select.gauss_select, "gauss_est": select.gauss_est_select,
+                    "gauss_mass": select.gauss_mass_select}[policy]
+            u_g = gpu["ub"][b, g, :n, :].T.cpu().numpy() if gpu.get("ub") is not None else ref["u"]
+            st, th_st = rule(u_g, gm, gv, ref["counts"], a_, d_)
+            assert st == got, f"stage-wise {policy} b{b} g{g} differs"
+            np.testing.assert_allclose(gpu["tau_hat"][b, g * G:(g + 1) * G].cpu().numpy(), th_st,
+                                       rtol=TAU_HAT_RTOL, atol=1e-300,
+                                       err_msg=f"stage-wise tau_hat b{b} g{g}")
     tau = gpu["tau"][b, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
     tol = np.maximum(TAU_TOL, TAU_TOL_REL * np.abs(ref["tau"]))
     assert np.all(np.abs(tau - ref["tau"]) <= tol), \

@@ -46,16 +46,46 @@ def check_properties(inp, gpu, policy, top_k):
 
 
 def decoder_matches(inp, gpu, policy, alpha, top_k, delta, scale, q):
-    """The benchmark's call sequence gives bit-identical results."""
+    """The benchmark's call sequence gives bit-identical results.
+
+    For the top-k policy that is the fused ekv_score_select_pages (arrival
+    counters, device-coherent bound stores, the top-k run by the last
+    workgroup of each pair) followed by the pruned ekv_entmax_decode, exactly
+    as bench.py's Layer issues them; ekv_decode_step (the same two calls
+    behind one entry point) is checked too.  Every output must equal the
+    separate score / select / decode calls of `gpu`, which the oracle checked.
+    """
     s = cache_shape(inp)
+    fused = policy == "topk"
     dec = PagedEntmaxDecoder(s, policy=policy, top_k=top_k, alpha=alpha, scale=scale,
-                             delta=delta)
+                             delta=delta, fused=fused)
     dec.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
-    out, tau = dec.step(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
+    if fused:
+        dec.score_select(q, inp["K"], inp["block_table"], inp["seq_lens"])
+        dec.decode(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
+    else:
+        dec.step(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
     torch.cuda.synchronize()
-    assert torch.equal(out, gpu["out"]) and torch.equal(tau, gpu["tau"])
+    assert torch.equal(dec.out, gpu["out"]) and torch.equal(dec.tau, gpu["tau"])
+    assert torch.equal(dec.n_support, gpu["n_support"])
     if policy != "dense":
         assert torch.equal(dec.n_sel, gpu["n_sel"])
+        for b in range(s.batch):
+            for g in range(s.num_kv_heads):
+                n = int(gpu["n_sel"][b, g])
+                assert torch.equal(dec.sel[b, g, :n], gpu["sel"][b, g, :n]), f"sel b{b} g{g}"
+        npg = torch.tensor(inp["npages"], device=DEV)
+        live = torch.arange(s.max_pages_per_seq, device=DEV)[None, :] < npg[:, None]
+        live = live[:, None, :].expand_as(gpu["ubg"])
+        assert torch.equal(dec.ubg[live], gpu["ubg"][live])
+    if fused:
+        out1, tau1 = dec.out.clone(), dec.tau.clone()
+        ns1 = dec.n_support.clone()
+        dec.out.fill_(float("nan"))
+        dec.fused_step(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out, out1) and torch.equal(dec.tau, tau1)
+        assert torch.equal(dec.n_support, ns1)
     return dec
 
 
@@ -146,3 +176,5 @@ def test_fullsize_stress(stress_inputs, alpha, ti, policy, top_k):
     check_properties(inp, gpu, policy, w.top_k)
     check_pair(inp, gpu, 0, 0, policy, top_k=w.top_k, check_meta=(ti == 0 and alpha == 1.25))
     check_pair(inp, gpu, 31, 7, policy, top_k=w.top_k, check_meta=False)
+    if policy == "topk":
+        decoder_matches(inp, gpu, policy, alpha, w.top_k, w.delta, w.scale, q)
