@@ -46,7 +46,8 @@
  *    invalid slots of a row's last page are never read.
  *  * Supported: head_dim in {64, 128}; page_size in {1,2,4,8,16,32,64};
  *    Hq % Hkv == 0 and Hq/Hkv in {1,2,4,8}; kv dtype bf16 or fp32.
- *  * Calls are thread-safe: the library holds no mutable global state.
+ *  * Calls are thread-safe: the library holds no mutable global state, except
+ *    the per-device scratch of ekv_decode_step_noalloc (see there).
  */
 #ifndef ENTMAXKV_H
 #define ENTMAXKV_H
@@ -334,6 +335,32 @@ ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float sca
 
 /* Scratch bytes ekv_decode_step needs (0 if desc is invalid or top_k < 1). */
 size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k);
+
+/*
+ * ekv_decode_step for callers that cannot allocate device memory (code under
+ * stream capture, serving loops and harnesses that forbid allocation): the
+ * same arguments and results, minus ws / ws_bytes.  The step's scratch lives
+ * in a device array of the library, EKV_NOALLOC_SCRATCH_BYTES bytes on each
+ * GPU it runs on, held until the process ends: the arrival counters in its
+ * first EKV_NOALLOC_COUNTER_BYTES (one int per (row, KV head) pair), the rest
+ * of ekv_step_workspace_bytes(desc, top_k) after them.  A shape whose pairs or
+ * scratch do not fit returns EKV_ERR_WORKSPACE before anything is launched;
+ * nothing is allocated or freed.  The first call on a device looks up the
+ * array's address on that device (with it current) and clears the counters
+ * with a kernel on `stream`; every completed call leaves them zero.
+ * All calls on one GPU share its array and keep the last call's contents:
+ * calls that overlap in time on one GPU (different streams, or unordered host
+ * threads) race on it and must not be issued.
+ */
+#define EKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define EKV_NOALLOC_COUNTER_BYTES ((size_t)64 << 10)
+ekv_status ekv_decode_step_noalloc(const ekv_cache_desc* desc, const float* q, float scale,
+                                   float alpha, const void* K, const void* V,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int32_t refresh_last_page, int32_t top_k, void* kmin,
+                                   void* kmax, float* ubg, int32_t* sel, int32_t* n_sel,
+                                   float* out, float* tau_out, int32_t* n_support,
+                                   hipStream_t stream);
 
 /* Scratch bytes ekv_entmax_decode needs for this cache shape and max_sel
  * (0 if desc is invalid). */

@@ -37,6 +37,7 @@ EXPORTED = (
     "ekv_score_select_workspace_bytes",
     "ekv_decode_step",
     "ekv_step_workspace_bytes",
+    "ekv_decode_step_noalloc",
     "ekv_gauss_expected_max",
     "ekv_status_string",
 )
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, vp, vp, sz, vp]
     lib.ekv_decode_step.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp, sz, vp]
+    lib.ekv_decode_step_noalloc.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, i32, i32, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, vp]
     lib.ekv_score_select_pages.argtypes = [dp, vp, f32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                            vp, vp, sz, vp]
     lib.ekv_score_select_workspace_bytes.argtypes = [dp]
@@ -107,7 +110,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_status_string.argtypes = [ctypes.c_int]
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
-                 "ekv_entmax_decode", "ekv_decode_step", "ekv_score_select_pages",
+                 "ekv_entmax_decode", "ekv_decode_step", "ekv_decode_step_noalloc",
+                 "ekv_score_select_pages",
                  "ekv_entmax_decode_fused", "ekv_append_token", "ekv_validate_cache",
                  "ekv_softmax_decode"):
         getattr(lib, name).restype = ctypes.c_int
@@ -401,6 +405,42 @@ def decode_step(s: CacheShape, q, scale: float, alpha: float, K, V, block_table,
         _ptr(block_table), _ptr(seq_lens), int(bool(refresh_last_page)), int(top_k), _ptr(kmin),
         _ptr(kmax), _ptr(ubg), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(tau), _ptr(n_support),
         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # EKV_NOALLOC_SCRATCH_BYTES
+NOALLOC_COUNTER_BYTES = 64 << 10   # EKV_NOALLOC_COUNTER_BYTES
+
+
+def decode_step_noalloc(s: CacheShape, q, scale: float, alpha: float, K, V, block_table,
+                        seq_lens, top_k: int, kmin, kmax, ubg, sel, n_sel, out,
+                        refresh_last_page: bool = False, tau=None, n_support=None):
+    """ekv_decode_step_noalloc: decode_step with the library's own per-device
+    scratch instead of a workspace (no device allocation anywhere); shapes whose
+    scratch exceeds NOALLOC_SCRATCH_BYTES are refused.  Calls on one GPU must
+    not overlap in time."""
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(V, "V", s.kv_dtype, _kv_shape(s))
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    mshape = (s.num_phys_pages, Hkv, d)
+    _need(kmin, "kmin", s.kv_dtype, mshape)
+    _need(kmax, "kmax", s.kv_dtype, mshape)
+    _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
+    _need(sel, "sel", torch.int32, (B, Hkv, mp))
+    _need(n_sel, "n_sel", torch.int32, (B, Hkv))
+    _need(out, "out", torch.float32, (B, Hq, d))
+    if tau is not None:
+        _need(tau, "tau", torch.float32, (B, Hq))
+    if n_support is not None:
+        _need(n_support, "n_support", torch.int32, (B, Hq))
+    d_ = s.desc()
+    _check("ekv_decode_step_noalloc", load_library().ekv_decode_step_noalloc(
+        ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
+        _ptr(block_table), _ptr(seq_lens), int(bool(refresh_last_page)), int(top_k), _ptr(kmin),
+        _ptr(kmax), _ptr(ubg), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(tau), _ptr(n_support),
+        _stream()))
 
 
 def score_select_workspace_bytes(s: CacheShape) -> int:

@@ -295,30 +295,85 @@ ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float sca
   Shape s;
   ekv_status st = make_shape(desc, &s);
   if (st != EKV_OK) return st;
-  if (!ok_vec(V) || !ok_vec(out)) return EKV_ERR_INVALID_ARG;
-  if (tau_out != nullptr && !aligned(tau_out, 4)) return EKV_ERR_INVALID_ARG;
-  if (n_support != nullptr && !aligned(n_support, 4)) return EKV_ERR_INVALID_ARG;
-  if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
-  if (top_k < 1) return EKV_ERR_INVALID_ARG;
-  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
-  if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
+  // counters first, then the rest (an unusable workspace is reported after
+  // the other arguments have been validated)
   const size_t cbytes = step_counter_bytes(s);
-  const size_t ubytes = step_bound_bytes(s);
-  const size_t zbytes = step_zlb_bytes(s);
-  const size_t dbytes = ekv::make_decode_plan(s, max_sel, false).total;
-  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < cbytes + ubytes + zbytes + dbytes)
-    return EKV_ERR_WORKSPACE;
-  float* ub = (float*)((char*)ws + cbytes);
-  float* zlb = (float*)((char*)ws + cbytes + ubytes);
-  st = ekv_score_select_pages(desc, q, scale, K, block_table, seq_lens, refresh_last_page, top_k,
-                              kmin, kmax, ub, ubg, sel, n_sel, ws, cbytes, stream);
-  if (st != EKV_OK) return st;
-  return ekv_entmax_decode(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel,
-                           max_sel, ub, zlb, out, tau_out, n_support,
-                           (char*)ws + cbytes + ubytes + zbytes, dbytes, stream);
+  const bool fits = ws != nullptr && ws_bytes >= cbytes;
+  return ekv::decode_step_parts(desc, q, scale, alpha, K, V, block_table, seq_lens,
+                                refresh_last_page, top_k, kmin, kmax, ubg, sel, n_sel, out,
+                                tau_out, n_support, fits ? ws : nullptr, fits ? cbytes : 0,
+                                fits ? (char*)ws + cbytes : nullptr, fits ? ws_bytes - cbytes : 0,
+                                stream);
 }
 
 }  // extern "C"
+
+// The decode step with its arrival counters and the rest of its scratch in
+// two separate buffers (ekv_decode_step cuts one workspace in two;
+// ekv_decode_step_noalloc keeps the counters in a region of their own).
+ekv_status ekv::decode_step_parts(const ekv_cache_desc* desc, const float* q, float scale,
+                                  float alpha, const void* K, const void* V,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t refresh_last_page, int32_t top_k, void* kmin,
+                                  void* kmax, float* ubg, int32_t* sel, int32_t* n_sel,
+                                  float* out, float* tau_out, int32_t* n_support,
+                                  void* counters, size_t counter_bytes, void* rest,
+                                  size_t rest_bytes, hipStream_t stream) {
+  ekv_status st = ekv::validate_step(desc, q, scale, alpha, K, V, block_table, seq_lens, top_k,
+                                     kmin, kmax, ubg, sel, n_sel, out, tau_out, n_support);
+  if (st != EKV_OK) return st;
+  Shape s;
+  make_shape(desc, &s);
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  const size_t ubytes = step_bound_bytes(s);
+  const size_t zbytes = step_zlb_bytes(s);
+  const size_t dbytes = ekv::make_decode_plan(s, max_sel, false).total;
+  if (counters == nullptr || !aligned(counters, 256) || counter_bytes < step_counter_bytes(s))
+    return EKV_ERR_WORKSPACE;
+  if (rest == nullptr || !aligned(rest, 256) || rest_bytes < ubytes + zbytes + dbytes)
+    return EKV_ERR_WORKSPACE;
+  float* ub = (float*)rest;
+  float* zlb = (float*)((char*)rest + ubytes);
+  st = ekv_score_select_pages(desc, q, scale, K, block_table, seq_lens, refresh_last_page, top_k,
+                              kmin, kmax, ub, ubg, sel, n_sel, counters, counter_bytes, stream);
+  if (st != EKV_OK) return st;
+  return ekv_entmax_decode(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel,
+                           max_sel, ub, zlb, out, tau_out, n_support,
+                           (char*)rest + ubytes + zbytes, dbytes, stream);
+}
+
+ekv_status ekv::validate_step(const ekv_cache_desc* desc, const float* q, float scale,
+                              float alpha, const void* K, const void* V,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t top_k, const void* kmin, const void* kmax,
+                              const float* ubg, const int32_t* sel, const int32_t* n_sel,
+                              const float* out, const float* tau_out,
+                              const int32_t* n_support) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(q) || !ok_vec(K) || !ok_vec(V) || !ok_i32(block_table) || !ok_i32(seq_lens) ||
+      !ok_vec(kmin) || !ok_vec(kmax) || !ok_i32(ubg) || !ok_i32(sel) || !ok_i32(n_sel) ||
+      !ok_vec(out))
+    return EKV_ERR_INVALID_ARG;
+  if (tau_out != nullptr && !aligned(tau_out, 4)) return EKV_ERR_INVALID_ARG;
+  if (n_support != nullptr && !aligned(n_support, 4)) return EKV_ERR_INVALID_ARG;
+  if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
+  if (top_k < 1) return EKV_ERR_INVALID_ARG;
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
+  return EKV_OK;
+}
+
+size_t ekv::step_scratch_bytes(const ekv_cache_desc* desc, int32_t top_k, size_t* counter_bytes) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK || top_k < 1) return 0;
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return 0;
+  *counter_bytes = step_counter_bytes(s);
+  return step_bound_bytes(s) + step_zlb_bytes(s) + ekv::make_decode_plan(s, max_sel, false).total;
+}
 
 extern "C" {
 

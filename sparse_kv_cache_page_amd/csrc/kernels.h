@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "entmaxkv.h"
+
 namespace ekv {
 
 constexpr int kMaxPageSize = 64;  // largest supported tokens per page
@@ -105,5 +107,29 @@ hipError_t launch_softmax(const Shape& s, const SoftmaxPlan& plan, const float* 
                           const void* K, const void* V, const int32_t* bt, const int32_t* lens,
                           const int32_t* sel, const int32_t* n_sel, float* out, float* lse,
                           void* ws, hipStream_t stream);
+
+// The decode step (ekv_decode_step) with its arrival counters and the rest of
+// its scratch in separate buffers; validates like the public entry point.
+ekv_status decode_step_parts(const ekv_cache_desc* desc, const float* q, float scale,
+                             float alpha, const void* K, const void* V,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int32_t refresh_last_page, int32_t top_k, void* kmin, void* kmax,
+                             float* ubg, int32_t* sel, int32_t* n_sel, float* out,
+                             float* tau_out, int32_t* n_support, void* counters,
+                             size_t counter_bytes, void* rest, size_t rest_bytes,
+                             hipStream_t stream);
+
+// Host-side validation of the decode step's arguments (everything but its
+// scratch), as ekv_decode_step reports it.
+ekv_status validate_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
+                         const void* K, const void* V, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t top_k, const void* kmin,
+                         const void* kmax, const float* ubg, const int32_t* sel,
+                         const int32_t* n_sel, const float* out, const float* tau_out,
+                         const int32_t* n_support);
+
+// Scratch of the decode step besides its counters (0 if the shape, top_k or
+// the decode plan is invalid); the counters' bytes go to *counter_bytes.
+size_t step_scratch_bytes(const ekv_cache_desc* desc, int32_t top_k, size_t* counter_bytes);
 
 }  // namespace ekv

@@ -251,6 +251,38 @@ def test_step_argument_errors(lib):
     assert call(ws_bytes=need - 1) == WORKSPACE
 
 
+def test_noalloc_step_limits_and_argument_errors(lib):
+    # ekv_decode_step_noalloc validates and sizes its scratch on the host before
+    # any device call: argument errors as ekv_decode_step reports them, and
+    # shapes whose step scratch exceeds the library's fixed array refused
+    def call(d, alpha=1.5, top_k=4, q=FAKE, sel=FAKE):
+        return lib.ekv_decode_step_noalloc(ctypes.byref(d), q, 1.0, alpha, FAKE, FAKE, FAKE,
+                                           FAKE, 0, top_k, FAKE, FAKE, FAKE, sel, FAKE, FAKE,
+                                           None, None, None)
+
+    d = desc()
+    assert call(d, alpha=1.0) == INVALID
+    assert call(d, top_k=0) == INVALID
+    assert call(d, q=None) == INVALID
+    assert call(d, sel=None) == INVALID
+    assert call(desc(head_dim=96)) == UNSUPPORTED
+    # batch 64 x 32 heads x 8192 pages with top-1024: far beyond the array
+    big = desc(batch=64, num_q_heads=32, num_kv_heads=8, max_pages_per_seq=8192,
+               num_phys_pages=64 * 8192)
+    assert lib.ekv_step_workspace_bytes(ctypes.byref(big), 1024) > B.NOALLOC_SCRATCH_BYTES
+    assert call(big, top_k=1024) == WORKSPACE
+    # more (row, KV head) pairs than the counter region holds
+    pairs = desc(batch=B.NOALLOC_COUNTER_BYTES // 4 + 1, num_q_heads=1, num_kv_heads=1,
+                 head_dim=128, page_size=1, max_pages_per_seq=1, num_phys_pages=1)
+    assert lib.ekv_step_workspace_bytes(ctypes.byref(pairs), 1) < B.NOALLOC_SCRATCH_BYTES
+    assert call(pairs, top_k=1) == WORKSPACE
+    # the header's limits are the binding's
+    text = open(HEADER).read()
+    assert "#define EKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert "#define EKV_NOALLOC_COUNTER_BYTES ((size_t)64 << 10)" in text
+    assert B.NOALLOC_SCRATCH_BYTES == 64 << 20 and B.NOALLOC_COUNTER_BYTES == 64 << 10
+
+
 def test_append_argument_errors(lib):
     d = desc()
 
