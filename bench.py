@@ -39,10 +39,13 @@ KERNEL_SOURCES = {  # the HIP file of each entry point; local includes are follo
     "ekv_select_pages": "select.hip",
     "ekv_build_page_meta": "meta.hip",
     "ekv_append_token": "meta.hip",
+    "ekv_topk_decode": "step.hip",
+    "ekv_score_box_pages": "score.hip",
 }
 ENTRY_POINT = {"refresh": "ekv_build_page_meta", "score": "ekv_score_pages",
                "select": "ekv_select_pages", "decode": "ekv_entmax_decode",
-               "score_select": "ekv_score_select_pages", "append": "ekv_append_token"}
+               "score_select": "ekv_score_select_pages", "append": "ekv_append_token",
+               "topk_decode": "ekv_topk_decode", "score_box": "ekv_score_box_pages"}
 METRIC = "decode steps/s + effective KV GB/s (fraction of HBM peak), batch×ctx sweep"
 
 
@@ -110,7 +113,7 @@ class Layer:
     @property
     def stages(self):
         if self.w.policy == "topk":
-            return ["score_select", "decode"]
+            return ["score_box", "topk_decode"]
         if self.w.policy == "dense":
             return ["decode"]
         return ["score", "select", "decode"]
@@ -139,6 +142,15 @@ class Layer:
     def decode(self):
         i = self.inp
         self.dec.decode(i["q"], i["K"], i["V"], i["block_table"], i["seq_lens"])
+
+    def score_box(self):
+        i = self.inp
+        self.dec.score_box(i["q"], i["block_table"], i["seq_lens"])
+
+    def topk_decode(self):
+        i = self.inp
+        self.dec.topk_decode(i["q"], i["K"], i["V"], i["block_table"], i["seq_lens"],
+                             use_hint=True)
 
     def step(self):
         for n in self.stages:
@@ -210,9 +222,10 @@ def stage_bytes(layer):
     meta_pp = 2 * d * e + (2 * d * mom_e if gauss else 0)
     refresh = sum(Hkv * (v * d * e + meta_pp) for v in last_valid)
     pages = sum(npg) * Hkv
-    # per query head: ub (box-bound reading only) and the fp64 moments
-    score = pages * (meta_pp + 4 + (w.group * ((4 if w.policy == "gauss" else 0) + 16)
-                                    if gauss else 0))
+    # per query head: ub (the box-bound Gaussian reading, and the per-head
+    # bounds the pruned top-k decode reads) and the fp64 moments
+    ub_pp = 4 * w.group if (w.policy == "gauss" or getattr(dec, "prune", False)) else 0
+    score = pages * (meta_pp + 4 + ub_pp + (w.group * 16 if gauss else 0))
     if w.policy == "dense":
         n_sel = torch.tensor(npg)[:, None].expand(w.batch, Hkv)
     else:
@@ -246,7 +259,7 @@ def stage_bytes(layer):
         append = w.batch * Hkv * (4 * d * e + 2 * 2 * d * e)
     return dict(refresh=refresh, append=append, score=score if w.policy != "dense" else 0,
                 select=select if w.policy != "dense" else 0, decode=decode,
-                score_select=score + select,
+                score_select=score + select, topk_decode=select + decode, score_box=score,
                 kv_bytes=(pages * meta_pp if w.policy != "dense" else 0) + decode,
                 full_cache=full, k_tokens=ktok, v_rows=vrows)
 

@@ -318,13 +318,66 @@ ekv_status ekv_score_select_pages(const ekv_cache_desc* desc, const float* q, fl
 size_t ekv_score_select_workspace_bytes(const ekv_cache_desc* desc);
 
 /*
+ * Top-k selection and sparse alpha-entmax decode in one call (§2.B(1) then
+ * §2.C): the same sel, n_sel, out, tau_out and n_support as
+ *   ekv_select_pages(TOPK, top_k, ubg)  ->
+ *   ekv_entmax_decode(sel, n_sel, max_sel = min(top_k, max_pages_per_seq),
+ *                     ub, zlb)
+ * (ub NULL: without page pruning).  Where the shape allows (at most 1024
+ * selected pages, max_pages_per_seq <= 8192) the selection runs inside the
+ * decode's key launch: each of its workgroups selects the pair's pages itself
+ * from ubg, probes each query head's best selected page for the pruning
+ * bound, and scores an even share of the pages left to read; the selection
+ * list never makes a round trip through memory before it is used.  Otherwise
+ * the separate select and decode kernels run.  Two or three launches.
+ * ubg [B][Hkv][maxP] and ub [B][Hkv][maxP][G] (16-byte aligned) as written by
+ * ekv_score_pages or ekv_score_box_pages for the same query; hint: NULL, or
+ * the hints ekv_score_box_pages wrote with them (used only with ub).  sel and
+ * n_sel are outputs.
+ * ws / ws_bytes: at least ekv_topk_decode_workspace_bytes(desc, top_k) bytes,
+ * 256-byte aligned; no initialisation needed, garbage afterwards.
+ */
+ekv_status ekv_topk_decode(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
+                           const void* K, const void* V, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t top_k, const float* ub,
+                           const float* ubg, const void* hint, int32_t* sel, int32_t* n_sel,
+                           float* out, float* tau_out, int32_t* n_support, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Box bounds only, the scoring of the top-k step (§2.A): ub and ubg exactly as
+ * ekv_score_pages writes them (gm = gv = NULL), with each row's last page's
+ * box first rebuilt from K when refresh_last_page is set (as
+ * ekv_score_select_pages does; K may be NULL otherwise).  hint (or NULL):
+ * ekv_score_hint_bytes(desc) bytes, 16-byte aligned, receive each page
+ * slice's best page per query head; passed with ub to ekv_topk_decode for the
+ * same query, they let each head's pruning probe be requested before the
+ * selection runs (results unchanged).  Their content is internal to the
+ * library.  One launch.
+ */
+ekv_status ekv_score_box_pages(const ekv_cache_desc* desc, const float* q, float scale,
+                               const void* K, const int32_t* block_table,
+                               const int32_t* seq_lens, int32_t refresh_last_page, void* kmin,
+                               void* kmax, float* ub, float* ubg, void* hint,
+                               hipStream_t stream);
+
+/* Bytes of the best-page hints of ekv_score_box_pages (0 if desc is invalid). */
+size_t ekv_score_hint_bytes(const ekv_cache_desc* desc);
+
+/* Scratch bytes ekv_topk_decode needs (0 if desc is invalid or top_k < 1). */
+size_t ekv_topk_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k);
+
+/*
  * One whole decode step with the top-k policy (the pipeline of §2: scoring
  * from page metadata, candidate selection, sparse entmax over the selected
- * pages): ekv_score_select_pages (per-head bounds written to the workspace)
- * followed by ekv_entmax_decode(sel, n_sel, max_sel = min(top_k,
- * max_pages_per_seq)) with page pruning on those bounds, sharing one
- * workspace of ekv_step_workspace_bytes(desc, top_k) bytes (zero-filled
- * before first use, reusable afterwards, as for ekv_score_select_pages).
+ * pages): ekv_score_box_pages with the per-head bounds and hints written to
+ * the workspace (and, with refresh_last_page, each row's last page's box
+ * rebuilt from K first), then ekv_topk_decode with page pruning on those
+ * bounds; one workspace of ekv_step_workspace_bytes(desc,
+ * top_k) bytes (zero-filled before first use, reusable afterwards).  With
+ * refresh_last_page set, a row's last page must not be referenced by another
+ * row.  The results equal those of ekv_score_select_pages followed by
+ * ekv_entmax_decode with pruning.
  */
 ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
                            const void* K, const void* V, const int32_t* block_table,

@@ -38,6 +38,10 @@ EXPORTED = (
     "ekv_decode_step",
     "ekv_step_workspace_bytes",
     "ekv_decode_step_noalloc",
+    "ekv_topk_decode",
+    "ekv_topk_decode_workspace_bytes",
+    "ekv_score_box_pages",
+    "ekv_score_hint_bytes",
     "ekv_gauss_expected_max",
     "ekv_status_string",
 )
@@ -85,6 +89,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, vp, vp, sz, vp]
     lib.ekv_decode_step.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp, sz, vp]
+    lib.ekv_topk_decode.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, vp, sz, vp]
+    lib.ekv_score_box_pages.argtypes = [dp, vp, f32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.ekv_score_hint_bytes.argtypes = [dp]
+    lib.ekv_score_hint_bytes.restype = sz
+    lib.ekv_topk_decode_workspace_bytes.argtypes = [dp, i32]
+    lib.ekv_topk_decode_workspace_bytes.restype = sz
     lib.ekv_decode_step_noalloc.argtypes = [dp, vp, f32, f32, vp, vp, vp, vp, i32, i32, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp]
     lib.ekv_score_select_pages.argtypes = [dp, vp, f32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
@@ -111,6 +122,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ekv_status_string.restype = ctypes.c_char_p
     for name in ("ekv_build_page_meta", "ekv_score_pages", "ekv_select_pages",
                  "ekv_entmax_decode", "ekv_decode_step", "ekv_decode_step_noalloc",
+                 "ekv_topk_decode", "ekv_score_box_pages",
                  "ekv_score_select_pages",
                  "ekv_entmax_decode_fused", "ekv_append_token", "ekv_validate_cache",
                  "ekv_softmax_decode"):
@@ -405,6 +417,76 @@ def decode_step(s: CacheShape, q, scale: float, alpha: float, K, V, block_table,
         _ptr(block_table), _ptr(seq_lens), int(bool(refresh_last_page)), int(top_k), _ptr(kmin),
         _ptr(kmax), _ptr(ubg), _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(tau), _ptr(n_support),
         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()))
+
+
+def topk_decode_workspace_bytes(s: CacheShape, top_k: int) -> int:
+    d = s.desc()
+    return int(load_library().ekv_topk_decode_workspace_bytes(ctypes.byref(d), int(top_k)))
+
+
+def score_hint_bytes(s: CacheShape) -> int:
+    d = s.desc()
+    return int(load_library().ekv_score_hint_bytes(ctypes.byref(d)))
+
+
+def score_box_pages(s: CacheShape, q, scale: float, block_table, seq_lens, kmin, kmax, ubg,
+                    ub=None, hint=None, K=None, refresh_last_page: bool = False):
+    """ekv_score_box_pages: box bounds (ub, ubg) and, into `hint` (uint8 GPU tensor of
+    score_hint_bytes()), each page slice's best page per head for ekv_topk_decode."""
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    mshape = (s.num_phys_pages, Hkv, d)
+    _need(kmin, "kmin", s.kv_dtype, mshape)
+    _need(kmax, "kmax", s.kv_dtype, mshape)
+    _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
+    if ub is not None:
+        _need(ub, "ub", torch.float32, (B, Hkv, mp, Hq // Hkv))
+    if hint is not None and not (isinstance(hint, torch.Tensor) and hint.is_cuda and
+                                 hint.dtype == torch.uint8 and hint.is_contiguous() and
+                                 hint.numel() >= score_hint_bytes(s)):
+        raise TypeError("hint must be a contiguous uint8 GPU tensor of score_hint_bytes() bytes")
+    if refresh_last_page:
+        _need(K, "K", s.kv_dtype, _kv_shape(s))
+    d_ = s.desc()
+    _check("ekv_score_box_pages", load_library().ekv_score_box_pages(
+        ctypes.byref(d_), _ptr(q), float(scale), _ptr(K), _ptr(block_table), _ptr(seq_lens),
+        int(bool(refresh_last_page)), _ptr(kmin), _ptr(kmax), _ptr(ub), _ptr(ubg), _ptr(hint),
+        _stream()))
+
+
+def topk_decode(s: CacheShape, q, scale: float, alpha: float, K, V, block_table, seq_lens,
+                top_k: int, ubg, sel, n_sel, out, ws, ub=None, tau=None, n_support=None,
+                hint=None):
+    """ekv_topk_decode: top-k selection from ubg and the sparse entmax decode over it
+    (with page pruning when the per-head bounds ub [B, Hkv, maxP, G] are given, and
+    the scorer's hints when `hint` is)."""
+    B, Hq, Hkv, d, mp = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, s.max_pages_per_seq
+    _need(q, "q", torch.float32, (B, Hq, d))
+    _need(K, "K", s.kv_dtype, _kv_shape(s))
+    _need(V, "V", s.kv_dtype, _kv_shape(s))
+    _need(block_table, "block_table", torch.int32, (B, mp))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(ubg, "ubg", torch.float32, (B, Hkv, mp))
+    _need(sel, "sel", torch.int32, (B, Hkv, mp))
+    _need(n_sel, "n_sel", torch.int32, (B, Hkv))
+    _need(out, "out", torch.float32, (B, Hq, d))
+    if ub is not None:
+        _need(ub, "ub", torch.float32, (B, Hkv, mp, Hq // Hkv))
+    if tau is not None:
+        _need(tau, "tau", torch.float32, (B, Hq))
+    if n_support is not None:
+        _need(n_support, "n_support", torch.int32, (B, Hq))
+    if not (isinstance(ws, torch.Tensor) and ws.is_cuda and ws.dtype == torch.uint8
+            and ws.is_contiguous()):
+        raise TypeError("ws must be a contiguous uint8 GPU tensor")
+    d_ = s.desc()
+    _check("ekv_topk_decode", load_library().ekv_topk_decode(
+        ctypes.byref(d_), _ptr(q), float(scale), float(alpha), _ptr(K), _ptr(V),
+        _ptr(block_table), _ptr(seq_lens), int(top_k), _ptr(ub), _ptr(ubg), _ptr(hint),
+        _ptr(sel), _ptr(n_sel), _ptr(out), _ptr(tau), _ptr(n_support), _ptr(ws),
+        ctypes.c_size_t(ws.numel()), _stream()))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # EKV_NOALLOC_SCRATCH_BYTES

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libentmaxkv.so")
 ARCH = os.environ.get("EKV_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "meta.hip", "score.hip", "select.hip", "decode.hip", "softmax.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "step.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -277,13 +277,110 @@ static size_t step_zlb_bytes(const Shape& s) {
   return (((size_t)s.B * s.Hq * sizeof(float)) + 255) & ~(size_t)255;
 }
 
+// The box scorer's best-page hints of the decode step: int4 [pairs][slices][G].
+static size_t step_hint_bytes(const Shape& s) {
+  const ekv::ScoreSlices sl = ekv::score_box_slices(s);
+  return (((size_t)s.B * s.Hkv * sl.count * s.G * 16) + 255) & ~(size_t)255;
+}
+
+// Workspace of the top-k decode: the decode plan's candidate lists, then the
+// z_max lower bounds that the general path (shapes outside the fused
+// selection's limits) keeps between its launches.
+static size_t topk_decode_bytes(const Shape& s, int max_sel) {
+  return ekv::make_decode_plan(s, max_sel, false).total + step_zlb_bytes(s);
+}
+
+// Top-k selection and the pruned (ub != NULL) sparse entmax decode: fused
+// selection where the shape allows, else ekv_select_pages(TOPK) followed by
+// ekv_entmax_decode; the same results either way.  Arguments validated.
+static ekv_status topk_decode_launch(const Shape& s, const float* q, float scale, float alpha,
+                                     const void* K, const void* V, const int32_t* block_table,
+                                     const int32_t* seq_lens, int top_k, const float* ub,
+                                     const float* ubg, int32_t* sel, int32_t* n_sel, float* out,
+                                     float* tau_out, int32_t* n_support, void* ws,
+                                     const ekv::TopkHint& hint, hipStream_t stream) {
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  const ekv::DecodePlan plan = ekv::make_decode_plan(s, max_sel, false);
+  if (ekv::topk_decode_fast(s, max_sel))
+    return from_hip(ekv::launch_topk_decode(s, plan, q, scale, alpha, K, V, block_table, seq_lens,
+                                            top_k, ub, ubg, sel, n_sel, out, tau_out, n_support,
+                                            ws, hint, stream));
+  const hipError_t e = ekv::launch_topk(s, seq_lens, top_k, ubg, sel, n_sel, stream);
+  if (e != hipSuccess) return EKV_ERR_HIP;
+  float* zlb = ub != nullptr ? (float*)((char*)ws + plan.total) : nullptr;
+  return from_hip(ekv::launch_decode(s, plan, q, scale, alpha, K, V, block_table, seq_lens, sel,
+                                     n_sel, ub, zlb, out, tau_out, n_support, ws, false, stream));
+}
+
+size_t ekv_topk_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK || top_k < 1) return 0;
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return 0;
+  return topk_decode_bytes(s, max_sel);
+}
+
+ekv_status ekv_topk_decode(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
+                           const void* K, const void* V, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t top_k, const float* ub,
+                           const float* ubg, const void* hint, int32_t* sel, int32_t* n_sel,
+                           float* out, float* tau_out, int32_t* n_support, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(q) || !ok_vec(K) || !ok_vec(V) || !ok_i32(block_table) || !ok_i32(seq_lens) ||
+      !ok_i32(ubg) || !ok_i32(sel) || !ok_i32(n_sel) || !ok_vec(out))
+    return EKV_ERR_INVALID_ARG;
+  if (ub != nullptr && !aligned(ub, 16)) return EKV_ERR_INVALID_ARG;
+  if (tau_out != nullptr && !aligned(tau_out, 4)) return EKV_ERR_INVALID_ARG;
+  if (n_support != nullptr && !aligned(n_support, 4)) return EKV_ERR_INVALID_ARG;
+  if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
+  if (top_k < 1) return EKV_ERR_INVALID_ARG;
+  const int max_sel = top_k < s.maxP ? top_k : s.maxP;
+  if (!ekv::decode_shape_supported(s, max_sel)) return EKV_ERR_UNSUPPORTED;
+  if (hint != nullptr && !aligned(hint, 16)) return EKV_ERR_INVALID_ARG;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < topk_decode_bytes(s, max_sel))
+    return EKV_ERR_WORKSPACE;
+  const ekv::ScoreSlices sl = ekv::score_box_slices(s);
+  return topk_decode_launch(s, q, scale, alpha, K, V, block_table, seq_lens, top_k, ub, ubg, sel,
+                            n_sel, out, tau_out, n_support, ws,
+                            ekv::TopkHint{(const int4*)hint, sl.pages, sl.count}, stream);
+}
+
+size_t ekv_score_hint_bytes(const ekv_cache_desc* desc) {
+  Shape s;
+  if (make_shape(desc, &s) != EKV_OK) return 0;
+  return step_hint_bytes(s);
+}
+
+ekv_status ekv_score_box_pages(const ekv_cache_desc* desc, const float* q, float scale,
+                               const void* K, const int32_t* block_table,
+                               const int32_t* seq_lens, int32_t refresh_last_page, void* kmin,
+                               void* kmax, float* ub, float* ubg, void* hint,
+                               hipStream_t stream) {
+  Shape s;
+  ekv_status st = make_shape(desc, &s);
+  if (st != EKV_OK) return st;
+  if (!ok_vec(q) || !ok_i32(block_table) || !ok_i32(seq_lens) || !ok_vec(kmin) ||
+      !ok_vec(kmax) || !ok_i32(ubg))
+    return EKV_ERR_INVALID_ARG;
+  if (refresh_last_page && !ok_vec(K)) return EKV_ERR_INVALID_ARG;
+  if (ub != nullptr && !aligned(ub, 16)) return EKV_ERR_INVALID_ARG;
+  if (hint != nullptr && !aligned(hint, 16)) return EKV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return EKV_ERR_INVALID_ARG;
+  return from_hip(ekv::launch_score_box(s, q, scale, K, kmin, kmax, block_table, seq_lens,
+                                        refresh_last_page ? 1 : 0, ub, ubg, (int4*)hint, stream));
+}
+
 size_t ekv_step_workspace_bytes(const ekv_cache_desc* desc, int32_t top_k) {
   Shape s;
   if (make_shape(desc, &s) != EKV_OK || top_k < 1) return 0;
   const int max_sel = top_k < s.maxP ? top_k : s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return 0;
-  return step_counter_bytes(s) + step_bound_bytes(s) + step_zlb_bytes(s) +
-         ekv::make_decode_plan(s, max_sel, false).total;
+  return step_counter_bytes(s) + step_bound_bytes(s) + step_hint_bytes(s) +
+         topk_decode_bytes(s, max_sel);
 }
 
 ekv_status ekv_decode_step(const ekv_cache_desc* desc, const float* q, float scale, float alpha,
@@ -326,20 +423,21 @@ ekv_status ekv::decode_step_parts(const ekv_cache_desc* desc, const float* q, fl
   make_shape(desc, &s);
   const int max_sel = top_k < s.maxP ? top_k : s.maxP;
   const size_t ubytes = step_bound_bytes(s);
-  const size_t zbytes = step_zlb_bytes(s);
-  const size_t dbytes = ekv::make_decode_plan(s, max_sel, false).total;
+  const size_t hbytes = step_hint_bytes(s);
+  const size_t tbytes = topk_decode_bytes(s, max_sel);
   if (counters == nullptr || !aligned(counters, 256) || counter_bytes < step_counter_bytes(s))
     return EKV_ERR_WORKSPACE;
-  if (rest == nullptr || !aligned(rest, 256) || rest_bytes < ubytes + zbytes + dbytes)
+  if (rest == nullptr || !aligned(rest, 256) || rest_bytes < ubytes + hbytes + tbytes)
     return EKV_ERR_WORKSPACE;
   float* ub = (float*)rest;
-  float* zlb = (float*)((char*)rest + ubytes);
-  st = ekv_score_select_pages(desc, q, scale, K, block_table, seq_lens, refresh_last_page, top_k,
-                              kmin, kmax, ub, ubg, sel, n_sel, counters, counter_bytes, stream);
-  if (st != EKV_OK) return st;
-  return ekv_entmax_decode(desc, q, scale, alpha, K, V, block_table, seq_lens, sel, n_sel,
-                           max_sel, ub, zlb, out, tau_out, n_support,
-                           (char*)rest + ubytes + zbytes, dbytes, stream);
+  int4* hint = (int4*)((char*)rest + ubytes);
+  const ekv::ScoreSlices sl = ekv::score_box_slices(s);
+  const hipError_t e = ekv::launch_score_box(s, q, scale, K, kmin, kmax, block_table, seq_lens,
+                                             refresh_last_page ? 1 : 0, ub, ubg, hint, stream);
+  if (e != hipSuccess) return EKV_ERR_HIP;
+  return topk_decode_launch(s, q, scale, alpha, K, V, block_table, seq_lens, top_k, ub, ubg, sel,
+                            n_sel, out, tau_out, n_support, (char*)rest + ubytes + hbytes,
+                            ekv::TopkHint{hint, sl.pages, sl.count}, stream);
 }
 
 ekv_status ekv::validate_step(const ekv_cache_desc* desc, const float* q, float scale,
@@ -372,7 +470,7 @@ size_t ekv::step_scratch_bytes(const ekv_cache_desc* desc, int32_t top_k, size_t
   const int max_sel = top_k < s.maxP ? top_k : s.maxP;
   if (!ekv::decode_shape_supported(s, max_sel)) return 0;
   *counter_bytes = step_counter_bytes(s);
-  return step_bound_bytes(s) + step_zlb_bytes(s) + ekv::make_decode_plan(s, max_sel, false).total;
+  return step_bound_bytes(s) + step_hint_bytes(s) + topk_decode_bytes(s, max_sel);
 }
 
 extern "C" {

@@ -172,15 +172,170 @@ struct alignas(16) TopkRegLds {
   int wsum2[4];
   uint32_t mm[8];
   int s_digit, s_above, s_cnt;
+  // the few keys of the threshold bin, ranked exactly (topk_threshold)
+  uint32_t cand_key[kWave];
+  int cand_page[kWave];
+  int cand_n;
+  uint32_t res_T;
+  int res_rem;
 };
 
-template <int kPerThread, bool kCoherentU>
-__device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int n, int k,
-                                               int32_t* __restrict__ out, TopkRegLds& sm) {
+// Inclusive prefix sum over a 256-thread block with LDS-only barriers (global
+// loads in flight stay in flight); `sh` holds 4 ints of LDS.
+__device__ __forceinline__ int block_incl_scan_lds(int x, int* sh) {
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+  x = wave_incl_scan_i32(x);
+  if (lane == kWave - 1) sh[w] = x;
+  lds_barrier();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += sh[i];
+  lds_barrier();
+  return x + add;
+}
+
+// Threshold of a top-k selection: every key > T is selected, and of the keys
+// equal to T the first `rem` in page order (cut: every key >= T, rem unused).
+struct TopkThr {
+  uint32_t T;
+  int rem;
+  bool cut;
+};
+
+// Top-k threshold over order keys in registers (thread t holds pages
+// t * kPerThread + i for i < nv; k < n <= 256 * kPerThread): range-adaptive
+// radix passes as in topk_reg_keys, but as soon as the bin that holds the k-th
+// key has at most 64 keys they are gathered into LDS and one wave ranks them
+// exactly (by key, then page), which replaces the remaining passes.  Only LDS
+// and registers are used, so the barriers are LDS-only: global loads the
+// caller issued before stay in flight.
+template <int kPerThread>
+__device__ __forceinline__ TopkThr topk_threshold(const uint32_t (&key)[kPerThread], int nv, int k,
+                                                 TopkRegLds& sm) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int p0 = tid * kPerThread;
+  // the first histogram buffer is cleared here, the second during pass 0
+  for (int i = tid; i < 2048; i += kBlk) sm.hist[0][i] = 0;
+  if (tid == 0) sm.cand_n = 0;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (i < nv) {
+      kmn = min(kmn, key[i]);
+      kmx = max(kmx, key[i]);
+    }
+  kmn = wave_min_u32(kmn);
+  kmx = wave_max_u32(kmx);
+  if (lane == 0) {
+    sm.mm[wave] = kmn;
+    sm.mm[4 + wave] = kmx;
+  }
+  lds_barrier();
+  uint32_t lo = min(min(sm.mm[0], sm.mm[1]), min(sm.mm[2], sm.mm[3]));
+  uint32_t hi = max(max(sm.mm[4], sm.mm[5]), max(sm.mm[6], sm.mm[7]));
+  int remaining = k;
+  bool cut = false;
+  for (int pass = 0; pass < 4; ++pass) {
+    int* hist = sm.hist[pass & 1];
+    int* next = sm.hist[(pass + 1) & 1];
+    const uint32_t span = hi - lo;
+    const int width = span == 0u ? 0 : 32 - __clz((int)span);
+    const int shift = width > 11 ? width - 11 : 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      if (i < nv && key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> shift], 1);
+    lds_barrier();                                     // (1) histogram complete
+    const int4* h4 = reinterpret_cast<const int4*>(hist + 2040 - 8 * tid);
+    const int4 a = h4[0], b = h4[1];
+    const int bins[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};  // bins[7] = highest digit
+    reinterpret_cast<int4*>(next + 2040 - 8 * tid)[0] = make_int4(0, 0, 0, 0);
+    reinterpret_cast<int4*>(next + 2040 - 8 * tid)[1] = make_int4(0, 0, 0, 0);
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) local += bins[i];
+    int incl = wave_incl_scan(local);
+    if (lane == kWave - 1) sm.wsum[wave] = incl;
+    lds_barrier();                                     // (2) wave totals
+    for (int w = 0; w < wave; ++w) incl += sm.wsum[w];
+    const int excl = incl - local;
+    if (excl < remaining && remaining <= incl) {
+      int acc = excl;
+      bool found = false;
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        if (!found && acc + bins[i] >= remaining) {
+          sm.s_digit = 2040 - 8 * tid + i;
+          sm.s_above = acc;
+          sm.s_cnt = bins[i];
+          found = true;
+        }
+        if (!found) acc += bins[i];
+      }
+    }
+    lds_barrier();                                     // (3) chosen bin
+    const int digit = sm.s_digit, above = sm.s_above, cnt = sm.s_cnt;
+    const uint32_t nlo = lo + ((uint32_t)digit << shift);
+    const uint32_t top = shift == 0 ? nlo : nlo + ((1u << shift) - 1u);
+    hi = top < hi ? top : hi;
+    lo = nlo;
+    remaining -= above;
+    cut = (cnt == remaining);
+    if (cut || shift == 0) break;
+    if (cnt <= kWave) {
+      // the bin's keys (at most 64), in any order; the wsum of this pass has
+      // been read by every thread (barrier 3), the LDS below is not used yet
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i)
+        if (i < nv && key[i] >= lo && key[i] <= hi) {
+          const int slot = atomicAdd(&sm.cand_n, 1);
+          sm.cand_key[slot] = key[i];
+          sm.cand_page[slot] = p0 + i;
+        }
+      lds_barrier();
+      if (wave == 0) {
+        // rank = keys before this one in the order (larger key, then lower
+        // page); lane j's key and page come back through readlane, so the
+        // loop has no memory access
+        const bool live = lane < cnt;
+        const uint32_t mk = live ? sm.cand_key[lane] : 0u;
+        const int mp = live ? sm.cand_page[lane] : 0;
+        int rank = 0;
+        for (int j = 0; j < cnt; ++j) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+          const int pj = __builtin_amdgcn_readlane(mp, j);
+          rank += (kj > mk || (kj == mk && pj < mp)) ? 1 : 0;
+        }
+        // the remaining-th key of the bin is the threshold; keys above it in
+        // the bin are all selected, of those equal to it the first rem
+        const uint64_t at = __ballot(live && rank == remaining - 1);
+        const int src = __ffsll((long long)at) - 1;
+        const uint32_t T = (uint32_t)__builtin_amdgcn_readlane((int)mk, src);
+        const int gt = __popcll(__ballot(live && mk > T));
+        if (lane == 0) {
+          sm.res_T = T;
+          sm.res_rem = remaining - gt;
+        }
+      }
+      lds_barrier();
+      return TopkThr{sm.res_T, sm.res_rem, false};
+    }
+  }
+  return TopkThr{lo, remaining, cut};
+}
+
+// The selection itself, on keys already in registers: thread t holds the
+// order keys of pages t * kPerThread + i for i < nv (n pages in all, k < n);
+// the selected pages are written ascending to out[0 .. k) (global or LDS).
+template <int kPerThread, typename OutT>
+__device__ __forceinline__ void topk_reg_keys(const uint32_t (&key)[kPerThread], int nv, int k,
+                                              OutT* __restrict__ out, TopkRegLds& sm);
+
+template <int kPerThread, bool kCoherentU>
+__device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int n, int k,
+                                               int32_t* __restrict__ out, TopkRegLds& sm) {
+  const int p0 = threadIdx.x * kPerThread;
   const int nv = max(0, min(kPerThread, n - p0));
   uint32_t key[kPerThread];
 #pragma unroll
@@ -194,6 +349,16 @@ __device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int 
     }
     key[i] = order_key(u);
   }
+  topk_reg_keys<kPerThread>(key, nv, k, out, sm);
+}
+
+template <int kPerThread, typename OutT>
+__device__ __forceinline__ void topk_reg_keys(const uint32_t (&key)[kPerThread], int nv, int k,
+                                              OutT* __restrict__ out, TopkRegLds& sm) {
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int p0 = tid * kPerThread;
   // clear both histogram buffers; min / max of the keys
   for (int i = tid; i < 2 * 2048; i += kBlk) (&sm.hist[0][0])[i] = 0;
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;

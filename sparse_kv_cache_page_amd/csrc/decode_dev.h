@@ -458,36 +458,23 @@ struct QkLds {
   __attribute__((aligned(16))) uint16_t qparts[kMfma ? G : 1][3][kMfma ? D : 8];
 };
 
-// What a qk item was about (for the callers' arrival protocols).
-struct QkItemInfo {
-  bool ran;
-  int pair, b, g, L, np, nsel;
-};
-
-// One qk work item: scores of one split of a (row, KV head)'s selected token
-// slots for the G heads of the group, then per head the split maximum and the
-// candidates z > split_max - 1.  kOutCoherent: the candidates, counts and
-// maxima are read by another workgroup of the same launch (device-coherent
-// stores).  Called by all threads of the workgroup; ends with the LDS of `sm`
-// still in use (callers barrier before reuse).
-template <typename T, int D, int G, bool kOutCoherent, bool kMfma = std::is_same<T, bf16_t>::value>
-__device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item,
-                                              QkLds<T, D, G, kMfma>& sm) {
+// Scores of the token slots [r_begin, r_end) of an item for the G heads of a
+// group into sm.zl[h][r - r_begin]: slot r is token r & (P-1) of page-map
+// entry (r >> log2P) - j_begin (physical page sm.pg_phys, valid tokens
+// sm.pg_valid; a token at or past the valid count gets -inf and is not read).
+// qg: the group's queries [G][D]; qv: for the matrix-core path, this thread's
+// elements idx = threadIdx.x + u * kBlock of qg, loaded by the caller (so the
+// load can share an earlier round trip).  Called by all threads; ends with a
+// barrier (zl complete).
+template <typename T, int D, int G, bool kMfma>
+__device__ __forceinline__ void qk_score_slots(const float* __restrict__ qg,
+                                               const float (&qv)[kMfma ? (G * D + kBlock - 1) / kBlock : 1],
+                                               float zscale, const T* __restrict__ K, int Hkv,
+                                               int g, int P, int log2P, int r_begin, int r_end,
+                                               int j_begin, QkLds<T, D, G, kMfma>& sm) {
   using GE = Geo<T, D>;
   constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kRowsPerPass = GE::kRowsPerPass, kR = GE::kR;
-  static_assert(G <= kLpr, "lane c < G stores head c");
-  const float* __restrict__ q = a.q;
-  const float zscale = a.zscale;
-  const T* __restrict__ K = a.K;
-  const int32_t* __restrict__ bt = a.bt;
-  const int32_t* __restrict__ lens = a.lens;
-  const int32_t* sel = a.sel;
-  const int32_t* n_sel = a.n_sel;
-  const int max_sel = a.max_sel, Hkv = a.Hkv, P = a.P, log2P = a.log2P, maxP = a.maxP;
-  const int splits = a.splits;
-  float2* __restrict__ cand = a.cand;
-  int* __restrict__ cnt = a.cnt;
-  float* __restrict__ smax = a.smax;
+  constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
   auto& zl = sm.zl;
   auto& pg_phys = sm.pg_phys;
   auto& pg_valid = sm.pg_valid;
@@ -496,73 +483,10 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   const int rg = threadIdx.x / kLpr;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int Hq = Hkv * G;
   const size_t tile_stride = (size_t)P * D;
-  (void)rg;
-  (void)kRowsPerPass;
-  QkItemInfo info{false, 0, 0, 0, 0, 0, 0};
-  // split-major numbering: consecutive items are the same split of
-  // consecutive pairs, so a workgroup striding over the items visits many
-  // splits, and the low splits that short selections use spread over all
-  // workgroups (pair-major numbering gave workgroup i only split i % splits)
-  const int pair = (int)(item % a.npairs);
-  const int s = (int)(item / a.npairs);
-  const int b = pair / Hkv;
-  const int g = pair % Hkv;
-  const int r_begin = s * kR;
-  const int j_begin = r_begin >> log2P;
-  // the selected page indices this split can cover, loaded before the row
-  // length and the selection count are known (same round trip); entries past
-  // the count are in bounds but never used
-  constexpr int kSpec = (kR + kBlock - 1) / kBlock;
-  int spec[kSpec];
-#pragma unroll
-  for (int u = 0; u < kSpec; ++u) {
-    const int i = threadIdx.x + u * kBlock;
-    spec[u] = 0;
-    if (sel && i < kR && j_begin + i < maxP) spec[u] = sel[(size_t)pair * maxP + j_begin + i];
-  }
-  // the group's queries (matrix-core path), also requested in that round trip
-  constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
-  float qv[kMfma ? kQPer : 1];
-  if constexpr (kMfma) {
-#pragma unroll
-    for (int u = 0; u < kQPer; ++u) {
-      const int idx = threadIdx.x + u * kBlock;
-      qv[u] = idx < G * D ? q[((size_t)b * Hq + g * G) * D + idx] : 0.0f;
-    }
-  }
-  const int L = lens[b];
-  const int np = (L + P - 1) / P;
-  const int nsel = min(sel ? n_sel[pair] : np, max_sel);
-  const int r_end = min(nsel << log2P, r_begin + kR);
-  if (r_begin >= r_end) return info;  // uniform over the block
-  const int n_pg = ((r_end - 1) >> log2P) - j_begin + 1;  // <= kR
-
-  // page map of this split: physical page and valid tokens per selected page
-  // (0 for a page below every head's support, which is then not read)
-  float zlb_h[G];
-  if (a.ub) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) zlb_h[h] = a.zlb[(size_t)b * Hq + g * G + h];
-  }
-#pragma unroll
-  for (int u = 0; u < kSpec; ++u) {
-    const int i = threadIdx.x + u * kBlock;
-    if (i < n_pg) {
-      const int page = sel ? spec[u] : j_begin + i;
-      pg_phys[i] = bt[(size_t)b * maxP + page];
-      bool needed = true;
-      if (a.ub) {
-        needed = false;
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          needed |= !page_below_support(a.a1 * a.ub[((size_t)pair * maxP + page) * G + h],
-                                        zlb_h[h]);
-      }
-      pg_valid[i] = needed ? page_valid(L, page, P) : 0;
-    }
-  }
+  (void)kQPer;
+  (void)qparts;
+  (void)lane;
   if constexpr (kMfma) {
     // ---- matrix cores: [16 tokens x d] . [d x (G heads x 3 bf16 parts)] ----
     // A rows m = 4*head + part hold q split exactly into three bf16 parts
@@ -644,7 +568,7 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   float qf[G][kVec];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float4* qh = reinterpret_cast<const float4*>(q + ((size_t)b * Hq + g * G + h) * D + c * kVec);
+    const float4* qh = reinterpret_cast<const float4*>(qg + (size_t)h * D + c * kVec);
 #pragma unroll
     for (int v4 = 0; v4 < kVec / 4; ++v4) {
       const float4 x = qh[v4];
@@ -693,15 +617,29 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   __syncthreads();
 
   }
+}
 
+// One wave per head: the item's maximum over its nrows scores in sm.zl, then
+// the candidates z > max - 1 as (z, physical token) pairs in slot order, their
+// count and the maximum, at split s of head bh0 + h.  kOutCoherent: another
+// workgroup of the same launch reads them (device-coherent stores).
+template <typename T, int D, int G, bool kOutCoherent, bool kMfma>
+__device__ __forceinline__ void qk_emit(QkLds<T, D, G, kMfma>& sm, int nrows, int r_begin,
+                                        int j_begin, int P, int log2P, float2* __restrict__ cand,
+                                        int* __restrict__ cnt, float* __restrict__ smax,
+                                        size_t bh0, int splits, int s) {
+  constexpr int kR = Geo<T, D>::kR;
+  auto& zl = sm.zl;
+  auto& pg_phys = sm.pg_phys;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
   // one wave per head: split maximum, then the candidates z > max - 1
-  const int nrows = r_end - r_begin;
   for (int h = wave; h < G; h += kBlock / kWave) {
     float m = -__builtin_huge_valf();
     for (int r = lane; r < nrows; r += kWave) m = fmaxf(m, zl[h][r]);
     m = wave_max_f32(m);
     const double thr = (double)m - 1.0;
-    const size_t bh = (size_t)b * Hq + g * G + h;
+    const size_t bh = bh0 + h;
     float2* out = cand + (bh * splits + s) * kR;
     int total = 0;
     for (int r0 = 0; r0 < nrows; r0 += kWave) {
@@ -732,6 +670,108 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
       }
     }
   }
+}
+
+// What a qk item was about (for the callers' arrival protocols).
+struct QkItemInfo {
+  bool ran;
+  int pair, b, g, L, np, nsel;
+};
+
+// One qk work item: scores of one split of a (row, KV head)'s selected token
+// slots for the G heads of the group, then per head the split maximum and the
+// candidates z > split_max - 1.  kOutCoherent: the candidates, counts and
+// maxima are read by another workgroup of the same launch (device-coherent
+// stores).  Called by all threads of the workgroup; ends with the LDS of `sm`
+// still in use (callers barrier before reuse).
+template <typename T, int D, int G, bool kOutCoherent, bool kMfma = std::is_same<T, bf16_t>::value>
+__device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item,
+                                              QkLds<T, D, G, kMfma>& sm) {
+  using GE = Geo<T, D>;
+  constexpr int kLpr = GE::kLpr, kR = GE::kR;
+  static_assert(G <= kLpr, "lane c < G stores head c");
+  const float* __restrict__ q = a.q;
+  const float zscale = a.zscale;
+  const T* __restrict__ K = a.K;
+  const int32_t* __restrict__ bt = a.bt;
+  const int32_t* __restrict__ lens = a.lens;
+  const int32_t* sel = a.sel;
+  const int32_t* n_sel = a.n_sel;
+  const int max_sel = a.max_sel, Hkv = a.Hkv, P = a.P, log2P = a.log2P, maxP = a.maxP;
+  const int splits = a.splits;
+  float2* __restrict__ cand = a.cand;
+  int* __restrict__ cnt = a.cnt;
+  float* __restrict__ smax = a.smax;
+  auto& pg_phys = sm.pg_phys;
+  auto& pg_valid = sm.pg_valid;
+  const int Hq = Hkv * G;
+  QkItemInfo info{false, 0, 0, 0, 0, 0, 0};
+  // split-major numbering: consecutive items are the same split of
+  // consecutive pairs, so a workgroup striding over the items visits many
+  // splits, and the low splits that short selections use spread over all
+  // workgroups (pair-major numbering gave workgroup i only split i % splits)
+  const int pair = (int)(item % a.npairs);
+  const int s = (int)(item / a.npairs);
+  const int b = pair / Hkv;
+  const int g = pair % Hkv;
+  const int r_begin = s * kR;
+  const int j_begin = r_begin >> log2P;
+  // the selected page indices this split can cover, loaded before the row
+  // length and the selection count are known (same round trip); entries past
+  // the count are in bounds but never used
+  constexpr int kSpec = (kR + kBlock - 1) / kBlock;
+  int spec[kSpec];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int i = threadIdx.x + u * kBlock;
+    spec[u] = 0;
+    if (sel && i < kR && j_begin + i < maxP) spec[u] = sel[(size_t)pair * maxP + j_begin + i];
+  }
+  // the group's queries (matrix-core path), also requested in that round trip
+  constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
+  float qv[kMfma ? kQPer : 1];
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int idx = threadIdx.x + u * kBlock;
+      qv[u] = idx < G * D ? q[((size_t)b * Hq + g * G) * D + idx] : 0.0f;
+    }
+  }
+  const int L = lens[b];
+  const int np = (L + P - 1) / P;
+  const int nsel = min(sel ? n_sel[pair] : np, max_sel);
+  const int r_end = min(nsel << log2P, r_begin + kR);
+  if (r_begin >= r_end) return info;  // uniform over the block
+  const int n_pg = ((r_end - 1) >> log2P) - j_begin + 1;  // <= kR
+
+  // page map of this split: physical page and valid tokens per selected page
+  // (0 for a page below every head's support, which is then not read)
+  float zlb_h[G];
+  if (a.ub) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) zlb_h[h] = a.zlb[(size_t)b * Hq + g * G + h];
+  }
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int i = threadIdx.x + u * kBlock;
+    if (i < n_pg) {
+      const int page = sel ? spec[u] : j_begin + i;
+      pg_phys[i] = bt[(size_t)b * maxP + page];
+      bool needed = true;
+      if (a.ub) {
+        needed = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          needed |= !page_below_support(a.a1 * a.ub[((size_t)pair * maxP + page) * G + h],
+                                        zlb_h[h]);
+      }
+      pg_valid[i] = needed ? page_valid(L, page, P) : 0;
+    }
+  }
+  qk_score_slots<T, D, G, kMfma>(q + ((size_t)b * Hq + g * G) * D, qv, zscale, K, Hkv, g, P,
+                                 log2P, r_begin, r_end, j_begin, sm);
+  qk_emit<T, D, G, kOutCoherent, kMfma>(sm, r_end - r_begin, r_begin, j_begin, P, log2P, cand, cnt,
+                                        smax, (size_t)b * Hq + g * G, splits, s);
   info = QkItemInfo{true, pair, b, g, L, np, nsel};
   return info;
 }

@@ -48,6 +48,19 @@ hipError_t launch_score_select(const Shape& s, const float* q, float scale, cons
                                int refresh, float* ub, float* ubg, int top_k, int32_t* sel,
                                int32_t* n_sel, int* counters, hipStream_t stream);
 
+// Box-bound scores only (top-k policy metadata), with an optional rebuild of
+// each row's last page's box first (refresh).  hint (or NULL): per (pair,
+// page slice, head) the slice's best page, {bound bits, page, physical page,
+// 0} as int4 [pairs][score_box_slices(s).count][G].
+struct ScoreSlices {
+  int pages;  // pages per slice (one workgroup each)
+  int count;  // slices per pair at max_pages_per_seq
+};
+ScoreSlices score_box_slices(const Shape& s);
+hipError_t launch_score_box(const Shape& s, const float* q, float scale, const void* K,
+                            void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
+                            int refresh, float* ub, float* ubg, int4* hint, hipStream_t stream);
+
 hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const float* ubg,
                        int32_t* sel, int32_t* n_sel, hipStream_t stream);
 
@@ -89,6 +102,25 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& plan, const float* q,
                          const int32_t* lens, const int32_t* sel, const int32_t* n_sel,
                          const float* ub, float* zlb, float* out, float* tau_out,
                          int32_t* n_support, void* ws, bool fused, hipStream_t stream);
+
+// Top-k selection fused into the decode's key stage (one launch: every work
+// item selects, probes its pair's heads with ub (NULL: no pruning) and scores
+// an even share of the pages read), then the tau / PV stage.  Only for shapes
+// with topk_decode_fast(s, plan.max_sel).
+// hint: the box scorer's best page per (pair, page slice, head) for this
+// query (NULL: none); with it each head's probe page is known before the
+// selection runs.
+struct TopkHint {
+  const int4* hint;
+  int slice_pages, nslices;
+};
+bool topk_decode_fast(const Shape& s, int max_sel);
+hipError_t launch_topk_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,
+                              float alpha, const void* K, const void* V, const int32_t* bt,
+                              const int32_t* lens, int top_k, const float* ub, const float* ubg,
+                              int32_t* sel, int32_t* n_sel, float* out, float* tau_out,
+                              int32_t* n_support, void* ws, const TopkHint& hint,
+                              hipStream_t stream);
 
 // Softmax decode (the comparison path): split-page partials (m, l, o) of
 // `slots` token slots each, merged per query head.

@@ -104,6 +104,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (slot, c) adds column c of the kLpr rows of its page slot in a fixed order,
 // so every (page, head) total is finished by one lane, and the group maximum
 // is taken over the G lanes that hold one page's heads.
+//
+// lbest / lbestp: this lane's largest bound and its page so far (the lane
+// finishes the bounds of head lane % G only, in increasing page order).
 template <typename T, int D, int G, int kVec, bool kGauss, bool kCoherentU = false,
           typename M = float>
 __device__ __forceinline__ void score_range(
@@ -111,7 +114,8 @@ __device__ __forceinline__ void score_range(
     const T* __restrict__ kmax, const M* __restrict__ mean, const M* __restrict__ var,
     const int* s_pi, int b, int g, int pair, int Hkv, int maxP, int p_begin, int p_end,
     float* __restrict__ ub, float* __restrict__ ubg, double* __restrict__ gm,
-    double* __restrict__ gv, double (*red)[ScoreGeo<D, G, kVec, kGauss>::kPitch]) {
+    double* __restrict__ gv, double (*red)[ScoreGeo<D, G, kVec, kGauss>::kPitch],
+    float& lbest, int& lbestp) {
   using Geo = ScoreGeo<D, G, kVec, kGauss>;
   constexpr int kLpr = Geo::kLpr;
   constexpr int kPagesPerWave = kWave / kLpr;
@@ -246,6 +250,10 @@ __device__ __forceinline__ void score_range(
       // in adjacent lanes and adjacent words, so the stores coalesce and a
       // reader of one page gets all its heads from one 4G-byte chunk
       if (kind == 0 && live && ub != nullptr) ub[((size_t)pair * maxP + p) * G + h] = uh;
+      if (kind == 0 && live && uh > lbest) {  // pages increase: ties keep the lower
+        lbest = uh;
+        lbestp = p;
+      }
       if constexpr (kGauss) {
         if (kind == 1 && live) gm[o] = dscale * t;
         if (kind == 2 && live) gv[o] = dscale * dscale * t;
@@ -280,6 +288,44 @@ __device__ __forceinline__ void score_range(
   }
 }
 
+// The slice's best page for each head of the group (largest bound, lowest
+// page on ties) from the lanes' running bests: lane l follows head l % G.
+// Written as {bound bits, page, physical page, 0} to
+// hint[(pair * nslices + slice) * G + h]; a slice without a finite bound
+// gets page -1.  Called by all threads after the scoring loop.
+template <int G>
+__device__ __forceinline__ void write_slice_best(float lbest, int lbestp, const int* s_pi,
+                                                 int p_begin, int4* __restrict__ hint,
+                                                 float (*sb)[G], int (*sp)[G]) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const bool mine = lane % G == h;
+    const float wb = wave_max_f32(mine ? lbest : -__builtin_huge_valf());
+    const uint32_t wp =
+        wave_min_u32(mine && lbest == wb ? (uint32_t)lbestp : 0xFFFFFFFFu);
+    if (lane == 0) {
+      sb[wave][h] = wb;
+      sp[wave][h] = (int)wp;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float bv = sb[0][h];
+    int bp = sp[0][h];
+#pragma unroll
+    for (int w = 1; w < kScoreWaves; ++w)
+      if (sb[w][h] > bv || (sb[w][h] == bv && (uint32_t)sp[w][h] < (uint32_t)bp)) {
+        bv = sb[w][h];
+        bp = sp[w][h];
+      }
+    const bool ok = bv > -__builtin_huge_valf() && bp >= p_begin;
+    hint[h] = make_int4(__float_as_int(bv), ok ? bp : -1, ok ? s_pi[bp - p_begin] : 0, 0);
+  }
+}
+
 // Pages per workgroup: whole batches of per_iter pages, enough workgroups to
 // fill the chip once (kScoreResidentBlocks) for short batches, and at most
 // kSlicePages, so long rows are cut into many slices that later workgroups
@@ -296,16 +342,23 @@ int slice_pages(const Shape& s, int per_iter) {
   return per_iter * iters;
 }
 
+// refresh (box-only metadata): the workgroup holding a row's last page first
+// rebuilds that page's bounding box from the K rows (the page a decode step
+// has just appended to); only this workgroup reads it, so the barrier below,
+// which waits for the stores, publishes it.
 template <typename T, int D, int G, int kVec, bool kGauss, typename M = float>
 __global__ __launch_bounds__(kScoreBlock) void score_kernel(
-    const float* __restrict__ q, float scale, const T* __restrict__ kmin,
-    const T* __restrict__ kmax, const M* __restrict__ mean, const M* __restrict__ var,
+    const float* __restrict__ q, float scale, T* __restrict__ kmin,
+    T* __restrict__ kmax, const M* __restrict__ mean, const M* __restrict__ var,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ lens, int Hkv, int P, int maxP,
     int pages_per_block, int npairs, float* __restrict__ ub, float* __restrict__ ubg,
-    double* __restrict__ gm, double* __restrict__ gv) {
+    double* __restrict__ gm, double* __restrict__ gv, const T* __restrict__ K, int refresh,
+    int4* __restrict__ hint, int nslices) {
   using Geo = ScoreGeo<D, G, kVec, kGauss>;
   __shared__ int s_pi[kMaxPagesPerBlock];
   __shared__ ScoreRedLds<Geo::kPitch> red;
+  __shared__ float s_hb[kScoreWaves][G];
+  __shared__ int s_hp[kScoreWaves][G];
   const int pair = (int)(blockIdx.x % (unsigned)npairs);
   const int b = pair / Hkv;
   const int g = pair % Hkv;
@@ -318,11 +371,21 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
   const int np = (L + P - 1) / P;
   if (p_begin >= np) return;
   const int p_end = min(np, p_begin + pages_per_block);
+  if constexpr (!kGauss) {
+    if (refresh && p_end == np && threadIdx.x < kWave)
+      meta_tile<T, D, float>(K, Hkv, P, bt[(size_t)b * maxP + np - 1], g,
+                             page_valid(L, np - 1, P), kmin, kmax, nullptr, nullptr);
+  }
   __syncthreads();
+  float lbest = -__builtin_huge_valf();
+  int lbestp = 0x7fffffff;
   score_range<T, D, G, kVec, kGauss, false, M>(q, scale, kmin, kmax, mean, var, s_pi, b, g, pair,
-                                               Hkv, maxP,
-                                     p_begin, p_end, ub, ubg, gm, gv,
-                                     red.v[threadIdx.x / kWave]);
+                                               Hkv, maxP, p_begin, p_end, ub, ubg, gm, gv,
+                                               red.v[threadIdx.x / kWave], lbest, lbestp);
+  if (hint != nullptr)
+    write_slice_best<G>(lbest, lbestp, s_pi, p_begin,
+                        hint + ((size_t)pair * nslices + p_begin / pages_per_block) * G, s_hb,
+                        s_hp);
 }
 
 // Fused first half of a decode step (top-k policy): optionally rebuild the
@@ -372,10 +435,12 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
                            page_valid(L, np - 1, P), kmin, kmax, nullptr, nullptr);
   }
   __syncthreads();
+  float lbest = -__builtin_huge_valf();
+  int lbestp = 0x7fffffff;
   score_range<T, D, G, kVec, false, true, float>(q, scale, kmin, kmax, nullptr, nullptr, s_pi, b,
-                                                 g, pair,
-                                          Hkv, maxP, p_begin, p_end, ub, ubg, nullptr,
-                                          nullptr, sm.red.v[threadIdx.x / kWave]);
+                                                 g, pair, Hkv, maxP, p_begin, p_end, ub, ubg,
+                                                 nullptr, nullptr, sm.red.v[threadIdx.x / kWave],
+                                                 lbest, lbestp);
   // arrival: every wave waits until its device-coherent bound stores have
   // completed, the barrier gathers the waves, then one relaxed device-scope
   // increment counts the block; the last block of the pair reads every bound
@@ -407,39 +472,46 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   }
 }
 
+}  // namespace
+ScoreSlices score_box_slices(const Shape& s);
+namespace {
+
 template <typename T, int D, int G, int kVec>
 hipError_t launch_score_t(const Shape& s, const float* q, float scale, const void* kmin,
                           const void* kmax, const void* mean, const void* var,
                           const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
-                          double* gm, double* gv, hipStream_t stream) {
+                          double* gm, double* gv, const void* K, int refresh, int4* hint,
+                          hipStream_t stream) {
   constexpr int kLpr = D / kVec;
   constexpr int kPagesPerStep = (kWave / kLpr) * kScoreWaves;
   const bool gauss = gm != nullptr;
   const int per_iter = kPagesPerStep * (gauss ? ScoreGeo<D, G, kVec, true>::kU
                                               : ScoreGeo<D, G, kVec, false>::kU);
   // enough blocks to spread the pairs over the chip (~4 per CU), each block
-  // a whole number of iterations
+  // a whole number of iterations (for the box bounds alone, the slices that
+  // score_box_slices reports, which size the best-page hints)
   const long long pairs = (long long)s.B * s.Hkv;
-  const int ppb = slice_pages(s, per_iter);
+  const int ppb = gauss ? slice_pages(s, per_iter) : score_box_slices(s).pages;
+  if (!gauss && ppb != slice_pages(s, per_iter)) return hipErrorInvalidValue;
   const long long nblocks = (long long)((s.maxP + ppb - 1) / ppb) * pairs;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)nblocks);
   const int npairs = (int)pairs;
   if (gauss && s.mom16) {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, true, bf16_t>), grid, dim3(kScoreBlock), 0,
-                       stream, q, scale, (const T*)kmin, (const T*)kmax, (const bf16_t*)mean,
+                       stream, q, scale, (T*)kmin, (T*)kmax, (const bf16_t*)mean,
                        (const bf16_t*)var, bt, lens, s.Hkv, s.P, s.maxP, ppb, npairs, ub, ubg, gm,
-                       gv);
+                       gv, (const T*)K, 0, nullptr, 0);
   } else if (gauss) {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, true>), grid, dim3(kScoreBlock), 0, stream, q,
-                       scale, (const T*)kmin, (const T*)kmax, (const float*)mean,
+                       scale, (T*)kmin, (T*)kmax, (const float*)mean,
                        (const float*)var, bt, lens, s.Hkv, s.P, s.maxP, ppb, npairs, ub, ubg, gm,
-                       gv);
+                       gv, (const T*)K, 0, nullptr, 0);
   } else {
     hipLaunchKernelGGL((score_kernel<T, D, G, kVec, false>), grid, dim3(kScoreBlock), 0, stream,
-                       q, scale, (const T*)kmin, (const T*)kmax, (const float*)nullptr,
+                       q, scale, (T*)kmin, (T*)kmax, (const float*)nullptr,
                        (const float*)nullptr, bt, lens, s.Hkv, s.P, s.maxP, ppb, npairs, ub, ubg,
-                       gm, gv);
+                       gm, gv, (const T*)K, refresh, hint, (s.maxP + ppb - 1) / ppb);
   }
   return hipGetLastError();
 }
@@ -448,7 +520,8 @@ template <typename T, int D>
 hipError_t launch_score_d(const Shape& s, const float* q, float scale, const void* kmin,
                           const void* kmax, const void* mean, const void* var,
                           const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
-                          double* gm, double* gv, hipStream_t stream) {
+                          double* gm, double* gv, const void* K, int refresh, int4* hint,
+                          hipStream_t stream) {
   // 16-byte loads while q+/q- fit comfortably in registers, 8-byte loads for
   // the 8-head group (halves the per-lane coordinates, hence the registers),
   // and for the 4-head group when the Gaussian moments are summed too: with
@@ -457,13 +530,13 @@ hipError_t launch_score_d(const Shape& s, const float* q, float scale, const voi
   constexpr int kV16 = 16 / sizeof(T);
   constexpr int kV8 = 8 / sizeof(T);
   switch (s.G) {
-    case 1: return launch_score_t<T, D, 1, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
-    case 2: return launch_score_t<T, D, 2, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
+    case 1: return launch_score_t<T, D, 1, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
+    case 2: return launch_score_t<T, D, 2, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
     case 4:
       if (gm != nullptr)
-        return launch_score_t<T, D, 4, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
-      return launch_score_t<T, D, 4, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
-    case 8: return launch_score_t<T, D, 8, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
+        return launch_score_t<T, D, 4, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
+      return launch_score_t<T, D, 4, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
+    case 8: return launch_score_t<T, D, 8, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -516,11 +589,36 @@ hipError_t launch_score(const Shape& s, const float* q, float scale, const void*
                         const int32_t* bt, const int32_t* lens, float* ub, float* ubg,
                         double* gm, double* gv, hipStream_t stream) {
   if (s.bf16) {
-    if (s.D == 128) return launch_score_d<bf16_t, 128>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
-    return launch_score_d<bf16_t, 64>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
+    if (s.D == 128) return launch_score_d<bf16_t, 128>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, nullptr, 0, nullptr, stream);
+    return launch_score_d<bf16_t, 64>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, nullptr, 0, nullptr, stream);
   }
-  if (s.D == 128) return launch_score_d<float, 128>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
-  return launch_score_d<float, 64>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, stream);
+  if (s.D == 128) return launch_score_d<float, 128>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, nullptr, 0, nullptr, stream);
+  return launch_score_d<float, 64>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, nullptr, 0, nullptr, stream);
+}
+
+ScoreSlices score_box_slices(const Shape& s) {
+  // the geometry launch_score_t uses for the box-only kernel
+  const int kv = s.bf16 ? (s.G == 8 ? 4 : 8) : (s.G == 8 ? 2 : 4);
+  const int lpr = s.D / kv;
+  const int per_step = (kWave / lpr) * kScoreWaves;
+  const int kinds_lanes = lpr < 16 ? lpr : 16;
+  int ku = kinds_lanes / s.G;
+  ku = ku < 1 ? 1 : (ku > 4 ? 4 : ku);
+  ScoreSlices r;
+  r.pages = slice_pages(s, per_step * ku);
+  r.count = (s.maxP + r.pages - 1) / r.pages;
+  return r;
+}
+
+hipError_t launch_score_box(const Shape& s, const float* q, float scale, const void* K,
+                            void* kmin, void* kmax, const int32_t* bt, const int32_t* lens,
+                            int refresh, float* ub, float* ubg, int4* hint, hipStream_t stream) {
+  if (s.bf16) {
+    if (s.D == 128) return launch_score_d<bf16_t, 128>(s, q, scale, kmin, kmax, nullptr, nullptr, bt, lens, ub, ubg, nullptr, nullptr, K, refresh, hint, stream);
+    return launch_score_d<bf16_t, 64>(s, q, scale, kmin, kmax, nullptr, nullptr, bt, lens, ub, ubg, nullptr, nullptr, K, refresh, hint, stream);
+  }
+  if (s.D == 128) return launch_score_d<float, 128>(s, q, scale, kmin, kmax, nullptr, nullptr, bt, lens, ub, ubg, nullptr, nullptr, K, refresh, hint, stream);
+  return launch_score_d<float, 64>(s, q, scale, kmin, kmax, nullptr, nullptr, bt, lens, ub, ubg, nullptr, nullptr, K, refresh, hint, stream);
 }
 
 hipError_t launch_score_select(const Shape& s, const float* q, float scale, const void* K,

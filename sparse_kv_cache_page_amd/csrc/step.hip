@@ -1,0 +1,712 @@
+// Top-k selection fused into the sparse alpha-entmax decode (EntmaxKV summary
+// page: §2.B(1) keep the k pages with the largest bounds; §2.C load only the
+// selected pages' keys and values; §3 only the support decides the output).
+//
+// One launch does what ekv_select_pages(TOPK) and the first stage of
+// ekv_entmax_decode do, without a round trip through a selection list in
+// memory and without a serial per-pair tail:
+//
+//   every work item (row, KV head, split) reads the pair's group bounds U,
+//   runs the top-k radix select itself (the items of a pair reach the same
+//   selection; split 0 also writes it out as sel / n_sel), and, with the
+//   per-head bounds, probes each query head's best selected page for a lower
+//   bound zlb of its largest score.  A selected page whose bound is below
+//   zlb - 1 for every head of the group holds no support token (tau >=
+//   z_max - 1), so its keys are not read.  The pages that remain are shared
+//   out evenly over the pair's items in ascending order (every item computes
+//   the same list), so the key stream is balanced over the workgroups; each
+//   item scores its pages for the G heads from one read (matrix cores for
+//   bf16) and writes its candidates z > item_max - 1.
+//
+// The tau / PV stage then runs as in ekv_entmax_decode.  Because the final
+// candidate set of a head is {z > z_max - 1} over the tokens read, in
+// ascending slot order, results are bit-identical to ekv_select_pages followed
+// by the pruned ekv_entmax_decode.
+#include "decode_dev.h"
+#include "kernels.h"
+
+namespace ekv {
+namespace {
+
+constexpr int kSelCap = 1024;                 // selected pages per pair held in LDS
+constexpr int kSelPer = kSelCap / kBlock;     // of them per thread
+constexpr int kProbeBatch = 4;                // probe key rows per thread in flight
+
+template <typename T>
+struct SelQkArgs {
+  const float* q;
+  float zscale;     // (alpha - 1) * scale
+  float a1;         // alpha - 1
+  const T* K;
+  const int32_t* bt;
+  const int32_t* lens;
+  const float* ub;   // [pairs][maxP][G] per-head page bounds, or NULL (no pruning)
+  const float* ubg;  // [pairs][maxP] group bounds
+  int32_t* sel;      // [pairs][maxP] written by split 0
+  int32_t* n_sel;    // [pairs] written by split 0
+  int top_k, Hkv, P, log2P, maxP, splits, npairs;
+  float2* cand;
+  int* cnt;
+  float* smax;
+  // the scorer's best page per (pair, page slice, head), or NULL:
+  // {bound bits, page, physical page, 0} [pairs][nslices][G], slices of
+  // slice_pages pages
+  const int4* hint;
+  int slice_pages, nslices;
+};
+
+template <typename T, int D, int G>
+struct SelQkLds {
+  union {
+    TopkRegLds tk;
+    QkLds<T, D, G> qk;
+  } u;
+  int s_sel[kSelCap];    // selected pages, ascending
+  int s_phys[kSelCap];   // their physical pages
+  int s_surv[kSelCap];   // pages read (indices into s_sel), ascending
+  unsigned char s_flag[kSelCap];
+  float rowz[G * kMaxPageSize];
+  float s_best[kBlock / kWave][G];
+  int s_bestj[kBlock / kWave][G];   // the page
+  int s_bestph[kBlock / kWave][G];  // its physical page
+  float zlb[G];
+  int probe_phys[G];
+  int probe_nv[G];
+  int probe_page[G];
+  int probe_sel[G];
+  int sh4[4];
+  int s_m;
+  float qraw[G * D];  // the group's queries (the probe of the hinted kernel)
+};
+
+// One work item per workgroup: item = split * pairs + pair (split-major: with
+// a multiple of 8 pairs, all items of a pair run on one XCD and share its L2
+// lines of the pair's bounds and probe rows).
+template <typename T, int D, int G, int kPer>
+__global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
+  using GE = Geo<T, D>;
+  constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kR = GE::kR;
+  constexpr int kRowsPerPass = kBlock / kLpr;
+  constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
+  constexpr bool kMfma = std::is_same<T, bf16_t>::value;
+  __shared__ SelQkLds<T, D, G> sm;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int pair = (int)(blockIdx.x % (unsigned)a.npairs);
+  const int s = (int)(blockIdx.x / (unsigned)a.npairs);
+  const int b = pair / a.Hkv;
+  const int g = pair % a.Hkv;
+  const int Hq = a.Hkv * G;
+  const int P = a.P, log2P = a.log2P, maxP = a.maxP;
+  const size_t bh0 = (size_t)b * Hq + (size_t)g * G;
+  const float* qg = a.q + bh0 * D;
+  const bool prune = a.ub != nullptr;
+
+  // ---- round trip 1: the row length, the pair's group bounds (kPer
+  // consecutive pages per thread; entries past the row's pages are in bounds
+  // and masked below) and the group's queries
+  const int p0 = tid * kPer;
+  const float* Ug = a.ubg + (size_t)pair * maxP;
+  float uv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) uv[i] = p0 + i < maxP ? Ug[p0 + i] : 0.0f;
+  float qv[kMfma ? kQPer : 1];
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int idx = tid + u * kBlock;
+      qv[u] = idx < G * D ? qg[idx] : 0.0f;
+    }
+  }
+  const int L = a.lens[b];
+  const int np = (L + P - 1) >> log2P;
+  const int nsel = min(a.top_k, np);
+  const int nsplit = ((nsel << log2P) + kR - 1) / kR;
+  if (s >= nsplit) {  // uniform: nothing to read for this item
+    if (s == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
+    return;
+  }
+
+  // ---- top-k: the nsel largest U, lowest page on ties, placed ascending
+  // (thread t's pages precede thread t+1's, so one block scan orders them)
+  {
+    const int nv = max(0, min(kPer, np - p0));
+    uint32_t key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) key[i] = order_key(uv[i]);
+    TopkThr th{0u, 0, true};  // nsel >= np: every page
+    if (nsel < np) th = topk_threshold<kPer>(key, nv, nsel, sm.u.tk);
+    bool take[kPer], eq[kPer];
+    int cg = 0, ce = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool v = i < nv;
+      take[i] = v && (th.cut ? key[i] >= th.T : key[i] > th.T);
+      eq[i] = v && !th.cut && key[i] == th.T;
+      cg += take[i] ? 1 : 0;
+      ce += eq[i] ? 1 : 0;
+    }
+    // counts below 2^16 each: one scan of both
+    const int both = cg | (ce << 16);
+    const int excl = block_incl_scan(both, sm.sh4) - both;
+    int eq_seen = excl >> 16;
+    int pos = (excl & 0xFFFF) + min(eq_seen, th.rem);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool tk = take[i] || (eq[i] && eq_seen < th.rem);
+      eq_seen += eq[i] ? 1 : 0;
+      if (tk) sm.s_sel[pos] = p0 + i;
+      pos += tk ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (s == 0) {
+    for (int j = tid; j < nsel; j += kBlock) a.sel[(size_t)pair * maxP + j] = sm.s_sel[j];
+    if (tid == 0) a.n_sel[pair] = nsel;
+  }
+
+  // ---- the pages to read: all selected pages, or those that can hold a
+  // support token of some head of the group
+  int m = nsel;
+  if (prune) {
+    // round trip 2: the selected pages' bounds and physical pages (slots
+    // tid + i * kBlock); per head the selected page with the largest bound,
+    // lowest page on ties
+    float ubs[kSelPer][G];
+    float best[G];
+    int bestp[G], bestph[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      best[h] = -__builtin_huge_valf();
+      bestp[h] = 0x7fffffff;
+      bestph[h] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) {
+      const int j = tid + i * kBlock;
+#pragma unroll
+      for (int h = 0; h < G; ++h) ubs[i][h] = -__builtin_huge_valf();
+      if (j < nsel) {
+        const int page = sm.s_sel[j];
+        const float* up = a.ub + ((size_t)pair * maxP + page) * G;
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+          for (int h4 = 0; h4 < G; h4 += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(up + h4);
+            ubs[i][h4] = v.x;
+            ubs[i][h4 + 1] = v.y;
+            ubs[i][h4 + 2] = v.z;
+            ubs[i][h4 + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) ubs[i][h] = up[h];
+        }
+        const int phys = a.bt[(size_t)b * maxP + page];
+        sm.s_phys[j] = phys;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if (ubs[i][h] > best[h]) {  // slots ascending in i: ties keep the lower page
+            best[h] = ubs[i][h];
+            bestp[h] = page;
+            bestph[h] = phys;
+          }
+      }
+    }
+    // per wave: the largest bound (DPP), then the lowest page among the lanes
+    // that hold it (DPP), then that lane's physical page (readlane)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float wb = wave_max_f32(best[h]);
+      const uint32_t wp = wave_min_u32(best[h] == wb ? (uint32_t)bestp[h] : 0xFFFFFFFFu);
+      const uint64_t at = __ballot(best[h] == wb && (uint32_t)bestp[h] == wp);
+      const int src = at ? __ffsll((long long)at) - 1 : 0;
+      const int wph = __builtin_amdgcn_readlane(bestph[h], src);
+      if (lane == 0) {
+        sm.s_best[wave][h] = wb;
+        sm.s_bestj[wave][h] = (int)wp;
+        sm.s_bestph[wave][h] = wph;
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int h = tid;
+      float bv = sm.s_best[0][h];
+      int bp = sm.s_bestj[0][h], bph = sm.s_bestph[0][h];
+#pragma unroll
+      for (int w = 1; w < kBlock / kWave; ++w)
+        if (sm.s_best[w][h] > bv || (sm.s_best[w][h] == bv && sm.s_bestj[w][h] < bp)) {
+          bv = sm.s_best[w][h];
+          bp = sm.s_bestj[w][h];
+          bph = sm.s_bestph[w][h];
+        }
+      // bounds are finite unless the inputs are not: fall back to the first
+      // selected page
+      if (bp < 0 || bp >= np) {
+        bp = sm.s_sel[0];
+        bph = sm.s_phys[0];
+      }
+      sm.probe_phys[h] = bph;
+      sm.probe_nv[h] = page_valid(L, bp, P);
+    }
+    __syncthreads();
+
+    // round trip 3: the probe rows; zlb[h] = the largest fp32 z of head h's
+    // best page's valid tokens (kLpr lanes per key row)
+    {
+      const int c = tid % kLpr;
+      const int rg = tid / kLpr;
+      const int nrows = G * P;
+      for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass * kProbeBatch) {
+        uint4 w[kProbeBatch];
+        float qx[kProbeBatch][kVec];
+        bool ok[kProbeBatch];
+#pragma unroll
+        for (int u = 0; u < kProbeBatch; ++u) {
+          const int r = r0 + rg + u * kRowsPerPass;
+          const int h = r >> log2P;
+          const int t = r & (P - 1);
+          ok[u] = r < nrows && t < sm.probe_nv[h < G ? h : 0];
+          w[u] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+          for (int v = 0; v < kVec; ++v) qx[u][v] = 0.0f;
+          if (ok[u]) {
+            w[u] = load16_stream(a.K + ((size_t)sm.probe_phys[h] * a.Hkv + g) * (size_t)P * D +
+                                 (size_t)t * D + c * kVec);
+            const float4* qh = reinterpret_cast<const float4*>(qg + (size_t)h * D + c * kVec);
+#pragma unroll
+            for (int v4 = 0; v4 < kVec / 4; ++v4) {
+              const float4 x = qh[v4];
+              qx[u][4 * v4] = x.x;
+              qx[u][4 * v4 + 1] = x.y;
+              qx[u][4 * v4 + 2] = x.z;
+              qx[u][4 * v4 + 3] = x.w;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kProbeBatch; ++u) {
+          const int r = r0 + rg + u * kRowsPerPass;
+          float x[kVec];
+          Elem<T>::unpack(w[u], x);
+          float acc = 0.0f;
+#pragma unroll
+          for (int v = 0; v < kVec; ++v) acc = fmaf(qx[u][v], x[v], acc);
+          acc = group_sum_f32<kLpr>(acc);  // all lanes of a row group agree on ok[u]
+          if (c == 0 && r < nrows) sm.rowz[r] = ok[u] ? acc * a.zscale : -__builtin_huge_valf();
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float zm = -__builtin_huge_valf();
+      for (int t = 0; t < P; ++t) zm = fmaxf(zm, sm.rowz[tid * P + t]);
+      sm.zlb[tid] = zm;
+    }
+    __syncthreads();
+    float zl_h[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) zl_h[h] = sm.zlb[h];
+    // keep flags of the strided slots through LDS, then contiguous chunks of
+    // slots per thread, compacted by a block scan into the ascending list of
+    // selected slots to read
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) {
+      const int j = tid + i * kBlock;
+      bool nd = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) nd |= !page_below_support(a.a1 * ubs[i][h], zl_h[h]);
+      if (j < nsel) sm.s_flag[j] = nd ? 1 : 0;
+    }
+    __syncthreads();
+    int cntf = 0;
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) {
+      const int j = tid * kSelPer + i;
+      cntf += (j < nsel && sm.s_flag[j]) ? 1 : 0;
+    }
+    const int incl = block_incl_scan(cntf, sm.sh4);
+    int pos = incl - cntf;
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) {
+      const int j = tid * kSelPer + i;
+      if (j < nsel && sm.s_flag[j]) sm.s_surv[pos++] = j;
+    }
+    if (tid == kBlock - 1) sm.s_m = incl;
+    __syncthreads();
+    m = sm.s_m;
+  }
+
+  // ---- this item's even share of the pages to read (ascending)
+  const int lo = (int)(((long long)s * m) / nsplit);
+  const int hi = (int)(((long long)(s + 1) * m) / nsplit);
+  const int n_pg = hi - lo;  // <= kR / P (up to 512 pages of one token)
+  auto& qk = sm.u.qk;
+  for (int i = tid; i < n_pg; i += kBlock) {
+    const int idx = lo + i;
+    const int j = prune ? sm.s_surv[idx] : idx;
+    const int page = sm.s_sel[j];
+    qk.pg_phys[i] = prune ? sm.s_phys[j] : a.bt[(size_t)b * maxP + page];
+    qk.pg_valid[i] = page_valid(L, page, P);
+  }
+  const int r_end = n_pg << log2P;
+  // (qk_score_slots barriers before it reads the page map)
+  if (n_pg > 0)
+    qk_score_slots<T, D, G, kMfma>(qg, qv, a.zscale, a.K, a.Hkv, g, P, log2P, 0, r_end, 0, qk);
+  qk_emit<T, D, G, false, kMfma>(qk, r_end, 0, 0, P, log2P, a.cand, a.cnt, a.smax, bh0, a.splits,
+                                 s);
+}
+
+// The same work item with the scorer's hints (the step's path): each head's
+// probe page is the best page of its whole row (the best of the slice bests,
+// lowest page on ties), known after the first round trip, so the probe rows
+// are requested before the selection runs and arrive during it (the
+// selection uses LDS-only barriers).  The probe counts only if that page is
+// selected (else the head has no bound and nothing is skipped), and the
+// pages left to read are those whose group bound U clears some head's
+// zlb - 1: U >= every head's bound, so this skips a subset of what the
+// per-head test would and every skipped page is still below every head's
+// support.  The probe rows of a group must fit one batch
+// (G * P <= kProbeBatch * kBlock / kLpr).
+template <typename T, int D, int G, int kPer>
+__global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
+  using GE = Geo<T, D>;
+  constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kR = GE::kR;
+  constexpr int kRowsPerPass = kBlock / kLpr;
+  constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
+  constexpr bool kMfma = std::is_same<T, bf16_t>::value;
+  constexpr int kHintPer = 4;  // hint entries per lane of wave 0 (<= 256 in all)
+  __shared__ SelQkLds<T, D, G> sm;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int pair = (int)(blockIdx.x % (unsigned)a.npairs);
+  const int s = (int)(blockIdx.x / (unsigned)a.npairs);
+  const int b = pair / a.Hkv;
+  const int g = pair % a.Hkv;
+  const int Hq = a.Hkv * G;
+  const int P = a.P, log2P = a.log2P, maxP = a.maxP;
+  const size_t bh0 = (size_t)b * Hq + (size_t)g * G;
+  const float* qg = a.q + bh0 * D;
+
+  // ---- round trip 1: group bounds and block-table entries of this thread's
+  // kPer pages, the group's queries, the slice hints (wave 0), the row length
+  const int p0 = tid * kPer;
+  const float* Ug = a.ubg + (size_t)pair * maxP;
+  const int32_t* btrow = a.bt + (size_t)b * maxP;
+  float uv[kPer];
+  int btr[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool in = p0 + i < maxP;
+    uv[i] = in ? Ug[p0 + i] : 0.0f;
+    btr[i] = in ? btrow[p0 + i] : 0;
+  }
+  float qv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int idx = tid + u * kBlock;
+    qv[u] = idx < G * D ? qg[idx] : 0.0f;
+  }
+  int4 hv[kHintPer];
+  const int nhint = a.nslices * G;
+#pragma unroll
+  for (int u = 0; u < kHintPer; ++u) {
+    const int e = lane + u * kWave;
+    hv[u] = make_int4(0, -1, 0, 0);
+    if (wave == 0 && e < nhint) hv[u] = a.hint[(size_t)pair * nhint + e];
+  }
+  const int L = a.lens[b];
+  const int np = (L + P - 1) >> log2P;
+  const int nsel = min(a.top_k, np);
+  const int nsplit = ((nsel << log2P) + kR - 1) / kR;
+  if (s >= nsplit) {  // uniform: nothing to read for this item
+    if (s == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
+    return;
+  }
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int idx = tid + u * kBlock;
+    if (idx < G * D) sm.qraw[idx] = qv[u];
+  }
+  // each head's best page over the row's slices (lane l follows head l % G)
+  if (wave == 0) {
+    const int nsl = (np + a.slice_pages - 1) / a.slice_pages;
+    float lb = -__builtin_huge_valf();
+    int lp = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < kHintPer; ++u) {
+      const int e = lane + u * kWave;
+      const float hu = __int_as_float(hv[u].x);
+      const int hp = hv[u].y;
+      // slices in order, each with its lowest page among equals: keep the first
+      if (e < nsl * G && hp >= 0 && hp < np && hu > lb) {
+        lb = hu;
+        lp = hp;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bool mine = lane % G == h;
+      const float wb = wave_max_f32(mine ? lb : -__builtin_huge_valf());
+      const uint32_t wp = wave_min_u32(mine && lb == wb ? (uint32_t)lp : 0xFFFFFFFFu);
+      if (lane == 0) {
+        const bool ok = wp < (uint32_t)np;
+        sm.probe_page[h] = ok ? (int)wp : -1;
+        sm.probe_nv[h] = ok ? page_valid(L, (int)wp, P) : 0;
+        sm.probe_sel[h] = 0;
+      }
+    }
+  }
+  lds_barrier();
+  // the probe pages' physical pages from their owners' block-table entries
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int pg = sm.probe_page[h];
+    if (pg >= p0 && pg < p0 + kPer) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (p0 + i == pg) sm.probe_phys[h] = btr[i];
+    }
+  }
+  lds_barrier();
+  // ---- round trip 2, in flight during the selection: the probe rows
+  const int c = tid % kLpr;
+  const int rg = tid / kLpr;
+  uint4 w[kProbeBatch];
+  bool okr[kProbeBatch];
+#pragma unroll
+  for (int u = 0; u < kProbeBatch; ++u) {
+    const int r = rg + u * kRowsPerPass;
+    const int h = r >> log2P;
+    const int t = r & (P - 1);
+    okr[u] = r < G * P && t < sm.probe_nv[h < G ? h : 0];
+    w[u] = make_uint4(0u, 0u, 0u, 0u);
+    if (okr[u])
+      w[u] = load16_stream(a.K + ((size_t)sm.probe_phys[h] * a.Hkv + g) * (size_t)P * D +
+                           (size_t)t * D + c * kVec);
+  }
+
+  // ---- top-k: the nsel largest U, lowest page on ties, placed ascending
+  const int nv = max(0, min(kPer, np - p0));
+  bool take[kPer];
+  {
+    uint32_t key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) key[i] = order_key(uv[i]);
+    TopkThr th{0u, 0, true};  // nsel >= np: every page
+    if (nsel < np) th = topk_threshold<kPer>(key, nv, nsel, sm.u.tk);
+    bool eq[kPer];
+    int cg = 0, ce = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool v = i < nv;
+      take[i] = v && (th.cut ? key[i] >= th.T : key[i] > th.T);
+      eq[i] = v && !th.cut && key[i] == th.T;
+      cg += take[i] ? 1 : 0;
+      ce += eq[i] ? 1 : 0;
+    }
+    const int both = cg | (ce << 16);
+    const int excl = block_incl_scan_lds(both, sm.sh4) - both;
+    int eq_seen = excl >> 16;
+    int pos = (excl & 0xFFFF) + min(eq_seen, th.rem);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      take[i] = take[i] || (eq[i] && eq_seen < th.rem);
+      eq_seen += eq[i] ? 1 : 0;
+      if (take[i]) sm.s_sel[pos] = p0 + i;
+      pos += take[i] ? 1 : 0;
+    }
+  }
+  // whether each head's probe page is selected
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int pg = sm.probe_page[h];
+    if (pg >= p0 && pg < p0 + kPer) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (p0 + i == pg) sm.probe_sel[h] = take[i] ? 1 : 0;
+    }
+  }
+  lds_barrier();
+  if (s == 0) {
+    for (int j = tid; j < nsel; j += kBlock) a.sel[(size_t)pair * maxP + j] = sm.s_sel[j];
+    if (tid == 0) a.n_sel[pair] = nsel;
+  }
+
+  // ---- zlb[h]: the largest fp32 z of the probe page's valid tokens (kLpr
+  // lanes per key row), if that page is selected
+#pragma unroll
+  for (int u = 0; u < kProbeBatch; ++u) {
+    const int r = rg + u * kRowsPerPass;
+    const int h = r >> log2P;
+    float x[kVec];
+    Elem<T>::unpack(w[u], x);
+    float acc = 0.0f;
+    if (okr[u]) {
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) acc = fmaf(sm.qraw[h * D + c * kVec + v], x[v], acc);
+    }
+    acc = group_sum_f32<kLpr>(acc);  // all lanes of a row group agree on okr[u]
+    if (c == 0 && r < G * P) sm.rowz[r] = okr[u] ? acc * a.zscale : -__builtin_huge_valf();
+  }
+  lds_barrier();
+  if (tid < G) {
+    float zm = -__builtin_huge_valf();
+    if (sm.probe_sel[tid])
+      for (int t = 0; t < P; ++t) zm = fmaxf(zm, sm.rowz[tid * P + t]);
+    sm.zlb[tid] = zm;
+  }
+  lds_barrier();
+  float zl_h[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) zl_h[h] = sm.zlb[h];
+
+  // ---- the pages to read, ascending: selected, and U clears some head's
+  // zlb - 1 (with the rounding slacks of page_below_support)
+  int cntf = 0;
+  bool need[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    bool nd = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) nd |= !page_below_support(a.a1 * uv[i], zl_h[h]);
+    need[i] = take[i] && nd;
+    cntf += need[i] ? 1 : 0;
+  }
+  const int incl = block_incl_scan_lds(cntf, sm.sh4);
+  int pos = incl - cntf;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (need[i]) {
+      sm.s_surv[pos] = p0 + i;
+      sm.s_phys[pos] = btr[i];
+    }
+    pos += need[i] ? 1 : 0;
+  }
+  if (tid == kBlock - 1) sm.s_m = incl;
+  lds_barrier();
+  const int m = sm.s_m;
+
+  // ---- this item's even share of them
+  const int lo = (int)(((long long)s * m) / nsplit);
+  const int hi = (int)(((long long)(s + 1) * m) / nsplit);
+  const int n_pg = hi - lo;
+  auto& qk = sm.u.qk;
+  for (int i = tid; i < n_pg; i += kBlock) {
+    qk.pg_phys[i] = sm.s_phys[lo + i];
+    qk.pg_valid[i] = page_valid(L, sm.s_surv[lo + i], P);
+  }
+  const int r_end = n_pg << log2P;
+  float qmv[kMfma ? kQPer : 1];
+#pragma unroll
+  for (int u = 0; u < (kMfma ? kQPer : 1); ++u) qmv[u] = qv[u < kQPer ? u : 0];
+  if (n_pg > 0)
+    qk_score_slots<T, D, G, kMfma>(qg, qmv, a.zscale, a.K, a.Hkv, g, P, log2P, 0, r_end, 0, qk);
+  qk_emit<T, D, G, false, kMfma>(qk, r_end, 0, 0, P, log2P, a.cand, a.cnt, a.smax, bh0, a.splits,
+                                 s);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void tau_pv_step_kernel(TauArgs<T> a) {
+  __shared__ TauLds<T, D> sm;
+  tau_head<T, D>(a, blockIdx.x, sm);
+}
+
+// Whether the hinted kernel takes this shape: at most 4 hints per lane of one
+// wave, and the probe rows of a group in one batch.
+template <typename T, int D, int G>
+bool hint_fits(const Shape& s, const TopkHint& h) {
+  constexpr int kLpr = Geo<T, D>::kLpr;
+  return h.hint != nullptr && h.nslices * G <= 4 * kWave &&
+         G * s.P <= kProbeBatch * (kBlock / kLpr);
+}
+
+template <typename T, int D, int G, int kPer>
+hipError_t launch_t(const Shape& s, const DecodePlan& pl, const float* q, float zscale, float a1,
+                    const void* K, const int32_t* bt, const int32_t* lens, int top_k,
+                    const float* ub, const float* ubg, int32_t* sel, int32_t* n_sel,
+                    float2* cand, int* cnt, float* smax, const TopkHint& hint,
+                    hipStream_t stream) {
+  const long long npairs = (long long)s.B * s.Hkv;
+  const long long items = npairs * pl.splits;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const SelQkArgs<T> a{q,      zscale,    a1,          (const T*)K, bt,      lens,
+                       ub,     ubg,       sel,         n_sel,       top_k,   s.Hkv,
+                       s.P,    s.log2P,   s.maxP,      pl.splits,   (int)npairs, cand,
+                       cnt,    smax,      hint.hint,   hint.slice_pages, hint.nslices};
+  if (ub != nullptr && hint_fits<T, D, G>(s, hint))
+    hipLaunchKernelGGL((sel_qk_hint_kernel<T, D, G, kPer>), dim3((unsigned)items), dim3(kBlock),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((sel_qk_kernel<T, D, G, kPer>), dim3((unsigned)items), dim3(kBlock), 0,
+                       stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t launch_g(const Shape& s, const DecodePlan& pl, const float* q, float zscale, float a1,
+                    const void* K, const int32_t* bt, const int32_t* lens, int top_k,
+                    const float* ub, const float* ubg, int32_t* sel, int32_t* n_sel,
+                    float2* cand, int* cnt, float* smax, const TopkHint& hint,
+                    hipStream_t stream) {
+  if (s.maxP <= kBlock * 8)
+    return launch_t<T, D, G, 8>(s, pl, q, zscale, a1, K, bt, lens, top_k, ub, ubg, sel, n_sel, cand, cnt, smax, hint, stream);
+  if (s.maxP <= kBlock * 16)
+    return launch_t<T, D, G, 16>(s, pl, q, zscale, a1, K, bt, lens, top_k, ub, ubg, sel, n_sel, cand, cnt, smax, hint, stream);
+  return launch_t<T, D, G, 32>(s, pl, q, zscale, a1, K, bt, lens, top_k, ub, ubg, sel, n_sel, cand, cnt, smax, hint, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_d(const Shape& s, const DecodePlan& pl, const float* q, float scale,
+                    float alpha, const void* K, const void* V, const int32_t* bt,
+                    const int32_t* lens, int top_k, const float* ub, const float* ubg,
+                    int32_t* sel, int32_t* n_sel, float* out, float* tau_out, int32_t* n_support,
+                    void* ws, const TopkHint& hint, hipStream_t stream) {
+  float2* cand = (float2*)((char*)ws + pl.cand_off);
+  int* cnt = (int*)((char*)ws + pl.cnt_off);
+  float* smax = (float*)((char*)ws + pl.smax_off);
+  const double a1 = (double)alpha - 1.0;
+  const float zscale = (float)(a1 * (double)scale);
+  hipError_t e = hipErrorInvalidValue;
+  switch (s.G) {
+    case 1: e = launch_g<T, D, 1>(s, pl, q, zscale, (float)a1, K, bt, lens, top_k, ub, ubg, sel, n_sel, cand, cnt, smax, hint, stream); break;
+    case 2: e = launch_g<T, D, 2>(s, pl, q, zscale, (float)a1, K, bt, lens, top_k, ub, ubg, sel, n_sel, cand, cnt, smax, hint, stream); break;
+    case 4: e = launch_g<T, D, 4>(s, pl, q, zscale, (float)a1, K, bt, lens, top_k, ub, ubg, sel, n_sel, cand, cnt, smax, hint, stream); break;
+    case 8: e = launch_g<T, D, 8>(s, pl, q, zscale, (float)a1, K, bt, lens, top_k, ub, ubg, sel, n_sel, cand, cnt, smax, hint, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  const double gamma = 1.0 / a1;
+  const double gr = rint(gamma);
+  const int gamma_int = (gr >= 1.0 && gr <= 64.0 && fabs(gamma - gr) <= 1e-12 * gr) ? (int)gr : 0;
+  const TauArgs<T> ta{cand,   cnt,  smax,  pl.splits, (const T*)V, lens,    n_sel,
+                      true,   pl.max_sel, s.Hq, s.Hkv, s.P,       s.log2P, (double)alpha,
+                      gamma_int ? gr : gamma, gamma_int, out, tau_out, n_support};
+  hipLaunchKernelGGL((tau_pv_step_kernel<T, D>), dim3(s.B * s.Hq), dim3(kBlock), 0, stream, ta);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool topk_decode_fast(const Shape& s, int max_sel) {
+  return max_sel <= kSelCap && s.maxP <= kBlock * 32 && decode_shape_supported(s, max_sel);
+}
+
+hipError_t launch_topk_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,
+                              float alpha, const void* K, const void* V, const int32_t* bt,
+                              const int32_t* lens, int top_k, const float* ub, const float* ubg,
+                              int32_t* sel, int32_t* n_sel, float* out, float* tau_out,
+                              int32_t* n_support, void* ws, const TopkHint& hint,
+                              hipStream_t stream) {
+  if (s.bf16) {
+    if (s.D == 128)
+      return launch_d<bf16_t, 128>(s, plan, q, scale, alpha, K, V, bt, lens, top_k, ub, ubg, sel, n_sel, out, tau_out, n_support, ws, hint, stream);
+    return launch_d<bf16_t, 64>(s, plan, q, scale, alpha, K, V, bt, lens, top_k, ub, ubg, sel, n_sel, out, tau_out, n_support, ws, hint, stream);
+  }
+  if (s.D == 128)
+    return launch_d<float, 128>(s, plan, q, scale, alpha, K, V, bt, lens, top_k, ub, ubg, sel, n_sel, out, tau_out, n_support, ws, hint, stream);
+  return launch_d<float, 64>(s, plan, q, scale, alpha, K, V, bt, lens, top_k, ub, ubg, sel, n_sel, out, tau_out, n_support, ws, hint, stream);
+}
+
+}  // namespace ekv

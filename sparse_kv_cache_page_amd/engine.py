@@ -67,8 +67,15 @@ class PagedEntmaxDecoder:
         self.out = torch.empty(Bt, Hq, d, dtype=torch.float32, device=dev)
         self.tau = torch.empty(Bt, Hq, dtype=torch.float32, device=dev)
         self.n_support = torch.empty(Bt, Hq, dtype=torch.int32, device=dev)
+        # the box scorer's best-page hints (top-k with pruning): ekv_score_box_pages
+        # writes them, ekv_topk_decode reads them
+        self.hint = (torch.empty(max(B.score_hint_bytes(s), 256), dtype=torch.uint8, device=dev)
+                     if policy == "topk" and self.prune else None)
         self.max_sel = min(self.top_k, mp) if policy == "topk" else mp
         ws_bytes = B.decode_workspace_bytes(s, self.max_sel)
+        if policy == "topk":
+            # the same workspace serves ekv_topk_decode (a little larger)
+            ws_bytes = max(ws_bytes, B.topk_decode_workspace_bytes(s, self.top_k))
         self.ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         # the fused step (top-k only) keeps arrival counters in its workspace:
         # zero-filled once here, left zeroed by every call
@@ -113,6 +120,21 @@ class PagedEntmaxDecoder:
                         n_sel=None if dense else self.n_sel, max_sel=self.max_sel, tau=self.tau,
                         n_support=self.n_support, ub=self.ub if self.prune else None,
                         zlb=self.zlb)
+
+    def score_box(self, q, block_table, seq_lens, K=None, refresh_last_page: bool = False):
+        """Box bounds (and the best-page hints) of the top-k step, one launch."""
+        B.score_box_pages(self.shape, q, self.scale, block_table, seq_lens, self.kmin, self.kmax,
+                          self.ubg, ub=self.ub, hint=self.hint, K=K,
+                          refresh_last_page=refresh_last_page)
+
+    def topk_decode(self, q, K, V, block_table, seq_lens, use_hint: bool = False):
+        """Top-k selection from the group bounds and the (pruned) decode over it, in
+        one entry point (after score(), or after score_box() with use_hint)."""
+        B.topk_decode(self.shape, q, self.scale, self.alpha, K, V, block_table, seq_lens,
+                      self.top_k, self.ubg, self.sel, self.n_sel, self.out, self.ws,
+                      ub=self.ub if self.prune else None, tau=self.tau,
+                      n_support=self.n_support,
+                      hint=self.hint if (use_hint and self.prune) else None)
 
     def score_select(self, q, K, block_table, seq_lens, refresh_last_page: bool = False):
         """[last-page refresh] + scores + top-k in one fused launch."""

@@ -48,9 +48,8 @@ def check_properties(inp, gpu, policy, top_k):
 def decoder_matches(inp, gpu, policy, alpha, top_k, delta, scale, q):
     """The benchmark's call sequence gives bit-identical results.
 
-    For the top-k policy that is the fused ekv_score_select_pages (arrival
-    counters, device-coherent bound stores, the top-k run by the last
-    workgroup of each pair) followed by the pruned ekv_entmax_decode, exactly
+    For the top-k policy that is ekv_score_pages followed by ekv_topk_decode
+    (top-k selection inside the decode's key launch, page pruning), exactly
     as bench.py's Layer issues them; ekv_decode_step (the same two calls
     behind one entry point) is checked too.  Every output must equal the
     separate score / select / decode calls of `gpu`, which the oracle checked.
@@ -61,8 +60,8 @@ def decoder_matches(inp, gpu, policy, alpha, top_k, delta, scale, q):
                              delta=delta, fused=fused)
     dec.build_meta(inp["K"], inp["block_table"], inp["seq_lens"])
     if fused:
-        dec.score_select(q, inp["K"], inp["block_table"], inp["seq_lens"])
-        dec.decode(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
+        dec.score(q, inp["block_table"], inp["seq_lens"])
+        dec.topk_decode(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
     else:
         dec.step(q, inp["K"], inp["V"], inp["block_table"], inp["seq_lens"])
     torch.cuda.synchronize()
