@@ -64,6 +64,8 @@ def parse():
                     help="skip the batch x ctx sweep that the gqa run reports with its line")
     ap.add_argument("--no-comparison", action="store_true",
                     help="skip the softmax / full-cache comparison of the gqa run")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the ragged and stress workloads the gqa run reports with its line")
     ap.add_argument("--comparison", action="store_true",
                     help="also run the softmax / full-cache comparison on a top-k workload "
                          "other than gqa")
@@ -286,6 +288,82 @@ def page_read_mask(layer):
     return (~below).numpy()
 
 
+def diagnostics(layer):
+    """Diagnostics of one step on one layer (reported, never compared): pages
+    selected per (row, KV head), support sizes, how many heads have their
+    full-cache entmax support inside the kept pages (the sparse output then
+    equals the full-cache one, §3 of the EntmaxKV page), and the entmax mass
+    the selection drops, delta = 1 - sum over kept tokens of
+    [z - tau_full]_+^gamma with tau_full from the library's full-cache decode.
+
+    The full-cache decode and the step run in the library; the kept-token sum
+    for delta is formed here with torch (fp32 scores of the gathered kept keys,
+    fp64 sum), which is diagnostics only and not part of the step."""
+    import torch
+    from sparse_kv_cache_page_amd import binding as Bd
+    w, inp, dec, s = layer.w, layer.inp, layer.dec, layer.shape
+    layer.step()
+    torch.cuda.synchronize()
+    Bt, Hq, Hkv, d, G, P = s.batch, s.num_q_heads, s.num_kv_heads, s.head_dim, w.group, w.page_size
+    npg = torch.tensor(inp["npages"], device=inp["K"].device)
+    if w.policy == "dense":
+        n_sel = npg[:, None].expand(Bt, Hkv)
+    else:
+        n_sel = dec.n_sel.long()
+    out_s, tau_s, sup_s = dec.out.clone(), dec.tau.clone(), dec.n_support.clone()
+    out_f = torch.empty_like(out_s)
+    tau_f = torch.empty_like(tau_s)
+    sup_f = torch.empty_like(sup_s)
+    ws = torch.empty(Bd.decode_workspace_bytes(s, 0), dtype=torch.uint8, device=out_s.device)
+    Bd.entmax_decode(s, inp["q"], w.scale, w.alpha, inp["K"], inp["V"], inp["block_table"],
+                     inp["seq_lens"], out_f, ws, tau=tau_f, n_support=sup_f)
+    torch.cuda.synchronize()
+    rel = (out_s - out_f).norm(dim=-1) / out_f.norm(dim=-1).clamp_min(1e-30)
+    res = {"n_sel": {"mean": float(n_sel.float().mean()), "max": int(n_sel.max())},
+           "pages": {"mean": float(npg.float().mean()), "max": int(npg.max())},
+           "support_tokens": {"mean": float(sup_f.float().mean()), "max": int(sup_f.max())},
+           "heads": int(rel.numel()),
+           "sparse_vs_full_output_rel_err": {"median": float(rel.median()),
+                                             "max": float(rel.max())}}
+    if w.policy == "dense":
+        res["entmax_dropped_mass"] = {"mean": 0.0, "max": 0.0, "note": "nothing dropped"}
+        res["support_recovery_rate"] = 1.0
+        return res
+    # kept mass under tau_full, per (row, query head)
+    gamma = 1.0 / (w.alpha - 1.0)
+    zs = float(w.alpha - 1.0) * float(w.scale)
+    mx = int(n_sel.max())
+    sel = dec.sel[:, :, :mx].long().clamp(min=0)                        # [B][Hkv][mx]
+    live = torch.arange(mx, device=sel.device)[None, None, :] < n_sel[:, :, None]
+    page = torch.where(live, sel, torch.zeros_like(sel))
+    phys = torch.gather(inp["block_table"].long()[:, None, :].expand(Bt, Hkv, -1), 2, page)
+    kept = torch.zeros(Bt, Hq, dtype=torch.float64, device=sel.device)
+    for g in range(Hkv):
+        kt = inp["K"][phys[:, g], g].float()                              # [B][mx][P][d]
+        qh = inp["q"][:, g * G:(g + 1) * G].float()                       # [B][G][d]
+        z = zs * torch.matmul(kt.reshape(Bt, mx * P, d), qh.transpose(1, 2).contiguous())
+        tok = torch.arange(P, device=sel.device)
+        last = page == (npg[:, None, None] - 1)
+        nvalid = torch.where(last, (torch.tensor(inp["lens"], device=sel.device)[:, None, None]
+                                    - (npg[:, None, None] - 1) * P).expand_as(page),
+                             torch.full_like(page, P))
+        ok = (live[:, g, :, None] & (tok[None, None, :] < nvalid[:, g, :, None]))
+        ok = ok.reshape(Bt, mx * P, 1)
+        t = tau_f[:, g * G:(g + 1) * G].double()[:, None, :]
+        x = (z.double() - t).clamp(min=0.0) ** gamma
+        kept[:, g * G:(g + 1) * G] = torch.where(ok, x, torch.zeros_like(x)).sum(dim=1)
+        del kt, z, x
+    delta = (1.0 - kept).clamp(min=0.0)
+    # a head's support is recovered when the kept pages hold all of its
+    # full-cache entmax mass (to the resolution of the fp32 scores)
+    recovered = (delta <= 1e-5) & (sup_s == sup_f)
+    res["support_recovery_rate"] = float(recovered.float().mean())
+    res["entmax_dropped_mass"] = {"mean": float(delta.mean()), "max": float(delta.max()),
+                                  "note": "1 - kept entmax mass at the full-cache tau (fp64 "
+                                          "sum of fp32 scores, resolution ~1e-6)"}
+    return res
+
+
 def time_steps(layers, steps, warmup, graph):
     import torch
     R = len(layers)
@@ -447,7 +525,26 @@ def cpu_baseline(layer, budget_s):
             "sample": f"{done} of {len(pairs)} (row, KV head) pairs of one {w.name} step "
                       f"(score + select + decode, metadata prebuilt), scaled linearly to "
                       f"all pairs; fp64 numpy, 1 BLAS thread",
-            "seconds_per_step": per_step}
+            "seconds_per_step": per_step, "host": host_cpu()}
+
+
+def host_cpu():
+    """The host the CPU baseline ran on: logical CPUs and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = None
+    return {"nproc": os.cpu_count(), "usable_cpus": avail, "cpu_model": model,
+            "blas_threads": 1}
 
 
 def workload_config(w, R, graph, inp):
@@ -463,7 +560,9 @@ def workload_config(w, R, graph, inp):
             "graph_scope": "one graph per pass over the rotated layers" if graph else None}
 
 
-def run(w, args, dev, emit_cpu=True):
+def run(w, args, dev, emit_cpu=True, light=False):
+    """Time one workload's step.  light: a shorter run for the extra workloads
+    reported with the headline line (fewer steps, no per-step distribution)."""
     import torch
     R = args.layers
     if R <= 0:
@@ -474,12 +573,14 @@ def run(w, args, dev, emit_cpu=True):
     else:
         layers = [Layer(w, 7919 * i, dev) for i in range(R)]
     graph = not args.no_graph
-    ms, wall = time_steps(layers, args.steps, args.warmup, graph)
-    dist = {"graph": step_distribution(layers, 100, True),
-            "eager": step_distribution(layers, 100, False)}
-    stages = time_stages(layers, max(20, min(args.steps, 400)), graph)
-    refresh_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["refresh"])["refresh"]
-    append_ms = time_stages(layers, max(20, min(args.steps, 400)), graph, ["append"])["append"]
+    steps = min(args.steps, 100) if light else args.steps
+    ms, wall = time_steps(layers, steps, min(args.warmup, 10) if light else args.warmup, graph)
+    dist = None if light else {"graph": step_distribution(layers, 100, True),
+                               "eager": step_distribution(layers, 100, False)}
+    nst = max(20, min(steps, 400))
+    stages = time_stages(layers, nst, graph)
+    refresh_ms = time_stages(layers, nst, graph, ["refresh"])["refresh"]
+    append_ms = time_stages(layers, nst, graph, ["append"])["append"]
     copy_gbps = measured_copy_gbps(dev)
     nb = stage_bytes(layers[0])
     eff = nb["kv_bytes"] / (ms * 1e-3) / 1e9
@@ -496,10 +597,7 @@ def run(w, args, dev, emit_cpu=True):
         "kv_bytes_per_step": nb["kv_bytes"], "full_cache_bytes": nb["full_cache"],
         "read_fraction_of_full_cache": nb["kv_bytes"] / nb["full_cache"],
         "stage_ms": stages, "stage_bytes": {k: nb[k] for k in stages},
-        "host_wall_ms_per_step": wall * 1000.0 / args.steps,
-        "step_ms_distribution": dict(dist, note="100 steps each timed by its own HIP events: "
-                                     "graph = replay of the layer's captured step, eager = "
-                                     "the step's launches"),
+        "host_wall_ms_per_step": wall * 1000.0 / steps,
         "last_page_refresh": {"ms": refresh_ms, "bytes": nb["refresh"],
                               "gbps": nb["refresh"] / (refresh_ms * 1e-3) / 1e9,
                               "note": "build_page_meta of each row's last page, timed "
@@ -513,6 +611,13 @@ def run(w, args, dev, emit_cpu=True):
                      "traffic": recorded_traffic(ENTRY_POINT[dom], w.name),
                      "algorithmic_bytes": dom_bytes, "launch_ms": stages[dom]},
     }
+    if dist is not None:
+        rec["step_ms_distribution"] = dict(dist, note="100 steps each timed by its own HIP "
+                                           "events: graph = replay of the layer's captured "
+                                           "step, eager = the step's launches")
+    if light:
+        rec["steps"] = steps
+    rec["diagnostics"] = diagnostics(layers[0])
     if emit_cpu and args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
     del layers
@@ -632,13 +737,14 @@ def build_workload(args):
 
 def sweep(dev, steps=100, warmup=10):
     """batch x ctx sweep on the gqa decode heads (32 query / 8 KV heads, d 128, page 16,
-    bf16, alpha 1.5), top-k = 1/8 of the pages: one graph-replayed step per point,
-    with its algorithmic bytes (the same accounting as the main line)."""
+    bf16, alpha 1.5), batch 1/8/32/64 x context 8k/32k/128k, top-k = 1/8 of the pages:
+    one graph-replayed step per point, with its algorithmic bytes (the same
+    accounting as the main line)."""
     import gc
     import torch
     from sparse_kv_cache_page_amd import workloads as wl
     out = []
-    for B in (1, 8, 32):
+    for B in (1, 8, 32, 64):
         for ctx in (8192, 32768, 131072):
             w = wl.variant("gqa", batch=B, seq_len=ctx, top_k=ctx // 16 // 8,
                            name=f"gqa_b{B}_ctx{ctx}")
@@ -681,7 +787,31 @@ def comparison(w, args, dev, step_ms, copy_gbps):
         getattr(L0, n)()
     torch.cuda.synchronize()
     c = L0.cmp
-    delta = (1.0 - torch.exp(c["lse_sel"].double() - c["lse_full"].double())).flatten()
+    # the dropped softmax mass directly: softmax over the pages NOT selected,
+    # delta = exp(lse_dropped - lse_full) (1 - exp(lse_sel - lse_full) loses
+    # everything below fp32 resolution of lse)
+    from sparse_kv_cache_page_amd import binding as Bd
+    s0, dec0, inp0 = L0.shape, L0.dec, L0.inp
+    mp = s0.max_pages_per_seq
+    npg = torch.tensor(inp0["npages"], device=dec0.sel.device)
+    idx = torch.arange(mp, device=dec0.sel.device)
+    # selected pages marked in a table with one spare column for the unused slots
+    taken = torch.zeros(s0.batch, s0.num_kv_heads, mp + 1, dtype=torch.bool, device=idx.device)
+    live = idx[None, None, :] < dec0.n_sel.long()[:, :, None]
+    taken.scatter_(2, torch.where(live, dec0.sel.long().clamp(0, mp - 1),
+                                  torch.full_like(dec0.sel.long(), mp)), True)
+    dropped = (~taken[:, :, :mp]) & (idx[None, None, :] < npg[:, None, None])
+    # dropped pages first, ascending (stable sort on "not dropped")
+    comp = torch.sort((~dropped).to(torch.int8), dim=2, stable=True).indices.to(torch.int32)
+    n_comp = dropped.sum(dim=2).to(torch.int32)
+    lse_d = torch.empty_like(c["lse_full"])
+    o_d = torch.empty_like(c["o_sm_full"])
+    ws_d = torch.empty(Bd.softmax_workspace_bytes(s0, 0), dtype=torch.uint8, device=idx.device)
+    Bd.softmax_decode(s0, inp0["q"], L0.w.scale, inp0["K"], inp0["V"], inp0["block_table"],
+                      inp0["seq_lens"], o_d, ws_d, sel=comp.contiguous(), n_sel=n_comp,
+                      max_sel=mp, lse=lse_d)
+    torch.cuda.synchronize()
+    delta = torch.exp(lse_d.double() - c["lse_full"].double()).flatten()
 
     def rel(a, b):
         return ((a - b).norm(dim=-1) / b.norm(dim=-1).clamp_min(1e-30)).flatten()
@@ -701,7 +831,9 @@ def comparison(w, args, dev, step_ms, copy_gbps):
         "speedup_vs_full_cache_read_at_copy_rate":
             full_kv / (copy_gbps * 1e9) / (step_ms * 1e-3),
         "softmax_full_cache_hbm_frac": full_kv / (t["softmax_full"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "softmax_dropped_mass": {"mean": float(delta.mean()), "max": float(delta.max())},
+        "softmax_dropped_mass": {"mean": float(delta.mean()), "max": float(delta.max()),
+                                 "min": float(delta.min()),
+                                 "note": "exp(lse of the dropped pages - lse of all pages)"},
         "sparse_vs_full_output_rel_err": {
             "entmax": {"median": float(e_ent.median()), "max": float(e_ent.max())},
             "softmax": {"median": float(e_sm.median()), "max": float(e_sm.max())}},
@@ -714,6 +846,31 @@ def comparison(w, args, dev, step_ms, copy_gbps):
     gc.collect()
     torch.cuda.empty_cache()
     return res
+
+
+def extra_workloads(args, dev):
+    """The larger single-GPU workloads, reported with the headline line: ragged
+    (batch 64, lengths U[4096, 65536], top-512) and stress (batch 32, context
+    131072, 64/8 heads, page 32, alpha 1.25) with top-512 pages and with the
+    full-cache dense pass.  Each: steps/s, effective KV bandwidth, per entry
+    point times and bytes, the roofline of its dominant entry point and the
+    step diagnostics."""
+    import gc
+    import torch
+    from sparse_kv_cache_page_amd import workloads as wl
+    out = []
+    for w in (wl.CONFIGS["ragged"], wl.CONFIGS["stress"],
+              wl.variant("stress", policy="dense", name="stress_dense")):
+        print(f"[workloads] {w.name}", file=sys.stderr, flush=True)
+        r = run(w, args, dev, emit_cpu=False, light=True)
+        keep = ("config", "value", "unit", "ms_per_step", "steps", "effective_kv_gbps",
+                "hbm_frac", "frac_of_measured_copy", "kv_bytes_per_step", "full_cache_bytes",
+                "read_fraction_of_full_cache", "stage_ms", "stage_bytes", "roofline",
+                "diagnostics")
+        out.append({k: r[k] for k in keep if k in r})
+        gc.collect()
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -747,6 +904,8 @@ def main():
     if (w.name == "gqa" or (args.comparison and w.policy == "topk")) and not args.no_comparison:
         rec["comparison"] = comparison(w, args, dev, rec["ms_per_step"],
                                        rec["measured_copy_gbps"])
+    if w.name == "gqa" and not args.no_extra:
+        rec["workloads"] = extra_workloads(args, dev)
     if w.name == "gqa" and not args.no_sweep:
         rec["sweep"] = sweep(dev)
     print(json.dumps(rec), flush=True)
