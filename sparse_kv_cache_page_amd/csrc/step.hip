@@ -6,9 +6,11 @@
 // ekv_entmax_decode do, without a round trip through a selection list in
 // memory and without a serial per-pair tail:
 //
-//   every work item (row, KV head, split) reads the pair's group bounds U,
-//   runs the top-k radix select itself (the items of a pair reach the same
-//   selection; split 0 also writes it out as sel / n_sel), and, with the
+//   every work item (row, KV head, a run of consecutive splits) reads the
+//   pair's group bounds U, runs the top-k radix select itself (the items of a
+//   pair reach the same selection; item 0 also writes it out as sel / n_sel;
+//   the launch holds about 256 items, one per compute unit, so the repeated
+//   selection stays cheap next to the key reads), and, with the
 //   per-head bounds, probes each query head's best selected page for a lower
 //   bound zlb of its largest score.  A selected page whose bound is below
 //   zlb - 1 for every head of the group holds no support token (tau >=
@@ -16,7 +18,8 @@
 //   out evenly over the pair's items in ascending order (every item computes
 //   the same list), so the key stream is balanced over the workgroups; each
 //   item scores its pages for the G heads from one read (matrix cores for
-//   bf16) and writes its candidates z > item_max - 1.
+//   bf16), in chunks of one split's token slots, and writes each chunk's
+//   candidates z > chunk_max - 1 as one split.
 //
 // The tau / PV stage then runs as in ekv_entmax_decode.  Because the final
 // candidate set of a head is {z > z_max - 1} over the tokens read, in
@@ -31,6 +34,10 @@ namespace {
 constexpr int kSelCap = 1024;                 // selected pages per pair held in LDS
 constexpr int kSelPer = kSelCap / kBlock;     // of them per thread
 constexpr int kProbeBatch = 4;                // probe key rows per thread in flight
+#ifndef EKV_STEP_ITEMS
+#define EKV_STEP_ITEMS 256
+#endif
+constexpr long long kStepItems = EKV_STEP_ITEMS;  // workgroups to aim for per launch
 
 template <typename T>
 struct SelQkArgs {
@@ -45,6 +52,7 @@ struct SelQkArgs {
   int32_t* sel;      // [pairs][maxP] written by split 0
   int32_t* n_sel;    // [pairs] written by split 0
   int top_k, Hkv, P, log2P, maxP, splits, npairs;
+  int spi;           // splits per work item
   float2* cand;
   int* cnt;
   float* smax;
@@ -79,9 +87,50 @@ struct SelQkLds {
   float qraw[G * D];  // the group's queries (the probe of the hinted kernel)
 };
 
-// One work item per workgroup: item = split * pairs + pair (split-major: with
-// a multiple of 8 pairs, all items of a pair run on one XCD and share its L2
-// lines of the pair's bounds and probe rows).
+// The keys of an item's share of the m pages to read (ascending), then its
+// candidates: the item holds splits [s0, s1) of the pair's nsplit, and split
+// s owns pages [s * m / nsplit, (s + 1) * m / nsplit) of the list, at most
+// kR / P of them since m <= nsplit * kR / P; the union of the item's shares
+// is scored in chunks of kR token slots, chunk c written out as split s0 + c,
+// and the splits left over as empty (no candidate, maximum -inf).  Every head
+// then sees its candidates z > split_max - 1 over all the pages read, in
+// ascending slot order, whatever the item boundaries.  page_at(i) gives
+// {physical page, page} of list entry i.
+template <typename T, int D, int G, bool kMfma, typename PageAt>
+__device__ __forceinline__ void read_share(const SelQkArgs<T>& a, QkLds<T, D, G>& qk,
+                                           const float* qg,
+                                           const float (&qv)[kMfma ? (G * D + kBlock - 1) / kBlock : 1],
+                                           int g, int L, size_t bh0, int s0, int s1, int nsplit,
+                                           int m, PageAt page_at) {
+  constexpr int kR = Geo<T, D>::kR;
+  const int P = a.P, log2P = a.log2P;
+  const int lo = (int)(((long long)s0 * m) / nsplit);
+  const int hi = (int)(((long long)s1 * m) / nsplit);
+  const int per = kR >> log2P;  // pages per chunk
+  int s = s0;
+  for (int base = lo; base < hi; base += per, ++s) {
+    if (base > lo) __syncthreads();  // the previous chunk's emit has read the page map
+    const int n_pg = min(per, hi - base);
+    for (int i = threadIdx.x; i < n_pg; i += kBlock) {
+      const int2 pp = page_at(base + i);
+      qk.pg_phys[i] = pp.x;
+      qk.pg_valid[i] = page_valid(L, pp.y, P);
+    }
+    // (qk_score_slots barriers before it reads the page map)
+    qk_score_slots<T, D, G, kMfma>(qg, qv, a.zscale, a.K, a.Hkv, g, P, log2P, 0, n_pg << log2P,
+                                   0, qk);
+    qk_emit<T, D, G, false, kMfma>(qk, n_pg << log2P, 0, 0, P, log2P, a.cand, a.cnt, a.smax,
+                                   bh0, a.splits, s);
+  }
+  for (; s < s1; ++s)
+    qk_emit<T, D, G, false, kMfma>(qk, 0, 0, 0, P, log2P, a.cand, a.cnt, a.smax, bh0, a.splits,
+                                   s);
+}
+
+// One work item per workgroup: item = it * pairs + pair, item it of a pair
+// holding its splits [it * spi, (it + 1) * spi) (item-major: with a multiple
+// of 8 pairs, all items of a pair run on one XCD and share its L2 lines of
+// the pair's bounds and probe rows).
 template <typename T, int D, int G, int kPer>
 __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   using GE = Geo<T, D>;
@@ -94,7 +143,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int pair = (int)(blockIdx.x % (unsigned)a.npairs);
-  const int s = (int)(blockIdx.x / (unsigned)a.npairs);
+  const int it = (int)(blockIdx.x / (unsigned)a.npairs);
   const int b = pair / a.Hkv;
   const int g = pair % a.Hkv;
   const int Hq = a.Hkv * G;
@@ -123,8 +172,10 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   const int np = (L + P - 1) >> log2P;
   const int nsel = min(a.top_k, np);
   const int nsplit = ((nsel << log2P) + kR - 1) / kR;
-  if (s >= nsplit) {  // uniform: nothing to read for this item
-    if (s == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
+  const int s0 = it * a.spi;
+  const int s1 = min(s0 + a.spi, nsplit);
+  if (s0 >= nsplit) {  // uniform: nothing to read for this item
+    if (it == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
     return;
   }
 
@@ -161,7 +212,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
     }
   }
   __syncthreads();
-  if (s == 0) {
+  if (it == 0) {
     for (int j = tid; j < nsel; j += kBlock) a.sel[(size_t)pair * maxP + j] = sm.s_sel[j];
     if (tid == 0) a.n_sel[pair] = nsel;
   }
@@ -338,24 +389,12 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
     m = sm.s_m;
   }
 
-  // ---- this item's even share of the pages to read (ascending)
-  const int lo = (int)(((long long)s * m) / nsplit);
-  const int hi = (int)(((long long)(s + 1) * m) / nsplit);
-  const int n_pg = hi - lo;  // <= kR / P (up to 512 pages of one token)
-  auto& qk = sm.u.qk;
-  for (int i = tid; i < n_pg; i += kBlock) {
-    const int idx = lo + i;
+  // ---- this item's share of the pages to read (ascending)
+  read_share<T, D, G, kMfma>(a, sm.u.qk, qg, qv, g, L, bh0, s0, s1, nsplit, m, [&](int idx) {
     const int j = prune ? sm.s_surv[idx] : idx;
     const int page = sm.s_sel[j];
-    qk.pg_phys[i] = prune ? sm.s_phys[j] : a.bt[(size_t)b * maxP + page];
-    qk.pg_valid[i] = page_valid(L, page, P);
-  }
-  const int r_end = n_pg << log2P;
-  // (qk_score_slots barriers before it reads the page map)
-  if (n_pg > 0)
-    qk_score_slots<T, D, G, kMfma>(qg, qv, a.zscale, a.K, a.Hkv, g, P, log2P, 0, r_end, 0, qk);
-  qk_emit<T, D, G, false, kMfma>(qk, r_end, 0, 0, P, log2P, a.cand, a.cnt, a.smax, bh0, a.splits,
-                                 s);
+    return make_int2(prune ? sm.s_phys[j] : a.bt[(size_t)b * maxP + page], page);
+  });
 }
 
 // The same work item with the scorer's hints (the step's path): each head's
@@ -382,7 +421,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int pair = (int)(blockIdx.x % (unsigned)a.npairs);
-  const int s = (int)(blockIdx.x / (unsigned)a.npairs);
+  const int it = (int)(blockIdx.x / (unsigned)a.npairs);
   const int b = pair / a.Hkv;
   const int g = pair % a.Hkv;
   const int Hq = a.Hkv * G;
@@ -421,8 +460,10 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   const int np = (L + P - 1) >> log2P;
   const int nsel = min(a.top_k, np);
   const int nsplit = ((nsel << log2P) + kR - 1) / kR;
-  if (s >= nsplit) {  // uniform: nothing to read for this item
-    if (s == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
+  const int s0 = it * a.spi;
+  const int s1 = min(s0 + a.spi, nsplit);
+  if (s0 >= nsplit) {  // uniform: nothing to read for this item
+    if (it == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
     return;
   }
 #pragma unroll
@@ -530,7 +571,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
     }
   }
   lds_barrier();
-  if (s == 0) {
+  if (it == 0) {
     for (int j = tid; j < nsel; j += kBlock) a.sel[(size_t)pair * maxP + j] = sm.s_sel[j];
     if (tid == 0) a.n_sel[pair] = nsel;
   }
@@ -589,23 +630,13 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   lds_barrier();
   const int m = sm.s_m;
 
-  // ---- this item's even share of them
-  const int lo = (int)(((long long)s * m) / nsplit);
-  const int hi = (int)(((long long)(s + 1) * m) / nsplit);
-  const int n_pg = hi - lo;
-  auto& qk = sm.u.qk;
-  for (int i = tid; i < n_pg; i += kBlock) {
-    qk.pg_phys[i] = sm.s_phys[lo + i];
-    qk.pg_valid[i] = page_valid(L, sm.s_surv[lo + i], P);
-  }
-  const int r_end = n_pg << log2P;
+  // ---- this item's share of them
   float qmv[kMfma ? kQPer : 1];
 #pragma unroll
   for (int u = 0; u < (kMfma ? kQPer : 1); ++u) qmv[u] = qv[u < kQPer ? u : 0];
-  if (n_pg > 0)
-    qk_score_slots<T, D, G, kMfma>(qg, qmv, a.zscale, a.K, a.Hkv, g, P, log2P, 0, r_end, 0, qk);
-  qk_emit<T, D, G, false, kMfma>(qk, r_end, 0, 0, P, log2P, a.cand, a.cnt, a.smax, bh0, a.splits,
-                                 s);
+  read_share<T, D, G, kMfma>(a, sm.u.qk, qg, qmv, g, L, bh0, s0, s1, nsplit, m, [&](int idx) {
+    return make_int2(sm.s_phys[idx], sm.s_surv[idx]);
+  });
 }
 
 template <typename T, int D>
@@ -630,12 +661,20 @@ hipError_t launch_t(const Shape& s, const DecodePlan& pl, const float* q, float 
                     float2* cand, int* cnt, float* smax, const TopkHint& hint,
                     hipStream_t stream) {
   const long long npairs = (long long)s.B * s.Hkv;
-  const long long items = npairs * pl.splits;
+  // items per pair: enough for about kStepItems workgroups in all (every item
+  // repeats the pair's selection, so no more than that), each holding spi
+  // consecutive splits
+  long long nit = (kStepItems + npairs - 1) / npairs;
+  nit = nit < 1 ? 1 : (nit > pl.splits ? pl.splits : nit);
+  const int spi = (int)((pl.splits + nit - 1) / nit);
+  nit = (pl.splits + spi - 1) / spi;
+  const long long items = npairs * nit;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const SelQkArgs<T> a{q,      zscale,    a1,          (const T*)K, bt,      lens,
                        ub,     ubg,       sel,         n_sel,       top_k,   s.Hkv,
-                       s.P,    s.log2P,   s.maxP,      pl.splits,   (int)npairs, cand,
-                       cnt,    smax,      hint.hint,   hint.slice_pages, hint.nslices};
+                       s.P,    s.log2P,   s.maxP,      pl.splits,   (int)npairs, spi,
+                       cand,   cnt,       smax,        hint.hint,   hint.slice_pages,
+                       hint.nslices};
   if (ub != nullptr && hint_fits<T, D, G>(s, hint))
     hipLaunchKernelGGL((sel_qk_hint_kernel<T, D, G, kPer>), dim3((unsigned)items), dim3(kBlock),
                        0, stream, a);
