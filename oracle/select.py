@@ -43,12 +43,24 @@ Gaussian partial moments, I_g(h) = E[(Z + h)_+^g] for Z ~ N(0, 1):
    I_0 = Phi(h),  I_1 = h Phi(h) + phi(h),  I_g = h I_{g-1} + (g-1) I_{g-2}
 (the last by Stein's identity E[Z f(Z)] = E[f'(Z)]), and for X ~ N(mu, s^2),
    E[(X - c)_+^g] = s^g I_g((mu - c)/s).
+For a gamma that is not an integer (1 < alpha < 2, alpha not 1 + 1/n) the
+oracle evaluates the defining integral I_g(h) = int_0^inf x^g phi(x - h) dx by
+adaptive quadrature.  The reading stops at alpha <= 2 (gamma >= 1): F_h is
+then convex as well as decreasing, and the solvers (the oracle's bisection and
+the device's monotone Newton) are defined on that range only.
 F_h is continuous and decreasing; at tau = max_p (alpha-1) m_{h,p} - 1 the page
-with the largest mean alone contributes at least 1 (Jensen), so F_h >= 1 there.
+with the largest mean alone contributes at least 1 (Jensen, x -> x_+^g being
+convex for g >= 1), so F_h >= 1 there.
 
 Pins (tests/test_oracle_select.py): top-k against a brute-force full sort and
 hand-built tie cases; e_n against the closed forms known for n <= 5 and a
 Monte Carlo estimate; I_g against numerical quadrature (scipy.integrate.quad);
+for non-integer g, the quadrature against the parabolic-cylinder closed form
+I_g(h) = Gamma(g+1) e^(-h^2/4) D_{-g-1}(-h) / sqrt(2 pi) (mpmath, 40 digits),
+against the integer recurrence when g is an integer, and against Stein's
+recurrence between g - 1, g and g + 1; tau-hat for non-integer g approaches
+the integer-g solutions as g -> 1, 2 and, for zero-variance pages, equals the
+exact entmax threshold (oracle.entmax.threshold) of the expanded multiset;
 tau-hat for zero-variance pages equals the exact entmax threshold of the
 expanded token multiset (checked against the sort-based sparsemax closed form);
 the box-bound keep rule on hand-worked pages at alpha = 1.5 and 1.25 (literal
@@ -91,28 +103,64 @@ def partial_moment(h, g: int):
     return i_cur
 
 
-def integer_gamma(alpha: float) -> int:
-    g = 1.0 / (float(alpha) - 1.0)
+def selection_gamma(alpha: float):
+    """gamma = 1/(alpha-1) for the Gaussian rules: an int when it is one (to
+    within 1e-6 relative, the integer recurrence), else the float; alpha must
+    lie in (1, 2] (gamma >= 1)."""
+    a = float(alpha)
+    if not (1.0 < a <= 2.0):
+        raise ValueError("the Gaussian rules are read for 1 < alpha <= 2 (gamma >= 1)")
+    g = 1.0 / (a - 1.0)
     gi = int(round(g))
-    if gi < 1 or abs(g - gi) > 1e-6 * gi:
-        raise ValueError("Gaussian selection needs 1/(alpha-1) to be an integer")
-    return gi
+    if abs(g - gi) <= 1e-6 * gi:
+        return gi
+    return g
 
 
-def gauss_F(tau, mu_z, sig_z, counts, g: int) -> float:
-    """F(tau) = sum_p n_p E[(X_p - tau)_+^g] with X_p ~ N(mu_z[p], sig_z[p]^2)."""
+def partial_moment_quad(h: float, g: float) -> float:
+    """I_g(h) = int_0^inf x^g phi(x - h) dx by adaptive quadrature (any real g > -1)."""
+    h = float(h)
+    g = float(g)
+
+    def f(x):
+        return x ** g * math.exp(-0.5 * (x - h) * (x - h)) / math.sqrt(2.0 * math.pi)
+
+    # the integrand is negligible beyond max(h, 0) + 40; split at its peak
+    top = max(h, 0.0) + 40.0
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", integrate.IntegrationWarning)
+        if h > 0.0:
+            a = integrate.quad(f, 0.0, h, epsabs=0.0, epsrel=2e-14, limit=500)[0]
+            b = integrate.quad(f, h, top, epsabs=0.0, epsrel=2e-14, limit=500)[0]
+            return a + b
+        return integrate.quad(f, 0.0, top, epsabs=0.0, epsrel=2e-14, limit=500)[0]
+
+
+def partial_moment_real(h, g):
+    """I_g(h) for a real g >= 0: the integer recurrence for an int g, else
+    quadrature of the definition (vectorised in h)."""
+    if isinstance(g, (int, np.integer)):
+        return partial_moment(h, int(g))
+    h = np.asarray(h, dtype=np.float64)
+    out = np.array([partial_moment_quad(x, g) for x in h.ravel()], dtype=np.float64)
+    return out.reshape(h.shape)
+
+
+def gauss_F(tau, mu_z, sig_z, counts, g) -> float:
+    """F(tau) = sum_p n_p E[(X_p - tau)_+^g] with X_p ~ N(mu_z[p], sig_z[p]^2)
+    (g an int, or a real g >= 1)."""
     mu_z = np.asarray(mu_z, dtype=np.float64)
     sig_z = np.asarray(sig_z, dtype=np.float64)
     counts = np.asarray(counts, dtype=np.float64)
     pos = sig_z > 0.0
     terms = np.empty_like(mu_z)
     sp = sig_z[pos]
-    terms[pos] = sp ** g * partial_moment((mu_z[pos] - tau) / sp, g)
+    terms[pos] = sp ** g * partial_moment_real((mu_z[pos] - tau) / sp, g)
     terms[~pos] = np.maximum(mu_z[~pos] - tau, 0.0) ** g
     return math.fsum(counts * terms)
 
 
-def gauss_tau_hat(mu_z, sig_z, counts, g: int, max_iter: int = 400) -> float:
+def gauss_tau_hat(mu_z, sig_z, counts, g, max_iter: int = 400) -> float:
     """Root of F(tau) = 1 by bracketing then bisection to fp64 convergence."""
     mu_z = np.asarray(mu_z, dtype=np.float64)
     lo = float(mu_z.max()) - 1.0
@@ -141,7 +189,7 @@ def gauss_select(u_heads, m_heads, v_heads, counts, alpha: float, delta: float):
     moments; counts: valid tokens per page [n].
     Returns (ascending page list, tau_hat [G]).
     """
-    g = integer_gamma(alpha)
+    g = selection_gamma(alpha)
     a1 = float(alpha) - 1.0
     u_heads = np.asarray(u_heads, dtype=np.float32)
     G, n = u_heads.shape
@@ -184,7 +232,7 @@ def gauss_est_select(u_heads, m_heads, v_heads, counts, alpha: float, delta: flo
     Same arguments and results as gauss_select; page p is kept when
     (alpha-1) * (m + e_{n_p} * sqrt(v)) >= tau_hat - delta for a head of the group.
     """
-    g = integer_gamma(alpha)
+    g = selection_gamma(alpha)
     a1 = float(alpha) - 1.0
     u_heads = np.asarray(u_heads, dtype=np.float32)
     G, n = u_heads.shape
@@ -206,7 +254,7 @@ def gauss_est_select(u_heads, m_heads, v_heads, counts, alpha: float, delta: flo
     return [int(p) for p in np.nonzero(keep)[0]], taus
 
 
-def gauss_page_masses(mu_z, sig_z, counts, g: int, tau: float) -> np.ndarray:
+def gauss_page_masses(mu_z, sig_z, counts, g, tau: float) -> np.ndarray:
     """M_p = n_p E[(X_p - tau)_+^g], X_p ~ N(mu_z[p], sig_z[p]^2) (zero sig: a point mass)."""
     mu_z = np.asarray(mu_z, dtype=np.float64)
     sig_z = np.asarray(sig_z, dtype=np.float64)
@@ -214,7 +262,7 @@ def gauss_page_masses(mu_z, sig_z, counts, g: int, tau: float) -> np.ndarray:
     pos = sig_z > 0.0
     terms = np.empty_like(mu_z)
     sp = sig_z[pos]
-    terms[pos] = sp ** g * partial_moment((mu_z[pos] - tau) / sp, g)
+    terms[pos] = sp ** g * partial_moment_real((mu_z[pos] - tau) / sp, g)
     terms[~pos] = np.maximum(mu_z[~pos] - tau, 0.0) ** g
     return counts * terms
 
@@ -226,7 +274,7 @@ def gauss_mass_select(u_heads, m_heads, v_heads, counts, alpha: float, eps: floa
     page p is kept when n_p E[(X_{h,p} - tau_hat_h)_+^gamma] >= eps for a head
     h of the group.
     """
-    g = integer_gamma(alpha)
+    g = selection_gamma(alpha)
     a1 = float(alpha) - 1.0
     u_heads = np.asarray(u_heads, dtype=np.float32)
     G, n = u_heads.shape

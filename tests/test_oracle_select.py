@@ -157,14 +157,6 @@ def test_gauss_select_hand_worked_alpha_scaling(alpha, u, m):
     assert sel2 == [0, 1, 2, 4]
 
 
-def test_integer_gamma_rule():
-    assert select.integer_gamma(1.5) == 2
-    assert select.integer_gamma(2.0) == 1
-    assert select.integer_gamma(1.25) == 4
-    with pytest.raises(ValueError):
-        select.integer_gamma(1.7)
-
-
 # Expected maximum of n independent standard normals: closed forms for n <= 5
 # (order statistics of the normal distribution): e_1 = 0, e_2 = 1/sqrt(pi),
 # e_3 = 3/(2 sqrt(pi)), e_4 = 6/pi^(3/2) * arctan(sqrt(2)),
@@ -291,3 +283,95 @@ def test_gauss_mass_select_rule_and_guard():
     u2 = np.array([[1.0, 7.0, 7.0]], np.float32)
     sel2, _ = select.gauss_mass_select(u2, np.zeros((1, 3)), np.ones((1, 3)), [4, 4, 4], 2.0, 1.5)
     assert sel2 == [1]
+
+
+# ---- non-integer gamma (1 < alpha < 2): the quadrature of I_g ----
+
+def _pcf_closed_form(h, g):
+    # I_g(h) = Gamma(g+1) exp(-h^2/4) D_{-g-1}(-h) / sqrt(2 pi), parabolic
+    # cylinder function D at 40 significant digits
+    import mpmath
+    with mpmath.workdps(40):
+        h = mpmath.mpf(h)
+        g = mpmath.mpf(g)
+        v = mpmath.gamma(g + 1) * mpmath.exp(-h * h / 4) * mpmath.pcfd(-g - 1, -h)
+        return float(v / mpmath.sqrt(2 * mpmath.pi))
+
+
+@pytest.mark.parametrize("g", [1.0 / 0.7, 1.0 / 0.7 - 1.0, 2.5, 1.5, 0.5, 3.3])
+@pytest.mark.parametrize("h", [-9.0, -5.0, -2.0, -0.5, 0.0, 0.3, 1.0, 2.5, 5.0, 8.0, 12.0])
+def test_partial_moment_quadrature_vs_parabolic_cylinder(g, h):
+    got = select.partial_moment_quad(h, g)
+    ref = _pcf_closed_form(h, g)
+    assert abs(got - ref) <= 1e-13 * abs(ref), (got, ref)
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4])
+@pytest.mark.parametrize("h", [-6.0, -1.0, 0.0, 0.7, 2.0, 5.0])
+def test_partial_moment_quadrature_matches_integer_recurrence(g, h):
+    got = select.partial_moment_quad(h, float(g))
+    ref = float(select.partial_moment(h, g))
+    # (the recurrence loses relative accuracy in the left tail, as above)
+    assert abs(got - ref) <= 1e-12 * abs(ref) + 1e-16, (g, h, got, ref)
+    if h >= -1.0:
+        assert abs(got - ref) <= 1e-13 * abs(ref), (g, h, got, ref)
+
+
+@pytest.mark.parametrize("g", [1.0 / 0.7, 2.5, 1.0 / 0.55])
+@pytest.mark.parametrize("h", [-3.0, -0.5, 0.0, 1.5, 4.0])
+def test_partial_moment_quadrature_stein_recurrence(g, h):
+    # E[(Z+h)_+^(g+1)] = h E[(Z+h)_+^g] + g E[(Z+h)_+^(g-1)] (Stein's identity)
+    lhs = select.partial_moment_quad(h, g + 1.0)
+    rhs = h * select.partial_moment_quad(h, g) + g * select.partial_moment_quad(h, g - 1.0)
+    assert abs(lhs - rhs) <= 1e-12 * abs(lhs), (lhs, rhs)
+
+
+def test_selection_gamma_rule():
+    assert select.selection_gamma(1.5) == 2 and isinstance(select.selection_gamma(1.5), int)
+    assert select.selection_gamma(2.0) == 1
+    g = select.selection_gamma(1.7)
+    assert isinstance(g, float) and abs(g - 1.0 / 0.7) < 1e-15
+    assert abs(select.selection_gamma(1.4) - 2.5) < 1e-15
+    for bad in (2.5, 1.0, 0.9, 3.0):
+        with pytest.raises(ValueError):
+            select.selection_gamma(bad)
+
+
+@pytest.mark.parametrize("alpha", [1.7, 1.4])
+@pytest.mark.parametrize("seed", range(3))
+def test_tau_hat_fractional_zero_variance_is_exact_threshold(alpha, seed):
+    # zero-variance pages: F is the exact entmax normalisation of the expanded
+    # multiset, whose threshold the decode oracle finds on the tokens directly
+    from oracle import entmax
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(2, 30))
+    mu_z = rng.normal(0, 1.5, n)
+    counts = rng.integers(1, 17, n)
+    g = select.selection_gamma(alpha)
+    t = select.gauss_tau_hat(mu_z, np.zeros(n), counts, g)
+    ref = entmax.threshold(_expand(mu_z, counts), alpha)  # z-space scores
+    assert abs(t - ref) < 1e-12 * max(1.0, abs(ref)), (t, ref)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_tau_hat_fractional_solves_normalisation_and_is_continuous(seed):
+    rng = np.random.default_rng(90 + seed)
+    n = 24
+    mu_z = rng.normal(0, 1, n)
+    sig = rng.uniform(0.05, 1.0, n)
+    sig[::5] = 0.0
+    counts = rng.integers(1, 17, n)
+    for g in (1.0 / 0.7, 2.5):
+        t = select.gauss_tau_hat(mu_z, sig, counts, g)
+        assert abs(select.gauss_F(t, mu_z, sig, counts, g) - 1.0) < 1e-12
+        assert select.gauss_F(t - 1e-6, mu_z, sig, counts, g) > 1.0
+        assert select.gauss_F(t + 1e-6, mu_z, sig, counts, g) < 1.0
+    # gamma -> 1, 2 from either side: the quadrature path approaches the
+    # integer recurrence's root (tau-hat is smooth in gamma)
+    for gi in (1, 2):
+        t0 = select.gauss_tau_hat(mu_z, sig, counts, gi)
+        for eps in (1e-7, -1e-7):
+            if gi == 1 and eps < 0:
+                continue  # gamma < 1 is outside the reading
+            t1 = select.gauss_tau_hat(mu_z, sig, counts, gi + eps)
+            assert abs(t1 - t0) < 1e-5 * max(1.0, abs(t0)), (gi, eps, t0, t1)
