@@ -193,9 +193,17 @@ ekv_status ekv_score_pages(const ekv_cache_desc* desc, const float* q, float sca
  *   of page p, gamma = 1/(alpha-1); page p is kept when
  *   (alpha-1) * ub[b][g][p][i] >= tau_hat[b][g G + i] - delta for some i < G
  *   (compared in fp64).  If no page is kept, the page with the largest ubg is
- *   (lowest index on ties).  Needs ub, ubg, gm, gv and tau_hat; gamma must be
- *   1, 2, 3 or 4 (alpha in {2, 1.5, 4/3, 1.25}) else EKV_ERR_UNSUPPORTED;
- *   delta >= 0.
+ *   (lowest index on ties).  Needs ub, ubg, gm, gv and tau_hat; delta >= 0.
+ *   alpha must lie in (1, 2] with gamma <= 64 (alpha >= 1 + 1/64), else
+ *   EKV_ERR_UNSUPPORTED: for alpha > 2 (gamma < 1) the normalisation is no
+ *   longer convex in tau and the monotone Newton solve does not apply.  A
+ *   gamma within 1e-6 of an integer is taken as that integer; E[(X - c)_+^g]
+ *   = s^g I_g((mu - c)/s), I_g(h) = E[(Z + h)_+^g], comes from the recurrence
+ *   I_g = h I_{g-1} + (g-1) I_{g-2} started at I_0 = Phi, I_1 = h Phi + phi
+ *   (integer g), or at I_f, I_{f+1} with f = g - floor(g), which each launch
+ *   tabulates per block over h (Chebyshev pieces from a Gauss-Jacobi /
+ *   Gauss-Legendre quadrature of their defining integrals, about 1e-13
+ *   relative).
  * EKV_SELECT_GAUSS_EST: as EKV_SELECT_GAUSS, but the estimated maximum score
  *   of page p for head h is the expected maximum of its n_p token scores
  *   modelled as independent N(gm, gv) draws (the estimated maximum of §2.B):

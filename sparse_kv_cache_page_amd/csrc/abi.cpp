@@ -156,11 +156,15 @@ ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
     return EKV_ERR_INVALID_ARG;
   if (!(alpha > 1.0f) || !isfinite(alpha)) return EKV_ERR_INVALID_ARG;
   if (!(delta >= 0.0f) || !isfinite(delta)) return EKV_ERR_INVALID_ARG;
-  const double gamma = 1.0 / ((double)alpha - 1.0);
+  // gamma = 1 / (alpha - 1) >= 1 (alpha <= 2), at most 64; within 1e-6 of an
+  // integer it is taken as that integer
+  if (!((double)alpha <= 2.0)) return EKV_ERR_UNSUPPORTED;
+  double gamma = 1.0 / ((double)alpha - 1.0);
   const double gr = rint(gamma);
-  if (gr < 1.0 || gr > 4.0 || fabs(gamma - gr) > 1e-6 * gr) return EKV_ERR_UNSUPPORTED;
-  return from_hip(ekv::launch_gauss(s, seq_lens, alpha, (int)gr, delta, rule, ub, ubg, gm, gv,
-                                    sel, n_sel, tau_hat, stream));
+  if (fabs(gamma - gr) <= 1e-6 * gr) gamma = gr;
+  if (gamma > 64.0) return EKV_ERR_UNSUPPORTED;
+  return from_hip(ekv::launch_gauss(s, seq_lens, alpha, gamma, delta, rule, ub, ubg, gm, gv, sel,
+                                    n_sel, tau_hat, stream));
 }
 
 size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel) {

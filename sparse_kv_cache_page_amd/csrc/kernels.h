@@ -70,8 +70,9 @@ double expected_max_std_normal(int n);
 
 // Gaussian-aware selection; `rule` 0 compares the box bound ub, 1 the
 // expected maximum m + e_n sqrt(v) of the page's scores, 2 the page's
-// expected entmax mass (against delta).
-hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int gamma,
+// expected entmax mass (against delta).  gamma = 1 / (alpha - 1) >= 1 (an
+// integer one exactly when the caller rounded it).
+hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, double gamma,
                         float delta, int rule, const float* ub, const float* ubg,
                         const double* gm, const double* gv, int32_t* sel, int32_t* n_sel,
                         double* tau_hat, hipStream_t stream);

@@ -22,6 +22,8 @@
 // m + e_n sqrt(v), the expected maximum of its n valid token scores drawn from
 // N(m, v) (expected-maximum reading), with e_n = E[max of n iid N(0,1)]
 // tabulated once on the host.
+#include <type_traits>
+
 #include "blocks.h"
 #include "kernels.h"
 
@@ -97,6 +99,180 @@ __device__ inline T ipow(T x) {
   return r;
 }
 
+// --------------------------------------------------------------------------
+// Non-integer gamma (1 < alpha < 2, alpha not 1 + 1/n): I_g for g = n + f,
+// n = floor(g) >= 1, f in (0, 1), from the pair (I_f, I_{f+1}) by the
+// recurrence above.  Per launch the pair is tabulated over h as Chebyshev
+// series on short pieces, the values at the Chebyshev points coming from a
+// quadrature of the defining integrals I_nu(h) = int_0^inf x^nu phi(x - h) dx.
+// --------------------------------------------------------------------------
+constexpr int kFracGj = 16;          // Gauss-Jacobi nodes on [0, 1], weight x^f
+constexpr int kFracGl = 12;          // Gauss-Legendre nodes per panel beyond x = 1
+constexpr double kFracPanel = 1.5;   // panel width beyond x = 1
+constexpr double kFracHmin = -9.0;   // I_nu(h) < 1e-19 below: taken as 0
+constexpr double kFracHmax = 8.5;    // asymptotic series from here on
+constexpr double kFracPiece = 0.5;   // Chebyshev piece width in h
+constexpr int kFracPieces = 35;      // (kFracHmax - kFracHmin) / kFracPiece
+constexpr int kFracN = 17;           // Chebyshev points (degree 16) per piece
+
+// Quadrature rules and exponents of one launch (built on the host).
+struct FracRule {
+  double gamma, f;  // gamma = n + f
+  int n;
+  double gj_x[kFracGj], gj_w[kFracGj];  // int_0^1 x^f g(x) dx ~ sum_i w_i g(x_i)
+  double gl_x[kFracGl], gl_w[kFracGl];  // int_0^1 g(x) dx ~ sum_i w_i g(x_i)
+};
+
+// c[0]: I_f, c[1]: I_{f+1}; piece k covers h in kFracHmin + [k, k+1) kFracPiece
+struct FracTable {
+  double c[2][kFracPieces][kFracN];
+};
+
+// I_f(h) and I_{f+1}(h) by quadrature: [0, 1] by Gauss-Jacobi with the weight
+// x^f (the factor that is not smooth at 0), then Gauss-Legendre panels of
+// width 1.5 over [max(1, h - 10), max(h, 0) + 10]; the integrand is below
+// phi(10) < 1e-22 of its peak outside.  About 4e-15 relative for h in
+// [-9, 8.5] (checked against the oracle's adaptive quadrature).
+__device__ inline void frac_quad(const FracRule& r, double h, double& i0, double& i1) {
+  double a0 = 0.0, a1 = 0.0;
+  for (int i = 0; i < kFracGj; ++i) {
+    const double x = r.gj_x[i];
+    const double ph = r.gj_w[i] * exp(-0.5 * (x - h) * (x - h));
+    a0 += ph;
+    a1 = fma(ph, x, a1);
+  }
+  const double lo = fmax(1.0, h - 10.0);
+  const double hi = fmax(h, 0.0) + 10.0;
+  for (int k = 0; lo + k * kFracPanel < hi; ++k) {
+    const double c = lo + k * kFracPanel;
+    const double w = fmin(kFracPanel, hi - c);
+    for (int i = 0; i < kFracGl; ++i) {
+      const double x = fma(w, r.gl_x[i], c);
+      const double t = w * r.gl_w[i] * exp(fma(r.f, log(x), -0.5 * (x - h) * (x - h)));
+      a0 += t;
+      a1 = fma(t, x, a1);
+    }
+  }
+  i0 = a0 * 0.39894228040143267794;
+  i1 = a1 * 0.39894228040143267794;
+}
+
+// I_nu(h) for h >= 8.5 as E[(h + Z)^nu] (Z below -h weighs less than 1e-17):
+// h^nu sum_j C(nu, 2j) (2j - 1)!! h^(-2j), an asymptotic series whose terms
+// shrink while 2j < h^2; summed until a term is below 1e-17 of the sum.
+__device__ inline double frac_asym(double nu, double h) {
+  const double r = 1.0 / (h * h);
+  double s = 1.0, t = 1.0;
+  for (int j = 1; j < 40; ++j) {
+    t *= (nu - 2 * j + 2) * (nu - 2 * j + 1) * (0.5 / j) * r;
+    s += t;
+    if (fabs(t) < 1e-17 * fabs(s)) break;
+  }
+  return exp(nu * log(h)) * s;
+}
+
+// The table of (I_f, I_{f+1}): values at the Chebyshev points of every piece
+// (frac_quad, one point per thread), then their cosine transforms.  Called by
+// all nthreads threads of the block; ends with a barrier.  val: LDS scratch.
+__device__ inline void build_frac_table(const FracRule& r, FracTable& t, FracTable& val,
+                                        int nthreads) {
+  for (int i = threadIdx.x; i < kFracPieces * kFracN; i += nthreads) {
+    const int k = i / kFracN, j = i % kFracN;
+    const double h = kFracHmin + (k + 0.5) * kFracPiece +
+                     0.5 * kFracPiece * cospi((j + 0.5) / kFracN);
+    frac_quad(r, h, val.c[0][k][j], val.c[1][k][j]);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * kFracPieces * kFracN; i += nthreads) {
+    const int q = i / (kFracPieces * kFracN);
+    const int k = (i / kFracN) % kFracPieces;
+    const int m = i % kFracN;
+    double a = 0.0;
+    for (int j = 0; j < kFracN; ++j) a = fma(val.c[q][k][j], cospi(m * (j + 0.5) / kFracN), a);
+    t.c[q][k][m] = (m == 0 ? 1.0 : 2.0) / kFracN * a;
+  }
+  __syncthreads();
+}
+
+// (I_f(h), I_{f+1}(h)) from the table (Clenshaw), the asymptotic series, or 0.
+__device__ inline void frac_pair(const FracRule& r, const FracTable& t, double h, double& i0,
+                                 double& i1) {
+  if (h >= kFracHmax) {
+    i0 = frac_asym(r.f, h);
+    i1 = frac_asym(r.f + 1.0, h);
+    return;
+  }
+  if (!(h >= kFracHmin)) {
+    i0 = 0.0;
+    i1 = 0.0;
+    return;
+  }
+  const int k = min((int)((h - kFracHmin) * (1.0 / kFracPiece)), kFracPieces - 1);
+  const double x = (h - (kFracHmin + (k + 0.5) * kFracPiece)) * (2.0 / kFracPiece);
+  double b1 = 0.0, b2 = 0.0, d1 = 0.0, d2 = 0.0;
+  for (int m = kFracN - 1; m >= 1; --m) {
+    const double nb = fma(2.0 * x, b1, t.c[0][k][m] - b2);
+    const double nd = fma(2.0 * x, d1, t.c[1][k][m] - d2);
+    b2 = b1;
+    b1 = nb;
+    d2 = d1;
+    d1 = nd;
+  }
+  i0 = fma(x, b1, t.c[0][k][0] - b2);
+  i1 = fma(x, d1, t.c[1][k][0] - d2);
+}
+
+// I_g(h), I_{g-1}(h) and J = g (g-1) I_{g-2}(h) for g = n + f: the base pair
+// (I_f, I_{f+1}) from the table, or (Phi, h Phi + phi) when f = 0 (an integer
+// g above the unrolled ones), then upwards I_{nu+1} = h I_nu + nu I_{nu-1};
+// I_{f-1} = (I_{f+1} - h I_f) / f is the same relation solved downwards.
+__device__ inline void partial_moments_rt(const FracRule& r, const FracTable& t, double h,
+                                          double& ig, double& igm1, double& jdd) {
+  double b0, b1, bm1;
+  if (r.f == 0.0) {
+    b0 = 0.5 * erfc(-h * 0.70710678118654752440);
+    bm1 = exp(-0.5 * h * h) * 0.39894228040143267794;
+    b1 = fma(h, b0, bm1);
+  } else {
+    frac_pair(r, t, h, b0, b1);
+    bm1 = (b1 - h * b0) / r.f;
+  }
+  double i_pp = bm1, i_prev = b0, i_cur = b1;
+  for (int k = 2; k <= r.n; ++k) {
+    const double nxt = fma(h, i_cur, (r.f + (double)(k - 1)) * i_prev);
+    i_pp = i_prev;
+    i_prev = i_cur;
+    i_cur = nxt;
+  }
+  ig = i_cur;
+  igm1 = i_prev;
+  jdd = r.gamma * (r.gamma - 1.0) * i_pp;
+}
+
+// gauss_term for a runtime gamma (fp64).
+__device__ inline void gauss_term_rt(const FracRule& r, const FracTable& t, double mz, double sd,
+                                     double rs, double tau, double cnt, double& f, double& fd,
+                                     double& fdd) {
+  if (sd > 0.0) {
+    const double h = (mz - tau) * rs;
+    if (!(h >= kFracHmin) && r.f != 0.0) return;  // below fp64 resolution of F
+    double ig, igm1, jdd;
+    partial_moments_rt(r, t, h, ig, igm1, jdd);
+    const double sg1 = exp((r.gamma - 1.0) * log(sd));
+    f = fma(cnt, sg1 * sd * ig, f);
+    fd = fma(cnt, r.gamma * sg1 * igm1, fd);
+    fdd = fma(cnt, sg1 * rs * jdd, fdd);
+  } else {
+    const double x = mz - tau;
+    if (x > 0.0) {
+      const double xg2 = exp((r.gamma - 2.0) * log(x));
+      f = fma(cnt, xg2 * x * x, f);
+      fd = fma(cnt, r.gamma * xg2 * x, fd);
+      fdd = fma(cnt, r.gamma * (r.gamma - 1.0) * xg2, fdd);
+    }
+  }
+}
+
 // One page's contribution to F(tau), -F'(tau) and (kCurv) F''(tau), counted
 // cnt times; rs = 1 / sd.
 template <int kG, bool kCurv, typename T>
@@ -163,18 +339,23 @@ __device__ inline void block_sum3(T& a, T& b, T& c, T* sh, int par) {
 // fp64 (any such point keeps Newton monotone), else at the proven start
 // max mu - 1, and stops when F - 1 or the step stops being positive, so its
 // result is the monotone Newton limit either way.
+// kG = 0: a runtime gamma (fr), whose coarse run is in fp64 as well (the
+// fp32 copies of the page statistics are then not kept).
 template <int kG, bool kLds>
 __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     const double* __restrict__ gm, const double* __restrict__ gv, const int32_t* __restrict__ lens,
-    int P, int maxP, int Hq, double a1, double* __restrict__ tau_hat) {
+    int P, int maxP, int Hq, double a1, double* __restrict__ tau_hat, FracRule fr) {
+  constexpr bool kLds32 = kLds && kG != 0;
   __shared__ double s_mu[kLds ? kGaussLdsPages : 1];
   __shared__ double s_sd[kLds ? kGaussLdsPages : 1];
-  __shared__ float s_mu32[kLds ? kGaussLdsPages : 1];
-  __shared__ float s_sd32[kLds ? kGaussLdsPages : 1];
+  __shared__ float s_mu32[kLds32 ? kGaussLdsPages : 1];
+  __shared__ float s_sd32[kLds32 ? kGaussLdsPages : 1];
   __shared__ double s_rs[kLds ? kGaussLdsPages : 1];
-  __shared__ float s_rs32[kLds ? kGaussLdsPages : 1];
+  __shared__ float s_rs32[kLds32 ? kGaussLdsPages : 1];
   __shared__ double red[6 * kTauWaves];
   __shared__ float redf[6 * kTauWaves];
+  struct NoTable {};
+  __shared__ std::conditional_t<kG == 0, FracTable, NoTable> s_ft, s_fv;
   const int bh = blockIdx.x;
   const int b = bh / Hq;
   const int L = lens[b];
@@ -183,6 +364,7 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     if (threadIdx.x == 0) tau_hat[bh] = __builtin_nan("");
     return;
   }
+  if constexpr (kG == 0) build_frac_table(fr, s_ft, s_fv, kTauBlock);
   const double* M = gm + (size_t)bh * maxP;
   const double* V = gv + (size_t)bh * maxP;
 
@@ -195,11 +377,11 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     else return a1 * sqrt(V[p]);
   };
   auto mu32_of = [&](int p) -> float {
-    if constexpr (kLds) return s_mu32[p];
+    if constexpr (kLds32) return s_mu32[p];
     else return (float)(a1 * M[p]);
   };
   auto sd32_of = [&](int p) -> float {
-    if constexpr (kLds) return s_sd32[p];
+    if constexpr (kLds32) return s_sd32[p];
     else return (float)(a1 * sqrt(V[p]));
   };
   auto inv = [](auto x) -> decltype(x) { return x > 0 ? (decltype(x))1 / x : (decltype(x))0; };
@@ -208,7 +390,7 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
     else return inv(a1 * sqrt(V[p]));
   };
   auto rs32_of = [&](int p) -> float {
-    if constexpr (kLds) return s_rs32[p];
+    if constexpr (kLds32) return s_rs32[p];
     else return inv((float)(a1 * sqrt(V[p])));
   };
   double zmax = -__builtin_huge_val();
@@ -218,10 +400,12 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
       const double sd = a1 * sqrt(V[p]);
       s_mu[p] = mz;
       s_sd[p] = sd;
-      s_mu32[p] = (float)mz;
-      s_sd32[p] = (float)sd;
       s_rs[p] = inv(sd);
-      s_rs32[p] = inv((float)sd);
+      if constexpr (kLds32) {
+        s_mu32[p] = (float)mz;
+        s_sd32[p] = (float)sd;
+        s_rs32[p] = inv((float)sd);
+      }
     }
     zmax = fmax(zmax, mz);
   }
@@ -242,18 +426,31 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
   const double huge = __builtin_huge_val();
   double lo = safe, hi = huge, t = safe;
   for (int it = 0; it < 48 && n > 0; ++it) {
-    float f = 0.0f, fd = 0.0f, fdd = 0.0f;  // fdd unused here
-    const float tf = (float)t;
-    for (int p = threadIdx.x; p < n; p += kTauBlock)
-      gauss_term<kG, false, float>(mu32_of(p), sd32_of(p), rs32_of(p), tf,
-                                   (float)page_valid(L, p, P), f, fd, fdd);
-    block_sum3(f, fd, fdd, redf, par);
+    double fs, fds, nxt;
+    if constexpr (kG != 0) {
+      float f = 0.0f, fd = 0.0f, fdd = 0.0f;  // fdd unused here
+      const float tf = (float)t;
+      for (int p = threadIdx.x; p < n; p += kTauBlock)
+        gauss_term<kG, false, float>(mu32_of(p), sd32_of(p), rs32_of(p), tf,
+                                     (float)page_valid(L, p, P), f, fd, fdd);
+      block_sum3(f, fd, fdd, redf, par);
+      fs = f;
+      fds = fd;
+      nxt = fs > 0.0 && fds > 0.0 ? t + (double)(logf(f) * f / fd) : t;
+    } else {
+      double f = 0.0, fd = 0.0, fdd = 0.0;
+      for (int p = threadIdx.x; p < n; p += kTauBlock)
+        gauss_term_rt(fr, s_ft, mu_of(p), sd_of(p), rs_of(p), t, (double)page_valid(L, p, P), f,
+                      fd, fdd);
+      block_sum3(f, fd, fdd, red, par);
+      fs = f;
+      fds = fd;
+      nxt = fs > 0.0 && fds > 0.0 ? t + log(f) * f / fd : t;
+    }
     par ^= 1;
-    const double fs = f, fds = fd;
     if (fs >= 1.0) lo = fmax(lo, t);
     else hi = fmin(hi, t);
     const bool ok = fs > 0.0 && fds > 0.0;
-    double nxt = ok ? t + (double)(logf(f) * f / fd) : t;
     if (ok && fabs(nxt - t) < 1e-6 * (1.0 + fabs(nxt))) {  // converged as far as fp32 goes
       t = nxt;
       break;
@@ -275,9 +472,14 @@ __global__ __launch_bounds__(kTauBlock) void gauss_tau_kernel(
   double tau = start;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fd = 0.0, fdd = 0.0;
-    for (int p = threadIdx.x; p < n; p += kTauBlock)
-      gauss_term<kG, true, double>(mu_of(p), sd_of(p), rs_of(p), tau, (double)page_valid(L, p, P),
-                                   f, fd, fdd);
+    for (int p = threadIdx.x; p < n; p += kTauBlock) {
+      if constexpr (kG != 0)
+        gauss_term<kG, true, double>(mu_of(p), sd_of(p), rs_of(p), tau,
+                                     (double)page_valid(L, p, P), f, fd, fdd);
+      else
+        gauss_term_rt(fr, s_ft, mu_of(p), sd_of(p), rs_of(p), tau, (double)page_valid(L, p, P),
+                      f, fd, fdd);
+    }
     block_sum3(f, fd, fdd, red, par);
     par ^= 1;
     f -= 1.0;
@@ -339,7 +541,10 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
     const float* __restrict__ ub, const float* __restrict__ ubg, const double* __restrict__ gm,
     const double* __restrict__ gv, const double* __restrict__ tau_hat,
     const int32_t* __restrict__ lens, int P, int maxP, int Hkv, double a1, double delta,
-    ExpMaxTable et, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
+    ExpMaxTable et, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, FracRule fr) {
+  constexpr bool kTable = kRule == kRuleMass && kG == 0;  // runtime gamma
+  struct NoTable {};
+  __shared__ std::conditional_t<kTable, FracTable, NoTable> s_ft, s_fv;
   __shared__ uint8_t s_flag[kMarkChunk];
   __shared__ int scan_sh[kMarkWaves + 1];
   __shared__ float s_best[kMarkWaves];
@@ -354,6 +559,7 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
     if (threadIdx.x == 0) n_sel[pair] = 0;
     return;
   }
+  if constexpr (kTable) build_frac_table(fr, s_ft, s_fv, kMarkBlock);
   const size_t head0 = ((size_t)b * Hq + g * G) * maxP;
   const double* th = tau_hat + (size_t)b * Hq + g * G;
   int32_t* out = sel + (size_t)pair * maxP;
@@ -373,7 +579,17 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
         const double sd = a1 * sqrt(gv[i]);
         const double cnt = p == n - 1 ? (double)n_last : (double)P;
         double mass;
-        if (sd > 0.0) {
+        if constexpr (kTable) {
+          double ig = 0.0, igm1, jdd;
+          if (sd > 0.0) {
+            const double hh = (mz - th[h]) / sd;
+            if (hh >= kFracHmin || fr.f == 0.0) partial_moments_rt(fr, s_ft, hh, ig, igm1, jdd);
+            mass = cnt * (exp(fr.gamma * log(sd)) * ig);
+          } else {
+            const double x = mz - th[h];
+            mass = x > 0.0 ? cnt * exp(fr.gamma * log(x)) : 0.0;
+          }
+        } else if (sd > 0.0) {
           double ig, igm1, jdd;
           partial_moments<kG>((mz - th[h]) / sd, ig, igm1, jdd);
           mass = cnt * (ipow<kG>(sd) * ig);
@@ -439,14 +655,126 @@ __global__ __launch_bounds__(kMarkBlock) void gauss_mark_kernel(
 
 template <int kG>
 hipError_t launch_gauss_tau(const Shape& s, const int32_t* lens, double a1, const double* gm,
-                            const double* gv, double* tau_hat, hipStream_t stream) {
+                            const double* gv, double* tau_hat, const FracRule& fr,
+                            hipStream_t stream) {
   if (s.maxP <= kGaussLdsPages)
     hipLaunchKernelGGL((gauss_tau_kernel<kG, true>), dim3(s.B * s.Hq), dim3(kTauBlock), 0, stream,
-                       gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat);
+                       gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat, fr);
   else
     hipLaunchKernelGGL((gauss_tau_kernel<kG, false>), dim3(s.B * s.Hq), dim3(kTauBlock), 0,
-                       stream, gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat);
+                       stream, gm, gv, lens, s.P, s.maxP, s.Hq, a1, tau_hat, fr);
   return hipGetLastError();
+}
+
+// Nodes and weights of the n-point Gauss-Jacobi rule for the weight
+// (1 - y)^a (1 + y)^b on [-1, 1], by the Golub-Welsch method: the nodes are
+// the eigenvalues of the symmetric tridiagonal Jacobi matrix of the
+// orthonormal Jacobi polynomials, the weights mu0 times the squared first
+// components of its unit eigenvectors.  The eigenproblem is solved by the
+// implicit-shift QL iteration, carrying only the first row of the
+// eigenvector matrix.  Returns false if it does not converge.
+bool gauss_jacobi(int n, double a, double b, double* x, double* w) {
+  double d[32], e[32], z[32];
+  if (n < 1 || n > 32) return false;
+  for (int i = 0; i < n; ++i) {
+    const double s = 2.0 * i + a + b;
+    d[i] = (s == 0.0) ? (b - a) / (a + b + 2.0) : (b * b - a * a) / (s * (s + 2.0));
+    if (i + 1 < n) {
+      const double k = i + 1.0;
+      const double t = 2.0 * k + a + b;
+      e[i] = sqrt(4.0 * k * (k + a) * (k + b) * (k + a + b) / (t * t * (t + 1.0) * (t - 1.0)));
+    } else {
+      e[i] = 0.0;
+    }
+    z[i] = i == 0 ? 1.0 : 0.0;
+  }
+  for (int l = 0; l < n; ++l) {
+    int iter = 0;
+    int m;
+    do {
+      for (m = l; m < n - 1; ++m) {
+        const double dd = fabs(d[m]) + fabs(d[m + 1]);
+        if (fabs(e[m]) <= 1e-17 * dd) break;
+      }
+      if (m != l) {
+        if (++iter > 60) return false;
+        double g = (d[l + 1] - d[l]) / (2.0 * e[l]);
+        double r = hypot(g, 1.0);
+        g = d[m] - d[l] + e[l] / (g + (g >= 0.0 ? r : -r));
+        double s = 1.0, c = 1.0, p = 0.0;
+        int i;
+        for (i = m - 1; i >= l; --i) {
+          double f = s * e[i];
+          const double bb = c * e[i];
+          r = hypot(f, g);
+          e[i + 1] = r;
+          if (r == 0.0) {
+            d[i + 1] -= p;
+            e[m] = 0.0;
+            break;
+          }
+          s = f / r;
+          c = g / r;
+          g = d[i + 1] - p;
+          r = (d[i] - g) * s + 2.0 * c * bb;
+          p = s * r;
+          d[i + 1] = g + p;
+          g = c * r - bb;
+          // the first component of eigenvectors i and i + 1
+          f = z[i + 1];
+          z[i + 1] = s * z[i] + c * f;
+          z[i] = c * z[i] - s * f;
+        }
+        if (r == 0.0 && i >= l) continue;
+        d[l] -= p;
+        e[l] = g;
+        e[m] = 0.0;
+      }
+    } while (m != l);
+  }
+  const double mu0 = exp((a + b + 1.0) * log(2.0) + lgamma(a + 1.0) + lgamma(b + 1.0) -
+                         lgamma(a + b + 2.0));
+  // ascending nodes
+  int idx[32];
+  for (int i = 0; i < n; ++i) idx[i] = i;
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && d[idx[j]] < d[idx[j - 1]]; --j) {
+      const int t = idx[j];
+      idx[j] = idx[j - 1];
+      idx[j - 1] = t;
+    }
+  double sw = 0.0;
+  for (int i = 0; i < n; ++i) {
+    x[i] = d[idx[i]];
+    w[i] = mu0 * z[idx[i]] * z[idx[i]];
+    sw += w[i];
+  }
+  return fabs(sw - mu0) <= 1e-12 * mu0;
+}
+
+// The quadrature rules of a runtime gamma, mapped to [0, 1]:
+// int_0^1 x^f g dx = 2^(-f-1) int_{-1}^1 (1 + y)^f g((1 + y) / 2) dy.
+bool make_frac_rule(double gamma, FracRule& r) {
+  r.gamma = gamma;
+  r.n = (int)floor(gamma);
+  r.f = gamma - r.n;
+  double y[32], w[32];
+  if (r.f > 0.0) {
+    if (!gauss_jacobi(kFracGj, 0.0, r.f, y, w)) return false;
+    const double sc = exp(-(r.f + 1.0) * log(2.0));
+    for (int i = 0; i < kFracGj; ++i) {
+      r.gj_x[i] = 0.5 * (1.0 + y[i]);
+      r.gj_w[i] = sc * w[i];
+    }
+  } else {
+    for (int i = 0; i < kFracGj; ++i) r.gj_x[i] = r.gj_w[i] = 0.0;
+  }
+  if (!gauss_jacobi(kFracGl, 0.0, 0.0, y, w)) return false;
+  for (int i = 0; i < kFracGl; ++i) {
+    r.gl_x[i] = 0.5 * (1.0 + y[i]);
+    r.gl_w[i] = 0.5 * w[i];
+  }
+  return true;
 }
 
 // e_n = integral of x n phi(x) Phi(x)^(n-1) dx by the trapezoidal rule on
@@ -487,25 +815,27 @@ template <int kRule, int G, int kG>
 void launch_mark_t(const Shape& s, const float* ub, const float* ubg, const double* gm,
                    const double* gv, const double* tau_hat, const int32_t* lens, double a1,
                    double delta, const ExpMaxTable& et, int32_t* sel, int32_t* n_sel,
-                   hipStream_t stream) {
+                   const FracRule& fr, hipStream_t stream) {
   hipLaunchKernelGGL((gauss_mark_kernel<kRule, G, kG>), dim3(s.B * s.Hkv), dim3(kMarkBlock), 0,
                      stream, ub, ubg, gm, gv, tau_hat, lens, s.P, s.maxP, s.Hkv, a1, delta, et,
-                     sel, n_sel);
+                     sel, n_sel, fr);
 }
 
+// gamma: 1 .. 4, or 0 for a runtime gamma (fr)
 template <int G>
 hipError_t launch_mark(const Shape& s, int rule, int gamma, const float* ub, const float* ubg,
                        const double* gm, const double* gv, const double* tau_hat,
                        const int32_t* lens, double a1, double delta, const ExpMaxTable& et,
-                       int32_t* sel, int32_t* n_sel, hipStream_t stream) {
+                       int32_t* sel, int32_t* n_sel, const FracRule& fr, hipStream_t stream) {
 #define EKV_MARK(R, KG) \
-  launch_mark_t<R, G, KG>(s, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream)
+  launch_mark_t<R, G, KG>(s, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, fr, stream)
   if (rule == kRuleBound) {
     EKV_MARK(kRuleBound, 1);
   } else if (rule == kRuleEstMax) {
     EKV_MARK(kRuleEstMax, 1);
   } else {
     switch (gamma) {
+      case 0: EKV_MARK(kRuleMass, 0); break;
       case 1: EKV_MARK(kRuleMass, 1); break;
       case 2: EKV_MARK(kRuleMass, 2); break;
       case 3: EKV_MARK(kRuleMass, 3); break;
@@ -535,25 +865,32 @@ hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, int gamma, float delta,
-                        int rule, const float* ub, const float* ubg, const double* gm,
-                        const double* gv, int32_t* sel, int32_t* n_sel, double* tau_hat,
-                        hipStream_t stream) {
+hipError_t launch_gauss(const Shape& s, const int32_t* lens, float alpha, double gamma,
+                        float delta, int rule, const float* ub, const float* ubg,
+                        const double* gm, const double* gv, int32_t* sel, int32_t* n_sel,
+                        double* tau_hat, hipStream_t stream) {
   const double a1 = (double)alpha - 1.0;
+  // gamma 1 .. 4: the unrolled recurrences; any other gamma >= 1 at run time
+  const int gi = (gamma == 1.0 || gamma == 2.0 || gamma == 3.0 || gamma == 4.0) ? (int)gamma : 0;
+  FracRule fr{};
+  if (gi == 0) {
+    if (!(gamma >= 1.0) || !make_frac_rule(gamma, fr)) return hipErrorInvalidValue;
+  }
   hipError_t e = hipErrorInvalidValue;
-  switch (gamma) {
-    case 1: e = launch_gauss_tau<1>(s, lens, a1, gm, gv, tau_hat, stream); break;
-    case 2: e = launch_gauss_tau<2>(s, lens, a1, gm, gv, tau_hat, stream); break;
-    case 3: e = launch_gauss_tau<3>(s, lens, a1, gm, gv, tau_hat, stream); break;
-    case 4: e = launch_gauss_tau<4>(s, lens, a1, gm, gv, tau_hat, stream); break;
+  switch (gi) {
+    case 0: e = launch_gauss_tau<0>(s, lens, a1, gm, gv, tau_hat, fr, stream); break;
+    case 1: e = launch_gauss_tau<1>(s, lens, a1, gm, gv, tau_hat, fr, stream); break;
+    case 2: e = launch_gauss_tau<2>(s, lens, a1, gm, gv, tau_hat, fr, stream); break;
+    case 3: e = launch_gauss_tau<3>(s, lens, a1, gm, gv, tau_hat, fr, stream); break;
+    case 4: e = launch_gauss_tau<4>(s, lens, a1, gm, gv, tau_hat, fr, stream); break;
   }
   if (e != hipSuccess) return e;
   const ExpMaxTable& et = exp_max_table();
   switch (s.G) {
-    case 1: e = launch_mark<1>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
-    case 2: e = launch_mark<2>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
-    case 4: e = launch_mark<4>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
-    case 8: e = launch_mark<8>(s, rule, gamma, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, stream); break;
+    case 1: e = launch_mark<1>(s, rule, gi, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, fr, stream); break;
+    case 2: e = launch_mark<2>(s, rule, gi, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, fr, stream); break;
+    case 4: e = launch_mark<4>(s, rule, gi, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, fr, stream); break;
+    case 8: e = launch_mark<8>(s, rule, gi, ub, ubg, gm, gv, tau_hat, lens, a1, delta, et, sel, n_sel, fr, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

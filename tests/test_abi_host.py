@@ -147,21 +147,21 @@ def test_select_argument_errors(lib):
     assert call(policy=1, alpha=1.0) == INVALID
     assert call(policy=1, delta=-0.1) == INVALID
     assert call(policy=1, delta=float("nan")) == INVALID
-    assert call(policy=1, alpha=1.7) == UNSUPPORTED    # gamma = 1/0.7 not an integer
-    assert call(policy=1, alpha=1.1) == UNSUPPORTED    # gamma = 10 > 4
+    assert call(policy=1, alpha=2.5) == UNSUPPORTED    # gamma = 2/3 < 1
+    assert call(policy=1, alpha=1.01) == UNSUPPORTED   # gamma = 100 > 64
     assert call(policy=1, tau=None) == INVALID
     assert call(policy=1, gm=None) == INVALID
     assert call(policy=1, ub=None) == INVALID
     # the expected-maximum policy: same checks, ub not needed
     assert call(policy=2, alpha=1.0, ub=None) == INVALID
     assert call(policy=2, delta=-0.1, ub=None) == INVALID
-    assert call(policy=2, alpha=1.7, ub=None) == UNSUPPORTED
+    assert call(policy=2, alpha=3.0, ub=None) == UNSUPPORTED
     assert call(policy=2, gv=None, ub=None) == INVALID
     assert call(policy=2, tau=None, ub=None) == INVALID
     # the expected-mass policy (delta is the mass threshold): same checks
     assert call(policy=3, alpha=1.0, ub=None) == INVALID
     assert call(policy=3, delta=-0.1, ub=None) == INVALID
-    assert call(policy=3, alpha=1.7, ub=None) == UNSUPPORTED
+    assert call(policy=3, alpha=2.0001, ub=None) == UNSUPPORTED
     assert call(policy=3, gm=None, ub=None) == INVALID
     assert call(policy=3, tau=None, ub=None) == INVALID
     assert call(policy=4) == INVALID
