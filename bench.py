@@ -850,9 +850,10 @@ def comparison(w, args, dev, step_ms, copy_gbps):
 
 def extra_workloads(args, dev):
     """The larger single-GPU workloads, reported with the headline line: ragged
-    (batch 64, lengths U[4096, 65536], top-512) and stress (batch 32, context
+    (batch 64, lengths U[4096, 65536], top-512), stress (batch 32, context
     131072, 64/8 heads, page 32, alpha 1.25) with top-512 pages and with the
-    full-cache dense pass.  Each: steps/s, effective KV bandwidth, per entry
+    full-cache dense pass, and one 1M-token row (4/1 heads, top-8192 pages and
+    the dense pass).  Each: steps/s, effective KV bandwidth, per entry
     point times and bytes, the roofline of its dominant entry point and the
     step diagnostics."""
     import gc
@@ -860,7 +861,8 @@ def extra_workloads(args, dev):
     from sparse_kv_cache_page_amd import workloads as wl
     out = []
     for w in (wl.CONFIGS["ragged"], wl.CONFIGS["stress"],
-              wl.variant("stress", policy="dense", name="stress_dense")):
+              wl.variant("stress", policy="dense", name="stress_dense"),
+              wl.CONFIGS["long1m"], wl.variant("long1m", policy="dense", name="long1m_dense")):
         print(f"[workloads] {w.name}", file=sys.stderr, flush=True)
         r = run(w, args, dev, emit_cpu=False, light=True)
         keep = ("config", "value", "unit", "ms_per_step", "steps", "effective_kv_gbps",

@@ -208,7 +208,7 @@ int slots_per_item(const Shape& s) {
 bool decode_shape_supported(const Shape& s, int max_sel) {
   const long long slots = (long long)max_sel * s.P;
   const long long splits = (slots + slots_per_item(s) - 1) / slots_per_item(s);
-  return splits <= kMaxSplits && (long long)s.Np * s.P < (1LL << 31);
+  return splits <= kMaxSplitsTotal && (long long)s.Np * s.P < (1LL << 31);
 }
 
 DecodePlan make_decode_plan(const Shape& s, int max_sel, bool fused) {

@@ -14,7 +14,8 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kRowsPerThread = 16;  // K rows each thread has in flight per item
 constexpr int kCandCap = 2048;      // LDS candidates per head; more falls back to global
-constexpr int kMaxSplits = 2048;    // splits per head whose offsets fit in LDS
+constexpr int kMaxSplits = 2048;    // splits per head whose offsets fit in LDS at once
+constexpr int kMaxSplitsTotal = 65536;  // splits per head (16M token slots at 256 a split)
 
 template <typename T, int D>
 struct Geo {
@@ -1039,8 +1040,51 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
       __syncthreads();
     }
   }
+  // Every candidate in split order, kBlock at a time: fn(k, e, valid) is
+  // called by all threads of the block the same number of times (it may hold
+  // block barriers), k the candidate's index, valid = k < total_c.  Up to
+  // kMaxSplits splits the exclusive offsets of the per-split lists sit in
+  // s_off once (filled below); beyond, they are rebuilt for each run of
+  // kMaxSplits splits as the walk reaches it.
+  auto walk_cands = [&](auto&& fn) {
+    if (nsplit <= kMaxSplits) {
+      for (int k0 = 0; k0 < total_c; k0 += kBlock) {
+        const int k = k0 + threadIdx.x;
+        float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
+        if (k < total_c) e = cand_at(cand_bh, s_off, nsplit, kR, k);
+        fn(k, e, k < total_c);
+      }
+      return;
+    }
+    int base = 0;
+    for (int c0 = 0; c0 < nsplit; c0 += kMaxSplits) {
+      const int c1 = min(nsplit, c0 + kMaxSplits);
+      int run = 0;
+      for (int s0 = c0; s0 < c1; s0 += kBlock) {
+        const int s = s0 + threadIdx.x;
+        const int v = s < c1 ? cnt_bh[s] : 0;
+        const int incl = block_incl_scan(v, sh4);
+        if (s < c1) s_off[s - c0] = run + incl - v;
+        if (threadIdx.x == kBlock - 1) sh4[0] = incl;
+        __syncthreads();
+        run += sh4[0];
+        __syncthreads();
+      }
+      if (threadIdx.x == 0) s_off[c1 - c0] = run;
+      __syncthreads();
+      for (int k0 = 0; k0 < run; k0 += kBlock) {
+        const int k = k0 + threadIdx.x;
+        float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
+        if (k < run) e = cand_at(cand_bh + (size_t)c0 * kR, s_off, c1 - c0, kR, k);
+        fn(base + k, e, k < run);
+      }
+      base += run;
+      __syncthreads();  // s_off is rebuilt for the next run of splits
+    }
+  };
   if (!spec) {
-    // global max and the exclusive offsets of the per-split candidate lists
+    // global max, the candidate total and (up to kMaxSplits splits) the
+    // exclusive offsets of the per-split candidate lists
     zm = -__builtin_huge_valf();
     int running = 0;
     for (int s0 = 0; s0 < nsplit; s0 += kBlock) {
@@ -1051,13 +1095,13 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
         v = cnt_bh[s];
       }
       const int incl = block_incl_scan(v, sh4);
-      if (s < nsplit) s_off[s] = running + incl - v;
+      if (s < nsplit && nsplit <= kMaxSplits) s_off[s] = running + incl - v;
       if (threadIdx.x == kBlock - 1) sh4[0] = incl;  // chunk total (read after the barrier)
       __syncthreads();
       running += sh4[0];
       __syncthreads();
     }
-    if (threadIdx.x == 0) s_off[nsplit] = running;
+    if (threadIdx.x == 0 && nsplit <= kMaxSplits) s_off[nsplit] = running;
     zm = wave_max_f32(zm);
     if (lane == 0) st_p[wave] = zm;
     __syncthreads();
@@ -1067,10 +1111,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
     total_c = running;
 
     // candidates that clear the global bar, in split order
-    for (int k0 = 0; k0 < total_c; k0 += kBlock) {
-      const int k = k0 + threadIdx.x;
-      float2 e = make_float2(-__builtin_huge_valf(), 0.0f);
-      if (k < total_c) e = cand_at(cand_bh, s_off, nsplit, kR, k);
+    walk_cands([&](int, float2 e, bool) {
       const bool flag = (double)e.x > thr;
       int tot;
       const int slot = chunk_slot(flag, sh4, tot);
@@ -1079,7 +1120,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
         c_t[count + slot] = bits_of(e.y);
       }
       count += tot;
-    }
+    });
     __syncthreads();
   }
   const bool overflow = count > kCandCap;
@@ -1171,8 +1212,9 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
       if (!overflow) {
         for (int k = threadIdx.x; k < count; k += kBlock) term((double)c_z[k], tt, f, fd);
       } else {
-        for (int k = threadIdx.x; k < total_c; k += kBlock)
-          term((double)cand_at(cand_bh, s_off, nsplit, kR, k).x, tt, f, fd);
+        walk_cands([&](int, float2 e, bool valid) {
+          if (valid) term((double)e.x, tt, f, fd);
+        });
       }
       block_sum2(f, fd, shd);
     });
@@ -1207,21 +1249,8 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
       }
     }
   } else {
-    const int lim = overflow ? total_c : count;
-    for (int base = 0; base < lim; base += kBlock) {
-      const int k = base + threadIdx.x;
-      float z = -__builtin_huge_valf();
-      int ptok = 0;
-      if (k < lim) {
-        if (overflow) {
-          const float2 e = cand_at(cand_bh, s_off, nsplit, kR, k);
-          z = e.x;
-          ptok = bits_of(e.y);
-        } else {
-          z = c_z[k];
-          ptok = c_t[k];
-        }
-      }
+    // one block of candidates: the support's weights and value rows
+    auto pv_block = [&](float z, int ptok) {
       const double x = (double)z - tau;
       const bool flag = x > 0.0;
       int m;
@@ -1246,6 +1275,14 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
         for (int v = 0; v < kVec; ++v) acc[v] = fmaf(p, xv[v], acc[v]);
       }
       __syncthreads();
+    };
+    if (overflow) {
+      walk_cands([&](int, float2 e, bool) { pv_block(e.x, bits_of(e.y)); });
+    } else {
+      for (int base = 0; base < count; base += kBlock) {
+        const int k = base + threadIdx.x;
+        pv_block(k < count ? c_z[k] : -__builtin_huge_valf(), k < count ? c_t[k] : 0);
+      }
     }
     if (threadIdx.x != 0) nsupp = 0;  // the chunk totals are block-wide
   }

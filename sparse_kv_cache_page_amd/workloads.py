@@ -109,6 +109,12 @@ CONFIGS = {
                    page_size=16, lens_range=(4096, 65536), kv_dtype="bf16",
                    q_std=2.0 / math.sqrt(128), scale=1.0, alpha=1.5, policy="topk",
                    top_k=512, planted_per_kv_head=64, permute_pool=True, seed=4004),
+    # one 1M-token row (the long-context point of the EntmaxKV page, §4): one
+    # KV head with a group of four
+    "long1m": _cfg(name="long1m", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                   page_size=16, seq_len=1 << 20, kv_dtype="bf16",
+                   q_std=2.0 / math.sqrt(128), scale=1.0, alpha=1.5, policy="topk",
+                   top_k=8192, planted_per_kv_head=64, seed=6006),
     "stress": _cfg(name="stress", batch=32, num_q_heads=64, num_kv_heads=8, head_dim=128,
                    page_size=32, seq_len=131072, kv_dtype="bf16",
                    q_std=3.99 / math.sqrt(128), scale=1.0, alpha=1.25, policy="topk",

@@ -177,3 +177,21 @@ def test_fullsize_stress(stress_inputs, alpha, ti, policy, top_k):
     check_pair(inp, gpu, 31, 7, policy, top_k=w.top_k, check_meta=False)
     if policy == "topk":
         decoder_matches(inp, gpu, policy, alpha, w.top_k, w.delta, w.scale, q)
+
+
+@pytest.mark.parametrize("policy", ["topk", "dense", "gauss_mass"])
+def test_million_token_row(policy):
+    # one 1M-token row (65536 pages): the dense decode splits it into 4096
+    # runs of 256 token slots, past the 2048 whose candidate offsets fit in LDS
+    # at once; top-8192 takes the separate selection and decode
+    w = wl.CONFIGS["long1m"]
+    if policy == "dense":
+        w = wl.variant(w, policy="dense")
+    elif policy == "gauss_mass":
+        w = wl.variant(w, policy="gauss_mass", alpha=2.0, delta=1e-4)
+    print(f"[fullsize] long1m {policy}: generating", flush=True)
+    inp = wl.make_inputs(w, device=DEV)
+    gpu = run_gpu(inp, policy)
+    check_properties(inp, gpu, policy, w.top_k)
+    print(f"[fullsize] long1m {policy}: oracle pair b0 g0", flush=True)
+    check_pair(inp, gpu, 0, 0, policy)
