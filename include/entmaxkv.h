@@ -235,6 +235,9 @@ ekv_status ekv_select_pages(const ekv_cache_desc* desc, const int32_t* seq_lens,
  * when the set contains the full distribution's support, §3).
  * For each row b and query head h (KV head g), over the valid tokens i of the
  * pages sel[b][g][0 .. n_sel[b][g]) (all pages 0 .. n_b-1 when sel is NULL):
+ * entries are logical pages of row b in [0, n_b), distinct, in any order; an
+ * entry outside [0, n_b) is taken as a page with no valid token (nothing is
+ * read through it).
  *   z_i   = (alpha-1) * scale * <q[b][h], k_i>           (fp32 accumulation)
  *   tau   : sum_i [z_i - tau]_+^(1/(alpha-1)) = 1         (solved in fp64)
  *   out[b][h] = sum_i p_i v_i / sum_i p_i,  p_i = [z_i - tau]_+^(1/(alpha-1))
@@ -435,7 +438,8 @@ size_t ekv_decode_workspace_bytes(const ekv_cache_desc* desc, int32_t max_sel);
  * method's speed is compared with a full-cache softmax decode of the
  * FlashDecoding kind).  For each row b and query head h (KV head g), over the
  * valid tokens i of the pages sel[b][g][0 .. n_sel[b][g]) (all pages
- * 0 .. n_b-1 when sel is NULL):
+ * 0 .. n_b-1 when sel is NULL; entries are logical pages in [0, n_b), and an
+ * entry outside that range is taken as a page with no valid token):
  *   s_i = scale * <q[b][h], k_i>                         (fp32 accumulation)
  *   out[b][h] = sum_i exp(s_i) v_i / sum_i exp(s_i)      (fp32, every value
  *                                                          row is read)

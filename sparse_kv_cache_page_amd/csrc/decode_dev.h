@@ -746,7 +746,8 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   const int n_pg = ((r_end - 1) >> log2P) - j_begin + 1;  // <= kR
 
   // page map of this split: physical page and valid tokens per selected page
-  // (0 for a page below every head's support, which is then not read)
+  // (0 for a page below every head's support, which is then not read, and for
+  // a caller's entry outside [0, np): such an entry reads nothing)
   float zlb_h[G];
   if (a.ub) {
 #pragma unroll
@@ -756,10 +757,12 @@ __device__ __forceinline__ QkItemInfo qk_item(const QkArgs<T>& a, long long item
   for (int u = 0; u < kSpec; ++u) {
     const int i = threadIdx.x + u * kBlock;
     if (i < n_pg) {
-      const int page = sel ? spec[u] : j_begin + i;
+      const int page_raw = sel ? spec[u] : j_begin + i;
+      const bool in_row = (unsigned)page_raw < (unsigned)np;
+      const int page = in_row ? page_raw : 0;
       pg_phys[i] = bt[(size_t)b * maxP + page];
-      bool needed = true;
-      if (a.ub) {
+      bool needed = in_row;
+      if (a.ub && in_row) {
         needed = false;
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -835,6 +838,7 @@ __device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
   float best = -__builtin_huge_valf();
   int bestp = 0x7fffffff, bestphys = 0;
   auto consider = [&](int page) {
+    if ((unsigned)page >= (unsigned)np) return;  // a caller's entry outside the row
     const float u = U[(size_t)page * G];
     const int phys = a.bt[(size_t)b * a.maxP + page];
     if (u > best || (u == best && page < bestp)) {

@@ -2,12 +2,16 @@
 // bound on the largest score of any token of a page from its bounding box, and
 // the Gaussian moments of the page's scores from its key mean/variance).
 //
-// For one query head and one page, with q+ = max(q, 0) and q- = min(q, 0),
-//     sum_j max(q_j kmin_j, q_j kmax_j) = sum_j q+_j kmax_j + q-_j kmin_j
-// because the larger end point is kmax when q_j >= 0 and kmin otherwise.  Both
-// products are exact in fp64 (fp32 x bf16 or fp32 x fp32 significands fit in
-// 53 bits) and one of them is an exact zero, so the fp64 FMA chain only rounds
-// in its additions; the bound is then scaled and rounded once to fp32.
+// For one query head and one page,
+//     sum_j max(q_j kmin_j, q_j kmax_j)
+//       = 1/2 sum_j q_j (kmax_j + kmin_j) + |q_j| (kmax_j - kmin_j)
+// because the larger end point is kmax when q_j >= 0 and kmin otherwise.  The
+// sum, the difference and the two products are formed in fp64 (exact unless
+// kmin_j and kmax_j differ by more than 2^45 in magnitude for bf16, 2^29 for
+// fp32; otherwise rounded to 53 bits), the terms are added by an fp64 FMA
+// chain, and the bound is then halved, scaled and rounded once to fp32: it is
+// within an fp32 rounding of the exact value.  This form keeps one fp64 copy
+// of q in registers instead of the two halves q+ and q-.
 //
 // Mapping: workgroup i scores page slice i / pairs of (row, KV head) pair
 // i % pairs.  Consecutive workgroups go to the 8 XCDs in turn, so with the
@@ -17,8 +21,8 @@
 // a few XCDs while the others idle.  kLpr lanes cover one page's d
 // coordinates with kVec coordinates each (16- or 8-byte loads of kmin and
 // kmax), so a wave scores 64/kLpr pages per step for all G query heads of the
-// group; the per-head partial sums are finished through LDS.  q+ and q- stay
-// in registers as fp64 for the whole launch.
+// group; the per-head partial sums are finished through LDS.  q stays in
+// registers as fp64 for the whole launch.
 #include "blocks.h"
 #include "kernels.h"
 
@@ -58,13 +62,27 @@ template <> struct Unpack<float, 2> {
   }
 };
 
+#ifndef EKV_SCORE_G4_BYTES
+#define EKV_SCORE_G4_BYTES 16
+#endif
+#ifndef EKV_SCORE_DEPTH
+#define EKV_SCORE_DEPTH 2
+#endif
+#ifndef EKV_SCORE_RESIDENT
+#define EKV_SCORE_RESIDENT 512
+#endif
+constexpr int kScoreDepth = EKV_SCORE_DEPTH;  // metadata batches per lane in flight
+#ifndef EKV_SCORE_MAX_U
+#define EKV_SCORE_MAX_U 4
+#endif
+constexpr int kScoreMaxU = EKV_SCORE_MAX_U;  // pages per lane per batch, at most
 constexpr int kScoreBlock = 256;
 constexpr int kScoreWaves = kScoreBlock / kWave;
 constexpr int kMaxPagesPerBlock = 512;  // block-table slice staged in LDS
 constexpr int kStepTopkKeys = 4096;
 // workgroups resident at once (256 CUs x 2 at this kernel's register use):
 // one round of blocks avoids a second ramp-up
-constexpr int kScoreResidentBlocks = 512;
+constexpr int kScoreResidentBlocks = EKV_SCORE_RESIDENT;
 
 // Work split of score_range.  kLpr lanes share one page (kVec coordinates
 // each); a lane scores kU pages per batch and keeps kKinds partial sums per
@@ -78,7 +96,7 @@ struct ScoreGeo {
   static constexpr int kKinds = kGauss ? 3 : 1;
   static constexpr int kLanesUsed = kLpr < 16 ? kLpr : 16;
   static constexpr int kUfit = kLanesUsed / (G * kKinds);
-  static constexpr int kU = kUfit < 1 ? 1 : (kUfit > 4 ? 4 : kUfit);
+  static constexpr int kU = kUfit < 1 ? 1 : (kUfit > kScoreMaxU ? kScoreMaxU : kUfit);
   static constexpr int kM = kU * kKinds * G;
   static constexpr int kPitch = kM + 1;
 };
@@ -95,8 +113,24 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// This lane's query coordinates for score_range, as fp64: heads of the
+// group, coordinates c * kVec .. of its page slot (loaded by the caller, so
+// that they share the round trip of the block-table slice).
+template <int D, int G, int kVec>
+__device__ __forceinline__ void load_q_lane(const float* __restrict__ q, int b, int g, int Hkv,
+                                            double (&qd)[G][kVec]) {
+  const int c = (threadIdx.x % kWave) % (D / kVec);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float* qh = q + ((size_t)b * Hkv * G + g * G + h) * D + c * kVec;
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) qd[h][v] = (double)qh[v];
+  }
+}
+
 // Scores of pages [p_begin, p_end) of one (row b, KV head g) for the G query
-// heads of the group; s_pi holds the block-table slice block_table[b][p_begin..),
+// heads of the group (qd: this lane's coordinates of the group's queries,
+// from load_q_lane); s_pi holds the block-table slice block_table[b][p_begin..),
 // red is this wave's reduction scratch (kWave rows of kPitch doubles).
 //
 // Each lane forms, for each of its kU pages and each head, the fp64 partial
@@ -110,7 +144,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <typename T, int D, int G, int kVec, bool kGauss, bool kCoherentU = false,
           typename M = float>
 __device__ __forceinline__ void score_range(
-    const float* __restrict__ q, float scale, const T* __restrict__ kmin,
+    const double (&qd)[G][kVec], float scale, const T* __restrict__ kmin,
     const T* __restrict__ kmax, const M* __restrict__ mean, const M* __restrict__ var,
     const int* s_pi, int b, int g, int pair, int Hkv, int maxP, int p_begin, int p_end,
     float* __restrict__ ub, float* __restrict__ ubg, double* __restrict__ gm,
@@ -133,17 +167,6 @@ __device__ __forceinline__ void score_range(
   const int slot = threadIdx.x / kLpr;  // page slot inside a step
   const int r0 = lane - c;              // first LDS row of this lane's slot
 
-  double qp[G][kVec], qn[G][kVec];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = q + ((size_t)b * Hq + g * G + h) * D + c * kVec;
-#pragma unroll
-    for (int v = 0; v < kVec; ++v) {
-      const float x = qh[v];
-      qp[h][v] = x > 0.0f ? (double)x : 0.0;
-      qn[h][v] = x < 0.0f ? (double)x : 0.0;
-    }
-  }
   const double dscale = (double)scale;
 
   // one batch = kU pages per lane; the next batch's loads are issued before
@@ -199,13 +222,21 @@ __device__ __forceinline__ void score_range(
       float lo[kVec], hi[kVec];
       Unpack<T, kVec>::run(bt_.lo[u], lo);
       Unpack<T, kVec>::run(bt_.hi[u], hi);
+      // max(x kmin, x kmax) = (x (kmax + kmin) + |x| (kmax - kmin)) / 2, the
+      // halving applied to the finished sum (exact)
+      double sm2[kVec], df2[kVec];
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        sm2[v] = (double)hi[v] + (double)lo[v];
+        df2[v] = (double)hi[v] - (double)lo[v];
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         double a = 0.0;
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
-          a = fma(qp[h][v], (double)hi[v], a);
-          a = fma(qn[h][v], (double)lo[v], a);
+          a = fma(qd[h][v], sm2[v], a);
+          a = fma(fabs(qd[h][v]), df2[v], a);
         }
         row[u * kKinds * G + h] = a;
       }
@@ -215,9 +246,8 @@ __device__ __forceinline__ void score_range(
           double am = 0.0, av = 0.0;
 #pragma unroll
           for (int v = 0; v < kVec; ++v) {
-            const double qd = qp[h][v] + qn[h][v];
-            am = fma(qd, (double)bt_.mu[u][v], am);
-            av = fma(qd * qd, (double)bt_.s2[u][v], av);
+            am = fma(qd[h][v], (double)bt_.mu[u][v], am);
+            av = fma(qd[h][v] * qd[h][v], (double)bt_.s2[u][v], av);
           }
           row[(u * kKinds + 1) * G + h] = am;
           row[(u * kKinds + 2) * G + h] = av;
@@ -245,7 +275,7 @@ __device__ __forceinline__ void score_range(
       const double t = part[0];
       const bool live = have && p < p_end;
       const size_t o = ((size_t)b * Hq + g * G + h) * maxP + p;
-      const float uh = (float)(dscale * t);
+      const float uh = (float)(dscale * (kind == 0 ? 0.5 * t : t));
       // per-head bounds page-major ([pair][page][G]): the G heads of a page sit
       // in adjacent lanes and adjacent words, so the stores coalesce and a
       // reader of one page gets all its heads from one 4G-byte chunk
@@ -271,20 +301,25 @@ __device__ __forceinline__ void score_range(
     }
     wave_lds_sync();
   };
+  // kDepth batches in a ring: while one is reduced, the next kDepth - 1 are
+  // in flight; a reduced batch's registers take the batch kDepth steps on
   constexpr int kStride = kPagesPerStep * kU;
-  Batch A, Bb;
-  int base = p_begin;
-  issue(base, A);
-  while (true) {
-    const int nb = base + kStride;
-    if (nb < p_end) issue(nb, Bb);
-    consume(base, A);
-    if (nb >= p_end) break;
-    const int nb2 = nb + kStride;
-    if (nb2 < p_end) issue(nb2, A);
-    consume(nb, Bb);
-    if (nb2 >= p_end) break;
-    base = nb2;
+  constexpr int kDepth = kScoreDepth;
+  Batch ring[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (p_begin + d * kStride < p_end) issue(p_begin + d * kStride, ring[d]);
+  bool done = false;
+  for (int base = p_begin; !done; base += kDepth * kStride) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int cur = base + d * kStride;
+      if (!done && cur >= p_end) done = true;
+      if (!done) {
+        consume(cur, ring[d]);
+        if (cur + kDepth * kStride < p_end) issue(cur + kDepth * kStride, ring[d]);
+      }
+    }
   }
 }
 
@@ -367,6 +402,8 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
   // (entries past the row's pages are in bounds and never used)
   for (int i = threadIdx.x; i < pages_per_block && p_begin + i < maxP; i += kScoreBlock)
     s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
+  double qd[G][kVec];
+  load_q_lane<D, G, kVec>(q, b, g, Hkv, qd);
   const int L = lens[b];
   const int np = (L + P - 1) / P;
   if (p_begin >= np) return;
@@ -379,7 +416,7 @@ __global__ __launch_bounds__(kScoreBlock) void score_kernel(
   __syncthreads();
   float lbest = -__builtin_huge_valf();
   int lbestp = 0x7fffffff;
-  score_range<T, D, G, kVec, kGauss, false, M>(q, scale, kmin, kmax, mean, var, s_pi, b, g, pair,
+  score_range<T, D, G, kVec, kGauss, false, M>(qd, scale, kmin, kmax, mean, var, s_pi, b, g, pair,
                                                Hkv, maxP, p_begin, p_end, ub, ubg, gm, gv,
                                                red.v[threadIdx.x / kWave], lbest, lbestp);
   if (hint != nullptr)
@@ -419,6 +456,8 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   // (entries past the row's pages are in bounds and never used)
   for (int i = threadIdx.x; i < pages_per_block && p_begin + i < maxP; i += kScoreBlock)
     s_pi[i] = bt[(size_t)b * maxP + p_begin + i];
+  double qd[G][kVec];
+  load_q_lane<D, G, kVec>(q, b, g, Hkv, qd);
   const int L = lens[b];
   const int np = (L + P - 1) / P;
   if (p_begin >= np) {
@@ -437,7 +476,7 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   __syncthreads();
   float lbest = -__builtin_huge_valf();
   int lbestp = 0x7fffffff;
-  score_range<T, D, G, kVec, false, true, float>(q, scale, kmin, kmax, nullptr, nullptr, s_pi, b,
+  score_range<T, D, G, kVec, false, true, float>(qd, scale, kmin, kmax, nullptr, nullptr, s_pi, b,
                                                  g, pair, Hkv, maxP, p_begin, p_end, ub, ubg,
                                                  nullptr, nullptr, sm.red.v[threadIdx.x / kWave],
                                                  lbest, lbestp);
@@ -529,13 +568,14 @@ hipError_t launch_score_d(const Shape& s, const float* q, float scale, const voi
   // SIMD); with 8-byte loads 234 VGPRs (two)
   constexpr int kV16 = 16 / sizeof(T);
   constexpr int kV8 = 8 / sizeof(T);
+  constexpr int kScoreV4 = EKV_SCORE_G4_BYTES / sizeof(T);
   switch (s.G) {
     case 1: return launch_score_t<T, D, 1, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
     case 2: return launch_score_t<T, D, 2, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
     case 4:
       if (gm != nullptr)
         return launch_score_t<T, D, 4, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
-      return launch_score_t<T, D, 4, kV16>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
+      return launch_score_t<T, D, 4, kScoreV4>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
     case 8: return launch_score_t<T, D, 8, kV8>(s, q, scale, kmin, kmax, mean, var, bt, lens, ub, ubg, gm, gv, K, refresh, hint, stream);
   }
   return hipErrorInvalidValue;
@@ -598,12 +638,13 @@ hipError_t launch_score(const Shape& s, const float* q, float scale, const void*
 
 ScoreSlices score_box_slices(const Shape& s) {
   // the geometry launch_score_t uses for the box-only kernel
-  const int kv = s.bf16 ? (s.G == 8 ? 4 : 8) : (s.G == 8 ? 2 : 4);
+  const int eb = s.bf16 ? 2 : 4;
+  const int kv = (s.G == 8 ? 8 : (s.G == 4 ? EKV_SCORE_G4_BYTES : 16)) / eb;
   const int lpr = s.D / kv;
   const int per_step = (kWave / lpr) * kScoreWaves;
   const int kinds_lanes = lpr < 16 ? lpr : 16;
   int ku = kinds_lanes / s.G;
-  ku = ku < 1 ? 1 : (ku > 4 ? 4 : ku);
+  ku = ku < 1 ? 1 : (ku > kScoreMaxU ? kScoreMaxU : ku);
   ScoreSlices r;
   r.pages = slice_pages(s, per_step * ku);
   r.count = (s.maxP + r.pages - 1) / r.pages;

@@ -92,7 +92,9 @@ __global__ __launch_bounds__(kSmBlock) void softmax_split_kernel(SmArgs<T> a) {
     const int32_t* btp = a.bt + (size_t)b * a.maxP;
     for (int k = threadIdx.x; k < np; k += kSmBlock) {
       const int lp = selp ? selp[p0 + k] : p0 + k;
-      sm_page[k] = make_int2(btp[lp], page_valid(L, lp, a.P));
+      // a caller's entry outside [0, n_b) is a page with no valid token
+      const bool in_row = (unsigned)lp < (unsigned)((L + a.P - 1) / a.P);
+      sm_page[k] = make_int2(btp[in_row ? lp : 0], in_row ? page_valid(L, lp, a.P) : 0);
     }
   }
   __syncthreads();

@@ -81,6 +81,52 @@ def test_dense_all_pages(alpha):
         check_pair(inp, gpu, b, g, "dense")
 
 
+def test_caller_page_list_out_of_range_entries():
+    # entries outside [0, n_b) in a caller's list read nothing: the decode (with
+    # and without page pruning) and the softmax path give the clean list's
+    # results (the oracle checks the clean list)
+    w = small(97, lens_range=(300, 1500))
+    inp = wl.make_inputs(w, device=DEV)
+    rng = np.random.default_rng(9)
+    mp = inp["max_pages"]
+    clean = np.full((w.batch, w.num_kv_heads, mp), -1, np.int32)
+    dirty = np.full((w.batch, w.num_kv_heads, mp), -1, np.int32)
+    nc = np.zeros((w.batch, w.num_kv_heads), np.int32)
+    nd = np.zeros((w.batch, w.num_kv_heads), np.int32)
+    lists = {}
+    for b, g in all_pairs(w):
+        n = inp["npages"][b]
+        pick = sorted(rng.choice(n, size=int(rng.integers(1, n - 3)), replace=False).tolist())
+        bad = [-5, n + 3, 1 << 30]
+        mixed = list(pick)
+        for x in bad:
+            mixed.insert(int(rng.integers(0, len(mixed) + 1)), x)
+        clean[b, g, :len(pick)] = pick
+        dirty[b, g, :len(mixed)] = mixed
+        nc[b, g], nd[b, g] = len(pick), len(mixed)
+        lists[(b, g)] = pick
+    t = lambda a: torch.tensor(a, device=DEV)
+    for prune in (True, False):
+        gc_ = run_gpu(inp, "topk", sel=t(clean), n_sel=t(nc), prune=prune)
+        gd = run_gpu(inp, "topk", sel=t(dirty), n_sel=t(nd), prune=prune)
+        for b, g in all_pairs(w):
+            check_pair(inp, gc_, b, g, "topk", sel_override=lists[(b, g)])
+        torch.testing.assert_close(gd["out"], gc_["out"], rtol=1e-6, atol=1e-7)
+        torch.testing.assert_close(gd["tau"], gc_["tau"], rtol=1e-6, atol=1e-6)
+        assert torch.equal(gd["n_support"], gc_["n_support"])
+    s = cache_shape(inp)
+    outs = []
+    for sel_, n_ in ((clean, nc), (dirty, nd)):
+        out = torch.empty_like(inp["q"])
+        ws = torch.empty(max(B.softmax_workspace_bytes(s, mp), 256), dtype=torch.uint8,
+                         device=DEV)
+        B.softmax_decode(s, inp["q"], w.scale, inp["K"], inp["V"], inp["block_table"],
+                         inp["seq_lens"], out, ws, sel=t(sel_), n_sel=t(n_), max_sel=mp)
+        outs.append(out)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(outs[1], outs[0], rtol=1e-6, atol=1e-7)
+
+
 def test_caller_page_list():
     # decode over an explicit random page list (no selection stage)
     w = small(61, lens_range=(300, 2500))
