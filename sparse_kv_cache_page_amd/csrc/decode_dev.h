@@ -850,8 +850,36 @@ __device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
 #pragma unroll
   for (int u = 0; u < kSpecSel; ++u)
     if (threadIdx.x + u * kBlock < nsel) consider(spec[u]);
-  for (int j = threadIdx.x + kSpecSel * kBlock; j < nsel; j += kBlock)
-    consider(a.sel ? a.sel[(size_t)pair * a.maxP + j] : j);
+  // longer selections: kBatch slots per thread per round, their page indices
+  // first, then all their bounds and block-table entries, so a round costs
+  // two dependent loads rather than two per slot
+  constexpr int kBatch = 16;
+  for (int j0 = kSpecSel * kBlock; j0 < nsel; j0 += kBatch * kBlock) {
+    int pg[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + threadIdx.x + u * kBlock;
+      pg[u] = -1;
+      if (j < nsel) pg[u] = a.sel ? a.sel[(size_t)pair * a.maxP + j] : j;
+    }
+    float uu[kBatch];
+    int ph[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool ok = (unsigned)pg[u] < (unsigned)np;
+      uu[u] = ok ? U[(size_t)pg[u] * G] : -__builtin_huge_valf();
+      ph[u] = ok ? a.bt[(size_t)b * a.maxP + pg[u]] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if ((unsigned)pg[u] < (unsigned)np &&
+          (uu[u] > best || (uu[u] == best && pg[u] < bestp))) {
+        best = uu[u];
+        bestp = pg[u];
+        bestphys = ph[u];
+      }
+    }
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ob = __shfl_xor(best, o, kWave);

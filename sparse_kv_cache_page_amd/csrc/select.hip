@@ -61,6 +61,164 @@ __global__ __launch_bounds__(kSelBlock) void topk_kernel(
   if (threadIdx.x == 0) n_sel[pair] = k;
 }
 
+// Top-k of long rows (4096 < n <= 65536 pages): one 1024-thread workgroup per
+// (row, KV head) with kPer consecutive keys per thread in registers (no key
+// re-reads from memory): range-adaptive 11-bit radix passes over a
+// double-buffered LDS histogram, thread t owning digits 2047-2t and 2046-2t
+// of the scan, then the same ordered placement as the 256-thread selection
+// (every key above the threshold, and the lowest pages among those equal to
+// it).  Past 32 keys per thread the rest sit in LDS ([key][thread], 128 KiB
+// at 64 keys per thread), where registers would spill.
+constexpr int kLongBlock = 1024;
+constexpr int kLongWaves = kLongBlock / kWave;
+constexpr int kLongRegKeys = 32;
+
+template <int kLdsKeys>
+struct TopkLongLds {
+  uint32_t lk[kLdsKeys > 0 ? kLdsKeys * kLongBlock : 1];
+  int hist[2][2048];
+  int wsum[kLongWaves];
+  int wsum2[kLongWaves];
+  uint32_t mn[kLongWaves], mx[kLongWaves];
+  int s_digit, s_above, s_cnt;
+};
+
+template <int kPer>
+__global__ __launch_bounds__(kLongBlock) void topk_long_kernel(
+    const float* __restrict__ ubg, const int32_t* __restrict__ lens, int P, int maxP, int Hkv,
+    int top_k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel) {
+  constexpr int kReg = kPer < kLongRegKeys ? kPer : kLongRegKeys;
+  __shared__ TopkLongLds<kPer - kReg> sm;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int pair = blockIdx.x;
+  const int b = pair / Hkv;
+  const int n = (lens[b] + P - 1) / P;
+  const int k = min(top_k, n);
+  int32_t* out = sel + (size_t)pair * maxP;
+  if (tid == 0) n_sel[pair] = k;
+  if (k >= n) {
+    for (int p = tid; p < n; p += kLongBlock) out[p] = p;
+    return;
+  }
+  const float* U = ubg + (size_t)pair * maxP;
+  const int p0 = tid * kPer;
+  const int nv = max(0, min(kPer, n - p0));
+  uint32_t key[kReg];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t kk = order_key(i < nv ? U[p0 + i] : 0.0f);
+    if (i < kReg) key[i < kReg ? i : 0] = kk;
+    else sm.lk[(i - kReg) * kLongBlock + tid] = kk;
+  }
+  // key i of this thread (registers, or LDS past kReg; i is a constant in
+  // every unrolled use)
+  auto key_at = [&](int i) -> uint32_t {
+    return i < kReg ? key[i < kReg ? i : 0] : sm.lk[(i - kReg) * kLongBlock + tid];
+  };
+  for (int i = tid; i < 2 * 2048; i += kLongBlock) (&sm.hist[0][0])[i] = 0;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (i < nv) {
+      kmn = min(kmn, key_at(i));
+      kmx = max(kmx, key_at(i));
+    }
+  kmn = wave_min_u32(kmn);
+  kmx = wave_max_u32(kmx);
+  if (lane == 0) {
+    sm.mn[wave] = kmn;
+    sm.mx[wave] = kmx;
+  }
+  __syncthreads();
+  uint32_t lo = sm.mn[0], hi = sm.mx[0];
+#pragma unroll
+  for (int w = 1; w < kLongWaves; ++w) {
+    lo = min(lo, sm.mn[w]);
+    hi = max(hi, sm.mx[w]);
+  }
+  int remaining = k;
+  bool cut = false;
+  for (int pass = 0; pass < 4; ++pass) {
+    int* hist = sm.hist[pass & 1];
+    int* next = sm.hist[(pass + 1) & 1];
+    const uint32_t span = hi - lo;
+    const int width = span == 0u ? 0 : 32 - __clz((int)span);
+    const int shift = width > 11 ? width - 11 : 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t kk = key_at(i);
+      if (i < nv && kk >= lo && kk <= hi) atomicAdd(&hist[(kk - lo) >> shift], 1);
+    }
+    __syncthreads();  // histogram complete
+    const int2 h2 = *reinterpret_cast<const int2*>(hist + 2046 - 2 * tid);  // .y higher digit
+    *reinterpret_cast<int2*>(next + 2046 - 2 * tid) = make_int2(0, 0);
+    const int local = h2.x + h2.y;
+    int incl = wave_incl_scan_i32(local);
+    if (lane == kWave - 1) sm.wsum[wave] = incl;
+    __syncthreads();  // wave totals
+    for (int w = 0; w < wave; ++w) incl += sm.wsum[w];
+    const int excl = incl - local;
+    if (excl < remaining && remaining <= incl) {
+      if (excl + h2.y >= remaining) {
+        sm.s_digit = 2047 - 2 * tid;
+        sm.s_above = excl;
+        sm.s_cnt = h2.y;
+      } else {
+        sm.s_digit = 2046 - 2 * tid;
+        sm.s_above = excl + h2.y;
+        sm.s_cnt = h2.x;
+      }
+    }
+    __syncthreads();  // chosen bin
+    const int digit = sm.s_digit, above = sm.s_above, cnt = sm.s_cnt;
+    const uint32_t nlo = lo + ((uint32_t)digit << shift);
+    const uint32_t top = shift == 0 ? nlo : nlo + ((1u << shift) - 1u);
+    hi = top < hi ? top : hi;
+    lo = nlo;
+    remaining -= above;
+    cut = (cnt == remaining);
+    if (cut || shift == 0) break;
+  }
+  // ordered placement: every key > T (>= T when the bin was cut whole), and
+  // the first `remaining` keys equal to T in page order
+  const uint32_t T = lo;
+  int cg = 0, ce = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool v = i < nv;
+    const uint32_t kk = key_at(i);
+    cg += (v && (cut ? kk >= T : kk > T)) ? 1 : 0;
+    ce += (v && !cut && kk == T) ? 1 : 0;
+  }
+  int gi = wave_incl_scan_i32(cg);
+  int ei = wave_incl_scan_i32(ce);
+  __syncthreads();  // every thread has read the last pass's wave totals
+  if (lane == kWave - 1) {
+    sm.wsum[wave] = gi;
+    sm.wsum2[wave] = ei;
+  }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    gi += sm.wsum[w];
+    ei += sm.wsum2[w];
+  }
+  int eq_seen = ei - ce;
+  int pos = (gi - cg) + min(eq_seen, remaining);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool v = i < nv;
+    const uint32_t kk = key_at(i);
+    const bool gt = v && (cut ? kk >= T : kk > T);
+    const bool eq = v && !cut && kk == T;
+    const bool take = gt || (eq && eq_seen < remaining);
+    if (take) out[pos] = p0 + i;
+    pos += take ? 1 : 0;
+    eq_seen += eq ? 1 : 0;
+  }
+}
+
 // --------------------------------------------------------------------------
 // Gaussian-aware selection
 // --------------------------------------------------------------------------
@@ -856,6 +1014,19 @@ double expected_max_std_normal(int n) {
 
 hipError_t launch_topk(const Shape& s, const int32_t* lens, int top_k, const float* ubg,
                        int32_t* sel, int32_t* n_sel, hipStream_t stream) {
+  const dim3 g((unsigned)(s.B * s.Hkv));
+  if (s.maxP > kBlk * 16 && s.maxP <= kLongBlock * 64) {
+    if (s.maxP <= kLongBlock * 16)
+      hipLaunchKernelGGL((topk_long_kernel<16>), g, dim3(kLongBlock), 0, stream, ubg, lens, s.P,
+                         s.maxP, s.Hkv, top_k, sel, n_sel);
+    else if (s.maxP <= kLongBlock * 32)
+      hipLaunchKernelGGL((topk_long_kernel<32>), g, dim3(kLongBlock), 0, stream, ubg, lens, s.P,
+                         s.maxP, s.Hkv, top_k, sel, n_sel);
+    else
+      hipLaunchKernelGGL((topk_long_kernel<64>), g, dim3(kLongBlock), 0, stream, ubg, lens, s.P,
+                         s.maxP, s.Hkv, top_k, sel, n_sel);
+    return hipGetLastError();
+  }
   if (s.maxP <= kTopkLdsKeys)
     hipLaunchKernelGGL((topk_kernel<true>), dim3(s.B * s.Hkv), dim3(kSelBlock), 0, stream, ubg,
                        lens, s.P, s.maxP, s.Hkv, top_k, sel, n_sel);
