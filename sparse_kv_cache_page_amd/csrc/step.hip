@@ -4,22 +4,25 @@
 //
 // One launch does what ekv_select_pages(TOPK) and the first stage of
 // ekv_entmax_decode do, without a round trip through a selection list in
-// memory and without a serial per-pair tail:
+// memory and without a serial per-pair tail.  Per (row, KV head) pair it
+// holds a few key items, each owning a run of consecutive splits (the launch
+// aims at about 256 key items, one per compute unit), and one selection item
+// that writes the top-k list out as sel / n_sel.
 //
-//   every work item (row, KV head, a run of consecutive splits) reads the
-//   pair's group bounds U, runs the top-k radix select itself (the items of a
-//   pair reach the same selection; item 0 also writes it out as sel / n_sel;
-//   the launch holds about 256 items, one per compute unit, so the repeated
-//   selection stays cheap next to the key reads), and, with the
-//   per-head bounds, probes each query head's best selected page for a lower
-//   bound zlb of its largest score.  A selected page whose bound is below
-//   zlb - 1 for every head of the group holds no support token (tau >=
-//   z_max - 1), so its keys are not read.  The pages that remain are shared
-//   out evenly over the pair's items in ascending order (every item computes
-//   the same list), so the key stream is balanced over the workgroups; each
-//   item scores its pages for the G heads from one read (matrix cores for
-//   bf16), in chunks of one split's token slots, and writes each chunk's
-//   candidates z > chunk_max - 1 as one split.
+// With the scorer's hints (the step's path) a key item reads the pair's group
+// bounds U and takes each query head's best page over the row as its probe;
+// the probe counts if the page is selected, i.e. fewer than k pages rank
+// ahead of it (a count, no selection needed), and then zlb, the largest z of
+// its tokens, bounds that head's z_max from below.  A page is read only if U
+// clears some head's zlb - 1 (tau >= z_max - 1; U >= every head's bound).
+// That test is monotone in U, so when at most k pages clear it they are all
+// selected and the top-k itself is skipped; otherwise every key item runs it
+// (range-adaptive radix select on keys in registers).  Without hints the key
+// item runs the top-k first and probes each head's best selected page.  The
+// pages to read are shared out over the pair's key items in ascending order
+// (every item computes the same list); each item scores its pages for the G
+// heads from one read (matrix cores for bf16), in chunks of one split's token
+// slots, and writes each chunk's candidates z > chunk_max - 1 as one split.
 //
 // The tau / PV stage then runs as in ekv_entmax_decode.  Because the final
 // candidate set of a head is {z > z_max - 1} over the tokens read, in
@@ -38,6 +41,12 @@ constexpr int kProbeBatch = 4;                // probe key rows per thread in fl
 #define EKV_STEP_ITEMS 256
 #endif
 constexpr long long kStepItems = EKV_STEP_ITEMS;  // workgroups to aim for per launch
+#ifndef EKV_STEP_MAX_SPI
+#define EKV_STEP_MAX_SPI 1024
+#endif
+#ifndef EKV_TOPK_FAST
+#define EKV_TOPK_FAST 1
+#endif
 
 template <typename T>
 struct SelQkArgs {
@@ -52,7 +61,8 @@ struct SelQkArgs {
   int32_t* sel;      // [pairs][maxP] written by split 0
   int32_t* n_sel;    // [pairs] written by split 0
   int top_k, Hkv, P, log2P, maxP, splits, npairs;
-  int spi;           // splits per work item
+  int spi;           // splits per key item
+  int nit;           // key items per pair; item nit of a pair writes sel / n_sel
   float2* cand;
   int* cnt;
   float* smax;
@@ -82,6 +92,8 @@ struct SelQkLds {
   int probe_nv[G];
   int probe_page[G];
   int probe_sel[G];
+  uint32_t probe_key[G];
+  int rank_part[kBlock / kWave][G];
   int sh4[4];
   int s_m;
   float qraw[G * D];  // the group's queries (the probe of the hinted kernel)
@@ -127,6 +139,23 @@ __device__ __forceinline__ void read_share(const SelQkArgs<T>& a, QkLds<T, D, G>
                                    s);
 }
 
+// The selection item of a pair (the last item index of the launch): the
+// top-k pages of the row, ascending, into sel / n_sel (the key items do not
+// need the list written out).
+template <typename T, int kPer>
+__device__ __forceinline__ void selection_item(const SelQkArgs<T>& a, int pair, TopkRegLds& tk) {
+  const int b = pair / a.Hkv;
+  const int np = (a.lens[b] + a.P - 1) >> a.log2P;
+  const int k = min(a.top_k, np);
+  int32_t* out = a.sel + (size_t)pair * a.maxP;
+  if (threadIdx.x == 0) a.n_sel[pair] = k;
+  if (k >= np) {
+    for (int p = threadIdx.x; p < np; p += kBlock) out[p] = p;
+    return;
+  }
+  topk_block_reg<kPer, false>(a.ubg + (size_t)pair * a.maxP, np, k, out, tk);
+}
+
 // One work item per workgroup: item = it * pairs + pair, item it of a pair
 // holding its splits [it * spi, (it + 1) * spi) (item-major: with a multiple
 // of 8 pairs, all items of a pair run on one XCD and share its L2 lines of
@@ -144,6 +173,10 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   const int wave = tid / kWave;
   const int pair = (int)(blockIdx.x % (unsigned)a.npairs);
   const int it = (int)(blockIdx.x / (unsigned)a.npairs);
+  if (it == a.nit) {  // uniform: the pair's selection list
+    selection_item<T, kPer>(a, pair, sm.u.tk);
+    return;
+  }
   const int b = pair / a.Hkv;
   const int g = pair % a.Hkv;
   const int Hq = a.Hkv * G;
@@ -174,10 +207,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   const int nsplit = ((nsel << log2P) + kR - 1) / kR;
   const int s0 = it * a.spi;
   const int s1 = min(s0 + a.spi, nsplit);
-  if (s0 >= nsplit) {  // uniform: nothing to read for this item
-    if (it == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
-    return;
-  }
+  if (s0 >= nsplit) return;  // uniform: nothing to read for this item
 
   // ---- top-k: the nsel largest U, lowest page on ties, placed ascending
   // (thread t's pages precede thread t+1's, so one block scan orders them)
@@ -212,10 +242,6 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
     }
   }
   __syncthreads();
-  if (it == 0) {
-    for (int j = tid; j < nsel; j += kBlock) a.sel[(size_t)pair * maxP + j] = sm.s_sel[j];
-    if (tid == 0) a.n_sel[pair] = nsel;
-  }
 
   // ---- the pages to read: all selected pages, or those that can hold a
   // support token of some head of the group
@@ -397,16 +423,16 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   });
 }
 
-// The same work item with the scorer's hints (the step's path): each head's
+// The same key item with the scorer's hints (the step's path): each head's
 // probe page is the best page of its whole row (the best of the slice bests,
 // lowest page on ties), known after the first round trip, so the probe rows
-// are requested before the selection runs and arrive during it (the
-// selection uses LDS-only barriers).  The probe counts only if that page is
-// selected (else the head has no bound and nothing is skipped), and the
-// pages left to read are those whose group bound U clears some head's
-// zlb - 1: U >= every head's bound, so this skips a subset of what the
-// per-head test would and every skipped page is still below every head's
-// support.  The probe rows of a group must fit one batch
+// are requested right away.  The probe counts only if that page is selected
+// (fewer than nsel pages rank ahead of it; else the head has no bound and
+// nothing is skipped), and the pages left to read are those whose group
+// bound U clears some head's zlb - 1: U >= every head's bound, so this skips
+// a subset of what the per-head test would and every skipped page is still
+// below every head's support.  The top-k runs only when more than nsel pages
+// clear.  The probe rows of a group must fit one batch
 // (G * P <= kProbeBatch * kBlock / kLpr).
 template <typename T, int D, int G, int kPer>
 __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
@@ -422,6 +448,10 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   const int wave = tid / kWave;
   const int pair = (int)(blockIdx.x % (unsigned)a.npairs);
   const int it = (int)(blockIdx.x / (unsigned)a.npairs);
+  if (it == a.nit) {  // uniform: the pair's selection list
+    selection_item<T, kPer>(a, pair, sm.u.tk);
+    return;
+  }
   const int b = pair / a.Hkv;
   const int g = pair % a.Hkv;
   const int Hq = a.Hkv * G;
@@ -462,10 +492,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   const int nsplit = ((nsel << log2P) + kR - 1) / kR;
   const int s0 = it * a.spi;
   const int s1 = min(s0 + a.spi, nsplit);
-  if (s0 >= nsplit) {  // uniform: nothing to read for this item
-    if (it == 0 && tid == 0) a.n_sel[pair] = 0;  // an empty row
-    return;
-  }
+  if (s0 >= nsplit) return;  // uniform: nothing to read for this item
 #pragma unroll
   for (int u = 0; u < kQPer; ++u) {
     const int idx = tid + u * kBlock;
@@ -501,14 +528,20 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
     }
   }
   lds_barrier();
-  // the probe pages' physical pages from their owners' block-table entries
+  // the probe pages' physical pages and bounds from their owners' entries
+  uint32_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) key[i] = order_key(uv[i]);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const int pg = sm.probe_page[h];
     if (pg >= p0 && pg < p0 + kPer) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        if (p0 + i == pg) sm.probe_phys[h] = btr[i];
+        if (p0 + i == pg) {
+          sm.probe_phys[h] = btr[i];
+          sm.probe_key[h] = key[i];
+        }
     }
   }
   lds_barrier();
@@ -529,52 +562,34 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
                            (size_t)t * D + c * kVec);
   }
 
-  // ---- top-k: the nsel largest U, lowest page on ties, placed ascending
+  // ---- whether each head's probe page is selected: fewer than nsel pages
+  // rank ahead of it (larger U, or equal U and a lower page)
   const int nv = max(0, min(kPer, np - p0));
-  bool take[kPer];
   {
-    uint32_t key[kPer];
+    int ahead[G];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) key[i] = order_key(uv[i]);
-    TopkThr th{0u, 0, true};  // nsel >= np: every page
-    if (nsel < np) th = topk_threshold<kPer>(key, nv, nsel, sm.u.tk);
-    bool eq[kPer];
-    int cg = 0, ce = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const bool v = i < nv;
-      take[i] = v && (th.cut ? key[i] >= th.T : key[i] > th.T);
-      eq[i] = v && !th.cut && key[i] == th.T;
-      cg += take[i] ? 1 : 0;
-      ce += eq[i] ? 1 : 0;
-    }
-    const int both = cg | (ce << 16);
-    const int excl = block_incl_scan_lds(both, sm.sh4) - both;
-    int eq_seen = excl >> 16;
-    int pos = (excl & 0xFFFF) + min(eq_seen, th.rem);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      take[i] = take[i] || (eq[i] && eq_seen < th.rem);
-      eq_seen += eq[i] ? 1 : 0;
-      if (take[i]) sm.s_sel[pos] = p0 + i;
-      pos += take[i] ? 1 : 0;
-    }
-  }
-  // whether each head's probe page is selected
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int pg = sm.probe_page[h];
-    if (pg >= p0 && pg < p0 + kPer) {
+    for (int h = 0; h < G; ++h) {
+      const int pg = sm.probe_page[h];
+      const uint32_t pk = sm.probe_key[h];
+      int c_ = 0;
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        if (p0 + i == pg) sm.probe_sel[h] = take[i] ? 1 : 0;
+        c_ += (i < nv && (key[i] > pk || (key[i] == pk && p0 + i < pg))) ? 1 : 0;
+      ahead[h] = wave_sum_i32(c_);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) sm.rank_part[wave][h] = ahead[h];
     }
   }
   lds_barrier();
-  if (it == 0) {
-    for (int j = tid; j < nsel; j += kBlock) a.sel[(size_t)pair * maxP + j] = sm.s_sel[j];
-    if (tid == 0) a.n_sel[pair] = nsel;
+  if (tid < G) {
+    int r = 0;
+#pragma unroll
+    for (int w_ = 0; w_ < kBlock / kWave; ++w_) r += sm.rank_part[w_][tid];
+    sm.probe_sel[tid] = sm.probe_page[tid] >= 0 && (nsel >= np || r < nsel);
   }
+  // (the barrier below, after the probe rows are reduced, publishes probe_sel)
 
   // ---- zlb[h]: the largest fp32 z of the probe page's valid tokens (kLpr
   // lanes per key row), if that page is selected
@@ -605,7 +620,10 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   for (int h = 0; h < G; ++h) zl_h[h] = sm.zlb[h];
 
   // ---- the pages to read, ascending: selected, and U clears some head's
-  // zlb - 1 (with the rounding slacks of page_below_support)
+  // zlb - 1 (with the rounding slacks of page_below_support).  The test is
+  // monotone in U, so every page that ranks ahead of a clearing page clears
+  // too: when at most nsel pages clear, all of them are selected and the
+  // top-k itself is not needed; otherwise it decides.
   int cntf = 0;
   bool need[kPer];
 #pragma unroll
@@ -613,10 +631,36 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
     bool nd = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) nd |= !page_below_support(a.a1 * uv[i], zl_h[h]);
-    need[i] = take[i] && nd;
+    need[i] = i < nv && nd;
     cntf += need[i] ? 1 : 0;
   }
-  const int incl = block_incl_scan_lds(cntf, sm.sh4);
+  int incl = block_incl_scan_lds(cntf, sm.sh4);
+  if (tid == kBlock - 1) sm.s_m = incl;
+  lds_barrier();
+  if (sm.s_m > nsel) {  // uniform: the top-k decides which clearing pages are read
+    TopkThr th = topk_threshold<kPer>(key, nv, nsel, sm.u.tk);
+    bool eq[kPer], take[kPer];
+    int cg = 0, ce = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool v = i < nv;
+      take[i] = v && (th.cut ? key[i] >= th.T : key[i] > th.T);
+      eq[i] = v && !th.cut && key[i] == th.T;
+      cg += take[i] ? 1 : 0;
+      ce += eq[i] ? 1 : 0;
+    }
+    const int both = cg | (ce << 16);
+    int eq_seen = (block_incl_scan_lds(both, sm.sh4) - both) >> 16;
+    cntf = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool tk = take[i] || (eq[i] && eq_seen < th.rem);
+      eq_seen += eq[i] ? 1 : 0;
+      need[i] = need[i] && tk;
+      cntf += need[i] ? 1 : 0;
+    }
+    incl = block_incl_scan_lds(cntf, sm.sh4);
+  }
   int pos = incl - cntf;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -666,15 +710,17 @@ hipError_t launch_t(const Shape& s, const DecodePlan& pl, const float* q, float 
   // consecutive splits
   long long nit = (kStepItems + npairs - 1) / npairs;
   nit = nit < 1 ? 1 : (nit > pl.splits ? pl.splits : nit);
-  const int spi = (int)((pl.splits + nit - 1) / nit);
+  int spi = (int)((pl.splits + nit - 1) / nit);
+  spi = spi > EKV_STEP_MAX_SPI ? EKV_STEP_MAX_SPI : spi;
   nit = (pl.splits + spi - 1) / spi;
-  const long long items = npairs * nit;
+  // key items, then one selection item per pair
+  const long long items = npairs * (nit + 1);
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const SelQkArgs<T> a{q,      zscale,    a1,          (const T*)K, bt,      lens,
                        ub,     ubg,       sel,         n_sel,       top_k,   s.Hkv,
                        s.P,    s.log2P,   s.maxP,      pl.splits,   (int)npairs, spi,
-                       cand,   cnt,       smax,        hint.hint,   hint.slice_pages,
-                       hint.nslices};
+                       (int)nit, cand,    cnt,         smax,        hint.hint,
+                       hint.slice_pages, hint.nslices};
   if (ub != nullptr && hint_fits<T, D, G>(s, hint))
     hipLaunchKernelGGL((sel_qk_hint_kernel<T, D, G, kPer>), dim3((unsigned)items), dim3(kBlock),
                        0, stream, a);
@@ -729,7 +775,8 @@ hipError_t launch_d(const Shape& s, const DecodePlan& pl, const float* q, float 
 }  // namespace
 
 bool topk_decode_fast(const Shape& s, int max_sel) {
-  return max_sel <= kSelCap && s.maxP <= kBlock * 32 && decode_shape_supported(s, max_sel);
+  return EKV_TOPK_FAST && max_sel <= kSelCap && s.maxP <= kBlock * 32 &&
+         decode_shape_supported(s, max_sel);
 }
 
 hipError_t launch_topk_decode(const Shape& s, const DecodePlan& plan, const float* q, float scale,
