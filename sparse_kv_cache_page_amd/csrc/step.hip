@@ -139,6 +139,157 @@ __device__ __forceinline__ void read_share(const SelQkArgs<T>& a, QkLds<T, D, G>
                                    s);
 }
 
+// read_share for bf16 keys with the chunks software-pipelined: the K rows of
+// chunk c + 1 are requested before chunk c is scored on the matrix cores and
+// emitted, so an item that reads many chunks (pairs whose pages do not prune)
+// keeps loads in flight while it computes instead of one round trip per
+// chunk.  Rows, chunks, scores and candidates are those of read_share
+// (the page map is looked up in the caller's list instead of being staged),
+// so the results are bit-identical.
+template <typename T, int D, int G, typename PageAt>
+__device__ __forceinline__ void read_share_mfma(const SelQkArgs<T>& a, QkLds<T, D, G>& qk,
+                                                const float (&qv)[(G * D + kBlock - 1) / kBlock],
+                                                int g, int L, size_t bh0, int s0, int s1,
+                                                int nsplit, int m, PageAt page_at) {
+  constexpr int kR = Geo<T, D>::kR;
+  constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
+  constexpr int kKK = D / 32;                       // k steps of 32 dims
+  constexpr int kBlocksA = G > 4 ? 2 : 1;
+  constexpr int kGPW = kR / 16 / (kBlock / kWave);  // 16-token groups per wave
+  const int P = a.P, log2P = a.log2P;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int mrow = lane % 16;
+  const int kq = lane / 16;
+  const size_t tile_stride = (size_t)P * D;
+  const int lo = (int)(((long long)s0 * m) / nsplit);
+  const int hi = (int)(((long long)s1 * m) / nsplit);
+  const int per = kR >> log2P;
+  const int nch = (hi - lo + per - 1) / per;  // <= s1 - s0
+  auto& zl = qk.zl;
+  // q split into three bf16 parts once (as in qk_score_slots)
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int idx = threadIdx.x + u * kBlock;
+    if (idx >= G * D) break;
+    const int h = idx / D, dd = idx % D;
+    const float x = qv[u];
+    const float q_hi = bf16_round(x);
+    const float q_mid = bf16_round(x - q_hi);
+    const float q_lo = bf16_round(x - q_hi - q_mid);
+    qk.qparts[h][0][dd] = (uint16_t)(__float_as_uint(q_hi) >> 16);
+    qk.qparts[h][1][dd] = (uint16_t)(__float_as_uint(q_mid) >> 16);
+    qk.qparts[h][2][dd] = (uint16_t)(__float_as_uint(q_lo) >> 16);
+  }
+  __syncthreads();
+  bf16x8_t qa[kBlocksA][kKK];
+#pragma unroll
+  for (int ab = 0; ab < kBlocksA; ++ab) {
+    const int h = ab * 4 + mrow / 4;
+    const int part = mrow % 4;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (h < G && part < 3) w = *reinterpret_cast<const uint4*>(&qk.qparts[h][part][kk * 32 + kq * 8]);
+      qa[ab][kk] = as_bf16x8(w);
+    }
+  }
+  struct Chunk {
+    uint4 kb[kGPW][kKK];
+    bool valid[kGPW];
+  };
+  // the K rows of chunk c: row r of the chunk is token r & (P-1) of list
+  // entry base + (r >> log2P).  Every lane issues all its loads: a row past
+  // the chunk or past its page's valid tokens reads the chunk's first row
+  // instead (in bounds, a cache hit) and is masked by `valid`, so the load
+  // count is fixed and the next chunk's loads stay in flight while this one
+  // is scored
+  auto issue = [&](int c, Chunk& ch) {
+    const int base = lo + c * per;
+    const int n_pg = min(per, hi - base);
+    const int r_end = n_pg << log2P;
+    const T* safe = a.K + ((size_t)page_at(base).x * a.Hkv + g) * tile_stride + kq * 8;
+#pragma unroll
+    for (int u = 0; u < kGPW; ++u) {
+      const int r = (wave * kGPW + u) * 16 + mrow;
+      const int2 pp = page_at(base + min(r >> log2P, n_pg - 1));
+      const int t = r & (P - 1);
+      ch.valid[u] = r < r_end && t < page_valid(L, pp.y, P);
+      const T* row = ch.valid[u] ? a.K + ((size_t)pp.x * a.Hkv + g) * tile_stride +
+                                       (size_t)t * D + kq * 8
+                                 : safe;
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) ch.kb[u][kk] = load16_stream(row + kk * 32);
+    }
+  };
+  // scores of chunk c into zl, then per head (one wave each) the chunk
+  // maximum and its candidates z > max - 1 as split s0 + c
+  auto score_emit = [&](int c, const Chunk& ch) {
+    const int base = lo + c * per;
+    const int nrows = min(per, hi - base) << log2P;
+#pragma unroll
+    for (int u = 0; u < kGPW; ++u) {
+      const int rl = (wave * kGPW + u) * 16 + mrow;
+#pragma unroll
+      for (int ab = 0; ab < kBlocksA; ++ab) {
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ab][kk], as_bf16x8(ch.kb[u][kk]), acc,
+                                                        0, 0, 0);
+        const int h = ab * 4 + kq;
+        if (h < G)
+          zl[h][rl] = ch.valid[u] ? ((acc[0] + acc[1]) + acc[2]) * a.zscale
+                                  : -__builtin_huge_valf();
+      }
+    }
+    __syncthreads();  // zl complete
+    const int s = s0 + c;
+    for (int h = wave; h < G; h += kBlock / kWave) {
+      float mz = -__builtin_huge_valf();
+      for (int r = lane; r < nrows; r += kWave) mz = fmaxf(mz, zl[h][r]);
+      mz = wave_max_f32(mz);
+      const double thr = (double)mz - 1.0;
+      const size_t bh = bh0 + h;
+      float2* out = a.cand + (bh * a.splits + s) * kR;
+      int total = 0;
+      for (int r0 = 0; r0 < nrows; r0 += kWave) {
+        const int r = r0 + lane;
+        const float z = r < nrows ? zl[h][r] : -__builtin_huge_valf();
+        const bool flag = (double)z > thr;
+        const uint64_t mask = __ballot(flag);
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+        if (flag) {
+          const int ptok = page_at(base + (r >> log2P)).x * P + (r & (P - 1));
+          out[total + __popcll(mask & lt)] = make_float2(z, __int_as_float(ptok));
+        }
+        total += __popcll(mask);
+      }
+      if (lane == 0) {
+        a.cnt[bh * a.splits + s] = total;
+        a.smax[bh * a.splits + s] = mz;
+      }
+    }
+    __syncthreads();  // zl is rewritten by the next chunk
+  };
+  Chunk A, Bc;
+  if (nch > 0) issue(0, A);
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) issue(c + 1, Bc);
+    score_emit(c, A);
+    if (c + 1 >= nch) break;
+    if (c + 2 < nch) issue(c + 2, A);
+    score_emit(c + 1, Bc);
+  }
+  // the item's splits past its last chunk: empty
+  for (int s = s0 + nch; s < s1; ++s)
+    for (int h = wave; h < G; h += kBlock / kWave)
+      if (lane == 0) {
+        a.cnt[(bh0 + h) * a.splits + s] = 0;
+        a.smax[(bh0 + h) * a.splits + s] = -__builtin_huge_valf();
+      }
+}
+
 // The selection item of a pair (the last item index of the launch): the
 // top-k pages of the row, ascending, into sel / n_sel (the key items do not
 // need the list written out).
@@ -416,11 +567,19 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   }
 
   // ---- this item's share of the pages to read (ascending)
-  read_share<T, D, G, kMfma>(a, sm.u.qk, qg, qv, g, L, bh0, s0, s1, nsplit, m, [&](int idx) {
+  if (!prune) {  // uniform: the selected pages' physical pages into LDS too
+    for (int j = tid; j < nsel; j += kBlock) sm.s_phys[j] = a.bt[(size_t)b * maxP + sm.s_sel[j]];
+    __syncthreads();
+  }
+  // (LDS only, so no key load waits behind a block-table load)
+  auto page_at = [&](int idx) {
     const int j = prune ? sm.s_surv[idx] : idx;
-    const int page = sm.s_sel[j];
-    return make_int2(prune ? sm.s_phys[j] : a.bt[(size_t)b * maxP + page], page);
-  });
+    return make_int2(sm.s_phys[j], sm.s_sel[j]);
+  };
+  if constexpr (kMfma)
+    read_share_mfma<T, D, G>(a, sm.u.qk, qv, g, L, bh0, s0, s1, nsplit, m, page_at);
+  else
+    read_share<T, D, G, kMfma>(a, sm.u.qk, qg, qv, g, L, bh0, s0, s1, nsplit, m, page_at);
 }
 
 // The same key item with the scorer's hints (the step's path): each head's
@@ -678,9 +837,11 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   float qmv[kMfma ? kQPer : 1];
 #pragma unroll
   for (int u = 0; u < (kMfma ? kQPer : 1); ++u) qmv[u] = qv[u < kQPer ? u : 0];
-  read_share<T, D, G, kMfma>(a, sm.u.qk, qg, qmv, g, L, bh0, s0, s1, nsplit, m, [&](int idx) {
-    return make_int2(sm.s_phys[idx], sm.s_surv[idx]);
-  });
+  auto page_at = [&](int idx) { return make_int2(sm.s_phys[idx], sm.s_surv[idx]); };
+  if constexpr (kMfma)
+    read_share_mfma<T, D, G>(a, sm.u.qk, qv, g, L, bh0, s0, s1, nsplit, m, page_at);
+  else
+    read_share<T, D, G, kMfma>(a, sm.u.qk, qg, qmv, g, L, bh0, s0, s1, nsplit, m, page_at);
 }
 
 template <typename T, int D>
