@@ -88,7 +88,11 @@ __global__ __launch_bounds__(kBlock) void qk_kernel(QkArgs<T> a, long long n_ite
     }
     if constexpr (kFused) {
       // arrival: this item's device-coherent stores drain, the block counts
-      // itself once, and the last item of the pair runs the tau / PV tail
+      // itself once, and the last item of the pair runs the tau / PV tail.
+      // Relaxed atomics are enough on gfx950 for the reason given at the
+      // scorer's arrival (score_select_kernel): the candidate stores and the
+      // tail's loads are agent-scope atomics, and s_waitcnt(0) waits for the
+      // stores' acknowledgement before the increment is issued.
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {

@@ -484,7 +484,15 @@ __global__ __launch_bounds__(kScoreBlock) void score_select_kernel(
   // completed, the barrier gathers the waves, then one relaxed device-scope
   // increment counts the block; the last block of the pair reads every bound
   // back with device-coherent loads.  No cache-wide write-back or
-  // invalidation is needed.
+  // invalidation is needed.  Why relaxed atomics suffice here (the HIP
+  // memory model alone would want a release on the increment and an acquire
+  // in the last block): the bound stores and the loads that read them back
+  // bypass the non-coherent caches (agent-scope atomic stores and loads), and
+  // s_waitcnt(0) returns only after each store has been acknowledged by the
+  // device-coherent level, before the increment is issued; a block that sees
+  // the final count therefore finds every other block's stores there.  This
+  // rests on how gfx950 executes these instructions, not on the language
+  // model; the fused decode's arrival relies on the same argument.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
