@@ -140,10 +140,10 @@ __device__ __forceinline__ void read_share(const SelQkArgs<T>& a, QkLds<T, D, G>
 }
 
 // read_share for bf16 keys with the chunks software-pipelined: the K rows of
-// chunk c + 1 are requested before chunk c is scored on the matrix cores and
-// emitted, so an item that reads many chunks (pairs whose pages do not prune)
-// keeps loads in flight while it computes instead of one round trip per
-// chunk.  Rows, chunks, scores and candidates are those of read_share
+// chunk c + 1 are requested as soon as chunk c's scores are formed on the
+// matrix cores (one chunk of registers), so an item that reads many chunks
+// (pairs whose pages do not prune) has them in flight while chunk c's
+// candidates are emitted.  Rows, chunks, scores and candidates are those of read_share
 // (the page map is looked up in the caller's list instead of being staged),
 // so the results are bit-identical.
 template <typename T, int D, int G, typename PageAt>
@@ -222,11 +222,8 @@ __device__ __forceinline__ void read_share_mfma(const SelQkArgs<T>& a, QkLds<T, 
       for (int kk = 0; kk < kKK; ++kk) ch.kb[u][kk] = load16_stream(row + kk * 32);
     }
   };
-  // scores of chunk c into zl, then per head (one wave each) the chunk
-  // maximum and its candidates z > max - 1 as split s0 + c
-  auto score_emit = [&](int c, const Chunk& ch) {
-    const int base = lo + c * per;
-    const int nrows = min(per, hi - base) << log2P;
+  // scores of chunk c into zl
+  auto score = [&](const Chunk& ch) {
 #pragma unroll
     for (int u = 0; u < kGPW; ++u) {
       const int rl = (wave * kGPW + u) * 16 + mrow;
@@ -243,7 +240,12 @@ __device__ __forceinline__ void read_share_mfma(const SelQkArgs<T>& a, QkLds<T, 
                                   : -__builtin_huge_valf();
       }
     }
-    __syncthreads();  // zl complete
+  };
+  // per head (one wave each) the chunk maximum and its candidates
+  // z > max - 1, as split s0 + c
+  auto emit = [&](int c) {
+    const int base = lo + c * per;
+    const int nrows = min(per, hi - base) << log2P;
     const int s = s0 + c;
     for (int h = wave; h < G; h += kBlock / kWave) {
       float mz = -__builtin_huge_valf();
@@ -272,14 +274,15 @@ __device__ __forceinline__ void read_share_mfma(const SelQkArgs<T>& a, QkLds<T, 
     }
     __syncthreads();  // zl is rewritten by the next chunk
   };
-  Chunk A, Bc;
-  if (nch > 0) issue(0, A);
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) issue(c + 1, Bc);
-    score_emit(c, A);
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) issue(c + 2, A);
-    score_emit(c + 1, Bc);
+  // the next chunk's rows are requested as soon as this chunk's scores are
+  // formed (its registers are free again), and arrive during the emit
+  Chunk ch;
+  if (nch > 0) issue(0, ch);
+  for (int c = 0; c < nch; ++c) {
+    score(ch);
+    if (c + 1 < nch) issue(c + 1, ch);
+    __syncthreads();  // zl complete
+    emit(c);
   }
   // the item's splits past its last chunk: empty
   for (int s = s0 + nch; s < s1; ++s)
