@@ -29,6 +29,38 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// A thread's run of kPer consecutive 32-bit entries src[p0 .. p0 + kPer) in
+// registers, entries at or past lim read as zero.  The runs of a wave's lanes
+// lie 4 kPer bytes apart, so every load instruction touches a separate cache
+// line per lane: 16-byte loads need a quarter of the instructions (and of the
+// cache-line lookups) of 4-byte ones.  They are used when the runs are 16-byte
+// aligned (src aligned and p0 a multiple of 4: the same for every lane of a
+// launch whose p0 are multiples of kPer); otherwise one load per entry.
+template <int kPer, typename V>
+__device__ __forceinline__ void load_run(const V* __restrict__ src, int p0, int lim,
+                                         V (&dst)[kPer]) {
+  static_assert(sizeof(V) == 4, "32-bit entries");
+  const bool vec = kPer % 4 == 0 && (p0 & 3) == 0 && ((uintptr_t)src & 15) == 0;
+  if (vec) {
+#pragma unroll
+    for (int j = 0; j < kPer; j += 4) {
+      if (p0 + j + 3 < lim) {
+        const uint4 w = *reinterpret_cast<const uint4*>(src + p0 + j);
+        dst[j] = __builtin_bit_cast(V, w.x);
+        dst[j + 1] = __builtin_bit_cast(V, w.y);
+        dst[j + 2] = __builtin_bit_cast(V, w.z);
+        dst[j + 3] = __builtin_bit_cast(V, w.w);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[j + i] = p0 + j + i < lim ? src[p0 + j + i] : V(0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dst[i] = p0 + i < lim ? src[p0 + i] : V(0);
+  }
+}
+
 // LDS scratch of one top-k selection (keys of rows up to kCap pages).
 template <int kCap = kTopkLdsKeys>
 struct alignas(16) TopkLds {
@@ -338,16 +370,18 @@ __device__ __forceinline__ void topk_block_reg(const float* __restrict__ U, int 
   const int p0 = threadIdx.x * kPerThread;
   const int nv = max(0, min(kPerThread, n - p0));
   uint32_t key[kPerThread];
+  if constexpr (kCoherentU) {
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    float u = 0.0f;
-    if (i < nv) {
-      if constexpr (kCoherentU)
-        u = __hip_atomic_load(U + p0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        u = U[p0 + i];
+    for (int i = 0; i < kPerThread; ++i) {
+      float u = 0.0f;
+      if (i < nv) u = __hip_atomic_load(U + p0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      key[i] = order_key(u);
     }
-    key[i] = order_key(u);
+  } else {
+    float u[kPerThread];
+    load_run<kPerThread>(U, p0, n, u);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) key[i] = order_key(u[i]);
   }
   topk_reg_keys<kPerThread>(key, nv, k, out, sm);
 }

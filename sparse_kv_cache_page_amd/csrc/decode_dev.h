@@ -444,10 +444,20 @@ struct QkArgs {
 // slack for the fp32 rounding of u and of the key scores (s1) and of zlb
 // against the scores the qk stage computes (s2), so a pruned token would have
 // been below every head's z_max - 1 in the unpruned computation too.
-__device__ inline bool page_below_support(float a1u, float zlb) {
-  const float s1 = 1e-3f * (1.0f + fabsf(a1u));
+// The test is split in its two sides: support_bar(zlb) = zlb - 1 - s2 depends
+// on the head only, so a page tested against several heads compares its one
+// left side with the smallest bar (a NaN bar keeps every page, as a NaN
+// comparison does in the per-head form).
+__device__ inline float support_bar(float zlb) {
   const float s2 = 1e-4f * (1.0f + fabsf(zlb));
-  return a1u + s1 < zlb - 1.0f - s2;
+  return zlb - 1.0f - s2;
+}
+__device__ inline bool page_below_bar(float a1u, float bar) {
+  const float s1 = 1e-3f * (1.0f + fabsf(a1u));
+  return a1u + s1 < bar;
+}
+__device__ inline bool page_below_support(float a1u, float zlb) {
+  return page_below_bar(a1u, support_bar(zlb));
 }
 
 template <typename T, int D, int G, bool kMfma = std::is_same<T, bf16_t>::value>

@@ -345,8 +345,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_kernel(SelQkArgs<T> a) {
   const int p0 = tid * kPer;
   const float* Ug = a.ubg + (size_t)pair * maxP;
   float uv[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) uv[i] = p0 + i < maxP ? Ug[p0 + i] : 0.0f;
+  load_run<kPer>(Ug, p0, maxP, uv);
   float qv[kMfma ? kQPer : 1];
   if constexpr (kMfma) {
 #pragma unroll
@@ -628,12 +627,8 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   const int32_t* btrow = a.bt + (size_t)b * maxP;
   float uv[kPer];
   int btr[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const bool in = p0 + i < maxP;
-    uv[i] = in ? Ug[p0 + i] : 0.0f;
-    btr[i] = in ? btrow[p0 + i] : 0;
-  }
+  load_run<kPer>(Ug, p0, maxP, uv);
+  load_run<kPer>(btrow, p0, maxP, btr);
   float qv[kQPer];
 #pragma unroll
   for (int u = 0; u < kQPer; ++u) {
@@ -725,31 +720,63 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   }
 
   // ---- whether each head's probe page is selected: fewer than nsel pages
-  // rank ahead of it (larger U, or equal U and a lower page)
+  // rank ahead of it (larger U, or equal U and a lower page).  The probe that
+  // ranks last (smallest U, then highest page) is counted first: if it is
+  // selected, so are the others, which is the usual case; otherwise each
+  // head's probe is counted.
   const int nv = max(0, min(kPer, np - p0));
   {
-    int ahead[G];
+    int wh = -1, wp = 0;
+    uint32_t wk = 0u;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const int pg = sm.probe_page[h];
       const uint32_t pk = sm.probe_key[h];
-      int c_ = 0;
+      if (pg >= 0 && (wh < 0 || pk < wk || (pk == wk && pg > wp))) {
+        wh = h;
+        wk = pk;
+        wp = pg;
+      }
+    }
+    int c_ = 0;
+    if (wh >= 0) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        c_ += (i < nv && (key[i] > pk || (key[i] == pk && p0 + i < pg))) ? 1 : 0;
-      ahead[h] = wave_sum_i32(c_);
+        c_ += (i < nv && (key[i] > wk || (key[i] == wk && p0 + i < wp))) ? 1 : 0;
     }
-    if (lane == 0) {
+    c_ = wave_sum_i32(c_);
+    if (lane == 0) sm.rank_part[wave][0] = c_;
+    lds_barrier();
+    int rw = 0;
 #pragma unroll
-      for (int h = 0; h < G; ++h) sm.rank_part[wave][h] = ahead[h];
+    for (int w_ = 0; w_ < kBlock / kWave; ++w_) rw += sm.rank_part[w_][0];
+    if (nsel >= np || rw < nsel) {  // uniform
+      if (tid < G) sm.probe_sel[tid] = sm.probe_page[tid] >= 0;
+    } else {
+      int ahead[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int pg = sm.probe_page[h];
+        const uint32_t pk = sm.probe_key[h];
+        int cc = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          cc += (i < nv && (key[i] > pk || (key[i] == pk && p0 + i < pg))) ? 1 : 0;
+        ahead[h] = wave_sum_i32(cc);
+      }
+      lds_barrier();  // every thread has read rank_part[.][0]
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sm.rank_part[wave][h] = ahead[h];
+      }
+      lds_barrier();
+      if (tid < G) {
+        int r = 0;
+#pragma unroll
+        for (int w_ = 0; w_ < kBlock / kWave; ++w_) r += sm.rank_part[w_][tid];
+        sm.probe_sel[tid] = sm.probe_page[tid] >= 0 && r < nsel;
+      }
     }
-  }
-  lds_barrier();
-  if (tid < G) {
-    int r = 0;
-#pragma unroll
-    for (int w_ = 0; w_ < kBlock / kWave; ++w_) r += sm.rank_part[w_][tid];
-    sm.probe_sel[tid] = sm.probe_page[tid] >= 0 && (nsel >= np || r < nsel);
   }
   // (the barrier below, after the probe rows are reduced, publishes probe_sel)
 
@@ -786,14 +813,19 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   // monotone in U, so every page that ranks ahead of a clearing page clears
   // too: when at most nsel pages clear, all of them are selected and the
   // top-k itself is not needed; otherwise it decides.
+  float bar = __builtin_huge_valf();
+  bool bar_nan = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float bh = support_bar(zl_h[h]);
+    bar_nan |= bh != bh;
+    bar = fminf(bar, bh);
+  }
   int cntf = 0;
   bool need[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    bool nd = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) nd |= !page_below_support(a.a1 * uv[i], zl_h[h]);
-    need[i] = i < nv && nd;
+    need[i] = i < nv && (bar_nan || !page_below_bar(a.a1 * uv[i], bar));
     cntf += need[i] ? 1 : 0;
   }
   int incl = block_incl_scan_lds(cntf, sm.sh4);
