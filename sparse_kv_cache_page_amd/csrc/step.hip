@@ -73,11 +73,12 @@ struct SelQkArgs {
   int slice_pages, nslices;
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int kStage = 1>
 struct SelQkLds {
   union {
     TopkRegLds tk;
     QkLds<T, D, G> qk;
+    uint4 stage[kStage];  // coalesced first-round loads on their way to the owning threads
   } u;
   int s_sel[kSelCap];    // selected pages, ascending
   int s_phys[kSelCap];   // their physical pages
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   constexpr int kQPer = (G * D + kBlock - 1) / kBlock;
   constexpr bool kMfma = std::is_same<T, bf16_t>::value;
   constexpr int kHintPer = 4;  // hint entries per lane of wave 0 (<= 256 in all)
-  __shared__ SelQkLds<T, D, G> sm;
+  __shared__ SelQkLds<T, D, G, kPer * kBlock / 4 * 9 / 8 + 1> sm;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
@@ -627,8 +628,32 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
   const int32_t* btrow = a.bt + (size_t)b * maxP;
   float uv[kPer];
   int btr[kPer];
-  load_run<kPer>(Ug, p0, maxP, uv);
-  load_run<kPer>(btrow, p0, maxP, btr);
+  // Thread t owns pages p0 .. p0 + kPer (the ordered compaction below needs
+  // each thread's pages consecutive).  When the rows are 16-byte aligned they
+  // are read coalesced instead (lane l of a wave takes 16-byte chunk l of a
+  // 1 KiB span: 8 cache lines per load instead of 64) and handed to the
+  // owning threads through LDS after this round trip.
+  constexpr int kC = kPer / 4;  // 16-byte chunks per thread
+  // (at 8 pages per thread the four extra barriers cost more than the loads
+  // save: gqa decode 19.0 -> 19.9 us; at 32, 25.2 -> 23.7 us on one 131072-token row)
+  const bool coal = kPer >= 16 && (maxP & 3) == 0 && ((uintptr_t)Ug & 15) == 0 &&
+                    ((uintptr_t)btrow & 15) == 0;
+  uint4 cu[kC], cb[kC];
+  if (coal) {
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      const int c = tid + j * kBlock;
+      cu[j] = make_uint4(0u, 0u, 0u, 0u);
+      cb[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (4 * c < maxP) {  // maxP % 4 == 0: the whole chunk is in the row
+        cu[j] = *reinterpret_cast<const uint4*>(Ug + 4 * c);
+        cb[j] = *reinterpret_cast<const uint4*>(btrow + 4 * c);
+      }
+    }
+  } else {
+    load_run<kPer>(Ug, p0, maxP, uv);
+    load_run<kPer>(btrow, p0, maxP, btr);
+  }
   float qv[kQPer];
 #pragma unroll
   for (int u = 0; u < kQPer; ++u) {
@@ -685,6 +710,35 @@ __global__ __launch_bounds__(kBlock) void sel_qk_hint_kernel(SelQkArgs<T> a) {
     }
   }
   lds_barrier();
+  if (coal) {
+    // chunk i sits at slot i + i / 8, so the owners' reads (kC consecutive
+    // chunks per thread) spread over the banks
+    uint4* st = sm.u.stage;
+#pragma unroll
+    for (int j = 0; j < kC; ++j) st[(tid + j * kBlock) * 9 / 8] = cu[j];
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      const uint4 w = st[(tid * kC + j) * 9 / 8];
+      uv[4 * j] = __uint_as_float(w.x);
+      uv[4 * j + 1] = __uint_as_float(w.y);
+      uv[4 * j + 2] = __uint_as_float(w.z);
+      uv[4 * j + 3] = __uint_as_float(w.w);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kC; ++j) st[(tid + j * kBlock) * 9 / 8] = cb[j];
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      const uint4 w = st[(tid * kC + j) * 9 / 8];
+      btr[4 * j] = (int)w.x;
+      btr[4 * j + 1] = (int)w.y;
+      btr[4 * j + 2] = (int)w.z;
+      btr[4 * j + 3] = (int)w.w;
+    }
+    lds_barrier();  // the staging area is reused below
+  }
   // the probe pages' physical pages and bounds from their owners' entries
   uint32_t key[kPer];
 #pragma unroll
@@ -905,6 +959,13 @@ hipError_t launch_t(const Shape& s, const DecodePlan& pl, const float* q, float 
   // repeats the pair's selection, so no more than that), each holding spi
   // consecutive splits
   long long nit = (kStepItems + npairs - 1) / npairs;
+  // without hints every item runs the pair's top-k and probe before its keys;
+  // a pair with many splits still gets two items, so two runs of key chunks
+  // are in flight per pair (64/8 heads, batch 32, context 131072, page 32:
+  // 349 -> 326 us; the hinted kernel measured slower with more items on every
+  // workload)
+  const bool hinted = ub != nullptr && hint_fits<T, D, G>(s, hint);
+  if (!hinted && nit < 2 && pl.splits >= 32) nit = 2;
   nit = nit < 1 ? 1 : (nit > pl.splits ? pl.splits : nit);
   int spi = (int)((pl.splits + nit - 1) / nit);
   spi = spi > EKV_STEP_MAX_SPI ? EKV_STEP_MAX_SPI : spi;
@@ -917,7 +978,7 @@ hipError_t launch_t(const Shape& s, const DecodePlan& pl, const float* q, float 
                        s.P,    s.log2P,   s.maxP,      pl.splits,   (int)npairs, spi,
                        (int)nit, cand,    cnt,         smax,        hint.hint,
                        hint.slice_pages, hint.nslices};
-  if (ub != nullptr && hint_fits<T, D, G>(s, hint))
+  if (hinted)
     hipLaunchKernelGGL((sel_qk_hint_kernel<T, D, G, kPer>), dim3((unsigned)items), dim3(kBlock),
                        0, stream, a);
   else
