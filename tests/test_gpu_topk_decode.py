@@ -115,6 +115,37 @@ def test_topk_decode_empty_rows():
     assert bool((f.out[1] == 0).all()) and bool(torch.isnan(f.tau[1]).all())
 
 
+@pytest.mark.parametrize("fill", ["random", "other_cache"])
+def test_topk_decode_foreign_hints(fill):
+    # hints that this call's scorer did not write (random bytes, or another
+    # cache's hints for the same shape): the probe reads a hinted physical page
+    # only inside the pool and uses it only where the block table agrees, so
+    # the results still equal the separate path's
+    lens = [1500, 700, 37]
+    w = small(411, lens_range=None)
+    inp = wl.make_inputs(w, device=DEV, lens=lens)
+    a, f = both(inp, True, hinted=True)
+    if fill == "random":
+        g = torch.Generator(device="cpu").manual_seed(5)
+        f.hint.copy_(torch.randint(0, 256, f.hint.shape, dtype=torch.uint8, generator=g))
+    else:
+        inp2 = wl.make_inputs(small(412, lens_range=None), device=DEV, lens=lens)
+        assert inp2["num_phys_pages"] == inp["num_phys_pages"]
+        assert not torch.equal(inp2["block_table"], inp["block_table"])
+        o = PagedEntmaxDecoder(cache_shape(inp2), policy="topk", top_k=w.top_k, alpha=w.alpha,
+                               scale=w.scale)
+        o.build_meta(inp2["K"], inp2["block_table"], inp2["seq_lens"])
+        o.score_box(inp2["q"], inp2["block_table"], inp2["seq_lens"])
+        f.hint.copy_(o.hint)
+    print(f"[topk_decode] foreign hints: {fill}", flush=True)
+    f.sel.fill_(-7)
+    f.out.fill_(float("nan"))
+    f.topk_decode(inp["q"], inp["K"], inp["V"], inp["block_table"], inp["seq_lens"],
+                  use_hint=True)
+    torch.cuda.synchronize()
+    assert_same(a, f, inp)
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(num_q_heads=16, num_kv_heads=2, page_size=32)])
 def test_topk_decode_against_oracle(kw):
     w = small(391, **kw)
