@@ -977,16 +977,22 @@ struct TauArgs {
 template <typename T, int D>
 struct TauLds {
   static constexpr int kRowsPerPass = Geo<T, D>::kRowsPerPass;
-  float c_z[kCandCap];
-  int c_t[kCandCap];
-  int s_off[kMaxSplits + 1];
+  // the value rows' partial sums are written only after the last read of the
+  // candidate lists and split offsets, so they share that storage (26 KiB in
+  // all instead of 34: six workgroups per compute unit instead of four)
+  union {
+    struct {
+      float c_z[kCandCap];
+      int c_t[kCandCap];
+      int s_off[kMaxSplits + 1];
+    } w;
+    float acc_sh[kRowsPerPass][D + 1];
+  } u;
   float st_p[kBlock];
   int st_t[kBlock];
-  float acc_sh[kRowsPerPass][D + 1];
   int sh4[4];
   double shd[8];
   double s_tau;
-
 };
 
 // tau and the output of one (row, query head) bh.  Called by all threads of
@@ -1009,12 +1015,12 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
   int32_t* __restrict__ n_support = a.n_support;
   using GE = Geo<T, D>;
   constexpr int kVec = GE::kVec, kLpr = GE::kLpr, kRowsPerPass = GE::kRowsPerPass, kR = GE::kR;
-  auto& c_z = sm.c_z;
-  auto& c_t = sm.c_t;
-  auto& s_off = sm.s_off;
+  auto& c_z = sm.u.w.c_z;
+  auto& c_t = sm.u.w.c_t;
+  auto& s_off = sm.u.w.s_off;
   auto& st_p = sm.st_p;
   auto& st_t = sm.st_t;
-  auto& acc_sh = sm.acc_sh;
+  auto& acc_sh = sm.u.acc_sh;
   auto& sh4 = sm.sh4;
   auto& shd = sm.shd;
   auto& s_tau = sm.s_tau;
@@ -1328,6 +1334,7 @@ __device__ __forceinline__ void tau_head(const TauArgs<T>& a, int bh, TauLds<T, 
     }
     if (threadIdx.x != 0) nsupp = 0;  // the chunk totals are block-wide
   }
+  __syncthreads();  // acc_sh overlays the candidate lists: every read of them is done
 #pragma unroll
   for (int v = 0; v < kVec; ++v) acc_sh[rg][c * kVec + v] = acc[v];
   double ps = psum, ns = (double)nsupp;
