@@ -343,7 +343,10 @@ size_t ekv_score_select_workspace_bytes(const ekv_cache_desc* desc);
  * the separate select and decode kernels run.  Two or three launches.
  * ubg [B][Hkv][maxP] and ub [B][Hkv][maxP][G] (16-byte aligned) as written by
  * ekv_score_pages or ekv_score_box_pages for the same query; hint: NULL, or
- * the hints ekv_score_box_pages wrote with them (used only with ub).  sel and
+ * the hints ekv_score_box_pages wrote with them (used only with ub; a hint
+ * buffer holding anything else only changes which selected page each head
+ * probes, never the results: the probed page's physical page is taken from
+ * block_table, and a page the top-k did not select is not used).  sel and
  * n_sel are outputs.
  * ws / ws_bytes: at least ekv_topk_decode_workspace_bytes(desc, top_k) bytes,
  * 256-byte aligned; no initialisation needed, garbage afterwards.
