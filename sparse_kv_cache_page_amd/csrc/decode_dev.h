@@ -815,7 +815,6 @@ __device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
   constexpr int kLpr = D / kVec;
   constexpr int kRowsPerPass = kBlock / kLpr;
   constexpr int kWaves = kBlock / kWave;
-  constexpr int kSpecSel = 2;  // selection slots per thread requested up front
   __shared__ float s_best[kWaves];
   __shared__ int s_bestp[kWaves];
   __shared__ int s_bestphys[kWaves];
@@ -829,66 +828,49 @@ __device__ __forceinline__ void zlb_head(const ZlbArgs<T>& a, int bh) {
   float qv[kVec];
 #pragma unroll
   for (int v = 0; v < kVec; ++v) qv[v] = a.q[(size_t)bh * D + c * kVec + v];
-  // the first slots of the selection are requested in the same round trip as
-  // the row length and the selection size (slots past n_sel are in bounds and
-  // never used)
-  int spec[kSpecSel];
-#pragma unroll
-  for (int u = 0; u < kSpecSel; ++u) {
-    const int j = threadIdx.x + u * kBlock;
-    spec[u] = j;
-    if (a.sel && j < a.max_sel) spec[u] = a.sel[(size_t)pair * a.maxP + j];
-  }
-  const int L = a.lens[b];
-  const int np = (L + a.P - 1) / a.P;
-  const int nsel = min(a.sel ? a.n_sel[pair] : np, a.max_sel);
+  // the selection's slots in rounds of kBatch per thread: a round's page
+  // indices, then all their bounds and block-table entries (two dependent
+  // loads per round); the first round's indices are requested in the same
+  // round trip as the row length and the selection size (slots past n_sel
+  // are in bounds, below max_sel, and masked), so up to kBatch * kBlock
+  // selected pages cost two round trips before the reduction
+  constexpr int kBatch = 32;
   const float* U = a.ub + (size_t)pair * a.maxP * G + (bh % a.Hq) % G;  // stride G per page
-  // each page's bound and block-table entry in one round; the winner's
-  // physical page travels with it through the reduction
+  int L = 0, np = 0, nsel = 0;
   float best = -__builtin_huge_valf();
   int bestp = 0x7fffffff, bestphys = 0;
-  auto consider = [&](int page) {
-    if ((unsigned)page >= (unsigned)np) return;  // a caller's entry outside the row
-    const float u = U[(size_t)page * G];
-    const int phys = a.bt[(size_t)b * a.maxP + page];
-    if (u > best || (u == best && page < bestp)) {
-      best = u;
-      bestp = page;
-      bestphys = phys;
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < kSpecSel; ++u)
-    if (threadIdx.x + u * kBlock < nsel) consider(spec[u]);
-  // longer selections: kBatch slots per thread per round, their page indices
-  // first, then all their bounds and block-table entries, so a round costs
-  // two dependent loads rather than two per slot
-  constexpr int kBatch = 16;
-  for (int j0 = kSpecSel * kBlock; j0 < nsel; j0 += kBatch * kBlock) {
+  for (int j0 = 0;; j0 += kBatch * kBlock) {
     int pg[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int j = j0 + threadIdx.x + u * kBlock;
       pg[u] = -1;
-      if (j < nsel) pg[u] = a.sel ? a.sel[(size_t)pair * a.maxP + j] : j;
+      if (j < a.max_sel) pg[u] = a.sel ? a.sel[(size_t)pair * a.maxP + j] : j;
+    }
+    if (j0 == 0) {
+      L = a.lens[b];
+      np = (L + a.P - 1) / a.P;
+      nsel = min(a.sel ? a.n_sel[pair] : np, a.max_sel);
     }
     float uu[kBatch];
     int ph[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const bool ok = (unsigned)pg[u] < (unsigned)np;
+      // a slot past n_sel, or a caller's entry outside the row, is skipped
+      const bool ok = j0 + (int)threadIdx.x + u * kBlock < nsel && (unsigned)pg[u] < (unsigned)np;
+      if (!ok) pg[u] = -1;
       uu[u] = ok ? U[(size_t)pg[u] * G] : -__builtin_huge_valf();
       ph[u] = ok ? a.bt[(size_t)b * a.maxP + pg[u]] : 0;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if ((unsigned)pg[u] < (unsigned)np &&
-          (uu[u] > best || (uu[u] == best && pg[u] < bestp))) {
+      if (pg[u] >= 0 && (uu[u] > best || (uu[u] == best && pg[u] < bestp))) {
         best = uu[u];
         bestp = pg[u];
         bestphys = ph[u];
       }
     }
+    if (j0 + kBatch * kBlock >= nsel) break;  // uniform
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {

@@ -105,12 +105,20 @@ __global__ __launch_bounds__(kLongBlock) void topk_long_kernel(
   const float* U = ubg + (size_t)pair * maxP;
   const int p0 = tid * kPer;
   const int nv = max(0, min(kPer, n - p0));
+  // (16-byte loads of each thread's run where the row is aligned: lanes kPer
+  // entries apart touch a cache line each per load instruction)
   uint32_t key[kReg];
+  {
+    float u[kReg];
+    load_run<kReg>(U, p0, p0 + nv, u);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const uint32_t kk = order_key(i < nv ? U[p0 + i] : 0.0f);
-    if (i < kReg) key[i < kReg ? i : 0] = kk;
-    else sm.lk[(i - kReg) * kLongBlock + tid] = kk;
+    for (int i = 0; i < kReg; ++i) key[i] = order_key(u[i]);
+  }
+  if constexpr (kPer > kReg) {
+    float u[kPer - kReg];
+    load_run<kPer - kReg>(U, p0 + kReg, p0 + nv, u);
+#pragma unroll
+    for (int i = 0; i < kPer - kReg; ++i) sm.lk[i * kLongBlock + tid] = order_key(u[i]);
   }
   // key i of this thread (registers, or LDS past kReg; i is a constant in
   // every unrolled use)
