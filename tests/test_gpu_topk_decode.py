@@ -115,6 +115,20 @@ def test_topk_decode_empty_rows():
     assert bool((f.out[1] == 0).all()) and bool(torch.isnan(f.tau[1]).all())
 
 
+@pytest.mark.parametrize("lens", [[3000, 4000], [3001, 4001], [6000, 8000], [6003, 8001]])
+def test_topk_decode_long_row_layouts(lens):
+    # 16 and 32 pages per thread (rows of up to 4096 and 8192 pages), with the
+    # block-table width a multiple of 4 (the bounds and block-table rows are
+    # read coalesced and handed out through LDS) or not (per-thread loads)
+    w = small(433, lens_range=None, page_size=1, top_k=300, batch=2, head_dim=64,
+              q_std=0.25)
+    inp = wl.make_inputs(w, device=DEV, lens=lens)
+    assert inp["max_pages"] == max(lens)
+    print(f"[topk_decode] long-row layout {lens}", flush=True)
+    a, f = both(inp, True, hinted=True)
+    assert_same(a, f, inp)
+
+
 @pytest.mark.parametrize("fill", ["random", "other_cache"])
 def test_topk_decode_foreign_hints(fill):
     # hints that this call's scorer did not write (random bytes, or another
