@@ -463,6 +463,21 @@ def test_topk_long_rows(lens):
         check_pair(inp, gpu, b, g, "topk")
 
 
+@pytest.mark.parametrize("lens", [[12000, 9000], [12001, 9000], [40000, 33000],
+                                  [40001, 33000]])
+def test_topk_long_row_widths(lens):
+    # the 1024-thread select with 16 and 64 keys per thread, its bounds read
+    # with 16-byte loads when the row width is a multiple of 4 and one load per
+    # key otherwise
+    w = small(157, page_size=1, lens_range=None, batch=2, num_q_heads=4, num_kv_heads=2,
+              head_dim=64, q_std=2.0 / 8.0, top_k=700, planted_per_kv_head=4)
+    inp = wl.make_inputs(w, device=DEV, lens=lens)
+    print(f"[parity] long-row widths {lens}", flush=True)
+    gpu = run_gpu(inp, "topk")
+    for b, g in [(0, 0), (1, 1)]:
+        check_pair(inp, gpu, b, g, "topk")
+
+
 @pytest.mark.parametrize("policy,prune", [("topk", True), ("topk", False), ("gauss", False),
                                           ("gauss_est", True), ("gauss_mass", False),
                                           ("dense", False)])
