@@ -478,6 +478,18 @@ def test_topk_long_row_widths(lens):
         check_pair(inp, gpu, b, g, "topk")
 
 
+def test_pruning_probe_long_selection():
+    # more than 8192 selected pages: the pruning probe walks the selection in
+    # two rounds of 32 slots per thread
+    w = small(163, page_size=1, lens_range=None, batch=2, num_q_heads=4, num_kv_heads=2,
+              head_dim=64, q_std=2.0 / 8.0, top_k=9000, planted_per_kv_head=4)
+    inp = wl.make_inputs(w, device=DEV, lens=[20000, 9500])
+    print("[parity] pruning probe over 9000 selected pages", flush=True)
+    gpu = run_gpu(inp, "topk", prune=True)
+    for b, g in [(0, 0), (0, 1), (1, 1)]:
+        check_pair(inp, gpu, b, g, "topk")
+
+
 @pytest.mark.parametrize("policy,prune", [("topk", True), ("topk", False), ("gauss", False),
                                           ("gauss_est", True), ("gauss_mass", False),
                                           ("dense", False)])
